@@ -1,0 +1,68 @@
+"""Brute-force scalar version of the layer forward (test infrastructure only).
+
+Pure-Python loops over Python floats (IEEE double), for tiny shapes. It follows
+the same steps as ``oracle.forward`` (see that module's docstring for the
+passages each step follows) but shares none of its code, so that a slip in
+the vectorised oracle (an index, an axis, a transposed operand) shows up as a
+disagreement. Inputs are nested lists or numpy arrays already decoded to
+float; experts are given as full [E][N][K] nested arrays.
+"""
+from __future__ import annotations
+
+import math
+import struct
+
+
+def _f32(v: float) -> float:
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def _matvec(W, v):
+    return [math.fsum(W[r][c] * v[c] for c in range(len(v))) for r in range(len(W))]
+
+
+def _rmsnorm(v, gamma, eps):
+    ms = math.fsum(z * z for z in v) / len(v)
+    d = math.sqrt(ms + eps)
+    return [v[i] / d * gamma[i] for i in range(len(v))]
+
+
+def forward(x, router, bias, pooler, pool_gamma, w_gate, w_up, w_down, expert_gamma,
+            unpooler, k, eps):
+    """Returns (out [T][H], ids [T][k], w [T][k]) as Python lists."""
+    T, E = len(x), len(router)
+    outs, all_ids, all_w = [], [], []
+    for t in range(T):
+        xt = [float(v) for v in x[t]]
+        logit = _matvec(router, xt)
+        if bias is not None:
+            logit = [logit[e] + float(bias[e]) for e in range(E)]
+        # selection on FP32-rounded logits; ties go to the lower expert index
+        chosen = []
+        remaining = list(range(E))
+        for _ in range(k):
+            best = remaining[0]
+            for e in remaining[1:]:
+                if _f32(logit[e]) > _f32(logit[best]):
+                    best = e
+            chosen.append(best)
+            remaining.remove(best)
+        mx = max(logit[e] for e in chosen)
+        ex = [math.exp(logit[e] - mx) for e in chosen]
+        s = math.fsum(ex)
+        wt = [v / s for v in ex]
+
+        u = _rmsnorm(_matvec(pooler, xt), pool_gamma, eps)
+        P = len(u)
+        y = [0.0] * P
+        for j, e in enumerate(chosen):
+            g = _matvec(w_gate[e], u)
+            v = _matvec(w_up[e], u)
+            a = [g[i] / (1.0 + math.exp(-g[i])) * v[i] for i in range(len(g))]
+            o = _matvec(w_down[e], a)
+            oh = _rmsnorm(o, expert_gamma[e], eps)
+            y = [y[p] + wt[j] * oh[p] for p in range(P)]
+        outs.append(_matvec(unpooler, y))
+        all_ids.append(chosen)
+        all_w.append(wt)
+    return outs, all_ids, all_w

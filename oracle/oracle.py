@@ -1,0 +1,213 @@
+"""FP64 oracle of the latent-MoE layer forward (test infrastructure only).
+
+What the layer computes, for each token t (all arithmetic in FP64 on the exact
+input values; BF16/FP32 inputs widen exactly, MXFP4 weights decode exactly):
+
+1. Router on the full-width token ([lmsys] "MoE with Pooler, Unpooler and
+   Per-Expert Normalization": the router reads the full-width representation;
+   [vllm] "硬件后端 / Nvidia": the router GEMM is driven by the norm's FP32
+   output):  l_t = Wr x_t + b.
+2. Top-k selection. The router works in FP32, so the selection is decided on
+   the FP32 rounding of l_t: experts ordered by (logit descending, index
+   ascending), the first k kept, slot j holding the j-th largest.
+3. Routing weights: softmax over the k selected (FP64) logits.
+4. Pooler and pre-expert RMSNorm ([lmsys] same section: the pooler compresses
+   the width, and the pooled expert input is normalised before the experts;
+   [vllm] "潜空间 MoE": an 8192x4096 pooler shared by all 256 experts):
+   h_t = Wp x_t,  u_t = h_t / sqrt(mean(h_t^2) + eps) * gamma_p.
+5. Each selected SwiGLU expert e ([lmsys] same section, "routed SwiGLU experts"):
+   g = Wg_e u_t, v = Wu_e u_t, a = silu(g) * v with silu(z) = z / (1 + e^-z),
+   o = Wd_e a.
+6. Per-expert RMSNorm before the routing weight ([lmsys] same section, and
+   "The Fused Post-per-expert Norm"):  o^ = o / sqrt(mean(o^2) + eps) * gamma_e.
+7. Routing-weighted sum ([lmsys] "Trainable Muse Spark Open Backend": each
+   expert output normalised independently, then summed with its routing
+   weight in FP32; here in FP64, slot order j = 1..k): y_t = sum_j w_tj o^_tj.
+8. Unpooler back to the model width ([lmsys] same MoE section; [vllm]
+   "潜空间 MoE"): out_t = Wun y_t.
+
+Readings where the pages are silent (each listed in the design notes): x is
+already the normed token (the sandwich norm sits outside the layer, [vllm]
+"三明治归一化"); gammas multiply directly; one eps for both norms; no biases
+in any linear except an optional router bias, which is part of the logits;
+per-expert gamma has shape [E, P].
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Callable, Sequence
+
+import numpy as np
+
+from .mx import to_f64
+
+NEAR_TIE = 1e-6
+
+
+@dataclass
+class OracleResult:
+    out: np.ndarray  # [T, H] f64
+    ids: np.ndarray  # [T, k] int64, slot order
+    w: np.ndarray  # [T, k] f64
+    logits: np.ndarray  # [T, E] f64
+    gaps: np.ndarray  # [T, k] f64: sorted-logit gaps l(j) - l(j+1), j = 1..k
+    h: np.ndarray  # [T, P] pooled, before the norm
+    u: np.ndarray  # [T, P] pooled and normed expert input
+    a: np.ndarray | None  # [T, k, I] SwiGLU output per slot
+    o: np.ndarray | None  # [T, k, P] expert output per slot (before its norm)
+    ohat: np.ndarray | None  # [T, k, P] normed expert output per slot
+    y: np.ndarray  # [T, P] combined
+    near_tie: np.ndarray  # [T] bool: some gap j <= k below NEAR_TIE
+
+
+def rms_norm(v: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """v / sqrt(mean(v^2) + eps) * gamma over the last axis."""
+    ms = np.mean(v * v, axis=-1, keepdims=True)
+    return v / np.sqrt(ms + eps) * gamma
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def router_logits(x: np.ndarray, router: np.ndarray, bias: np.ndarray | None) -> np.ndarray:
+    lg = x @ router.T
+    if bias is not None:
+        lg = lg + bias
+    return lg
+
+
+def select_topk(logits: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:
+    """Top-k ids decided on the FP32-rounded logits, ties to the lowest index.
+
+    Returns (ids [T, k], gaps [T, k]); gaps come from the FP64 logits sorted
+    descending (index ascending on equal values)."""
+    T, E = logits.shape
+    l32 = logits.astype(np.float32)
+    idx = np.broadcast_to(np.arange(E), (T, E))
+    # lexsort: last key is primary -> (-l32) primary, index secondary
+    order = np.lexsort((idx, -l32.astype(np.float64)), axis=-1)
+    ids = order[:, :k].astype(np.int64)
+    order64 = np.lexsort((idx, -logits), axis=-1)
+    srt = np.take_along_axis(logits, order64, axis=-1)
+    kk = min(k + 1, E)
+    g = srt[:, : kk - 1] - srt[:, 1:kk]
+    if kk - 1 < k:  # k == E: no (k+1)-th logit; last gap is infinite
+        g = np.concatenate([g, np.full((T, k - (kk - 1)), np.inf)], axis=1)
+    return ids, g
+
+
+def softmax_selected(logits: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    sel = np.take_along_axis(logits, ids, axis=-1)
+    m = sel.max(axis=-1, keepdims=True)
+    e = np.exp(sel - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+ExpertFn = Callable[[int], tuple[np.ndarray, np.ndarray, np.ndarray]]
+
+
+def experts_from_arrays(w_gate, w_up, w_down) -> ExpertFn:
+    """Expert accessor over stored arrays ([E, N, K] float32 / BF16 bits, or
+    MXFP4 (packed, scales) pairs); returns FP64 (Wg [I,P], Wu [I,P], Wd [P,I])."""
+
+    def pick(a, e):
+        return (a[0][e], a[1][e]) if isinstance(a, tuple) else a[e]
+
+    def fn(e: int):
+        return to_f64(pick(w_gate, e)), to_f64(pick(w_up, e)), to_f64(pick(w_down, e))
+
+    return fn
+
+
+def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, expert_gamma,
+            unpooler, k: int, eps: float, *, force_ids: dict | None = None,
+            order: str = "norm_then_sum", keep_pairs: bool = True,
+            round_bf16: Sequence[str] = ()) -> OracleResult:
+    """Layer forward on tokens x [T, H] (any stored dtype).
+
+    force_ids: {token: ids sequence} replaces the selection for those tokens
+      (weights recomputed from this oracle's own FP64 logits).
+    order: "norm_then_sum" is the layer; "sum_then_norm" normalises the
+      combined vector instead (used only to show that the two differ).
+    round_bf16: diagnostic emulation; any of "u", "a", "y" rounds that
+      intermediate to BF16 (nearest even) the way a BF16 datapath would.
+    """
+    x = to_f64(x)
+    Wr = to_f64(router)
+    b = None if router_bias is None else to_f64(router_bias)
+    Wp = to_f64(pooler)
+    gp = to_f64(pool_gamma)
+    ge = to_f64(expert_gamma)
+    Wun = to_f64(unpooler)
+    T = x.shape[0]
+    E = Wr.shape[0]
+    P = Wp.shape[0]
+
+    logits = router_logits(x, Wr, b)
+    ids, gaps = select_topk(logits, k)
+    if force_ids:
+        ids = ids.copy()
+        for t, seq in force_ids.items():
+            ids[t] = np.asarray(seq, dtype=np.int64)
+    w = softmax_selected(logits, ids)
+    near = (gaps < NEAR_TIE).any(axis=-1)
+
+    h = x @ Wp.T
+    u = rms_norm(h, gp, eps)
+    if "u" in round_bf16:
+        u = _bf16_round(u)
+
+    I = None
+    ohat = np.zeros((T, k, P))
+    o_all = np.zeros((T, k, P)) if keep_pairs else None
+    a_all = None
+    for e in np.unique(ids):
+        tt, jj = np.nonzero(ids == e)
+        Wg, Wu, Wd = experts(int(e))
+        if I is None:
+            I = Wg.shape[0]
+            a_all = np.zeros((T, k, I)) if keep_pairs else None
+        U = u[tt]
+        g = U @ Wg.T
+        v = U @ Wu.T
+        a = silu(g) * v
+        if "a" in round_bf16:
+            a = _bf16_round(a)
+        o = a @ Wd.T
+        if keep_pairs:
+            a_all[tt, jj] = a
+            o_all[tt, jj] = o
+        if order == "norm_then_sum":
+            ohat[tt, jj] = rms_norm(o, ge[e], eps)
+        else:
+            ohat[tt, jj] = o
+
+    y = np.zeros((T, P))
+    for j in range(k):  # slot order
+        y = y + w[:, j : j + 1] * ohat[:, j]
+    if order == "sum_then_norm":
+        y = rms_norm(y, np.ones(P), eps)
+    if "y" in round_bf16:
+        y = _bf16_round(y)
+    out = y @ Wun.T
+    return OracleResult(out=out, ids=ids, w=w, logits=logits, gaps=gaps, h=h, u=u, a=a_all,
+                        o=o_all, ohat=ohat if keep_pairs else None, y=y, near_tie=near)
+
+
+def _bf16_round(v: np.ndarray) -> np.ndarray:
+    """FP64 -> FP32 (nearest) -> BF16 (nearest even) -> FP64; diagnostic only."""
+    f = v.astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def forward_inputs(inp: dict, k: int, eps: float, **kw) -> OracleResult:
+    """Convenience: inputs as a dict of stored arrays (names as the layer's
+    weights: x, router, router_bias, pooler, pool_gamma, w_gate, w_up, w_down,
+    expert_gamma, unpooler)."""
+    ex = inp.get("experts") or experts_from_arrays(inp["w_gate"], inp["w_up"], inp["w_down"])
+    return forward(inp["x"], inp["router"], inp.get("router_bias"), inp["pooler"], inp["pool_gamma"],
+                   ex, inp["expert_gamma"], inp["unpooler"], k, eps, **kw)

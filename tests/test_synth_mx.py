@@ -1,0 +1,120 @@
+"""The seeded input generator and the oracle's MXFP4 decoder, pinned to the
+OCP Microscaling v1.0 definitions and to their own invariants."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import mx
+
+
+def test_e2m1_table_is_the_ocp_grid():
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(mx.E2M1[:8]) == grid
+    assert list(mx.E2M1[8:]) == [-v for v in grid]
+    assert np.signbit(mx.E2M1[8])  # code 8 is -0
+
+
+def test_e8m0_decode():
+    v = mx.e8m0_to_f64(np.array([0, 1, 126, 127, 128, 254, 255], np.uint8))
+    assert v[3] == 1.0 and v[2] == 0.5 and v[4] == 2.0
+    assert v[0] == 2.0 ** -127 and v[5] == 2.0 ** 127
+    assert np.isnan(v[6])
+
+
+def test_bf16_decode_exact():
+    f = np.array([1.0, -2.5, 3.140625, 0.0], np.float32)
+    u16 = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert list(mx.bf16_to_f64(u16)) == [1.0, -2.5, 3.140625, 0.0]
+
+
+def _rne_bf16(f32):
+    u = f32.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_generator_determinism_slices_and_threads():
+    s = synth.CONFIGS["decode"].with_(E=4, I=64, P=128, H=256)
+    a = synth.host(s, "w_gate", nthreads=1)
+    b = synth.host(s, "w_gate", nthreads=7)
+    assert np.array_equal(a, b)
+    c = synth.host(s, "w_gate", experts=(1, 3))
+    assert np.array_equal(c, a[1:3])
+    # different tensors / seeds / chunks differ
+    assert not np.array_equal(a, synth.host(s, "w_up"))
+    assert not np.array_equal(a, synth.host(s.with_(seed=1), "w_gate"))
+    x0 = synth.host(s, "x", chunk=0)
+    x1 = synth.host(s, "x", chunk=1)
+    assert not np.array_equal(x0, x1)
+
+
+def test_generator_distributions():
+    s = synth.CONFIGS["decode"].with_(E=8, I=256, P=512, H=1024)
+    f = synth.host(s.with_(expert_format="f32"), "w_down")
+    assert abs(f.mean()) < 2e-3 / np.sqrt(s.I)
+    assert abs(f.std() * np.sqrt(s.I) - 1) < 2e-3
+    # standardised 4th moment of a normal is 3
+    z = f.astype(np.float64) * np.sqrt(s.I)
+    assert abs((z ** 4).mean() - 3) < 0.03
+    g = synth.host(s, "expert_gamma").astype(np.float64)
+    assert abs(g.mean() - 1) < 1e-3 and abs(g.std() - 0.1) < 1e-3
+    x = synth.host(synth.CONFIGS["tiny"], "x").astype(np.float64)
+    assert abs(x.std() - 1) < 0.02
+
+
+def test_bf16_tensors_are_rne_of_the_fp32_draw():
+    s = synth.CONFIGS["decode"].with_(E=3, I=64, P=96, H=160)
+    f = synth.host(s.with_(expert_format="f32"), "w_up")
+    b = synth.host(s, "w_up")
+    assert np.array_equal(b, _rne_bf16(f))
+    fx = synth.host(s.with_(act_dtype="f32"), "pooler")
+    assert np.array_equal(synth.host(s, "pooler"), _rne_bf16(fx))
+
+
+def test_mxfp4_quantiser_matches_ocp_definition():
+    s = synth.CONFIGS["mxfp4"].with_(E=2, I=64, P=128, H=256)
+    f = synth.host(s.with_(expert_format="f32"), "w_gate").astype(np.float64)
+    packed, scales = synth.host(s, "w_gate")
+    deq = mx.mxfp4_to_f64(packed, scales)
+    blocks = f.reshape(-1, 32)
+    dq = deq.reshape(-1, 32)
+    sc = mx.e8m0_to_f64(scales.reshape(-1))
+    amax = np.abs(blocks).max(-1)
+    # scale = 2^(floor(log2 amax) - 2)
+    np.testing.assert_array_equal(sc, 2.0 ** (np.floor(np.log2(amax)) - 2))
+    # each element is a nearest grid point (ties: either neighbour is nearest)
+    grid = np.unique(np.abs(mx.E2M1))
+    v = np.abs(blocks) / sc[:, None]
+    best = np.abs(v[..., None] - grid).min(-1)
+    got = np.abs(np.abs(dq) / sc[:, None] - v)
+    np.testing.assert_allclose(got, best, atol=1e-12)
+    # sign preserved for non-zero codes
+    nz = dq != 0
+    assert (np.sign(dq[nz]) == np.sign(blocks[nz])).all()
+    # the block maximum lands on 4 or 6 times the scale
+    big = np.abs(dq).max(-1) / sc
+    assert set(np.unique(big)) <= {4.0, 6.0}
+
+
+def test_mxfp4_round_trip_and_ties_to_even():
+    # quantising already-representable values reproduces their codes exactly
+    s = synth.CONFIGS["mxfp4"].with_(E=1, I=32, P=64, H=64)
+    packed, scales = synth.host(s, "w_down")
+    deq = mx.mxfp4_to_f64(packed, scales)
+    # re-encode with the OCP nearest-even rule, written from the grid table
+    codes = np.stack([packed & 15, packed >> 4], -1).reshape(deq.shape)
+    sc = mx.e8m0_to_f64(scales)
+    v = (deq.reshape(-1, 32) / sc.reshape(-1, 1)).reshape(deq.shape)
+    re = np.array([np.argmin(np.abs(mx.E2M1[:8] - abs(t))) + (8 if (t < 0 or (t == 0 and c >= 8)) else 0)
+                   for t, c in zip(v.ravel(), codes.ravel())]).reshape(codes.shape)
+    assert np.array_equal(re, codes)
+
+
+def test_zipf_bias():
+    s = synth.CONFIGS["skew"]
+    b = synth.router_bias(s).astype(np.float64)
+    assert b.shape == (256,)
+    w = np.exp(b)
+    assert abs(w.sum() - 1) < 1e-5
+    r = np.sort(w)[::-1]
+    ranks = np.arange(1, 257)
+    np.testing.assert_allclose(r / r[0], ranks ** -1.1, rtol=1e-5)
