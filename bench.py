@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Throughput of the latent-MoE layer forward on one MI355X.
+
+One step = one forward of the whole layer (router, top-k, grouping, pooler,
+pre-expert norm, gate/up, down, per-expert norm + weighted sum, unpooler) over
+one batch of seeded synthetic tokens already resident in HBM. Default
+workload: 64-token decode at the real layer shapes (H=8192, P=4096, E=256,
+I=4096, k=8, BF16); the 16384-token prefill chunk on the same weights is
+measured in the same run and reported under "prefill".
+
+Prints one JSON line with tokens/s, the roofline of the dominant kernel (the
+gate/up grouped GEMM: HBM-bound at decode, MFMA-bound at prefill; its time
+comes from HIP events recorded on the forward's stream) and the FP64 CPU
+oracle timed on a bounded token sample on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def layer_bytes(spec, counts, T):
+    """Algorithmic HBM bytes of one forward: touched expert weights once, the
+    projections and router once, x in, out (FP32) out."""
+    import numpy as np
+
+    ew = 2 if spec.expert_format == "bf16" else (0.5 + 1 / 32)
+    touched = int((np.asarray(counts) > 0).sum())
+    experts = touched * 3 * spec.P * spec.I * ew
+    proj = 2 * spec.H * spec.P * 2 + spec.E * spec.H * 4
+    return experts + proj + T * spec.H * 2 + T * spec.H * 4, touched
+
+
+def gate_up_bytes(spec, counts, T):
+    import numpy as np
+
+    ew = 2 if spec.expert_format == "bf16" else (0.5 + 1 / 32)
+    touched = int((np.asarray(counts) > 0).sum())
+    pairs = T * spec.k
+    return touched * 2 * spec.I * spec.P * ew + pairs * spec.P * 2 + pairs * spec.I * 2
+
+
+def layer_flops(spec, T):
+    k, H, P, I = spec.k, spec.H, spec.P, spec.I
+    return T * (2 * H * P * 2 + k * 2 * P * 2 * I + k * 2 * I * P)
+
+
+def measure(spec, layer, x, steps, warmup, torch):
+    from latent_moe_layer_fp32_amd import binding as B
+
+    stream = torch.cuda.current_stream()
+    T = x.shape[0]
+    out = torch.empty((T, spec.H), dtype=torch.float32, device=x.device)
+    for _ in range(warmup):
+        layer.forward(x, out=out)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward(x, out=out)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / steps
+    # per-stage HIP events on the same stream, over the same number of steps
+    B.latent_moe_set_profiling(layer.handle, True)
+    acc = None
+    for _ in range(steps):
+        layer.forward(x, out=out)
+        st = B.latent_moe_stage_times(layer.handle)
+        acc = st if acc is None else {k: acc[k] + v for k, v in st.items()}
+    B.latent_moe_set_profiling(layer.handle, False)
+    stages = {k: v / steps for k, v in acc.items()}
+    v = layer.views(T)
+    return ms, wall, stages, v["counts"]
+
+
+def cpu_baseline(spec, xh, sample_tokens, budget_s=30.0):
+    """The FP64 oracle on the first tokens of the batch (bounded sample)."""
+    import numpy as np
+
+    from oracle import oracle as orc
+    from oracle.mx import to_f64
+    import synth
+
+    host = {n: synth.host(spec, n) for n in ("router", "router_bias", "pooler", "pool_gamma",
+                                            "expert_gamma", "unpooler")}
+    xs = xh[:sample_tokens]
+    lg = orc.router_logits(to_f64(xs), to_f64(host["router"]),
+                           None if host["router_bias"] is None else to_f64(host["router_bias"]))
+    ids, _ = orc.select_topk(lg, spec.k)
+    raw = {int(e): tuple(synth.host(spec, n, experts=(int(e), int(e) + 1)) for n in ("w_gate", "w_up", "w_down"))
+           for e in np.unique(ids)}
+
+    def first(a):
+        return (a[0][0], a[1][0]) if isinstance(a, tuple) else a[0]
+
+    def expert(e):
+        return tuple(to_f64(first(a)) for a in raw[e])
+
+    t0 = time.perf_counter()
+    orc.forward(xs, host["router"], host["router_bias"], host["pooler"], host["pool_gamma"], expert,
+                host["expert_gamma"], host["unpooler"], spec.k, spec.eps, keep_pairs=False)
+    dt = time.perf_counter() - t0
+    return sample_tokens / dt, dt, len(raw)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew"])
+    ap.add_argument("--also", default="prefill", help="extra workloads on the same weights (comma list)")
+    ap.add_argument("--cpu-tokens", type=int, default=24, help="token sample for the CPU oracle (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer runs unsharded on a single MI355X; "
+              "multi-GPU runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from latent_moe_layer_fp32_amd import LatentMoE
+
+    def make_layer(spec, w, max_tokens):
+        return LatentMoE(hidden=spec.H, pooled=spec.P, experts=spec.E, intermediate=spec.I,
+                         top_k=spec.k, eps=spec.eps, act_dtype=spec.act_dtype,
+                         expert_dtype=spec.expert_format, max_tokens=max_tokens, weights=w)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    tables = synth.DeviceTables("cuda:0")
+    base = synth.CONFIGS["prefill"]
+    log("generating weights on the device")
+    weights = {n: synth.device_tensor(base, n, tables) for n in synth.WEIGHT_NAMES}
+    torch.cuda.synchronize()
+
+    results = {}
+    for wl in [args.workload] + [w for w in args.also.split(",") if w and w != args.workload]:
+        spec = synth.CONFIGS[wl]
+        w = dict(weights)
+        if spec.router_bias != "none":
+            w["router_bias"] = synth.device_tensor(spec, "router_bias", tables)
+        layer = make_layer(spec, w, max_tokens=spec.T)
+        x = synth.device_tensor(spec, "x", tables)
+        steps = args.steps if wl == args.workload else max(3, args.steps // 4)
+        warm = args.warmup if wl == args.workload else max(1, args.warmup // 2)
+        log(f"{wl}: T={spec.T}, {warm} warmup + {steps} timed steps")
+        ms, wall, stages, counts = measure(spec, layer, x, steps, warm, torch)
+        lb, touched = layer_bytes(spec, counts, spec.T)
+        r = dict(spec=spec, ms=ms, wall=wall, stages=stages, touched=touched, layer_bytes=lb,
+                 tokens_per_s=spec.T / (ms / 1e3), steps=steps, warmup=warm)
+        gu = stages["gate_up"] / 1e3
+        if wl == "decode":
+            ach = gate_up_bytes(spec, counts, spec.T) / gu / 1e9
+            r["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                             "kernel": "gate_up grouped GEMM + SwiGLU",
+                             "kernel_ms": round(stages["gate_up"], 4)}
+            r["layer_frac"] = round(lb / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
+        else:
+            fl = 2 * spec.T * spec.k * spec.P * 2 * spec.I
+            ach = fl / gu / 1e12
+            r["roofline"] = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                             "kernel": "gate_up grouped GEMM + SwiGLU",
+                             "kernel_ms": round(stages["gate_up"], 4)}
+            r["layer_frac"] = round(layer_flops(spec, spec.T) / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+        log(f"{wl}: {ms:.3f} ms/step, {r['tokens_per_s']:.0f} tok/s, stages "
+            + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
+        results[wl] = r
+        layer.close()
+        del x
+
+    main_r = results[args.workload]
+    spec = main_r["spec"]
+    line = {
+        "metric": "latent-MoE layer tokens/s (16K prefill, 64-tok decode); % of MFMA/HBM peak",
+        "value": round(main_r["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": main_r["steps"],
+        "warmup": main_r["warmup"],
+        "ms_per_step": round(main_r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based N(0,1) inputs, N(0,1/fan_in) weights)",
+        "config": {"workload": f"{args.workload}: {spec.T} tokens, H={spec.H}, P={spec.P}, E={spec.E}, "
+                               f"I={spec.I}, top-{spec.k}, BF16 experts, FP32 router",
+                   "global_batch": spec.T, "parallelism": "none (one GPU)"},
+        "roofline": main_r["roofline"],
+        "layer_frac": main_r["layer_frac"],
+        "stages_ms": {k: round(v, 4) for k, v in main_r["stages"].items()},
+        "experts_touched": main_r["touched"],
+    }
+    for wl, r in results.items():
+        if wl == args.workload:
+            continue
+        line[wl] = {"value": round(r["tokens_per_s"], 1), "unit": "tokens/s", "ms_per_step": round(r["ms"], 4),
+                    "steps": r["steps"], "roofline": r["roofline"], "layer_frac": r["layer_frac"],
+                    "stages_ms": {k: round(v, 4) for k, v in r["stages"].items()}}
+    if args.cpu_tokens > 0:
+        xh = synth.host(spec, "x")
+        log(f"cpu oracle on {args.cpu_tokens} tokens")
+        v, dt, ne = cpu_baseline(spec, xh, args.cpu_tokens)
+        line["cpu_baseline"] = {"value": round(v, 4), "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+                                "kind": "oracle",
+                                "sample": f"first {args.cpu_tokens} tokens of the {args.workload} batch "
+                                          f"({ne} experts), FP64 numpy, {dt:.1f} s"}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+/*
+ * latent_moe.h -- C ABI of the latent-MoE layer forward for MI355X (gfx950).
+ *
+ * The layer (web page "SGLang and Miles Add Day-0 Support for Muse Spark
+ * Open", section "MoE with Pooler, Unpooler and Per-Expert Normalization";
+ * vLLM Day-0 post on Muse Spark Open, section on the latent MoE) maps each
+ * token x_t (model width H, already normed) to out_t (width H):
+ *
+ *   l_t  = Wr x_t + b                          router on the full width, FP32
+ *   S_t  = top-k of l_t (ties -> lowest index), slot j = j-th largest
+ *   w_tj = softmax over the k selected logits
+ *   u_t  = RMSNorm(Wp x_t) * gamma_p           pooler H -> P, pre-expert norm
+ *   o_tj = Wd_e (silu(Wg_e u_t) * (Wu_e u_t))   SwiGLU expert e = S_t[j]
+ *   y_t  = sum_j w_tj * RMSNorm(o_tj) * gamma_e  per-expert norm, FP32 sum
+ *   out_t = Wun y_t                            unpooler P -> H
+ *
+ * RMSNorm(v) = v / sqrt(mean(v^2) + eps).  The per-expert norm is applied to
+ * each selected expert's output before its routing weight (same section;
+ * "The Fused Post-per-expert Norm"), and the weighted sum is FP32 (section
+ * "Trainable Muse Spark Open Backend").
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers on the device that was current
+ *     when the handle was created; tensors are dense, row-major, in the
+ *     [out_features, in_features] convention of the linear maps above.
+ *   - Every pointer must be 16-byte aligned; H and P must be multiples of
+ *     64, I a multiple of 128; 1 <= E <= 1024.
+ *   - Calls return 0 (LMOE_OK) or a negative error code; no exception or
+ *     abort crosses the ABI. latent_moe_last_error() then holds a message for
+ *     the calling thread. All argument checks run on the host before any GPU
+ *     work is enqueued, so a failed call has launched nothing.
+ */
+#ifndef LATENT_MOE_H
+#define LATENT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LMOE_OK 0
+#define LMOE_ERR_INVALID_ARG (-1)     /* null pointer, bad dimension, misalignment */
+#define LMOE_ERR_UNSUPPORTED (-2)     /* a dtype combination this build lacks */
+#define LMOE_ERR_OOM (-3)             /* device allocation failed in create */
+#define LMOE_ERR_HIP (-4)             /* any HIP runtime error, including "no device" */
+#define LMOE_ERR_TOO_MANY_TOKENS (-5) /* T > max_tokens of the handle */
+
+/* Element formats. */
+#define LMOE_F32 0   /* IEEE binary32 */
+#define LMOE_BF16 1  /* bfloat16 (upper half of binary32), stored as 16-bit words */
+#define LMOE_MXFP4 2 /* OCP MX FP4: E2M1 elements, two per byte (element 2i in the
+                        low nibble), plus one E8M0 scale byte per 32 consecutive
+                        elements along the input (K) axis */
+
+typedef struct latent_moe latent_moe_t;
+
+typedef struct {
+  int64_t hidden;       /* H: model width (8192 for the published model) */
+  int64_t pooled;       /* P: expert width after the pooler (4096) */
+  int64_t experts;      /* E: routed experts per layer (256) */
+  int64_t intermediate; /* I: SwiGLU intermediate width per expert */
+  int32_t top_k;        /* k: experts per token, 1 <= k <= min(E, 16) */
+  float eps;            /* RMSNorm epsilon for both norms, finite, >= 0 */
+  int32_t act_dtype;    /* x, pooler and unpooler: LMOE_F32 or LMOE_BF16 */
+  int32_t expert_dtype; /* gate/up/down: LMOE_F32, LMOE_BF16 or LMOE_MXFP4.
+                           LMOE_F32 requires act_dtype LMOE_F32 and vice versa */
+  int64_t max_tokens;   /* upper bound on T per forward; sizes the workspace */
+} latent_moe_config;
+
+/* Layer weights (device pointers). They are BORROWED: the caller keeps them
+ * alive and unchanged until latent_moe_destroy returns. Only the router is
+ * repacked into library memory at create; nothing else is copied.
+ *   router       [E, H]   F32
+ *   router_bias  [E]      F32, or NULL for no bias (added to the logits)
+ *   pooler       [P, H]   act_dtype
+ *   pool_gamma   [P]      F32
+ *   w_gate, w_up [E, I, P] expert_dtype (MXFP4: [E, I, P/2] bytes)
+ *   w_down       [E, P, I] expert_dtype (MXFP4: [E, P, I/2] bytes)
+ *   s_gate, s_up [E, I, P/32], s_down [E, P, I/32]  E8M0 bytes (MXFP4 only,
+ *                 else ignored)
+ *   expert_gamma [E, P]   F32, one gamma row per expert
+ *   unpooler     [H, P]   act_dtype                                         */
+typedef struct {
+  const float* router;
+  const float* router_bias;
+  const void* pooler;
+  const float* pool_gamma;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const uint8_t* s_gate;
+  const uint8_t* s_up;
+  const uint8_t* s_down;
+  const float* expert_gamma;
+  const void* unpooler;
+} latent_moe_weights;
+
+/* Create a handle on the current device. Validates cfg and w, allocates the
+ * workspace for cfg->max_tokens tokens (never reallocated later), and splits
+ * the FP32 router into an exact sum of three BF16 matrices for the matrix
+ * cores (BF16 activations only), synchronising the device before returning.
+ * Errors: INVALID_ARG, UNSUPPORTED, OOM, HIP. On error *out is set to NULL
+ * and nothing is leaked. */
+int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const latent_moe_weights* w);
+
+/* Bytes of device workspace a handle with this config allocates (beyond the
+ * borrowed weights). Errors as for create's validation. */
+int latent_moe_workspace_bytes(const latent_moe_config* cfg, size_t* bytes);
+
+/* Run the layer on T tokens, asynchronously on `stream` (a hipStream_t; NULL =
+ * the null stream).
+ *   x            [T, H] act_dtype, read-only
+ *   out          [T, H] F32, written
+ *   topk_ids     [T, k] int32 or NULL: selected experts in slot order
+ *                (logit descending, index ascending on ties)
+ *   topk_weights [T, k] F32 or NULL: routing weights in the same order
+ * Caller-owned buffers must stay valid until the stream passes this call.
+ * T = 0 succeeds and enqueues nothing. One forward in flight per handle: the
+ * workspace is shared, so overlapping forwards of one handle on different
+ * streams race. The forward never allocates or synchronises the host.
+ * Errors: INVALID_ARG (null handle/x/out, misaligned pointer, T < 0),
+ * TOO_MANY_TOKENS, HIP (launch failure). */
+int latent_moe_forward(latent_moe_t* h, const void* x, int64_t T, float* out, int32_t* topk_ids,
+                       float* topk_weights, void* stream);
+
+/* Views of the last forward's intermediates, for inspection and per-stage
+ * tests. Pointers are into the handle's workspace (device memory), valid
+ * until the next forward or destroy; rows beyond the last forward's T (or
+ * its T*k routed pairs) hold stale data. Layouts:
+ *   logits   [T, E] F32 router logits (bias included)
+ *   ids      [T, k] int32, weights [T, k] F32 (as exported by forward)
+ *   counts   [E] int32 routed pairs per expert; offsets [E+1] int32 exclusive
+ *            prefix of counts
+ *   perm_token [T*k] int32: token of each routed pair, grouped by expert
+ *            (stable in (t, j) order within an expert)
+ *   pair_row [T*k] int32: for pair (t, j) at index t*k+j, its row in the
+ *            grouped order
+ *   pooled   [T, P] act_dtype: gamma_p * (Wp x_t), before the row scale
+ *   row_scale [T] F32: 1/sqrt(mean((Wp x_t)^2) + eps)
+ *   act      [T*k, I] (F32 if expert_dtype is F32, else BF16): SwiGLU
+ *            output, grouped order
+ *   expert_out [T*k, P] F32: o (before the per-expert norm), grouped order
+ *   combined [T, P] (F32 or BF16 per act_dtype): y                          */
+typedef struct {
+  const float* logits;
+  const int32_t* ids;
+  const float* weights;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* perm_token;
+  const int32_t* pair_row;
+  const void* pooled;
+  const float* row_scale;
+  const void* act;
+  const float* expert_out;
+  const void* combined;
+} latent_moe_views;
+
+int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v);
+
+/* Stage timing, for measurement. With profiling enabled, each forward records
+ * one HIP event on its stream before the first stage and after each of the
+ * LMOE_NUM_STAGES stages (events are created here, never in forward):
+ *   0 router GEMM          1 top-k/softmax      2 grouping by expert
+ *   3 pooler GEMM          4 pooled row scale   5 gate/up GEMM + SwiGLU
+ *   6 down GEMM            7 combine            8 unpooler GEMM
+ * latent_moe_stage_times waits for the last recorded event and writes the
+ * elapsed milliseconds of each stage of the last forward into ms[0..8].
+ * Errors: INVALID_ARG (NULL handle/ms, n < LMOE_NUM_STAGES, no profiled
+ * forward yet), HIP. */
+#define LMOE_NUM_STAGES 9
+int latent_moe_set_profiling(latent_moe_t* h, int enable);
+int latent_moe_stage_times(latent_moe_t* h, float* ms, int n);
+
+/* Wait for the handle's work, free its workspace and the handle. NULL returns
+ * INVALID_ARG. Using a handle after destroy is undefined. */
+int latent_moe_destroy(latent_moe_t* h);
+
+/* Message for the last failed call on this thread ("" if none). The string is
+ * owned by the library and valid until the thread's next call. */
+const char* latent_moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LATENT_MOE_H */

@@ -1,0 +1,276 @@
+"""ctypes binding of liblatent_moe.so (C ABI in include/latent_moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. torch is used for device memory (tensor data pointers) and streams.
+The functions below carry the C names; ``LatentMoE`` wraps them for torch
+callers. If the shared library is missing this module raises on import of
+``lib()``: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB_PATH = os.path.join(HERE, "liblatent_moe.so")
+HEADER = os.path.join(ROOT, "include", "latent_moe.h")
+
+LMOE_OK = 0
+LMOE_ERR_INVALID_ARG = -1
+LMOE_ERR_UNSUPPORTED = -2
+LMOE_ERR_OOM = -3
+LMOE_ERR_HIP = -4
+LMOE_ERR_TOO_MANY_TOKENS = -5
+LMOE_F32, LMOE_BF16, LMOE_MXFP4 = 0, 1, 2
+DTYPE_CODES = {"f32": LMOE_F32, "bf16": LMOE_BF16, "mxfp4": LMOE_MXFP4}
+
+
+class LatentMoEError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"latent_moe error {code}: {msg}")
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int64),
+        ("pooled", ctypes.c_int64),
+        ("experts", ctypes.c_int64),
+        ("intermediate", ctypes.c_int64),
+        ("top_k", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("act_dtype", ctypes.c_int32),
+        ("expert_dtype", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int64),
+    ]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "router", "router_bias", "pooler", "pool_gamma", "w_gate", "w_up", "w_down",
+        "s_gate", "s_up", "s_down", "expert_gamma", "unpooler")]
+
+
+class Views(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "logits", "ids", "weights", "counts", "offsets", "perm_token", "pair_row", "pooled",
+        "row_scale", "act", "expert_out", "combined")]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        # torch ships its own HIP runtime and puts it in the global symbol
+        # scope; importing it first makes this library bind to that same
+        # runtime, so torch tensors, streams and our kernels share one.
+        import torch  # noqa: F401
+
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        L.latent_moe_create.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(Config),
+                                        ctypes.POINTER(Weights)]
+        L.latent_moe_create.restype = ctypes.c_int
+        L.latent_moe_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_size_t)]
+        L.latent_moe_workspace_bytes.restype = ctypes.c_int
+        L.latent_moe_forward.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+        L.latent_moe_forward.restype = ctypes.c_int
+        L.latent_moe_debug_views.argtypes = [ctypes.c_void_p, ctypes.POINTER(Views)]
+        L.latent_moe_debug_views.restype = ctypes.c_int
+        L.latent_moe_set_profiling.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        L.latent_moe_set_profiling.restype = ctypes.c_int
+        L.latent_moe_stage_times.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int]
+        L.latent_moe_stage_times.restype = ctypes.c_int
+        L.latent_moe_destroy.argtypes = [ctypes.c_void_p]
+        L.latent_moe_destroy.restype = ctypes.c_int
+        L.latent_moe_last_error.argtypes = []
+        L.latent_moe_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> list[str]:
+    """Entry points declared in include/latent_moe.h."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(latent_moe_\w+)\s*\(", txt, re.M)))
+
+
+def latent_moe_last_error() -> str:
+    return lib().latent_moe_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != LMOE_OK:
+        raise LatentMoEError(rc, latent_moe_last_error())
+
+
+def make_config(hidden, pooled, experts, intermediate, top_k, eps, act_dtype, expert_dtype,
+                max_tokens) -> Config:
+    return Config(hidden, pooled, experts, intermediate, top_k, eps,
+                  DTYPE_CODES.get(act_dtype, act_dtype), DTYPE_CODES.get(expert_dtype, expert_dtype),
+                  max_tokens)
+
+
+def latent_moe_workspace_bytes(cfg: Config) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().latent_moe_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def latent_moe_create(cfg: Config, w: Weights) -> int:
+    h = ctypes.c_void_p(0)
+    _check(lib().latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)))
+    return h.value
+
+
+def latent_moe_forward(h: int, x: int, T: int, out: int, topk_ids: int | None,
+                       topk_weights: int | None, stream: int | None) -> None:
+    _check(lib().latent_moe_forward(h, x, T, out, topk_ids, topk_weights, stream))
+
+
+def latent_moe_debug_views(h: int) -> Views:
+    v = Views()
+    _check(lib().latent_moe_debug_views(h, ctypes.byref(v)))
+    return v
+
+
+STAGES = ("router", "topk", "group", "pooler", "rowscale", "gate_up", "down", "combine", "unpooler")
+
+
+def latent_moe_set_profiling(h: int, enable: bool) -> None:
+    _check(lib().latent_moe_set_profiling(h, 1 if enable else 0))
+
+
+def latent_moe_stage_times(h: int) -> dict:
+    a = (ctypes.c_float * len(STAGES))()
+    _check(lib().latent_moe_stage_times(h, a, len(STAGES)))
+    return dict(zip(STAGES, [float(v) for v in a]))
+
+
+def latent_moe_destroy(h: int) -> None:
+    _check(lib().latent_moe_destroy(h))
+
+
+# ------------------------------------------------------------- torch wrapper
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+class LatentMoE:
+    """A layer handle over borrowed torch device tensors.
+
+    weights: dict with router, router_bias (or None), pooler, pool_gamma,
+    w_gate, w_up, w_down (MXFP4: (packed, scales) pairs), expert_gamma,
+    unpooler. The tensors are referenced by this object so they outlive the
+    handle.
+    """
+
+    def __init__(self, *, hidden, pooled, experts, intermediate, top_k, eps, act_dtype,
+                 expert_dtype, max_tokens, weights: dict):
+        import torch
+
+        self.cfg = make_config(hidden, pooled, experts, intermediate, top_k, eps, act_dtype,
+                               expert_dtype, max_tokens)
+        self.top_k, self.hidden, self.pooled, self.experts = top_k, hidden, pooled, experts
+        self.intermediate = intermediate
+        self.act_dtype, self.expert_dtype = act_dtype, expert_dtype
+        self._keep = dict(weights)
+        w = Weights()
+        for name in ("router", "router_bias", "pooler", "pool_gamma", "expert_gamma", "unpooler"):
+            setattr(w, name, _ptr(weights.get(name)))
+        for name, sname in (("w_gate", "s_gate"), ("w_up", "s_up"), ("w_down", "s_down")):
+            v = weights[name]
+            if isinstance(v, tuple):
+                setattr(w, name, _ptr(v[0]))
+                setattr(w, sname, _ptr(v[1]))
+            else:
+                setattr(w, name, _ptr(v))
+        for name, v in weights.items():
+            for t in (v if isinstance(v, tuple) else (v,)):
+                if t is not None and (not t.is_cuda or not t.is_contiguous()):
+                    raise ValueError(f"weight {name} must be a contiguous device tensor")
+        self.device = torch.device("cuda", torch.cuda.current_device())
+        self.handle = latent_moe_create(self.cfg, w)
+
+    def forward(self, x, out=None, topk_ids=None, topk_weights=None, stream=None):
+        import torch
+
+        if not (x.is_cuda and x.is_contiguous() and x.dim() == 2 and x.shape[1] == self.hidden):
+            raise ValueError("x must be a contiguous [T, hidden] device tensor")
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty((T, self.hidden), dtype=torch.float32, device=x.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device)
+        latent_moe_forward(self.handle, x.data_ptr(), T, out.data_ptr(), _ptr(topk_ids),
+                           _ptr(topk_weights), stream.cuda_stream)
+        return out
+
+    __call__ = forward
+
+    def views(self, T: int) -> dict:
+        """Host copies (numpy) of the last forward's intermediates for T tokens."""
+        import numpy as np
+        import torch
+
+        torch.cuda.synchronize(self.device)
+        v = latent_moe_debug_views(self.handle)
+        k, E, P, I = self.top_k, self.experts, self.pooled, self.intermediate
+        act_np = np.float32 if self.act_dtype == "f32" else np.uint16
+        exp_np = np.float32 if self.expert_dtype == "f32" else np.uint16
+        spec = {
+            "logits": (v.logits, (T, E), np.float32),
+            "ids": (v.ids, (T, k), np.int32),
+            "weights": (v.weights, (T, k), np.float32),
+            "counts": (v.counts, (E,), np.int32),
+            "offsets": (v.offsets, (E + 1,), np.int32),
+            "perm_token": (v.perm_token, (T * k,), np.int32),
+            "pair_row": (v.pair_row, (T * k,), np.int32),
+            "pooled": (v.pooled, (T, P), act_np),
+            "row_scale": (v.row_scale, (T,), np.float32),
+            "act": (v.act, (T * k, I), exp_np),
+            "expert_out": (v.expert_out, (T * k, P), np.float32),
+            "combined": (v.combined, (T, P), act_np),
+        }
+        res = {}
+        for name, (ptr, shape, dt) in spec.items():
+            a = np.empty(shape, dt)
+            _memcpy_d2h(a.ctypes.data, ptr, a.nbytes)
+            res[name] = a
+        return res
+
+    def close(self):
+        if getattr(self, "handle", None):
+            latent_moe_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+_hip = None
+
+
+def _memcpy_d2h(dst: int, src: int, nbytes: int):
+    global _hip
+    if _hip is None:
+        import torch  # noqa: F401  (same runtime as the library, see lib())
+
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        _hip.hipMemcpy.restype = ctypes.c_int
+    rc = _hip.hipMemcpy(dst, src, nbytes, 2)  # hipMemcpyDeviceToHost
+    if rc != 0:
+        raise LatentMoEError(LMOE_ERR_HIP, f"hipMemcpy failed ({rc})")

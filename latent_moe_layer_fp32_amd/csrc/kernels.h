@@ -1,0 +1,563 @@
+// Kernels of the latent-MoE layer forward (gfx950).
+//
+// Step order (web page "SGLang and Miles Add Day-0 Support for Muse Spark
+// Open", section "MoE with Pooler, Unpooler and Per-Expert Normalization"):
+//   router logits (FP32)  -> top-k + softmax      lm_topk_kernel
+//   grouping by expert    (LDS histogram per block, then a stable scatter:
+//                          the "LDS kernel" replacing an atomic-add expert
+//                          sort, section "AMD Support / Day-0 Enablement")
+//   pooler GEMM + pre-expert RMSNorm statistics  PoolerProb, lm_rowscale_kernel
+//   gate/up GEMM per expert + SwiGLU             GateUpProb
+//   down GEMM per expert + per-row sum of squares partials (section "The
+//     Fused Post-per-expert Norm": each second-GEMM tile contributes a partial
+//     sum of squares; here written per tile and summed in a fixed order)
+//   per-expert RMSNorm, routing weight, FP32 sum  lm_combine_kernel
+//   unpooler GEMM                                 UnpoolerProb
+#pragma once
+#include "gemm.h"
+
+// ----------------------------------------------------------------- router
+// Partial logits over k-splits: part[s][t][e] = sum over split s of x[t,k] W[e,k],
+// accumulated as FP64 sums of per-k-tile FP32 matrix-core chains.
+// BF16 activations: W is [E, 3H] holding an exact three-piece BF16 split of
+// the FP32 router, and x is read three times (a_ktile wraps), so the matrix
+// cores see exact products and FP32 accumulation.
+template <class Cfg_>
+struct RouterProb {
+  using Cfg = Cfg_;
+  using E = typename Cfg::E;
+  const E* x;
+  const E* w;
+  double* part;
+  int T, Ew, H, Kw, kta, mt, nt, splits, kt_per;
+
+  LM_DEV bool tile(int bid, LmTile& t) const {
+    int L;
+    if (!lm_xcd_map(bid, mt * nt * splits, L)) return false;
+    const int s = L / (mt * nt);
+    int m, n;
+    lm_dense_order(L - s * mt * nt, mt, nt, 8, m, n);
+    t.m0 = m * Cfg::BM;
+    t.rows = min(Cfg::BM, T - t.m0);
+    t.n0 = n * Cfg::BN;
+    t.nt = n;
+    t.e = s;
+    t.kt0 = s * kt_per;
+    t.kt1 = min(Kw / Cfg::KT, t.kt0 + kt_per);
+    return true;
+  }
+  LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
+    return (const lm_u32x4*)(x + (size_t)(t.m0 + min(r, t.rows - 1)) * H);
+  }
+  LM_DEV const lm_u32x4* b_row(const LmTile& t, int r) const {
+    return (const lm_u32x4*)(w + (size_t)min(t.n0 + r, Ew - 1) * Kw);
+  }
+  LM_DEV int a_ktile(int kt) const { return kt % kta; }
+  LM_DEV void epilogue_f64(const LmTile& t, const double (&acc)[Cfg::TM][Cfg::TN][16], int wm,
+                           int wn, int lane) const {
+    double* dst = part + ((size_t)t.e * T + t.m0) * Ew + t.n0;
+#pragma unroll
+    for (int tm = 0; tm < Cfg::TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < Cfg::TN; ++tn) {
+        const int col = lm_acc_col<Cfg>(wn, tn, lane);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
+          if (row < t.rows && t.n0 + col < Ew) dst[(size_t)row * Ew + col] = acc[tm][tn][i];
+        }
+      }
+  }
+};
+
+// ----------------------------------------------------------------- pooler
+// h = x Wp^T. Writes pooled = gamma_p * h (activation dtype) and, per row and
+// n-tile, the partial sum of h^2 used by the pre-expert RMSNorm.
+template <class Cfg_>
+struct PoolerProb {
+  using Cfg = Cfg_;
+  using E = typename Cfg::E;
+  const E* x;
+  const E* w;
+  const float* gamma;
+  E* pooled;
+  float* ssq;  // [T, nt]
+  int T, H, P, mt, nt;
+
+  LM_DEV bool tile(int bid, LmTile& t) const {
+    int L;
+    if (!lm_xcd_map(bid, mt * nt, L)) return false;
+    int m, n;
+    lm_dense_order(L, mt, nt, 8, m, n);
+    t.m0 = m * Cfg::BM;
+    t.rows = min(Cfg::BM, T - t.m0);
+    t.n0 = n * Cfg::BN;
+    t.nt = n;
+    t.e = 0;
+    t.kt0 = 0;
+    t.kt1 = H / Cfg::KT;
+    return true;
+  }
+  LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
+    return (const lm_u32x4*)(x + (size_t)(t.m0 + min(r, t.rows - 1)) * H);
+  }
+  LM_DEV const lm_u32x4* b_row(const LmTile& t, int r) const {
+    return (const lm_u32x4*)(w + (size_t)min(t.n0 + r, P - 1) * H);
+  }
+  LM_DEV int a_ktile(int kt) const { return kt; }
+  LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
+                       int lane, void* smem) const {
+    float* red = (float*)smem;
+    lm_tile_row_ssq<Cfg>(acc, wm, wn, lane, P - t.n0, red, [](float v, int, int) { return v; });
+    if ((int)threadIdx.x < t.rows)
+      ssq[(size_t)(t.m0 + threadIdx.x) * nt + t.nt] = red[Cfg::WN * Cfg::BM + threadIdx.x];
+#pragma unroll
+    for (int tn = 0; tn < Cfg::TN; ++tn) {
+      const int col = t.n0 + lm_acc_col<Cfg>(wn, tn, lane);
+      if (col >= P) continue;
+      const float g = gamma[col];
+#pragma unroll
+      for (int tm = 0; tm < Cfg::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
+          if (row < t.rows)
+            pooled[(size_t)(t.m0 + row) * P + col] = LmElem<E>::from_f32(acc[tm][tn][i] * g);
+        }
+    }
+  }
+};
+
+// ------------------------------------------------------ grouped tile lookup
+// Tiles of all experts form one list: expert e owns tiles
+// [tile_off[e], tile_off[e+1]) (ceil(count_e / BM) of them), each walked over
+// all nt column tiles. Logical index L -> (expert, m-tile, n-tile) with the
+// m-tiles of one expert and one n-tile adjacent, so they share the weight
+// tile in L2.
+LM_DEV bool lm_group_tile(const int* tile_off, const int* offsets, const int* counts, int E, int BM,
+                          int nt, int cols, int bid, LmTile& t) {
+  const int total = tile_off[E] * nt;
+  int L;
+  if (!lm_xcd_map(bid, total, L)) return false;
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_off[mid] * nt <= L) lo = mid;
+    else hi = mid;
+  }
+  const int e = lo;
+  const int mte = tile_off[e + 1] - tile_off[e];
+  const int local = L - tile_off[e] * nt;
+  const int n = local / mte, mi = local - n * mte;
+  t.e = e;
+  t.m0 = offsets[e] + mi * BM;
+  t.rows = min(BM, counts[e] - mi * BM);
+  t.n0 = n * cols;
+  t.nt = n;
+  return true;
+}
+
+// --------------------------------------------------------------- gate / up
+// For the rows (routed pairs) of expert e: g = r * (pooled Wg_e^T),
+// v = r * (pooled Wu_e^T), act = silu(g) * v, with r the token's RMSNorm row
+// scale (the norm is linear in its input, so it is applied after the GEMM).
+// B tile rows: wave column wn owns rows [64 wn, 64 wn + 64): the first 32 are
+// gate rows, the next 32 the up rows of the same 32 output columns, so each
+// lane holds g and v of the same element.
+template <class Cfg_>
+struct GateUpProb {
+  using Cfg = Cfg_;
+  using E = typename Cfg::E;
+  static_assert(Cfg::TN == 2, "gate/up pairs");
+  static constexpr int kCols = Cfg::WN * 32;
+  const E* pooled;
+  const E* wg;
+  const E* wu;
+  const float* row_scale;
+  const int* perm_token;
+  const int* counts;
+  const int* offsets;
+  const int* tile_off;
+  E* act;  // [pairs, I]
+  int P, I, Ex, nt;
+
+  LM_DEV bool tile(int bid, LmTile& t) const {
+    if (!lm_group_tile(tile_off, offsets, counts, Ex, Cfg::BM, nt, kCols, bid, t)) return false;
+    t.kt0 = 0;
+    t.kt1 = P / Cfg::KT;
+    return true;
+  }
+  LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
+    const int tok = perm_token[t.m0 + min(r, t.rows - 1)];
+    return (const lm_u32x4*)(pooled + (size_t)tok * P);
+  }
+  LM_DEV const lm_u32x4* b_row(const LmTile& t, int r) const {
+    const int within = r & 63;
+    const int col = t.n0 + (r >> 6) * 32 + (within & 31);
+    const E* base = within >= 32 ? wu : wg;
+    return (const lm_u32x4*)(base + ((size_t)t.e * I + col) * P);
+  }
+  LM_DEV int a_ktile(int kt) const { return kt; }
+  LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
+                       int lane, void*) const {
+    const int col = t.n0 + wn * 32 + (lane & 31);
+#pragma unroll
+    for (int tm = 0; tm < Cfg::TM; ++tm)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
+        if (row < t.rows) {
+          const int pr = t.m0 + row;
+          const float r = row_scale[perm_token[pr]];
+          const float g = r * acc[tm][0][i];
+          const float v = r * acc[tm][1][i];
+          act[(size_t)pr * I + col] = LmElem<E>::from_f32(lm_silu(g) * v);
+        }
+      }
+  }
+};
+
+// -------------------------------------------------------------------- down
+// o = act Wd_e^T for the rows of expert e; writes o (FP32) and per row and
+// n-tile the partial sum of o^2 for the per-expert RMSNorm.
+template <class Cfg_>
+struct DownProb {
+  using Cfg = Cfg_;
+  using E = typename Cfg::E;
+  const E* act;
+  const E* wd;
+  const int* counts;
+  const int* offsets;
+  const int* tile_off;
+  float* out;  // [pairs, P]
+  float* ssq;  // [pairs, nt]
+  int P, I, Ex, nt;
+
+  LM_DEV bool tile(int bid, LmTile& t) const {
+    if (!lm_group_tile(tile_off, offsets, counts, Ex, Cfg::BM, nt, Cfg::BN, bid, t)) return false;
+    t.kt0 = 0;
+    t.kt1 = I / Cfg::KT;
+    return true;
+  }
+  LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
+    return (const lm_u32x4*)(act + (size_t)(t.m0 + min(r, t.rows - 1)) * I);
+  }
+  LM_DEV const lm_u32x4* b_row(const LmTile& t, int r) const {
+    return (const lm_u32x4*)(wd + ((size_t)t.e * P + min(t.n0 + r, P - 1)) * I);
+  }
+  LM_DEV int a_ktile(int kt) const { return kt; }
+  LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
+                       int lane, void* smem) const {
+    float* red = (float*)smem;
+    lm_tile_row_ssq<Cfg>(acc, wm, wn, lane, P - t.n0, red, [](float v, int, int) { return v; });
+    if ((int)threadIdx.x < t.rows)
+      ssq[(size_t)(t.m0 + threadIdx.x) * nt + t.nt] = red[Cfg::WN * Cfg::BM + threadIdx.x];
+#pragma unroll
+    for (int tn = 0; tn < Cfg::TN; ++tn) {
+      const int col = t.n0 + lm_acc_col<Cfg>(wn, tn, lane);
+      if (col >= P) continue;
+#pragma unroll
+      for (int tm = 0; tm < Cfg::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
+          if (row < t.rows) out[(size_t)(t.m0 + row) * P + col] = acc[tm][tn][i];
+        }
+    }
+  }
+};
+
+// ---------------------------------------------------------------- unpooler
+template <class Cfg_>
+struct UnpoolerProb {
+  using Cfg = Cfg_;
+  using E = typename Cfg::E;
+  const E* y;
+  const E* w;
+  float* out;  // [T, H]
+  int T, H, P, mt, nt;
+
+  LM_DEV bool tile(int bid, LmTile& t) const {
+    int L;
+    if (!lm_xcd_map(bid, mt * nt, L)) return false;
+    int m, n;
+    lm_dense_order(L, mt, nt, 8, m, n);
+    t.m0 = m * Cfg::BM;
+    t.rows = min(Cfg::BM, T - t.m0);
+    t.n0 = n * Cfg::BN;
+    t.nt = n;
+    t.e = 0;
+    t.kt0 = 0;
+    t.kt1 = P / Cfg::KT;
+    return true;
+  }
+  LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
+    return (const lm_u32x4*)(y + (size_t)(t.m0 + min(r, t.rows - 1)) * P);
+  }
+  LM_DEV const lm_u32x4* b_row(const LmTile& t, int r) const {
+    return (const lm_u32x4*)(w + (size_t)min(t.n0 + r, H - 1) * P);
+  }
+  LM_DEV int a_ktile(int kt) const { return kt; }
+  LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
+                       int lane, void*) const {
+#pragma unroll
+    for (int tn = 0; tn < Cfg::TN; ++tn) {
+      const int col = t.n0 + lm_acc_col<Cfg>(wn, tn, lane);
+      if (col >= H) continue;
+#pragma unroll
+      for (int tm = 0; tm < Cfg::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
+          if (row < t.rows) out[(size_t)(t.m0 + row) * H + col] = acc[tm][tn][i];
+        }
+    }
+  }
+};
+
+// ------------------------------------------------------------ small kernels
+
+__global__ void lm_fill_i32_kernel(int* p, int n, int v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Exact split of FP32 router weights into three BF16 pieces (w = b1 + b2 + b3
+// exactly for normal inputs: each remainder is exactly representable and the
+// third piece holds at most 8 significant bits). Layout [E, 3H]: piece q of
+// row e at columns [q H, (q+1) H).
+__global__ void lm_split_router_kernel(const float* w, uint16_t* w3, int E, int H) {
+  const size_t n = (size_t)E * H;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t e = i / H, h = i - e * H;
+    const float f = w[i];
+    const uint16_t b1 = lm_f32_to_bf16(f);
+    const float r1 = f - lm_bf16_to_f32(b1);
+    const uint16_t b2 = lm_f32_to_bf16(r1);
+    const float r2 = r1 - lm_bf16_to_f32(b2);
+    const uint16_t b3 = lm_f32_to_bf16(r2);
+    uint16_t* row = w3 + e * 3 * (size_t)H;
+    row[h] = b1;
+    row[H + h] = b2;
+    row[2 * H + h] = b3;
+  }
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger key).
+LM_DEV uint32_t lm_ord(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+LM_DEV float lm_unord(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+LM_DEV uint64_t lm_wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
+    const uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// One wavefront per token: sum the k-split partial logits in a fixed order
+// (FP64), add the bias, round once to FP32, pick the top k by (logit desc, index asc) and take the
+// softmax over them. Counts routed pairs per expert (LDS histogram per block,
+// one integer atomic per expert and block).
+template <int NV>
+__global__ __launch_bounds__(256) void lm_topk_kernel(const double* part, int splits, int T, int E,
+                                                      const float* bias, int k, float* logits,
+                                                      int* ids, float* wts, int* counts) {
+  __shared__ int hist[1024];
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int i = tid; i < E; i += 256) hist[i] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * 4 + (tid >> 6);
+  if (t < T) {
+    uint64_t key[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int e = lane + 64 * v;
+      key[v] = 0;
+      if (e < E) {
+        double sd = 0.0;
+        for (int sp = 0; sp < splits; ++sp) sd += part[((size_t)sp * T + t) * E + e];
+        if (bias) sd += (double)bias[e];
+        float s = (float)sd + 0.0f;  // one rounding to FP32; -0 -> +0
+        logits[(size_t)t * E + e] = s;
+        key[v] = ((uint64_t)lm_ord(s) << 32) | (uint32_t)(~(uint32_t)e);
+      }
+    }
+    float selv[16];
+    int seli[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < k) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) best = key[v] > best ? key[v] : best;
+        best = lm_wave_max_u64(best);
+        const int e = (int)(~(uint32_t)best);
+        selv[j] = lm_unord((uint32_t)(best >> 32));
+        seli[j] = e;
+        if ((e & 63) == lane) {
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            if (v == (e >> 6)) key[v] = 0;
+        }
+      }
+    }
+    float ex[16];
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < k) {
+        ex[j] = expf(selv[j] - selv[0]);
+        sum += ex[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < k && j == lane) {
+        ids[(size_t)t * k + j] = seli[j];
+        wts[(size_t)t * k + j] = ex[j] / sum;
+        atomicAdd(&hist[seli[j]], 1);
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < E; i += 256)
+    if (hist[i]) atomicAdd(&counts[i], hist[i]);
+}
+
+// Exclusive block-wide prefix sum over 256 threads (deterministic).
+LM_DEV int lm_block_exscan(int v, int* sbuf, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += n;
+  }
+  if (lane == 63) sbuf[wave] = inc;
+  __syncthreads();
+  int woff = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int s = sbuf[w];
+    woff += w < wave ? s : 0;
+    total += s;
+  }
+  __syncthreads();
+  return woff + inc - v;
+}
+
+// One workgroup per expert: its offset and first tile index (prefix over
+// lower experts), then a stable scatter of its routed pairs, in (t, j) order,
+// into the grouped order. Writes perm_token (grouped row -> token) and
+// pair_row (pair t*k+j -> grouped row).
+__global__ __launch_bounds__(256) void lm_permute_kernel(const int* ids, int npairs, int k,
+                                                         const int* counts, int E, int bm,
+                                                         int* offsets, int* tile_off,
+                                                         int* perm_token, int* pair_row) {
+  __shared__ int sbuf[8];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  int a = 0, b = 0;
+  for (int i = tid; i < e; i += 256) {
+    const int c = counts[i];
+    a += c;
+    b += (c + bm - 1) / bm;
+  }
+  int ta, tb;
+  lm_block_exscan(a, sbuf, ta);
+  lm_block_exscan(b, sbuf, tb);
+  const int off = ta, tbase = tb;
+  const int cnt = counts[e];
+  if (tid == 0) {
+    offsets[e] = off;
+    tile_off[e] = tbase;
+    if (e == E - 1) {
+      offsets[E] = off + cnt;
+      tile_off[E] = tbase + (cnt + bm - 1) / bm;
+    }
+  }
+  if (cnt == 0) return;
+  int base = 0;
+  for (int start = 0; start < npairs; start += 256 * 16) {
+    const int p0 = start + tid * 16;
+    unsigned mask = 0;
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int p = p0 + i;
+      const bool m = p < npairs && ids[p] == e;
+      mask |= (unsigned)m << i;
+      c += m;
+    }
+    int total;
+    int pos = off + base + lm_block_exscan(c, sbuf, total);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((mask >> i) & 1u) {
+        const int p = p0 + i;
+        perm_token[pos] = p / k;
+        pair_row[p] = pos;
+        ++pos;
+      }
+    }
+    base += total;
+    if (base >= cnt) break;
+  }
+}
+
+// r_t = 1 / sqrt(sum of the row's pooled partial sums of squares / P + eps).
+__global__ void lm_rowscale_kernel(const float* ssq, int nparts, int T, int P, float eps,
+                                   float* rs) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  float s = 0.0f;
+  for (int i = 0; i < nparts; ++i) s += ssq[(size_t)t * nparts + i];
+  rs[t] = 1.0f / sqrtf(s / (float)P + eps);
+}
+
+// One workgroup per token: y = sum over slots j (in order) of
+// w_j / sqrt(mean(o_j^2) + eps) * gamma_{e_j} * o_j, in FP32.
+template <typename Y>
+__global__ __launch_bounds__(256) void lm_combine_kernel(const float* O, const float* ossq,
+                                                         int nparts, const int* pair_row,
+                                                         const int* ids, const float* wts,
+                                                         const float* gamma, int k, int P,
+                                                         float eps, Y* y) {
+  __shared__ float s_coef[16];
+  __shared__ int s_row[16], s_e[16];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < k) {
+    const int p = pair_row[(size_t)t * k + tid];
+    float s = 0.0f;
+    for (int i = 0; i < nparts; ++i) s += ossq[(size_t)p * nparts + i];
+    s_coef[tid] = wts[(size_t)t * k + tid] * (1.0f / sqrtf(s / (float)P + eps));
+    s_row[tid] = p;
+    s_e[tid] = ids[(size_t)t * k + tid];
+  }
+  __syncthreads();
+  for (int c = tid * 4; c < P; c += 1024) {
+    lm_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < k; ++j) {
+      const lm_f32x4 o = *(const lm_f32x4*)(O + (size_t)s_row[j] * P + c);
+      const lm_f32x4 g = *(const lm_f32x4*)(gamma + (size_t)s_e[j] * P + c);
+      acc += s_coef[j] * (g * o);
+    }
+    if constexpr (sizeof(Y) == 4) {
+      *(lm_f32x4*)((float*)y + (size_t)t * P + c) = acc;
+    } else {
+      lm_u32x2 v;
+      v[0] = (uint32_t)lm_f32_to_bf16(acc[0]) | ((uint32_t)lm_f32_to_bf16(acc[1]) << 16);
+      v[1] = (uint32_t)lm_f32_to_bf16(acc[2]) | ((uint32_t)lm_f32_to_bf16(acc[3]) << 16);
+      *(lm_u32x2*)((uint16_t*)y + (size_t)t * P + c) = v;
+    }
+  }
+}

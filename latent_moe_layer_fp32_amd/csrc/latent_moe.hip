@@ -1,0 +1,519 @@
+// Host runtime and C ABI of the latent-MoE layer forward (see include/latent_moe.h).
+//
+// create(): validate, allocate one workspace sized by max_tokens, split the
+// FP32 router into three BF16 pieces (BF16 activations). forward(): enqueue
+// the kernel sequence on the caller's stream with no host synchronisation and
+// no allocation; per-expert tile counts stay on the device and the grouped
+// GEMMs are launched with upper-bound grids whose surplus blocks exit.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/latent_moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define LM_HIP(call)                                                                        \
+  do {                                                                                      \
+    hipError_t e_ = (call);                                                                 \
+    if (e_ != hipSuccess) return fail(LMOE_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Tile configurations: "wide" for many rows per expert (prefill-sized),
+// "narrow" for few (decode-sized).
+template <typename E> using CfgWide = LmGemmCfg<E, 2, 2, 2, 2>;
+template <typename E> using CfgNarrow = LmGemmCfg<E, 1, 4, 1, 2>;
+// Router: FP32 chains of one k-tile (64 BF16 products per lane pair), FP64 beyond.
+template <typename E> using CfgRouterWide = LmGemmCfg<E, 2, 2, 1, 2, 1>;
+template <typename E> using CfgRouterNarrow = LmGemmCfg<E, 1, 4, 1, 2, 1>;
+
+constexpr int kNarrowRowsPerExpert = 64;  // mean rows per expert below which "narrow" tiles run
+constexpr int kMinBN = 128;  // smallest BN of the tile configurations (sizes the ssq partials)
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+struct Layout {
+  size_t part, logits, ids, wts, counts, offsets, tile_off, perm_token, pair_row, pooled, pssq,
+      row_scale, act, O, ossq, y, wr3, total;
+};
+
+}  // namespace
+
+constexpr int kStages = LMOE_NUM_STAGES;
+
+struct latent_moe {
+  latent_moe_config cfg;
+  latent_moe_weights w;
+  int device;
+  char* ws;
+  Layout lay;
+  size_t part_floats;
+  bool prof;                       // record stage events in forward
+  bool prof_valid;                 // a forward has recorded a full set
+  hipEvent_t ev[kStages + 1];      // created by latent_moe_set_profiling
+};
+
+namespace {
+
+int esize_act(const latent_moe_config& c) { return c.act_dtype == LMOE_F32 ? 4 : 2; }
+int esize_exp(const latent_moe_config& c) { return c.expert_dtype == LMOE_F32 ? 4 : 2; }
+
+bool narrow_for(const latent_moe_config& c, int64_t T) {
+  return T * c.top_k < (int64_t)kNarrowRowsPerExpert * c.experts;
+}
+
+// Router k-splits: enough blocks to cover the chip, each split at least 4
+// k-tiles, all splits non-empty.
+void router_split(const latent_moe_config& c, int64_t T, int& splits, int& kt_per, int& mt,
+                  int& nt) {
+  const bool f32 = c.act_dtype == LMOE_F32;
+  const bool nar = narrow_for(c, T);
+  const int BM = nar ? 32 : 64, BN = nar ? 256 : 128;  // router tile shapes
+  const int KT = f32 ? 32 : 64;
+  const int64_t Kw = f32 ? c.hidden : 3 * c.hidden;
+  const int ktot = (int)(Kw / KT);
+  mt = ceil_div(T, BM);
+  nt = ceil_div(c.experts, BN);
+  int want = ceil_div(512, (int64_t)mt * nt);
+  int maxs = ktot / 4 > 0 ? ktot / 4 : 1;
+  splits = want < 1 ? 1 : (want > maxs ? maxs : want);
+  kt_per = ceil_div(ktot, splits);
+  splits = ceil_div(ktot, kt_per);
+}
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int validate_config(const latent_moe_config* c) {
+  if (!c) return fail(LMOE_ERR_INVALID_ARG, "config is NULL");
+  if (c->hidden <= 0 || c->pooled <= 0 || c->intermediate <= 0 || c->hidden % 64 ||
+      c->pooled % 64 || c->intermediate % 128)
+    return fail(LMOE_ERR_INVALID_ARG,
+                "hidden and pooled must be positive multiples of 64, intermediate of 128");
+  if (c->hidden > (1 << 20) || c->pooled > (1 << 20) || c->intermediate > (1 << 20))
+    return fail(LMOE_ERR_INVALID_ARG, "dimension too large");
+  if (c->experts < 1 || c->experts > 1024)
+    return fail(LMOE_ERR_INVALID_ARG, "experts must be in [1, 1024]");
+  if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->experts)
+    return fail(LMOE_ERR_INVALID_ARG, "top_k must be in [1, min(experts, 16)]");
+  if (!std::isfinite(c->eps) || c->eps < 0.0f)
+    return fail(LMOE_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (c->max_tokens < 1 || c->max_tokens * c->top_k > (1 << 28))
+    return fail(LMOE_ERR_INVALID_ARG, "max_tokens must be in [1, 2^28 / top_k]");
+  const bool act_ok = c->act_dtype == LMOE_F32 || c->act_dtype == LMOE_BF16;
+  const bool exp_ok = c->expert_dtype == LMOE_F32 || c->expert_dtype == LMOE_BF16 ||
+                      c->expert_dtype == LMOE_MXFP4;
+  if (!act_ok || !exp_ok) return fail(LMOE_ERR_INVALID_ARG, "unknown dtype code");
+  if ((c->act_dtype == LMOE_F32) != (c->expert_dtype == LMOE_F32))
+    return fail(LMOE_ERR_UNSUPPORTED, "FP32 experts need FP32 activations and vice versa");
+  if (c->expert_dtype == LMOE_MXFP4)
+    return fail(LMOE_ERR_UNSUPPORTED, "MXFP4 expert weights are not built into this library");
+  if ((size_t)c->pooled * c->intermediate * c->experts > ((size_t)1 << 40))
+    return fail(LMOE_ERR_INVALID_ARG, "expert tensors too large");
+  return LMOE_OK;
+}
+
+Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
+  const int64_t Tm = c.max_tokens, k = c.top_k, E = c.experts, P = c.pooled, I = c.intermediate;
+  const int64_t Mp = Tm * k;
+  // largest router partial buffer over T in [1, Tm]; beyond 65536 tokens a
+  // single split covers the chip, so T = Tm bounds the rest
+  size_t pf = 0;
+  const int64_t scan = Tm < 65536 ? Tm : 65536;
+  for (int64_t T = 1; T <= scan + 1; ++T) {
+    const int64_t TT = T <= scan ? T : Tm;
+    int s, kp, mt, nt;
+    router_split(c, TT, s, kp, mt, nt);
+    const size_t need = (size_t)s * TT * E;
+    if (need > pf) pf = need;
+  }
+  *part_floats = pf;
+  const int parts = ceil_div(P, kMinBN);  // n-tiles of the pooler / down GEMMs
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += up256(bytes);
+    return at;
+  };
+  L.part = take(pf * 8);
+  L.logits = take((size_t)Tm * E * 4);
+  L.ids = take((size_t)Mp * 4);
+  L.wts = take((size_t)Mp * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.tile_off = take((size_t)(E + 1) * 4);
+  L.perm_token = take((size_t)Mp * 4);
+  L.pair_row = take((size_t)Mp * 4);
+  L.pooled = take((size_t)Tm * P * esize_act(c));
+  L.pssq = take((size_t)Tm * parts * 4);
+  L.row_scale = take((size_t)Tm * 4);
+  L.act = take((size_t)Mp * I * esize_exp(c));
+  L.O = take((size_t)Mp * P * 4);
+  L.ossq = take((size_t)Mp * parts * 4);
+  L.y = take((size_t)Tm * P * esize_act(c));
+  L.wr3 = take(c.act_dtype == LMOE_BF16 ? (size_t)E * 3 * c.hidden * 2 : 0);
+  L.total = o;
+  return L;
+}
+
+template <class Prob>
+hipError_t launch(const Prob& p, int64_t units, hipStream_t s) {
+  if (units <= 0) return hipSuccess;
+  const int64_t g = (units + 7) / 8 * 8;
+  hipLaunchKernelGGL(lm_gemm_kernel<Prob>, dim3((unsigned)g), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+#define LM_MARK(i)                                       \
+  do {                                                   \
+    if (h->prof) LM_HIP(hipEventRecord(h->ev[(i)], s));  \
+  } while (0)
+
+template <typename Et, template <typename> class CW, template <typename> class CR>
+int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_t s) {
+  const latent_moe_config& c = h->cfg;
+  const latent_moe_weights& w = h->w;
+  const Layout& L = h->lay;
+  char* ws = h->ws;
+  const int E = (int)c.experts, k = c.top_k, H = (int)c.hidden, P = (int)c.pooled,
+            I = (int)c.intermediate;
+  const int npairs = (int)(T * k);
+  using Cw = CW<Et>;
+  using Cr = CR<Et>;
+  double* part = (double*)(ws + L.part);
+  float* logits = (float*)(ws + L.logits);
+  int* ids = (int*)(ws + L.ids);
+  float* wts = (float*)(ws + L.wts);
+  int* counts = (int*)(ws + L.counts);
+  int* offsets = (int*)(ws + L.offsets);
+  int* tile_off = (int*)(ws + L.tile_off);
+  int* perm_token = (int*)(ws + L.perm_token);
+  int* pair_row = (int*)(ws + L.pair_row);
+  Et* pooled = (Et*)(ws + L.pooled);
+  float* pssq = (float*)(ws + L.pssq);
+  float* row_scale = (float*)(ws + L.row_scale);
+  Et* act = (Et*)(ws + L.act);
+  float* O = (float*)(ws + L.O);
+  float* ossq = (float*)(ws + L.ossq);
+  Et* y = (Et*)(ws + L.y);
+
+  LM_MARK(0);
+  // 1. router: partial logits over k-splits
+  {
+    int splits, kt_per, mt, nt;
+    router_split(c, T, splits, kt_per, mt, nt);
+    RouterProb<Cr> p;
+    p.x = (const Et*)x;
+    p.w = sizeof(Et) == 2 ? (const Et*)(ws + L.wr3) : (const Et*)w.router;
+    p.part = part;
+    p.T = (int)T;
+    p.Ew = E;
+    p.H = H;
+    p.Kw = sizeof(Et) == 2 ? 3 * H : H;
+    p.kta = H / Cr::KT;
+    p.mt = mt;
+    p.nt = nt;
+    p.splits = splits;
+    p.kt_per = kt_per;
+    LM_HIP(launch(p, (int64_t)mt * nt * splits, s));
+    LM_MARK(1);
+    // 2. top-k + softmax + per-expert counts
+    hipLaunchKernelGGL(lm_fill_i32_kernel, dim3(ceil_div(E, 256)), dim3(256), 0, s, counts, E, 0);
+    const dim3 g(ceil_div(T, 4));
+    if (E <= 64)
+      hipLaunchKernelGGL(lm_topk_kernel<1>, g, dim3(256), 0, s, part, splits, (int)T, E, w.router_bias, k, logits, ids, wts, counts);
+    else if (E <= 128)
+      hipLaunchKernelGGL(lm_topk_kernel<2>, g, dim3(256), 0, s, part, splits, (int)T, E, w.router_bias, k, logits, ids, wts, counts);
+    else if (E <= 256)
+      hipLaunchKernelGGL(lm_topk_kernel<4>, g, dim3(256), 0, s, part, splits, (int)T, E, w.router_bias, k, logits, ids, wts, counts);
+    else if (E <= 512)
+      hipLaunchKernelGGL(lm_topk_kernel<8>, g, dim3(256), 0, s, part, splits, (int)T, E, w.router_bias, k, logits, ids, wts, counts);
+    else
+      hipLaunchKernelGGL(lm_topk_kernel<16>, g, dim3(256), 0, s, part, splits, (int)T, E, w.router_bias, k, logits, ids, wts, counts);
+    LM_HIP(hipGetLastError());
+  }
+  LM_MARK(2);
+  // 3. grouping by expert
+  hipLaunchKernelGGL(lm_permute_kernel, dim3(E), dim3(256), 0, s, ids, npairs, k, counts, E, Cw::BM,
+                     offsets, tile_off, perm_token, pair_row);
+  LM_HIP(hipGetLastError());
+  LM_MARK(3);
+  // 4. pooler + norm statistics
+  const int pnt = ceil_div(P, Cw::BN);
+  {
+    PoolerProb<Cw> p;
+    p.x = (const Et*)x;
+    p.w = (const Et*)w.pooler;
+    p.gamma = w.pool_gamma;
+    p.pooled = pooled;
+    p.ssq = pssq;
+    p.T = (int)T;
+    p.H = H;
+    p.P = P;
+    p.mt = ceil_div(T, Cw::BM);
+    p.nt = pnt;
+    LM_HIP(launch(p, (int64_t)p.mt * p.nt, s));
+  }
+  LM_MARK(4);
+  hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, pssq, pnt, (int)T,
+                     P, c.eps, row_scale);
+  LM_HIP(hipGetLastError());
+  LM_MARK(5);
+  const int64_t max_tiles = ceil_div(npairs, Cw::BM) + (npairs < E ? npairs : E);
+  // 5. gate/up + SwiGLU
+  {
+    GateUpProb<Cw> p;
+    p.pooled = pooled;
+    p.wg = (const Et*)w.w_gate;
+    p.wu = (const Et*)w.w_up;
+    p.row_scale = row_scale;
+    p.perm_token = perm_token;
+    p.counts = counts;
+    p.offsets = offsets;
+    p.tile_off = tile_off;
+    p.act = act;
+    p.P = P;
+    p.I = I;
+    p.Ex = E;
+    p.nt = I / GateUpProb<Cw>::kCols;
+    LM_HIP(launch(p, max_tiles * p.nt, s));
+  }
+  LM_MARK(6);
+  // 6. down + per-row sum of squares partials
+  const int dnt = ceil_div(P, Cw::BN);
+  {
+    DownProb<Cw> p;
+    p.act = act;
+    p.wd = (const Et*)w.w_down;
+    p.counts = counts;
+    p.offsets = offsets;
+    p.tile_off = tile_off;
+    p.out = O;
+    p.ssq = ossq;
+    p.P = P;
+    p.I = I;
+    p.Ex = E;
+    p.nt = dnt;
+    LM_HIP(launch(p, max_tiles * p.nt, s));
+  }
+  LM_MARK(7);
+  // 7. per-expert norm, routing weight, FP32 sum
+  hipLaunchKernelGGL(lm_combine_kernel<Et>, dim3((unsigned)T), dim3(256), 0, s, O, ossq, dnt, pair_row,
+                     ids, wts, w.expert_gamma, k, P, c.eps, y);
+  LM_HIP(hipGetLastError());
+  LM_MARK(8);
+  // 8. unpooler
+  {
+    UnpoolerProb<Cw> p;
+    p.y = y;
+    p.w = (const Et*)w.unpooler;
+    p.out = out;
+    p.T = (int)T;
+    p.H = H;
+    p.P = P;
+    p.mt = ceil_div(T, Cw::BM);
+    p.nt = ceil_div(H, Cw::BN);
+    LM_HIP(launch(p, (int64_t)p.mt * p.nt, s));
+  }
+  LM_MARK(9);
+  if (h->prof) h->prof_valid = true;
+  return LMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* latent_moe_last_error(void) { return g_err.c_str(); }
+
+int latent_moe_workspace_bytes(const latent_moe_config* cfg, size_t* bytes) {
+  g_err.clear();
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!bytes) return fail(LMOE_ERR_INVALID_ARG, "bytes is NULL");
+  size_t pf;
+  *bytes = make_layout(*cfg, &pf).total;
+  return LMOE_OK;
+}
+
+int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const latent_moe_weights* w) {
+  g_err.clear();
+  if (!out) return fail(LMOE_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!w) return fail(LMOE_ERR_INVALID_ARG, "weights is NULL");
+  const void* req[] = {w->router, w->pooler, w->pool_gamma, w->w_gate, w->w_up,
+                       w->w_down, w->expert_gamma, w->unpooler};
+  const char* names[] = {"router", "pooler", "pool_gamma", "w_gate", "w_up",
+                         "w_down", "expert_gamma", "unpooler"};
+  for (int i = 0; i < 8; ++i) {
+    if (!req[i]) return fail(LMOE_ERR_INVALID_ARG, "weight %s is NULL", names[i]);
+    if (!aligned16(req[i])) return fail(LMOE_ERR_INVALID_ARG, "weight %s is not 16-byte aligned", names[i]);
+  }
+  if (w->router_bias && !aligned16(w->router_bias))
+    return fail(LMOE_ERR_INVALID_ARG, "router_bias is not 16-byte aligned");
+
+  int ndev = 0;
+  hipError_t he = hipGetDeviceCount(&ndev);
+  if (he != hipSuccess || ndev == 0)
+    return fail(LMOE_ERR_HIP, "no HIP device available (%s)", hipGetErrorString(he));
+  int dev = 0;
+  LM_HIP(hipGetDevice(&dev));
+
+  latent_moe* h = new (std::nothrow) latent_moe();
+  if (!h) return fail(LMOE_ERR_OOM, "host allocation failed");
+  h->cfg = *cfg;
+  h->w = *w;
+  h->device = dev;
+  h->lay = make_layout(*cfg, &h->part_floats);
+  he = hipMalloc((void**)&h->ws, h->lay.total);
+  if (he != hipSuccess) {
+    delete h;
+    (void)hipGetLastError();
+    return fail(LMOE_ERR_OOM, "hipMalloc of %zu workspace bytes failed: %s", h->lay.total,
+                hipGetErrorString(he));
+  }
+  if (cfg->act_dtype == LMOE_BF16) {
+    const size_t n = (size_t)cfg->experts * cfg->hidden;
+    unsigned blocks = (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
+    hipLaunchKernelGGL(lm_split_router_kernel, dim3(blocks), dim3(256), 0, 0, w->router,
+                       (uint16_t*)(h->ws + h->lay.wr3), (int)cfg->experts, (int)cfg->hidden);
+    he = hipGetLastError();
+    if (he == hipSuccess) he = hipDeviceSynchronize();
+    if (he != hipSuccess) {
+      (void)hipFree(h->ws);
+      delete h;
+      return fail(LMOE_ERR_HIP, "router split failed: %s", hipGetErrorString(he));
+    }
+  }
+  *out = h;
+  return LMOE_OK;
+}
+
+int latent_moe_forward(latent_moe_t* h, const void* x, int64_t T, float* out, int32_t* topk_ids,
+                       float* topk_weights, void* stream) {
+  g_err.clear();
+  if (!h) return fail(LMOE_ERR_INVALID_ARG, "handle is NULL");
+  if (T < 0) return fail(LMOE_ERR_INVALID_ARG, "T must be >= 0");
+  if (T > h->cfg.max_tokens)
+    return fail(LMOE_ERR_TOO_MANY_TOKENS, "T=%lld exceeds max_tokens=%lld", (long long)T,
+                (long long)h->cfg.max_tokens);
+  if (T == 0) return LMOE_OK;
+  if (!x || !out) return fail(LMOE_ERR_INVALID_ARG, "x and out must be non-NULL");
+  if (!aligned16(x) || !aligned16(out) || (topk_ids && !aligned16(topk_ids)) ||
+      (topk_weights && !aligned16(topk_weights)))
+    return fail(LMOE_ERR_INVALID_ARG, "x, out, topk_ids and topk_weights must be 16-byte aligned");
+  int cur = -1;
+  LM_HIP(hipGetDevice(&cur));
+  if (cur != h->device) LM_HIP(hipSetDevice(h->device));
+  hipStream_t s = (hipStream_t)stream;
+  int rc;
+  const bool nar = narrow_for(h->cfg, T);
+  if (h->cfg.act_dtype == LMOE_F32)
+    rc = nar ? forward_impl<float, CfgNarrow, CfgRouterNarrow>(h, x, T, out, s)
+             : forward_impl<float, CfgWide, CfgRouterWide>(h, x, T, out, s);
+  else
+    rc = nar ? forward_impl<uint16_t, CfgNarrow, CfgRouterNarrow>(h, x, T, out, s)
+             : forward_impl<uint16_t, CfgWide, CfgRouterWide>(h, x, T, out, s);
+  if (rc == LMOE_OK) {
+    const size_t nk = (size_t)T * h->cfg.top_k;
+    if (topk_ids)
+      rc = hipMemcpyAsync(topk_ids, h->ws + h->lay.ids, nk * 4, hipMemcpyDeviceToDevice, s) == hipSuccess
+               ? LMOE_OK : fail(LMOE_ERR_HIP, "copy of topk_ids failed");
+    if (rc == LMOE_OK && topk_weights)
+      rc = hipMemcpyAsync(topk_weights, h->ws + h->lay.wts, nk * 4, hipMemcpyDeviceToDevice, s) == hipSuccess
+               ? LMOE_OK : fail(LMOE_ERR_HIP, "copy of topk_weights failed");
+  }
+  if (cur != h->device) (void)hipSetDevice(cur);
+  return rc;
+}
+
+int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v) {
+  g_err.clear();
+  if (!h || !v) return fail(LMOE_ERR_INVALID_ARG, "handle and views must be non-NULL");
+  char* ws = h->ws;
+  const Layout& L = h->lay;
+  v->logits = (const float*)(ws + L.logits);
+  v->ids = (const int32_t*)(ws + L.ids);
+  v->weights = (const float*)(ws + L.wts);
+  v->counts = (const int32_t*)(ws + L.counts);
+  v->offsets = (const int32_t*)(ws + L.offsets);
+  v->perm_token = (const int32_t*)(ws + L.perm_token);
+  v->pair_row = (const int32_t*)(ws + L.pair_row);
+  v->pooled = ws + L.pooled;
+  v->row_scale = (const float*)(ws + L.row_scale);
+  v->act = ws + L.act;
+  v->expert_out = (const float*)(ws + L.O);
+  v->combined = ws + L.y;
+  return LMOE_OK;
+}
+
+int latent_moe_set_profiling(latent_moe_t* h, int enable) {
+  g_err.clear();
+  if (!h) return fail(LMOE_ERR_INVALID_ARG, "handle is NULL");
+  if (enable && !h->ev[0]) {
+    for (int i = 0; i <= kStages; ++i) {
+      hipError_t e = hipEventCreate(&h->ev[i]);
+      if (e != hipSuccess) {
+        for (int j = 0; j < i; ++j) {
+          (void)hipEventDestroy(h->ev[j]);
+          h->ev[j] = nullptr;
+        }
+        return fail(LMOE_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+      }
+    }
+  }
+  h->prof = enable != 0;
+  h->prof_valid = false;
+  return LMOE_OK;
+}
+
+int latent_moe_stage_times(latent_moe_t* h, float* ms, int n) {
+  g_err.clear();
+  if (!h || !ms || n < kStages) return fail(LMOE_ERR_INVALID_ARG, "need a handle and %d floats", kStages);
+  if (!h->prof || !h->prof_valid)
+    return fail(LMOE_ERR_INVALID_ARG, "no profiled forward since profiling was enabled");
+  LM_HIP(hipEventSynchronize(h->ev[kStages]));
+  for (int i = 0; i < kStages; ++i) LM_HIP(hipEventElapsedTime(&ms[i], h->ev[i], h->ev[i + 1]));
+  return LMOE_OK;
+}
+
+int latent_moe_destroy(latent_moe_t* h) {
+  g_err.clear();
+  if (!h) return fail(LMOE_ERR_INVALID_ARG, "handle is NULL");
+  int cur = -1;
+  (void)hipGetDevice(&cur);
+  (void)hipSetDevice(h->device);
+  hipError_t e1 = hipDeviceSynchronize();
+  hipError_t e2 = hipFree(h->ws);
+  for (int i = 0; i <= kStages; ++i)
+    if (h->ev[i]) (void)hipEventDestroy(h->ev[i]);
+  if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
+  delete h;
+  if (e1 != hipSuccess || e2 != hipSuccess)
+    return fail(LMOE_ERR_HIP, "destroy: %s", hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+  return LMOE_OK;
+}
+
+}  // extern "C"

@@ -150,6 +150,11 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
+        # bind to torch's HIP runtime when torch drives the device memory
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(LIB_PATH):
             build()
         L = ctypes.CDLL(LIB_PATH)

@@ -1,0 +1,101 @@
+"""C ABI surface: the library loads, exports what the header declares, and
+rejects bad arguments on the host before touching a device."""
+import ctypes
+
+import pytest
+
+from latent_moe_layer_fp32_amd import binding as B
+
+
+def _has_device() -> bool:
+    try:
+        import torch
+
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def real_cfg(**kw):
+    d = dict(hidden=8192, pooled=4096, experts=256, intermediate=4096, top_k=8, eps=1e-6,
+             act_dtype="bf16", expert_dtype="bf16", max_tokens=16384)
+    d.update(kw)
+    return B.make_config(**d)
+
+
+def test_library_exports_every_header_symbol():
+    syms = B.header_symbols()
+    assert {"latent_moe_create", "latent_moe_forward", "latent_moe_destroy",
+            "latent_moe_last_error"} <= set(syms)
+    L = B.lib()
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_workspace_bytes_real_shapes():
+    n = B.latent_moe_workspace_bytes(real_cfg())
+    # pooled/combined BF16 [T,P] x2, act BF16 [T*k, I], expert out FP32 [T*k, P] ...
+    T, k, P, I = 16384, 8, 4096, 4096
+    floor = T * k * I * 2 + T * k * P * 4 + 2 * T * P * 2
+    assert floor <= n <= floor * 1.2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=100), B.LMOE_ERR_INVALID_ARG),
+    (dict(intermediate=192), B.LMOE_ERR_INVALID_ARG),
+    (dict(pooled=0), B.LMOE_ERR_INVALID_ARG),
+    (dict(experts=0), B.LMOE_ERR_INVALID_ARG),
+    (dict(experts=2000), B.LMOE_ERR_INVALID_ARG),
+    (dict(top_k=0), B.LMOE_ERR_INVALID_ARG),
+    (dict(top_k=17), B.LMOE_ERR_INVALID_ARG),
+    (dict(experts=4, top_k=5), B.LMOE_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), B.LMOE_ERR_INVALID_ARG),
+    (dict(eps=-1.0), B.LMOE_ERR_INVALID_ARG),
+    (dict(max_tokens=0), B.LMOE_ERR_INVALID_ARG),
+    (dict(act_dtype=7), B.LMOE_ERR_INVALID_ARG),
+    (dict(act_dtype="f32", expert_dtype="bf16"), B.LMOE_ERR_UNSUPPORTED),
+])
+def test_bad_configs_rejected(kw, code):
+    with pytest.raises(B.LatentMoEError) as ei:
+        B.latent_moe_workspace_bytes(real_cfg(**kw))
+    assert ei.value.code == code
+    assert B.latent_moe_last_error()
+
+
+def test_create_rejects_null_and_misaligned_weights():
+    L = B.lib()
+    cfg = real_cfg()
+    h = ctypes.c_void_p(123)
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), None) == B.LMOE_ERR_INVALID_ARG
+    assert h.value is None  # *out cleared on failure
+    w = B.Weights()
+    for n in ("router", "pooler", "pool_gamma", "w_gate", "w_up", "w_down", "expert_gamma", "unpooler"):
+        setattr(w, n, 4096)
+    w.pooler = None
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+    assert "pooler" in B.latent_moe_last_error()
+    w.pooler = 4096 + 8
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+    assert "aligned" in B.latent_moe_last_error()
+    assert L.latent_moe_create(None, ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(_has_device(), reason="checks the no-device error path")
+def test_create_without_device_reports_hip_error():
+    L = B.lib()
+    cfg = real_cfg()
+    w = B.Weights()
+    for n in ("router", "pooler", "pool_gamma", "w_gate", "w_up", "w_down", "expert_gamma", "unpooler"):
+        setattr(w, n, 4096)
+    h = ctypes.c_void_p(0)
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_HIP
+    assert "device" in B.latent_moe_last_error()
+
+
+def test_null_handle_calls():
+    L = B.lib()
+    assert L.latent_moe_forward(None, None, 1, None, None, None, None) == B.LMOE_ERR_INVALID_ARG
+    assert L.latent_moe_destroy(None) == B.LMOE_ERR_INVALID_ARG
+    v = B.Views()
+    assert L.latent_moe_debug_views(None, ctypes.byref(v)) == B.LMOE_ERR_INVALID_ARG
+    assert B.latent_moe_last_error()

@@ -1,0 +1,256 @@
+"""Parity of the HIP path against the FP64 oracle, through the C ABI.
+
+Tiny FP32 layer: every token, every stage. Real shapes (H=8192, P=4096,
+E=256, I=4096, k=8, BF16): routing on every token, outputs and stage
+intermediates on sampled tokens (the layer is token-local, so the oracle on a
+token subset is exact for those rows).
+
+Tolerances: routing ids bit-exact except reported near-ties (< 1e-6 apart in
+the FP64 logits), routing weights within 1e-6; outputs max-abs <= 2e-2 x RMS
+(BF16), <= 1e-4 x RMS for the FP32 layer (its expected error is ~1e-6).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from layer_cases import (HostLayer, bf16_to_f64, check_output, check_rel_l2, check_routing,
+                         device_weights, make_layer)
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+TOL_F32 = 1e-4
+STAGE_L2 = 1e-2  # relative L2 bound for BF16 intermediates (expected ~1e-3)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    return torch
+
+
+@pytest.fixture(scope="module")
+def tables(torch_dev):
+    return synth.DeviceTables("cuda:0")
+
+
+def run_layer(torch, layer, x):
+    T = x.shape[0]
+    k = layer.top_k
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    out = layer.forward(x, topk_ids=ids, topk_weights=w)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+
+
+# --------------------------------------------------------------- tiny FP32
+
+
+@pytest.fixture(scope="module")
+def tiny(torch_dev, tables):
+    spec = synth.CONFIGS["tiny"]
+    wts = device_weights(spec, tables)
+    layer = make_layer(spec, wts, max_tokens=spec.T)
+    host = HostLayer(spec)
+    yield spec, wts, layer, host
+    layer.close()
+
+
+def test_device_generator_matches_host(torch_dev, tables):
+    spec = synth.CONFIGS["tiny"]
+    for name in ("x", "router", "w_down", "expert_gamma"):
+        d = synth.device_tensor(spec, name, tables).cpu().numpy()
+        assert np.array_equal(d, synth.host(spec, name)), name
+    s2 = synth.CONFIGS["decode"].with_(E=2, I=128, P=256, H=512)
+    d = synth.device_tensor(s2, "w_gate", tables).view(torch_dev.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(d, synth.host(s2, "w_gate"))
+    s3 = s2.with_(expert_format="mxfp4")
+    dp, ds = synth.device_tensor(s3, "w_up", tables)
+    hp, hs = synth.host(s3, "w_up")
+    assert np.array_equal(dp.cpu().numpy(), hp) and np.array_equal(ds.cpu().numpy(), hs)
+
+
+def test_tiny_full_parity(torch_dev, tiny):
+    torch = torch_dev
+    spec, _, layer, host = tiny
+    say("case: tiny FP32, T=64")
+    x = synth.device_tensor(spec, "x", synth.DeviceTables("cuda:0"))
+    out, ids, w = run_layer(torch, layer, x)
+    v = layer.views(spec.T)
+    xh = host.x()
+    r = host.oracle(xh)
+    # routing
+    near, _ = check_routing(ids, w, r.logits, spec.k)
+    assert not near
+    assert np.abs(v["logits"] - r.logits).max() < 1e-5
+    # grouping: stable by expert
+    order = np.argsort(ids.ravel(), kind="stable")
+    assert np.array_equal(v["perm_token"], order // spec.k)
+    assert np.array_equal(v["pair_row"][order], np.arange(spec.T * spec.k))
+    assert np.array_equal(v["counts"], np.bincount(ids.ravel(), minlength=spec.E))
+    # stages
+    u = v["pooled"].astype(np.float64) * v["row_scale"][:, None]
+    check_output(u, r.u, 1e-5, "u")
+    pr = v["pair_row"].reshape(spec.T, spec.k)
+    check_output(v["act"][pr], r.a, 1e-5, "act")
+    check_output(v["expert_out"][pr], r.o, 1e-5, "expert out")
+    check_output(v["combined"], r.y, 1e-5, "y")
+    e = check_output(out, r.out, TOL_F32)
+    say(f"tiny: max-abs/RMS = {e:.3g}")
+
+
+@pytest.mark.parametrize("T", [1, 3, 33, 63])
+def test_tiny_ragged_token_counts(torch_dev, tiny, T):
+    torch = torch_dev
+    spec, _, layer, host = tiny
+    say(f"case: tiny FP32 ragged T={T}")
+    x = synth.device_tensor(spec, "x", synth.DeviceTables("cuda:0"))[:T].contiguous()
+    out, ids, w = run_layer(torch, layer, x)
+    r = host.oracle(host.x()[:T])
+    check_routing(ids, w, r.logits, spec.k)
+    check_output(out, r.out, TOL_F32)
+
+
+def test_tiny_empty_and_errors(torch_dev, tiny):
+    torch = torch_dev
+    from latent_moe_layer_fp32_amd import binding as B
+
+    spec, _, layer, _ = tiny
+    x = torch.zeros((0, spec.H), dtype=torch.float32, device="cuda:0")
+    out = layer.forward(x)
+    assert out.shape == (0, spec.H)
+    xb = torch.zeros((spec.T + 1, spec.H), dtype=torch.float32, device="cuda:0")
+    with pytest.raises(B.LatentMoEError) as ei:
+        layer.forward(xb)
+    assert ei.value.code == B.LMOE_ERR_TOO_MANY_TOKENS
+    buf = torch.zeros((spec.T * spec.H + 4,), dtype=torch.float32, device="cuda:0")
+    with pytest.raises(B.LatentMoEError) as ei:
+        B.latent_moe_forward(layer.handle, buf.data_ptr(), 4, buf.data_ptr() + 4, None, None, None)
+    assert ei.value.code == B.LMOE_ERR_INVALID_ARG
+
+
+def test_tiny_determinism_and_token_equivariance(torch_dev, tiny):
+    torch = torch_dev
+    spec, _, layer, _ = tiny
+    say("case: tiny determinism / permutation")
+    x = synth.device_tensor(spec, "x", synth.DeviceTables("cuda:0"))
+    o1, i1, w1 = run_layer(torch, layer, x)
+    o2, i2, w2 = run_layer(torch, layer, x)
+    assert np.array_equal(o1, o2) and np.array_equal(i1, i2) and np.array_equal(w1, w2)
+    perm = np.random.default_rng(3).permutation(spec.T)
+    xp = x[torch.from_numpy(perm).to(x.device)].contiguous()
+    op, ip, wp = run_layer(torch, layer, xp)
+    assert np.array_equal(ip, i1[perm])
+    assert np.array_equal(wp, w1[perm])
+    assert np.array_equal(op, o1[perm])
+
+
+def test_tiny_zero_input(torch_dev, tiny):
+    torch = torch_dev
+    spec, _, layer, _ = tiny
+    x = torch.zeros((5, spec.H), dtype=torch.float32, device="cuda:0")
+    out, ids, w = run_layer(torch, layer, x)
+    assert (ids == np.arange(spec.k)).all()
+    assert np.allclose(w, 1.0 / spec.k, atol=1e-7)
+    assert np.all(out == 0)
+
+
+# ------------------------------------------------------------ real shapes
+
+
+@pytest.fixture(scope="module")
+def real(torch_dev, tables):
+    spec = synth.CONFIGS["prefill"]
+    say("generating real-shape BF16 weights on the device")
+    wts = device_weights(spec, tables)
+    torch_dev.cuda.synchronize()
+    layer = make_layer(spec, wts, max_tokens=spec.T)
+    host = HostLayer(spec)
+    yield spec, wts, layer, host
+    layer.close()
+
+
+def _sampled_parity(torch, spec, layer, host, x_dev, xh, sample, tol, chunk_label):
+    out, ids, w = run_layer(torch, layer, x_dev)
+    T = x_dev.shape[0]
+    logits64 = host.logits(xh)
+    near, _ = check_routing(ids, w, logits64, spec.k)
+    if near:
+        say(f"{chunk_label}: near-ties at tokens {near}")
+    v = layer.views(T)
+    # FP32 logits: half an ulp of rounding plus a small accumulation error
+    dl = np.abs(v["logits"].astype(np.float64) - logits64)
+    gl = dl.max()
+    say(f"{chunk_label}: max |logit error| = {gl:.3g}")
+    assert np.all(dl <= 2.0 ** -24 * np.abs(logits64) + 2.5e-7)
+    order = np.argsort(ids.ravel(), kind="stable")
+    assert np.array_equal(v["perm_token"], order // spec.k)
+    assert np.array_equal(v["counts"], np.bincount(ids.ravel(), minlength=spec.E))
+    force = {i: ids[t] for i, t in enumerate(sample) if t in near}
+    r = host.oracle(xh[sample], force_ids=force or None)
+    assert np.array_equal(ids[sample], r.ids)
+    pr = v["pair_row"].reshape(T, spec.k)[sample]
+    u = bf16_to_f64(v["pooled"][sample]) * v["row_scale"][sample, None]
+    # one BF16 rounding of gamma_p * h: relative error <= 2^-9 per element
+    eu = float((np.abs(u - r.u) / (np.abs(r.u) + 1e-30)).max())
+    assert np.all(np.abs(u - r.u) <= 2.0 ** -8 * np.abs(r.u) + 1e-5), f"u: max relative error {eu:.3g}"
+    ea = check_rel_l2(bf16_to_f64(v["act"][pr]), r.a, STAGE_L2, "act")
+    eo = check_rel_l2(v["expert_out"][pr], r.o, STAGE_L2, "expert out")
+    ey = check_rel_l2(bf16_to_f64(v["combined"][sample]), r.y, STAGE_L2, "y")
+    e = check_output(out[sample], r.out, tol)
+    say(f"{chunk_label}: u max rel {eu:.3g}; rel L2 act {ea:.3g} o {eo:.3g} y {ey:.3g}; "
+        f"out max-abs {e:.3g} x RMS")
+    return out, ids
+
+
+def test_decode_parity(torch_dev, tables, real):
+    torch = torch_dev
+    spec, _, layer, host = real
+    dspec = synth.CONFIGS["decode"]
+    say("case: decode BF16, T=64")
+    x = synth.device_tensor(dspec, "x", tables)
+    xh = synth.host(dspec, "x")
+    sample = np.random.default_rng(1).choice(dspec.T, 6, replace=False)
+    _sampled_parity(torch, dspec, layer, host, x, xh, sample, TOL_BF16, "decode")
+
+
+@pytest.mark.parametrize("T", [16384, 4097, 1000])
+def test_prefill_parity(torch_dev, tables, real, T):
+    torch = torch_dev
+    spec, _, layer, host = real
+    say(f"case: prefill BF16, T={T}")
+    x = synth.device_tensor(spec, "x", tables)[:T].contiguous()
+    xh = synth.host(spec, "x")[:T]
+    sample = np.sort(np.random.default_rng(T).choice(T, 4, replace=False))
+    sample[-1] = T - 1  # ragged tail
+    _sampled_parity(torch, spec, layer, host, x, xh, sample, TOL_BF16, f"prefill T={T}")
+
+
+def test_skewed_chunk_parity(torch_dev, tables, real):
+    torch = torch_dev
+    spec, wts, _, _ = real
+    sspec = synth.CONFIGS["skew"]
+    say("case: skewed prefill chunk 1 (Zipf router bias)")
+    w2 = dict(wts)
+    w2["router_bias"] = synth.device_tensor(sspec, "router_bias", tables)
+    layer = make_layer(sspec, w2, max_tokens=sspec.T)
+    host = HostLayer(sspec)
+    x = synth.device_tensor(sspec, "x", tables, chunk=1)
+    xh = synth.host(sspec, "x", chunk=1)
+    sample = np.random.default_rng(5).choice(sspec.T, 4, replace=False)
+    _, ids = _sampled_parity(torch, sspec, layer, host, x, xh, sample, TOL_BF16, "skew chunk 1")
+    counts = np.bincount(ids.ravel(), minlength=sspec.E)
+    say(f"skew: max expert load {counts.max()} (mean {counts.mean():.0f}), idle experts {(counts == 0).sum()}")
+    assert counts.max() > 10 * counts.mean()
+    layer.close()
