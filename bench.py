@@ -85,8 +85,7 @@ def measure(spec, layer, x, steps, warmup, torch):
         acc = st if acc is None else {k: acc[k] + v for k, v in st.items()}
     B.latent_moe_set_profiling(layer.handle, False)
     stages = {k: v / steps for k, v in acc.items()}
-    v = layer.views(T)
-    return ms, wall, stages, v["counts"]
+    return ms, wall, stages, layer.views(T, names=("counts",))["counts"]
 
 
 def cpu_baseline(spec, xh, sample_tokens, budget_s=30.0):
@@ -126,7 +125,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew"])
     ap.add_argument("--also", default="prefill", help="extra workloads on the same weights (comma list)")
-    ap.add_argument("--cpu-tokens", type=int, default=24, help="token sample for the CPU oracle (0: skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=48, help="token sample for the CPU oracle (0: skip)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="also run a plain device copy of this many bytes (calibrates profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer runs unsharded on a single MI355X; "
@@ -150,6 +151,15 @@ def main():
     log("generating weights on the device")
     weights = {n: synth.device_tensor(base, n, tables) for n in synth.WEIGHT_NAMES}
     torch.cuda.synchronize()
+
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x {args.copy_bytes} bytes")
+        del src, dst
 
     results = {}
     for wl in [args.workload] + [w for w in args.also.split(",") if w and w != args.workload]:

@@ -24,7 +24,8 @@
  *     when the handle was created; tensors are dense, row-major, in the
  *     [out_features, in_features] convention of the linear maps above.
  *   - Every pointer must be 16-byte aligned; H and P must be multiples of
- *     64, I a multiple of 128; 1 <= E <= 1024.
+ *     64, I a multiple of 128 (with BF16 activations all three multiples of
+ *     256); 1 <= E <= 1024.
  *   - Calls return 0 (LMOE_OK) or a negative error code; no exception or
  *     abort crosses the ABI. latent_moe_last_error() then holds a message for
  *     the calling thread. All argument checks run on the host before any GPU
@@ -69,9 +70,12 @@ typedef struct {
   int64_t max_tokens;   /* upper bound on T per forward; sizes the workspace */
 } latent_moe_config;
 
-/* Layer weights (device pointers). They are BORROWED: the caller keeps them
- * alive and unchanged until latent_moe_destroy returns. Only the router is
- * repacked into library memory at create; nothing else is copied.
+/* Layer weights (device pointers), read in place unless stated otherwise; the
+ * caller keeps them alive and unchanged until latent_moe_destroy returns.
+ * With BF16 activations, create() also copies pooler, unpooler and the three
+ * expert matrices into library-owned memory in a matrix-core tiled layout
+ * (blocks of 32 rows x 64 columns ordered as the MFMA B fragments), and
+ * splits the router into three BF16 pieces; forward then reads those copies.
  *   router       [E, H]   F32
  *   router_bias  [E]      F32, or NULL for no bias (added to the logits)
  *   pooler       [P, H]   act_dtype
@@ -98,9 +102,9 @@ typedef struct {
 } latent_moe_weights;
 
 /* Create a handle on the current device. Validates cfg and w, allocates the
- * workspace for cfg->max_tokens tokens (never reallocated later), and splits
- * the FP32 router into an exact sum of three BF16 matrices for the matrix
- * cores (BF16 activations only), synchronising the device before returning.
+ * workspace for cfg->max_tokens tokens (never reallocated later) and, for
+ * BF16 activations, the repacked weight copies (about the size of the expert
+ * weights again), and synchronises the device before returning.
  * Errors: INVALID_ARG, UNSUPPORTED, OOM, HIP. On error *out is set to NULL
  * and nothing is leaked. */
 int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const latent_moe_weights* w);

@@ -14,7 +14,7 @@ import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-LIB_PATH = os.path.join(HERE, "liblatent_moe.so")
+LIB_PATH = os.environ.get("LATENT_MOE_LIB") or os.path.join(HERE, "liblatent_moe.so")
 HEADER = os.path.join(ROOT, "include", "latent_moe.h")
 
 LMOE_OK = 0
@@ -217,8 +217,9 @@ class LatentMoE:
 
     __call__ = forward
 
-    def views(self, T: int) -> dict:
-        """Host copies (numpy) of the last forward's intermediates for T tokens."""
+    def views(self, T: int, names=None) -> dict:
+        """Host copies (numpy) of the last forward's intermediates for T tokens
+        (all of them, or only those in ``names``)."""
         import numpy as np
         import torch
 
@@ -243,6 +244,8 @@ class LatentMoE:
         }
         res = {}
         for name, (ptr, shape, dt) in spec.items():
+            if names is not None and name not in names:
+                continue
             a = np.empty(shape, dt)
             _memcpy_d2h(a.ctypes.data, ptr, a.nbytes)
             res[name] = a

@@ -5,8 +5,11 @@
 // staged through LDS in two buffers: while the matrix cores consume one
 // buffer, the next k-tile is already in flight from global memory into
 // registers. LDS rows are 8 chunks of 16 bytes with the chunk index XORed by
-// (row & 7), so both the 16-byte stores and the MFMA operand reads of 8
-// consecutive rows hit 8 distinct bank groups.
+// (row / 2) % 8: a 16-byte LDS access is served 16 lanes (256 bytes) per
+// pass, and with that swizzle any 16 consecutive rows read at one logical
+// chunk, as well as the 16-byte stores of two consecutive rows, fall into 16
+// distinct 16-byte bank groups. (XOR by row % 8 leaves rows r and r+8 on
+// the same banks: a measured 2-way conflict on the operand reads.)
 //
 // Matrix instructions: BF16 uses v_mfma_f32_32x32x16_bf16, FP32 uses
 // v_mfma_f32_32x32x2_f32. A lane reads one 16-byte chunk of its A row and its
@@ -68,7 +71,7 @@ struct LmTile {
   int e;     // expert (grouped problems) or k-split index
 };
 
-LM_DEV int lm_swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+LM_DEV int lm_swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
 template <class Cfg>
 struct LmGemmSmem {

@@ -16,6 +16,35 @@
 #pragma once
 #include "gemm.h"
 
+// --------------------------------------------------- matrix-core B layout
+// Weights read by the streaming kernel are repacked once (at create) so that
+// one 16-byte load per lane fetches exactly the B fragment of a
+// v_mfma_f32_32x32x16_bf16 step, and the 64 lanes of that load read 1 KB of
+// contiguous memory. For a row-major [R, K] BF16 matrix (R % 32 == 0,
+// K % 64 == 0), 16-byte chunk c of row n lands at chunk index
+//   ((n/32 * K/64 + c/8) * 4 + (c%8)%4) * 64 + ((c%8)/4) * 32 + n%32
+// i.e. blocks of 32 rows x 64 columns, ordered by MFMA step s = (c%8)%4, then
+// by lane (h = (c%8)/4, r = n%32).
+template <typename E>
+LM_DEV const lm_u32x4* lm_packed_group(const E* base, int64_t row0, int K) {
+  return (const lm_u32x4*)base + (row0 / 32) * (int64_t)(K / 64) * 256;
+}
+
+__global__ void lm_pack_mfma_kernel(const lm_u32x4* src, lm_u32x4* dst, int64_t rows, int K) {
+  const int64_t n = rows * (K / 8);
+  const int ktiles = K / 64;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t blk = i >> 8;
+    const int within = (int)(i & 255);
+    const int s = within >> 6, lane = within & 63;
+    const int64_t g = blk / ktiles;
+    const int kt = (int)(blk - g * ktiles);
+    const int64_t row = g * 32 + (lane & 31);
+    dst[i] = src[row * (K / 8) + kt * 8 + 4 * (lane >> 5) + s];
+  }
+}
+
 // ----------------------------------------------------------------- router
 // Partial logits over k-splits: part[s][t][e] = sum over split s of x[t,k] W[e,k],
 // accumulated as FP64 sums of per-k-tile FP32 matrix-core chains.
@@ -103,6 +132,9 @@ struct PoolerProb {
   }
   LM_DEV const lm_u32x4* b_row(const LmTile& t, int r) const {
     return (const lm_u32x4*)(w + (size_t)min(t.n0 + r, P - 1) * H);
+  }
+  LM_DEV const lm_u32x4* b_group(const LmTile& t, int wv, int j) const {
+    return lm_packed_group(w, min(t.n0 + (wv * Cfg::TN + j) * 32, P - 32), H);
   }
   LM_DEV int a_ktile(int kt) const { return kt; }
   LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
@@ -197,6 +229,9 @@ struct GateUpProb {
     const E* base = within >= 32 ? wu : wg;
     return (const lm_u32x4*)(base + ((size_t)t.e * I + col) * P);
   }
+  LM_DEV const lm_u32x4* b_group(const LmTile& t, int wv, int j) const {
+    return lm_packed_group(j ? wu : wg, (int64_t)t.e * I + t.n0 + wv * 32, P);
+  }
   LM_DEV int a_ktile(int kt) const { return kt; }
   LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
                        int lane, void*) const {
@@ -244,6 +279,9 @@ struct DownProb {
   }
   LM_DEV const lm_u32x4* b_row(const LmTile& t, int r) const {
     return (const lm_u32x4*)(wd + ((size_t)t.e * P + min(t.n0 + r, P - 1)) * I);
+  }
+  LM_DEV const lm_u32x4* b_group(const LmTile& t, int wv, int j) const {
+    return lm_packed_group(wd, (int64_t)t.e * P + min(t.n0 + (wv * Cfg::TN + j) * 32, P - 32), I);
   }
   LM_DEV int a_ktile(int kt) const { return kt; }
   LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
@@ -296,6 +334,9 @@ struct UnpoolerProb {
   }
   LM_DEV const lm_u32x4* b_row(const LmTile& t, int r) const {
     return (const lm_u32x4*)(w + (size_t)min(t.n0 + r, H - 1) * P);
+  }
+  LM_DEV const lm_u32x4* b_group(const LmTile& t, int wv, int j) const {
+    return lm_packed_group(w, min(t.n0 + (wv * Cfg::TN + j) * 32, H - 32), P);
   }
   LM_DEV int a_ktile(int kt) const { return kt; }
   LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,

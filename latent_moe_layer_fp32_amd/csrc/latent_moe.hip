@@ -13,8 +13,10 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <type_traits>
 
 #include "../../include/latent_moe.h"
+#include "gemm_stream.h"
 #include "kernels.h"
 
 namespace {
@@ -40,8 +42,14 @@ int fail(int code, const char* fmt, ...) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Tile configurations: "wide" for many rows per expert (prefill-sized),
-// "narrow" for few (decode-sized).
-template <typename E> using CfgWide = LmGemmCfg<E, 2, 2, 2, 2>;
+// "narrow" for few (decode-sized). BF16 runs the streaming-B kernel (four
+// waves along N, BN = 256); FP32 runs the LDS-staged kernel.
+#ifndef LM_WIDE_TM
+#define LM_WIDE_TM 4
+#endif
+template <typename E>
+using CfgWide =
+    std::conditional_t<sizeof(E) == 2, LmGemmCfg<E, 1, 4, LM_WIDE_TM, 2>, LmGemmCfg<E, 2, 2, 2, 2>>;
 template <typename E> using CfgNarrow = LmGemmCfg<E, 1, 4, 1, 2>;
 // Router: FP32 chains of one k-tile (64 BF16 products per lane pair), FP64 beyond.
 template <typename E> using CfgRouterWide = LmGemmCfg<E, 2, 2, 1, 2, 1>;
@@ -68,6 +76,13 @@ struct latent_moe {
   char* ws;
   Layout lay;
   size_t part_floats;
+  char* packed;                    // BF16: weights in the matrix-core layout
+  size_t packed_bytes;
+  const void* pk_pooler;
+  const void* pk_unpooler;
+  const void* pk_gate;
+  const void* pk_up;
+  const void* pk_down;
   bool prof;                       // record stage events in forward
   bool prof_valid;                 // a forward has recorded a full set
   hipEvent_t ev[kStages + 1];      // created by latent_moe_set_profiling
@@ -125,6 +140,8 @@ int validate_config(const latent_moe_config* c) {
   if (!act_ok || !exp_ok) return fail(LMOE_ERR_INVALID_ARG, "unknown dtype code");
   if ((c->act_dtype == LMOE_F32) != (c->expert_dtype == LMOE_F32))
     return fail(LMOE_ERR_UNSUPPORTED, "FP32 experts need FP32 activations and vice versa");
+  if (c->act_dtype == LMOE_BF16 && (c->hidden % 256 || c->pooled % 256 || c->intermediate % 256))
+    return fail(LMOE_ERR_INVALID_ARG, "BF16 layers need hidden, pooled and intermediate to be multiples of 256");
   if (c->expert_dtype == LMOE_MXFP4)
     return fail(LMOE_ERR_UNSUPPORTED, "MXFP4 expert weights are not built into this library");
   if ((size_t)c->pooled * c->intermediate * c->experts > ((size_t)1 << 40))
@@ -180,7 +197,10 @@ template <class Prob>
 hipError_t launch(const Prob& p, int64_t units, hipStream_t s) {
   if (units <= 0) return hipSuccess;
   const int64_t g = (units + 7) / 8 * 8;
-  hipLaunchKernelGGL(lm_gemm_kernel<Prob>, dim3((unsigned)g), dim3(256), 0, s, p);
+  if constexpr (sizeof(typename Prob::Cfg::E) == 2 && Prob::Cfg::WM == 1 && !Prob::Cfg::FLUSH)
+    hipLaunchKernelGGL(lm_gemm_stream_kernel<Prob>, dim3((unsigned)g), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(lm_gemm_kernel<Prob>, dim3((unsigned)g), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -198,6 +218,12 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   const int E = (int)c.experts, k = c.top_k, H = (int)c.hidden, P = (int)c.pooled,
             I = (int)c.intermediate;
   const int npairs = (int)(T * k);
+  const bool packed = sizeof(Et) == 2;  // BF16 matrices read from the packed copies
+  const void* Wpool = packed ? h->pk_pooler : w.pooler;
+  const void* Wunpool = packed ? h->pk_unpooler : w.unpooler;
+  const void* Wgate = packed ? h->pk_gate : w.w_gate;
+  const void* Wup = packed ? h->pk_up : w.w_up;
+  const void* Wdown = packed ? h->pk_down : w.w_down;
   using Cw = CW<Et>;
   using Cr = CR<Et>;
   double* part = (double*)(ws + L.part);
@@ -263,7 +289,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   {
     PoolerProb<Cw> p;
     p.x = (const Et*)x;
-    p.w = (const Et*)w.pooler;
+    p.w = (const Et*)Wpool;
     p.gamma = w.pool_gamma;
     p.pooled = pooled;
     p.ssq = pssq;
@@ -284,8 +310,8 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   {
     GateUpProb<Cw> p;
     p.pooled = pooled;
-    p.wg = (const Et*)w.w_gate;
-    p.wu = (const Et*)w.w_up;
+    p.wg = (const Et*)Wgate;
+    p.wu = (const Et*)Wup;
     p.row_scale = row_scale;
     p.perm_token = perm_token;
     p.counts = counts;
@@ -304,7 +330,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   {
     DownProb<Cw> p;
     p.act = act;
-    p.wd = (const Et*)w.w_down;
+    p.wd = (const Et*)Wdown;
     p.counts = counts;
     p.offsets = offsets;
     p.tile_off = tile_off;
@@ -326,7 +352,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   {
     UnpoolerProb<Cw> p;
     p.y = y;
-    p.w = (const Et*)w.unpooler;
+    p.w = (const Et*)Wunpool;
     p.out = out;
     p.T = (int)T;
     p.H = H;
@@ -395,6 +421,31 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
                 hipGetErrorString(he));
   }
   if (cfg->act_dtype == LMOE_BF16) {
+    const size_t E = cfg->experts, H = cfg->hidden, P = cfg->pooled, I = cfg->intermediate;
+    const size_t sz_pool = H * P * 2, sz_exp = E * I * P * 2;
+    h->packed_bytes = 2 * sz_pool + 3 * sz_exp;
+    he = hipMalloc((void**)&h->packed, h->packed_bytes);
+    if (he != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipFree(h->ws);
+      delete h;
+      return fail(LMOE_ERR_OOM, "hipMalloc of %zu bytes for packed weights failed", 2 * sz_pool + 3 * sz_exp);
+    }
+    h->pk_pooler = h->packed;
+    h->pk_unpooler = h->packed + sz_pool;
+    h->pk_gate = h->packed + 2 * sz_pool;
+    h->pk_up = h->packed + 2 * sz_pool + sz_exp;
+    h->pk_down = h->packed + 2 * sz_pool + 2 * sz_exp;
+    struct Job { const void* src; const void* dst; int64_t rows; int K; };
+    const Job jobs[] = {{w->pooler, h->pk_pooler, (int64_t)P, (int)H},
+                        {w->unpooler, h->pk_unpooler, (int64_t)H, (int)P},
+                        {w->w_gate, h->pk_gate, (int64_t)(E * I), (int)P},
+                        {w->w_up, h->pk_up, (int64_t)(E * I), (int)P},
+                        {w->w_down, h->pk_down, (int64_t)(E * P), (int)I}};
+    for (const Job& j : jobs) {
+      hipLaunchKernelGGL(lm_pack_mfma_kernel, dim3(65536), dim3(256), 0, 0, (const lm_u32x4*)j.src,
+                         (lm_u32x4*)j.dst, j.rows, j.K);
+    }
     const size_t n = (size_t)cfg->experts * cfg->hidden;
     unsigned blocks = (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
     hipLaunchKernelGGL(lm_split_router_kernel, dim3(blocks), dim3(256), 0, 0, w->router,
@@ -403,8 +454,9 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
     if (he == hipSuccess) he = hipDeviceSynchronize();
     if (he != hipSuccess) {
       (void)hipFree(h->ws);
+      (void)hipFree(h->packed);
       delete h;
-      return fail(LMOE_ERR_HIP, "router split failed: %s", hipGetErrorString(he));
+      return fail(LMOE_ERR_HIP, "weight repack failed: %s", hipGetErrorString(he));
     }
   }
   *out = h;
@@ -507,6 +559,7 @@ int latent_moe_destroy(latent_moe_t* h) {
   (void)hipSetDevice(h->device);
   hipError_t e1 = hipDeviceSynchronize();
   hipError_t e2 = hipFree(h->ws);
+  if (h->packed && e2 == hipSuccess) e2 = hipFree(h->packed);
   for (int i = 0; i <= kStages; ++i)
     if (h->ev[i]) (void)hipEventDestroy(h->ev[i]);
   if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
