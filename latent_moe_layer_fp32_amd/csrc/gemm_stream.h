@@ -25,17 +25,13 @@
 
 #include "gemm.h"
 
-// Global prefetch distances in k-tiles. Deep: B 3 ahead, A 4 ahead (A(kt+2)
+// Global prefetch distances in k-tiles. Deep (TM < 4, few accumulators: the
+// decode-sized tiles that only stream weights): B 3 ahead, A 4 ahead (A(kt+2)
 // is written to LDS at iteration kt; since vmcnt retires in issue order, that
 // store then waits only on loads issued two iterations earlier), register
-// rings of four k-tiles, meant for one workgroup per CU. Lean: B 1 ahead, A
-// loaded and written within the iteration, rings of two, small enough for
-// two workgroups per CU to hide each other's latency.
-#ifndef LM_LEAN
-#define LM_LEAN 1
-#endif
-constexpr int kRing = LM_LEAN ? 2 : 4;
-constexpr int kDistB = LM_LEAN ? 1 : 3, kDistA = LM_LEAN ? 2 : 4;
+// rings of four k-tiles. Lean (TM = 4): B 1 ahead, A loaded and written
+// within the iteration, rings of two, small enough for two workgroups per CU
+// to hide each other's latency.
 #ifndef LM_WAVES_MAX
 #define LM_WAVES_MAX 2
 #endif
@@ -49,6 +45,9 @@ void lm_gemm_stream_kernel(const Prob p) {
   static_assert(Cfg::WM == 1 && Cfg::WN == 4, "streaming-B layout: four waves along N");
   static_assert(sizeof(typename Cfg::E) == 2, "BF16 operands");
   constexpr int TM = Cfg::TM, TN = Cfg::TN, BM = Cfg::BM;
+  constexpr bool kLean = TM >= 4;
+  constexpr int kRing = kLean ? 2 : 4;
+  constexpr int kDistB = kLean ? 1 : 3, kDistA = kLean ? 2 : 4;
   constexpr int kStage = BM * 8;  // 16-byte chunks per A stage
   constexpr int QA = BM * 8 / 256;  // A chunks per thread per k-tile (= TM)
   __shared__ lm_u32x4 sa[2 * kStage];
@@ -127,7 +126,7 @@ void lm_gemm_stream_kernel(const Prob p) {
 
   // Prologue: B(kt0 .. kt0+2) and A(kt0 .. kt0+3) in flight, A(kt0) and
   // A(kt0+1) in the two LDS stages, step 0 of kt0 in registers.
-  if constexpr (LM_LEAN) {
+  if constexpr (kLean) {
     load_b(0, kt0);
     load_a(0, kt0);
     load_a(1, kt0 + 1);
@@ -159,7 +158,7 @@ void lm_gemm_stream_kernel(const Prob p) {
     const int cur = q & 1, nxt = cur ^ 1;
     read_frag(1, cur, 1);
     load_b((q + kDistB) % kRing, kt + kDistB);
-    load_a(LM_LEAN ? 0 : (q + kDistA) % kRing, kt + kDistA);
+    load_a(kLean ? 0 : (q + kDistA) % kRing, kt + kDistA);
     mma_step(0, q % kRing, 0);
     pattern(std::true_type{});
     __builtin_amdgcn_sched_barrier(0);
@@ -176,7 +175,7 @@ void lm_gemm_stream_kernel(const Prob p) {
     mma_step(1, q % kRing, 3);
     pattern(std::false_type{});
     __builtin_amdgcn_sched_barrier(0);
-    store_a(LM_LEAN ? 0 : (q + 2) % kRing, cur);
+    store_a(kLean ? 0 : (q + 2) % kRing, cur);
   };
   for (int kt = kt0; kt < kt1; kt += 4) {
     iter(kt, 0);

@@ -356,6 +356,93 @@ struct UnpoolerProb {
   }
 };
 
+// ------------------------------------------- split-K dense projections
+// For few tokens the pooler / unpooler have too few output tiles to keep the
+// chip streaming weights, so K is split and each split writes FP32 partial
+// sums part[s][row][col]; a finish kernel adds them in split order.
+template <class Cfg_>
+struct DenseSplitProb {
+  using Cfg = Cfg_;
+  using E = typename Cfg::E;
+  const E* a;   // [T, K]
+  const E* w;   // packed [N, K]
+  float* part;  // [splits, T, N]
+  int T, N, K, mt, nt, splits, kt_per;
+
+  LM_DEV bool tile(int bid, LmTile& t) const {
+    int L;
+    if (!lm_xcd_map(bid, mt * nt * splits, L)) return false;
+    const int s = L / (mt * nt);
+    int m, n;
+    lm_dense_order(L - s * mt * nt, mt, nt, 8, m, n);
+    t.m0 = m * Cfg::BM;
+    t.rows = min(Cfg::BM, T - t.m0);
+    t.n0 = n * Cfg::BN;
+    t.nt = n;
+    t.e = s;
+    t.kt0 = s * kt_per;
+    t.kt1 = min(K / Cfg::KT, t.kt0 + kt_per);
+    return true;
+  }
+  LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
+    return (const lm_u32x4*)(a + (size_t)(t.m0 + min(r, t.rows - 1)) * K);
+  }
+  LM_DEV const lm_u32x4* b_group(const LmTile& t, int wv, int j) const {
+    return lm_packed_group(w, min(t.n0 + (wv * Cfg::TN + j) * 32, N - 32), K);
+  }
+  LM_DEV int a_ktile(int kt) const { return kt; }
+  LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
+                       int lane, void*) const {
+    float* dst = part + ((size_t)t.e * T + t.m0) * N;
+#pragma unroll
+    for (int tn = 0; tn < Cfg::TN; ++tn) {
+      const int col = t.n0 + lm_acc_col<Cfg>(wn, tn, lane);
+      if (col >= N) continue;
+#pragma unroll
+      for (int tm = 0; tm < Cfg::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
+          if (row < t.rows) dst[(size_t)row * N + col] = acc[tm][tn][i];
+        }
+    }
+  }
+};
+
+// Pooler finish, one workgroup per (token, 256 columns): h = sum of the
+// split partials in split order; pooled = BF16(gamma_p * h); the chunk's sum
+// of h^2 (fixed tree over the workgroup) goes to ssq[t][chunk], from which
+// lm_rowscale_kernel forms the row scale exactly as on the unsplit path.
+__global__ __launch_bounds__(256) void lm_pool_finish_kernel(const float* part, int splits, int T,
+                                                             int P, const float* gamma,
+                                                             uint16_t* pooled, float* ssq) {
+  __shared__ float red[256];
+  const int t = blockIdx.x, chunk = blockIdx.y, tid = threadIdx.x;
+  const int c = chunk * 256 + tid;
+  float h = 0.0f;
+  if (c < P) {
+    for (int sp = 0; sp < splits; ++sp) h += part[((size_t)sp * T + t) * P + c];
+    pooled[(size_t)t * P + c] = lm_f32_to_bf16(h * gamma[c]);
+  }
+  red[tid] = h * h;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) ssq[(size_t)t * gridDim.y + chunk] = red[0];
+}
+
+// Unpooler finish: out = sum of the split partials, in split order.
+__global__ void lm_unpool_finish_kernel(const float* part, int splits, int64_t n, float* out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float v = 0.0f;
+    for (int sp = 0; sp < splits; ++sp) v += part[(size_t)sp * n + i];
+    out[i] = v;
+  }
+}
+
 // ------------------------------------------------------------ small kernels
 
 __global__ void lm_fill_i32_kernel(int* p, int n, int v) {
@@ -404,33 +491,51 @@ LM_DEV uint64_t lm_wave_max_u64(uint64_t v) {
   return v;
 }
 
-// One wavefront per token: sum the k-split partial logits in a fixed order
-// (FP64), add the bias, round once to FP32, pick the top k by (logit desc, index asc) and take the
-// softmax over them. Counts routed pairs per expert (LDS histogram per block,
-// one integer atomic per expert and block).
-template <int NV>
+// Router logits and top-k, TPB tokens per workgroup. Phase 1: all 256
+// threads sum the k-split partial logits of the workgroup's tokens in a fixed
+// order (FP64), add the bias and round once to FP32. Phase 2: one wavefront
+// per token picks the top k by (logit desc, index asc) and takes the softmax
+// over them. Routed pairs per expert are counted in an LDS histogram, one
+// integer atomic per expert and workgroup.
+template <int NV, int TPB>
 __global__ __launch_bounds__(256) void lm_topk_kernel(const double* part, int splits, int T, int E,
                                                       const float* bias, int k, float* logits,
                                                       int* ids, float* wts, int* counts) {
+  static_assert(TPB >= 1 && TPB <= 4, "one wavefront per token");
   __shared__ int hist[1024];
+  __shared__ float sl[TPB][NV * 64];
   const int tid = threadIdx.x, lane = tid & 63;
+  const int t0 = blockIdx.x * TPB;
   for (int i = tid; i < E; i += 256) hist[i] = 0;
+  for (int i = tid; i < TPB * E; i += 256) {
+    const int tt = i / E, e = i - tt * E, t = t0 + tt;
+    if (t >= T) continue;
+    const double* src = part + (size_t)t * E + e;
+    const size_t stride = (size_t)T * E;
+    double sd = 0.0;
+    int sp = 0;
+    for (; sp + 4 <= splits; sp += 4) {
+      const double a = src[(size_t)sp * stride], b = src[(size_t)(sp + 1) * stride];
+      const double c = src[(size_t)(sp + 2) * stride], d = src[(size_t)(sp + 3) * stride];
+      sd += a;
+      sd += b;
+      sd += c;
+      sd += d;
+    }
+    for (; sp < splits; ++sp) sd += src[(size_t)sp * stride];
+    if (bias) sd += (double)bias[e];
+    const float v = (float)sd + 0.0f;  // one rounding to FP32; -0 -> +0
+    logits[(size_t)t * E + e] = v;
+    sl[tt][e] = v;
+  }
   __syncthreads();
-  const int t = blockIdx.x * 4 + (tid >> 6);
-  if (t < T) {
+  const int tt = tid >> 6, t = t0 + tt;
+  if (tt < TPB && t < T) {
     uint64_t key[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int e = lane + 64 * v;
-      key[v] = 0;
-      if (e < E) {
-        double sd = 0.0;
-        for (int sp = 0; sp < splits; ++sp) sd += part[((size_t)sp * T + t) * E + e];
-        if (bias) sd += (double)bias[e];
-        float s = (float)sd + 0.0f;  // one rounding to FP32; -0 -> +0
-        logits[(size_t)t * E + e] = s;
-        key[v] = ((uint64_t)lm_ord(s) << 32) | (uint32_t)(~(uint32_t)e);
-      }
+      key[v] = e < E ? ((uint64_t)lm_ord(sl[tt][e]) << 32) | (uint32_t)(~(uint32_t)e) : 0;
     }
     float selv[16];
     int seli[16];

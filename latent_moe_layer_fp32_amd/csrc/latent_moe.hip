@@ -62,8 +62,24 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 struct Layout {
   size_t part, logits, ids, wts, counts, offsets, tile_off, perm_token, pair_row, pooled, pssq,
-      row_scale, act, O, ossq, y, wr3, total;
+      row_scale, act, O, ossq, y, wr3, kpart, total;
 };
+
+// Split-K plan for a dense BF16 projection: split only when the output tiles
+// cannot cover the chip; each split a multiple of 4 k-tiles (the streaming
+// kernel's unroll).
+void dense_split(int64_t T, int64_t N, int64_t K, int BM, int BN, int& splits, int& kt_per) {
+  const int64_t tiles = ceil_div(T, BM) * (int64_t)ceil_div(N, BN);
+  const int ktiles = (int)(K / 64);
+  splits = 1;
+  kt_per = ktiles;
+  if (tiles >= 256) return;
+  int want = ceil_div(512, tiles);
+  if (want > ktiles / 4) want = ktiles / 4;
+  if (want <= 1) return;
+  kt_per = (ceil_div(ktiles, want) + 3) / 4 * 4;
+  splits = ceil_div(ktiles, kt_per);
+}
 
 }  // namespace
 
@@ -189,6 +205,19 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
   L.ossq = take((size_t)Mp * parts * 4);
   L.y = take((size_t)Tm * P * esize_act(c));
   L.wr3 = take(c.act_dtype == LMOE_BF16 ? (size_t)E * 3 * c.hidden * 2 : 0);
+  size_t kp = 0;
+  if (c.act_dtype == LMOE_BF16) {
+    for (int64_t T = 1; T <= (Tm < 65536 ? Tm : 65536); ++T) {
+      const bool nar = narrow_for(c, T);
+      const int BM = nar ? 32 : 32 * LM_WIDE_TM, BN = 256;
+      int sp, kpt;
+      dense_split(T, P, c.hidden, BM, BN, sp, kpt);
+      if (sp > 1 && (size_t)sp * T * P > kp) kp = (size_t)sp * T * P;
+      dense_split(T, c.hidden, P, BM, BN, sp, kpt);
+      if (sp > 1 && (size_t)sp * T * c.hidden > kp) kp = (size_t)sp * T * c.hidden;
+    }
+  }
+  L.kpart = take(kp * 4);
   L.total = o;
   return L;
 }
@@ -265,17 +294,25 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     LM_MARK(1);
     // 2. top-k + softmax + per-expert counts
     hipLaunchKernelGGL(lm_fill_i32_kernel, dim3(ceil_div(E, 256)), dim3(256), 0, s, counts, E, 0);
-    const dim3 g(ceil_div(T, 4));
-    if (E <= 64)
-      hipLaunchKernelGGL(lm_topk_kernel<1>, g, dim3(256), 0, s, part, splits, (int)T, E, w.router_bias, k, logits, ids, wts, counts);
-    else if (E <= 128)
-      hipLaunchKernelGGL(lm_topk_kernel<2>, g, dim3(256), 0, s, part, splits, (int)T, E, w.router_bias, k, logits, ids, wts, counts);
-    else if (E <= 256)
-      hipLaunchKernelGGL(lm_topk_kernel<4>, g, dim3(256), 0, s, part, splits, (int)T, E, w.router_bias, k, logits, ids, wts, counts);
-    else if (E <= 512)
-      hipLaunchKernelGGL(lm_topk_kernel<8>, g, dim3(256), 0, s, part, splits, (int)T, E, w.router_bias, k, logits, ids, wts, counts);
-    else
-      hipLaunchKernelGGL(lm_topk_kernel<16>, g, dim3(256), 0, s, part, splits, (int)T, E, w.router_bias, k, logits, ids, wts, counts);
+    // few tokens with many k-splits: one token per workgroup spreads the
+    // split sums over all threads; otherwise four tokens per workgroup
+    const bool one = splits > 4;
+    const dim3 g(one ? (unsigned)T : (unsigned)ceil_div(T, 4));
+#define LM_TOPK(NV)                                                                             \
+  do {                                                                                          \
+    if (one)                                                                                    \
+      hipLaunchKernelGGL((lm_topk_kernel<NV, 1>), g, dim3(256), 0, s, part, splits, (int)T, E, \
+                         w.router_bias, k, logits, ids, wts, counts);                           \
+    else                                                                                        \
+      hipLaunchKernelGGL((lm_topk_kernel<NV, 4>), g, dim3(256), 0, s, part, splits, (int)T, E, \
+                         w.router_bias, k, logits, ids, wts, counts);                           \
+  } while (0)
+    if (E <= 64) LM_TOPK(1);
+    else if (E <= 128) LM_TOPK(2);
+    else if (E <= 256) LM_TOPK(4);
+    else if (E <= 512) LM_TOPK(8);
+    else LM_TOPK(16);
+#undef LM_TOPK
     LM_HIP(hipGetLastError());
   }
   LM_MARK(2);
@@ -286,7 +323,33 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   LM_MARK(3);
   // 4. pooler + norm statistics
   const int pnt = ceil_div(P, Cw::BN);
-  {
+  int psplits = 1, pkt = 0;
+  if (packed) dense_split(T, P, H, Cw::BM, Cw::BN, psplits, pkt);
+  if (psplits > 1) {
+    if constexpr (sizeof(Et) == 2) {
+    DenseSplitProb<Cw> p;
+    p.a = (const Et*)x;
+    p.w = (const Et*)Wpool;
+    p.part = (float*)(ws + L.kpart);
+    p.T = (int)T;
+    p.N = P;
+    p.K = H;
+    p.mt = ceil_div(T, Cw::BM);
+    p.nt = pnt;
+    p.splits = psplits;
+    p.kt_per = pkt;
+    LM_HIP(launch(p, (int64_t)p.mt * p.nt * psplits, s));
+    LM_MARK(4);
+    const int chunks = ceil_div(P, 256);
+    hipLaunchKernelGGL(lm_pool_finish_kernel, dim3((unsigned)T, (unsigned)chunks), dim3(256), 0, s,
+                       (const float*)(ws + L.kpart), psplits, (int)T, P, w.pool_gamma,
+                       (uint16_t*)pooled, pssq);
+    LM_HIP(hipGetLastError());
+    hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, pssq, chunks,
+                       (int)T, P, c.eps, row_scale);
+    LM_HIP(hipGetLastError());
+    }
+  } else {
     PoolerProb<Cw> p;
     p.x = (const Et*)x;
     p.w = (const Et*)Wpool;
@@ -299,11 +362,11 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.mt = ceil_div(T, Cw::BM);
     p.nt = pnt;
     LM_HIP(launch(p, (int64_t)p.mt * p.nt, s));
+    LM_MARK(4);
+    hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, pssq, pnt,
+                       (int)T, P, c.eps, row_scale);
+    LM_HIP(hipGetLastError());
   }
-  LM_MARK(4);
-  hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, pssq, pnt, (int)T,
-                     P, c.eps, row_scale);
-  LM_HIP(hipGetLastError());
   LM_MARK(5);
   const int64_t max_tiles = ceil_div(npairs, Cw::BM) + (npairs < E ? npairs : E);
   // 5. gate/up + SwiGLU
@@ -349,7 +412,28 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   LM_HIP(hipGetLastError());
   LM_MARK(8);
   // 8. unpooler
-  {
+  int usplits = 1, ukt = 0;
+  if (packed) dense_split(T, H, P, Cw::BM, Cw::BN, usplits, ukt);
+  if (usplits > 1) {
+    if constexpr (sizeof(Et) == 2) {
+    DenseSplitProb<Cw> p;
+    p.a = y;
+    p.w = (const Et*)Wunpool;
+    p.part = (float*)(ws + L.kpart);
+    p.T = (int)T;
+    p.N = H;
+    p.K = P;
+    p.mt = ceil_div(T, Cw::BM);
+    p.nt = ceil_div(H, Cw::BN);
+    p.splits = usplits;
+    p.kt_per = ukt;
+    LM_HIP(launch(p, (int64_t)p.mt * p.nt * usplits, s));
+    const int64_t n = T * (int64_t)H;
+    hipLaunchKernelGGL(lm_unpool_finish_kernel, dim3((unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192)),
+                       dim3(256), 0, s, (const float*)(ws + L.kpart), usplits, n, out);
+    LM_HIP(hipGetLastError());
+    }
+  } else {
     UnpoolerProb<Cw> p;
     p.y = y;
     p.w = (const Et*)Wunpool;
