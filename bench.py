@@ -32,6 +32,37 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def source_hash() -> str:
+    """sha256 (first 16 hex digits) of the kernel sources and the C header."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "latent_moe_layer_fp32_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(csrc, "*.h")) + glob.glob(os.path.join(csrc, "*.hip"))
+                   + [os.path.join(ROOT, "include", "latent_moe.h")])
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k] = v
+    if kv.get("source_sha256") != source_hash():
+        return None
+    return int(float(kv["traffic_bytes"]))
+
+
 def layer_bytes(spec, counts, T):
     """Algorithmic HBM bytes of one forward: touched expert weights once, the
     projections and router once, x in, out (FP32) out."""
@@ -180,7 +211,8 @@ def main():
         if wl == "decode":
             ach = gate_up_bytes(spec, counts, spec.T) / gu / 1e9
             r["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                             "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                             "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                             "traffic": measured_traffic("decode", "gate_up"),
                              "kernel": "gate_up grouped GEMM + SwiGLU",
                              "kernel_ms": round(stages["gate_up"], 4)}
             r["layer_frac"] = round(lb / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
@@ -188,7 +220,8 @@ def main():
             fl = 2 * spec.T * spec.k * spec.P * 2 * spec.I
             ach = fl / gu / 1e12
             r["roofline"] = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                             "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                             "traffic": measured_traffic(wl, "gate_up"),
                              "kernel": "gate_up grouped GEMM + SwiGLU",
                              "kernel_ms": round(stages["gate_up"], 4)}
             r["layer_frac"] = round(layer_flops(spec, spec.T) / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)
