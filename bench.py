@@ -5,8 +5,9 @@ One step = one forward of the whole layer (router, top-k, grouping, pooler,
 pre-expert norm, gate/up, down, per-expert norm + weighted sum, unpooler) over
 one batch of seeded synthetic tokens already resident in HBM. Default
 workload: 64-token decode at the real layer shapes (H=8192, P=4096, E=256,
-I=4096, k=8, BF16); the 16384-token prefill chunk on the same weights is
-measured in the same run and reported under "prefill".
+I=4096, k=8, BF16); the 16384-token prefill chunk on the same weights, and
+the 64-token decode and 16384-token prefill with MXFP4 expert weights, are
+measured in the same run and reported under their workload names.
 
 Prints one JSON line with tokens/s, the roofline of the dominant kernel (the
 gate/up grouped GEMM: HBM-bound at decode, MFMA-bound at prefill; its time
@@ -154,8 +155,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew"])
-    ap.add_argument("--also", default="prefill", help="extra workloads on the same weights (comma list)")
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew", "mxfp4", "mxfp4_decode"])
+    ap.add_argument("--also", default="prefill,mxfp4_decode,mxfp4",
+                    help="extra workloads measured in the same run (comma list)")
     ap.add_argument("--cpu-tokens", type=int, default=48, help="token sample for the CPU oracle (0: skip)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run a plain device copy of this many bytes (calibrates profiler byte counters)")
@@ -178,10 +180,20 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     tables = synth.DeviceTables("cuda:0")
-    base = synth.CONFIGS["prefill"]
-    log("generating weights on the device")
-    weights = {n: synth.device_tensor(base, n, tables) for n in synth.WEIGHT_NAMES}
-    torch.cuda.synchronize()
+    wcache = {}
+
+    def weights_for(spec):
+        """Weights of the real layer shapes in the spec's expert format (one
+        format resident at a time)."""
+        fmt = spec.expert_format
+        if fmt not in wcache:
+            wcache.clear()
+            torch.cuda.empty_cache()
+            base = synth.CONFIGS["prefill"].with_(expert_format=fmt)
+            log(f"generating {fmt} weights on the device")
+            wcache[fmt] = {n: synth.device_tensor(base, n, tables) for n in synth.WEIGHT_NAMES}
+            torch.cuda.synchronize()
+        return wcache[fmt]
 
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
@@ -195,7 +207,7 @@ def main():
     results = {}
     for wl in [args.workload] + [w for w in args.also.split(",") if w and w != args.workload]:
         spec = synth.CONFIGS[wl]
-        w = dict(weights)
+        w = dict(weights_for(spec))
         if spec.router_bias != "none":
             w["router_bias"] = synth.device_tensor(spec, "router_bias", tables)
         layer = make_layer(spec, w, max_tokens=spec.T)
@@ -208,11 +220,11 @@ def main():
         r = dict(spec=spec, ms=ms, wall=wall, stages=stages, touched=touched, layer_bytes=lb,
                  tokens_per_s=spec.T / (ms / 1e3), steps=steps, warmup=warm)
         gu = stages["gate_up"] / 1e3
-        if wl == "decode":
+        if spec.T * spec.k < 64 * spec.E:  # decode-sized: the expert weights stream once
             ach = gate_up_bytes(spec, counts, spec.T) / gu / 1e9
             r["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                             "traffic": measured_traffic("decode", "gate_up"),
+                             "traffic": measured_traffic(wl, "gate_up"),
                              "kernel": "gate_up grouped GEMM + SwiGLU",
                              "kernel_ms": round(stages["gate_up"], 4)}
             r["layer_frac"] = round(lb / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
@@ -247,7 +259,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded counter-based N(0,1) inputs, N(0,1/fan_in) weights)",
         "config": {"workload": f"{args.workload}: {spec.T} tokens, H={spec.H}, P={spec.P}, E={spec.E}, "
-                               f"I={spec.I}, top-{spec.k}, BF16 experts, FP32 router",
+                               f"I={spec.I}, top-{spec.k}, {spec.expert_format.upper()} experts, FP32 router",
                    "global_batch": spec.T, "parallelism": "none (one GPU)"},
         "roofline": main_r["roofline"],
         "layer_frac": main_r["layer_frac"],

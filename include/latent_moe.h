@@ -24,8 +24,8 @@
  *     when the handle was created; tensors are dense, row-major, in the
  *     [out_features, in_features] convention of the linear maps above.
  *   - Every pointer must be 16-byte aligned; H and P must be multiples of
- *     64, I a multiple of 128 (with BF16 activations all three multiples of
- *     256); 1 <= E <= 1024.
+ *     64, I a multiple of 128 (with BF16 activations, whatever the expert
+ *     format, all three multiples of 512); 1 <= E <= 1024.
  *   - Calls return 0 (LMOE_OK) or a negative error code; no exception or
  *     abort crosses the ABI. latent_moe_last_error() then holds a message for
  *     the calling thread. All argument checks run on the host before any GPU
@@ -66,7 +66,11 @@ typedef struct {
   float eps;            /* RMSNorm epsilon for both norms, finite, >= 0 */
   int32_t act_dtype;    /* x, pooler and unpooler: LMOE_F32 or LMOE_BF16 */
   int32_t expert_dtype; /* gate/up/down: LMOE_F32, LMOE_BF16 or LMOE_MXFP4.
-                           LMOE_F32 requires act_dtype LMOE_F32 and vice versa */
+                           LMOE_F32 requires act_dtype LMOE_F32 and vice versa;
+                           LMOE_MXFP4 runs with BF16 activations: each element
+                           is decoded exactly (code value x 2^(scale-127)) to
+                           BF16 in registers, and the products accumulate in
+                           FP32 as for BF16 experts */
   int64_t max_tokens;   /* upper bound on T per forward; sizes the workspace */
 } latent_moe_config;
 
@@ -74,8 +78,10 @@ typedef struct {
  * caller keeps them alive and unchanged until latent_moe_destroy returns.
  * With BF16 activations, create() also copies pooler, unpooler and the three
  * expert matrices into library-owned memory in a matrix-core tiled layout
- * (blocks of 32 rows x 64 columns ordered as the MFMA B fragments), and
- * splits the router into three BF16 pieces; forward then reads those copies.
+ * (blocks of 32 rows x 64 columns ordered as the MFMA B fragments; MXFP4
+ * codes and scales likewise, the scale bytes of four k-tiles side by side),
+ * and splits the router into three BF16 pieces; forward then reads those
+ * copies. An MXFP4 scale byte 0xFF (NaN in E8M0) makes its 32 elements NaN.
  *   router       [E, H]   F32
  *   router_bias  [E]      F32, or NULL for no bias (added to the logits)
  *   pooler       [P, H]   act_dtype

@@ -7,11 +7,13 @@
 //     k-tiles ahead, written to the LDS double buffer two k-tiles ahead, and
 //     read into fragment registers one MFMA step ahead;
 //   * B (weights) is loaded from global memory straight into the registers
-//     the MFMA reads, three k-tiles ahead, and never touches LDS. The weights are
-//     stored in a matrix-core packed layout (lm_packed_group), so each such
-//     load reads 1 KB of contiguous memory per wave: loading the row-major
-//     layout straight into MFMA registers would touch 32 cache lines per
-//     instruction and throttle the vector memory path.
+//     the MFMA reads, one or three k-tiles ahead, and never touches LDS. The
+//     weights are stored in a matrix-core packed layout (lm_packed_group,
+//     lm_packed_mx_group), so each such load reads 1 KB of contiguous memory
+//     per wave: loading the row-major layout straight into MFMA registers
+//     would touch 32 cache lines per instruction and throttle the vector
+//     memory path. MXFP4 weights arrive as E2M1 codes plus E8M0 scales and
+//     are decoded exactly to BF16 in registers right before their MFMA.
 // Per 64-wide k-tile a wave issues TM*TN*4 v_mfma_f32_32x32x16_bf16 and reads
 // only A from LDS: with TM = 4 that is about 64 B/clk/CU of LDS reads at full
 // matrix rate, against ~135 B/clk measured on MI355X, where a 64x64 wave tile
@@ -25,30 +27,45 @@
 
 #include "gemm.h"
 
-// Global prefetch distances in k-tiles. Deep (TM < 4, few accumulators: the
-// decode-sized tiles that only stream weights): B 3 ahead, A 4 ahead (A(kt+2)
-// is written to LDS at iteration kt; since vmcnt retires in issue order, that
-// store then waits only on loads issued two iterations earlier), register
-// rings of four k-tiles. Lean (TM = 4): B 1 ahead, A loaded and written
-// within the iteration, rings of two, small enough for two workgroups per CU
-// to hide each other's latency.
 #ifndef LM_WAVES_MAX
 #define LM_WAVES_MAX 2
 #endif
 
-// One workgroup per CU is intended (the accumulators alone take 128 AGPRs at
-// TM = 4), so let the compiler use the whole register file.
+// Problems whose expert weights are MXFP4 declare kMx = true.
+template <class P, class = void>
+struct LmIsMx : std::false_type {};
+template <class P>
+struct LmIsMx<P, std::void_t<decltype(P::kMx)>> : std::integral_constant<bool, P::kMx> {};
+
+// E8M0 scale code -> FP32 2^(code-127) (code 0 is the subnormal 2^-127,
+// code 255 is NaN).
+LM_DEV float lm_e8m0_to_f32(uint32_t code) {
+  return __uint_as_float(code == 0 ? 0x00400000u : code == 255 ? 0x7fc00000u : code << 23);
+}
+
+// The register budget allows two workgroups per CU (see kLeanA, kLeanB below).
 template <class Prob>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LM_WAVES_MAX, LM_WAVES_MAX)))
 void lm_gemm_stream_kernel(const Prob p) {
   using Cfg = typename Prob::Cfg;
   static_assert(Cfg::WM == 1 && Cfg::WN == 4, "streaming-B layout: four waves along N");
-  static_assert(sizeof(typename Cfg::E) == 2, "BF16 operands");
+  static_assert(sizeof(typename Cfg::E) == 2, "BF16 activations");
+  constexpr bool kMx = LmIsMx<Prob>::value;
   constexpr int TM = Cfg::TM, TN = Cfg::TN, BM = Cfg::BM;
-  constexpr bool kLean = TM >= 4;
-  constexpr int kRing = kLean ? 2 : 4;
-  constexpr int kDistB = kLean ? 1 : 3, kDistA = kLean ? 2 : 4;
-  constexpr int kStage = BM * 8;  // 16-byte chunks per A stage
+  // A (TM = 4): loaded and written to LDS within the iteration, two k-tiles
+  // ahead. A (TM < 4, decode-sized tiles): loaded four k-tiles ahead into a
+  // ring of four; A(kt+2) is written to LDS at iteration kt and, since vmcnt
+  // retires in issue order, that store then waits only on loads issued two
+  // iterations earlier. B: one k-tile ahead in a ring of two for BF16 weights
+  // with TM = 4 (small enough for two workgroups per CU to hide each other's
+  // latency); otherwise (few B registers: narrow tiles, MXFP4 codes) three
+  // ahead in a ring of four.
+  constexpr bool kLeanA = TM >= 4;
+  constexpr bool kLeanB = kLeanA && !kMx;
+  constexpr int kRingA = kLeanA ? 2 : 4, kRingB = kLeanB ? 2 : 4;
+  constexpr int kDistB = kLeanB ? 1 : 3, kDistA = kLeanA ? 2 : 4;
+  constexpr int kBq = kMx ? 1 : 4;  // 16-byte B loads per 32-row group and k-tile
+  constexpr int kStage = BM * 8;    // 16-byte chunks per A stage
   constexpr int QA = BM * 8 / 256;  // A chunks per thread per k-tile (= TM)
   __shared__ lm_u32x4 sa[2 * kStage];
 
@@ -63,16 +80,24 @@ void lm_gemm_stream_kernel(const Prob p) {
   const lm_u32x4* asrc[QA];
 #pragma unroll
   for (int q = 0; q < QA; ++q) asrc[q] = p.a_row(t, lr + 32 * q);
-  // B: wave w's j-th 32-row group in the matrix-core packed layout; the
-  // fragment of step s of k-tile kt is 1 KB at (kt*4 + s)*64 chunks.
+  // B: wave w's j-th 32-row group in the packed layout. BF16: the fragment
+  // of step s of k-tile kt is 1 KB at (kt*4 + s)*64 chunks. MXFP4: all four
+  // steps of k-tile kt are 1 KB at kt*64 chunks, scales a dword per lane per
+  // four k-tiles.
   const lm_u32x4* bsrc[TN];
+  const uint32_t* ssrc[TN];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) bsrc[j] = p.b_group(t, w, j) + lane;
+  for (int j = 0; j < TN; ++j) {
+    bsrc[j] = p.b_group(t, w, j) + lane;
+    if constexpr (kMx) ssrc[j] = p.b_scales(t, w, j) + lane;
+  }
 
   const int kt0 = t.kt0, kt1 = t.kt1, klast = kt1 - 1;
-  // Register rings: slot q holds A / B of the k-tile with kt % kRing == q
-  // (lean: A uses slot 0 only).
-  lm_u32x4 ra[kRing][QA], rb[kRing][TN][4];
+  // Register rings: slot q holds A / B of the k-tile with kt % ring == q
+  // (A with TM = 4 uses slot 0 past the prologue); MXFP4 scale dwords
+  // alternate per four k-tiles.
+  lm_u32x4 ra[kRingA][QA], rb[kRingB][TN][kBq];
+  uint32_t rsc[2][TN];
   auto load_a = [&](int slot, int kt) {
     const int ka = p.a_ktile(min(kt, klast));
 #pragma unroll
@@ -85,9 +110,21 @@ void lm_gemm_stream_kernel(const Prob p) {
   auto load_b = [&](int slot, int kt) {
     const int kc = min(kt, klast);
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (kMx) {
+        rb[slot][j][0] = bsrc[j][kc * 64];
+      } else {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) rb[slot][j][s] = bsrc[j][(kc * 4 + s) * 64];
+        for (int s = 0; s < 4; ++s) rb[slot][j][s] = bsrc[j][(kc * 4 + s) * 64];
+      }
+    }
+  };
+  auto load_scales = [&](int sslot, int kt) {
+    if constexpr (kMx) {
+      const int kc4 = min(kt, klast) >> 2;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) rsc[sslot][j] = ssrc[j][kc4 * 64];
+    }
   };
   // A fragments of one MFMA step, double-buffered across steps.
   lm_u32x4 fa[2][TM];
@@ -105,11 +142,29 @@ void lm_gemm_stream_kernel(const Prob p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  auto mma_step = [&](int fb, int slot, int s) {
+  // B fragment of step s: BF16 straight from the ring; MXFP4 decoded here,
+  // exactly, four codes pairs at a time (v_cvt_scalef32_pk_bf16_fp4).
+  auto b_frag = [&](int slot, int j, int s, int sq, int kb) -> lm_u32x4 {
+    if constexpr (kMx) {
+      const uint32_t codes = rb[slot][j][0][s];
+      const float scale = lm_e8m0_to_f32((rsc[sq][j] >> (8 * kb)) & 0xffu);
+      lm_u32x4 f;
+      f[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
+      f[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
+      f[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
+      f[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
+      return f;
+    } else {
+      return rb[slot][j][s];
+    }
+  };
+  auto mma_step = [&](int fb, int slot, int s, int sq, int kb) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < TN; ++j) {
+      const lm_u32x4 bf = b_frag(slot, j, s, sq, kb);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) LmElem<uint16_t>::mma(acc[i][j], fa[fb][i], rb[slot][j][s]);
+      for (int i = 0; i < TM; ++i) LmElem<uint16_t>::mma(acc[i][j], fa[fb][i], bf);
+    }
   };
   // Interleave within a step: the step's TM*TN MFMAs with the TM LDS reads
   // of the next step (and, where given, global loads), so LDS and memory
@@ -120,31 +175,27 @@ void lm_gemm_stream_kernel(const Prob p) {
       __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
       if constexpr (decltype(with_vmem)::value)
-        __builtin_amdgcn_sched_group_barrier(0x020, (QA + 4 * TN) / TM, 0);  // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x020, (QA + TN * kBq + TM - 1) / TM, 0);  // VMEM read
     }
   };
 
-  // Prologue: B(kt0 .. kt0+2) and A(kt0 .. kt0+3) in flight, A(kt0) and
-  // A(kt0+1) in the two LDS stages, step 0 of kt0 in registers.
-  if constexpr (kLean) {
-    load_b(0, kt0);
-    load_a(0, kt0);
-    load_a(1, kt0 + 1);
-  } else {
+  // Prologue: the first k-tiles in flight, A(kt0) and A(kt0+1) in the two LDS
+  // stages, step 0 of kt0 in registers.
 #pragma unroll
-    for (int d = 0; d < kDistA; ++d) {
-      if (d < kDistB) load_b(d, kt0 + d);
-      load_a(d, kt0 + d);
-    }
+  for (int d = 0; d < 4; ++d) {
+    if (d < kDistB) load_b(d, kt0 + d);
+    if (d < (kLeanA ? 2 : kDistA)) load_a(d, kt0 + d);
   }
+  load_scales(0, kt0);
   store_a(0, 0);
   store_a(1, 1);
   __syncthreads();
   read_frag(0, 0, 0);
 
-  // Iteration kt. On entry LDS stage kt&1 holds A(kt), stage (kt+1)&1 holds
-  // A(kt+1), fa[0] holds the fragments of (kt, step 0).
-  //   step 0: MFMA(kt,0) | LDS reads (kt,1) | global loads B(kt+3), A(kt+4)
+  // Iteration kt (q = kt % 8). On entry LDS stage kt&1 holds A(kt), stage
+  // (kt+1)&1 holds A(kt+1), fa[0] holds the fragments of (kt, step 0).
+  //   step 0: MFMA(kt,0) | LDS reads (kt,1) | global loads of B(kt+kDistB),
+  //           A(kt+kDistA) and, every fourth k-tile, MXFP4 scales
   //   step 1: MFMA(kt,1) | LDS reads (kt,2)
   //   step 2: MFMA(kt,2) | LDS reads (kt,3)
   //   barrier: every wave's reads of stage kt&1 are done, and A(kt+1)
@@ -153,35 +204,44 @@ void lm_gemm_stream_kernel(const Prob p) {
   //   store A(kt+2) into stage kt&1 (published by the next iteration's
   //   barrier, before its step 3 reads it)
   // One barrier per k-tile, and the matrix pipe never waits for LDS data
-  // issued in the same step.
-  auto iter = [&](int kt, int q) {
-    const int cur = q & 1, nxt = cur ^ 1;
+  // issued in the same step. The k-tile count is a multiple of 8 and kt0 a
+  // multiple of 8 (validated on the host), so ring slots are compile-time;
+  // indices past the end are clamped: those loads are issued but unused.
+  auto iter = [&](int kt, auto qc) {
+    constexpr int q = decltype(qc)::value;
+    constexpr int cur = q & 1, nxt = cur ^ 1, slot = q % kRingB;
+    constexpr int sq = (q >> 2) & 1, kb = q & 3;
     read_frag(1, cur, 1);
-    load_b((q + kDistB) % kRing, kt + kDistB);
-    load_a(kLean ? 0 : (q + kDistA) % kRing, kt + kDistA);
-    mma_step(0, q % kRing, 0);
+    load_b((q + kDistB) % kRingB, kt + kDistB);
+    if constexpr ((q + kDistB) % 4 == 0) load_scales(((q + kDistB) >> 2) & 1, kt + kDistB);
+    load_a(kLeanA ? 0 : (q + kDistA) % kRingA, kt + kDistA);
+    mma_step(0, slot, 0, sq, kb);
     pattern(std::true_type{});
     __builtin_amdgcn_sched_barrier(0);
     read_frag(0, cur, 2);
-    mma_step(1, q % kRing, 1);
+    mma_step(1, slot, 1, sq, kb);
     pattern(std::false_type{});
     __builtin_amdgcn_sched_barrier(0);
     read_frag(1, cur, 3);
-    mma_step(0, q % kRing, 2);
+    mma_step(0, slot, 2, sq, kb);
     pattern(std::false_type{});
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     read_frag(0, nxt, 0);
-    mma_step(1, q % kRing, 3);
+    mma_step(1, slot, 3, sq, kb);
     pattern(std::false_type{});
     __builtin_amdgcn_sched_barrier(0);
-    store_a(kLean ? 0 : (q + 2) % kRing, cur);
+    store_a(kLeanA ? 0 : (q + 2) % kRingA, cur);
   };
-  for (int kt = kt0; kt < kt1; kt += 4) {
-    iter(kt, 0);
-    iter(kt + 1, 1);
-    iter(kt + 2, 2);
-    iter(kt + 3, 3);
+  for (int kt = kt0; kt < kt1; kt += 8) {
+    iter(kt, std::integral_constant<int, 0>{});
+    iter(kt + 1, std::integral_constant<int, 1>{});
+    iter(kt + 2, std::integral_constant<int, 2>{});
+    iter(kt + 3, std::integral_constant<int, 3>{});
+    iter(kt + 4, std::integral_constant<int, 4>{});
+    iter(kt + 5, std::integral_constant<int, 5>{});
+    iter(kt + 6, std::integral_constant<int, 6>{});
+    iter(kt + 7, std::integral_constant<int, 7>{});
   }
   __syncthreads();
   p.epilogue(t, acc, 0, w, lane, (void*)sa);

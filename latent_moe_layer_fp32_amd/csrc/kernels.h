@@ -45,6 +45,38 @@ __global__ void lm_pack_mfma_kernel(const lm_u32x4* src, lm_u32x4* dst, int64_t 
   }
 }
 
+// MXFP4 weights use the same 32-row blocks: for k-tile kt (64 columns) of a
+// 32-row group, lane L = 32h + r holds the 32 E2M1 codes of row r, columns
+// [64kt + 32h, 64kt + 32h + 32) as 16 bytes (element 2i in the low nibble):
+// exactly one 32-element scale block, and bytes 4s..4s+3 are the B fragment
+// of MFMA step s. The 64 lanes of a k-tile are 1 KB contiguous. Scales: one
+// byte per lane and k-tile, packed as a dword per lane for four k-tiles:
+//   scale byte of (group g, k-tile kt, lane L) at ((g*K/256 + kt/4)*64 + L)*4 + kt%4.
+LM_DEV const lm_u32x4* lm_packed_mx_group(const void* base, int64_t row0, int K) {
+  return (const lm_u32x4*)base + (row0 / 32) * (int64_t)(K / 64) * 64;
+}
+LM_DEV const uint32_t* lm_packed_mx_scales(const void* base, int64_t row0, int K) {
+  return (const uint32_t*)base + (row0 / 32) * (int64_t)(K / 256) * 64;
+}
+
+__global__ void lm_pack_mx_kernel(const lm_u32x4* src, const uint8_t* src_scales, lm_u32x4* dst,
+                                  uint8_t* dst_scales, int64_t rows, int K) {
+  const int64_t n = rows * (K / 32);  // 16-byte chunks (32 codes each)
+  const int ktiles = K / 64;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t blk = i >> 6;
+    const int lane = (int)(i & 63);
+    const int64_t g = blk / ktiles;
+    const int kt = (int)(blk - g * ktiles);
+    const int h = lane >> 5;
+    const int64_t row = g * 32 + (lane & 31);
+    const int64_t sidx = row * (K / 32) + 2 * kt + h;  // source chunk == source scale index
+    dst[i] = src[sidx];
+    dst_scales[((g * (K / 256) + kt / 4) * 64 + lane) * 4 + (kt & 3)] = src_scales[sidx];
+  }
+}
+
 // ----------------------------------------------------------------- router
 // Partial logits over k-splits: part[s][t][e] = sum over split s of x[t,k] W[e,k],
 // accumulated as FP64 sums of per-k-tile FP32 matrix-core chains.
@@ -196,12 +228,15 @@ LM_DEV bool lm_group_tile(const int* tile_off, const int* offsets, const int* co
 // B tile rows: wave column wn owns rows [64 wn, 64 wn + 64): the first 32 are
 // gate rows, the next 32 the up rows of the same 32 output columns, so each
 // lane holds g and v of the same element.
-template <class Cfg_>
+template <class Cfg_, bool MX_ = false>
 struct GateUpProb {
   using Cfg = Cfg_;
   using E = typename Cfg::E;
   static_assert(Cfg::TN == 2, "gate/up pairs");
   static constexpr int kCols = Cfg::WN * 32;
+  static constexpr bool kMx = MX_;  // weights in the packed MXFP4 layout
+  const void* sg = nullptr;  // packed scales (MXFP4)
+  const void* su = nullptr;
   const E* pooled;
   const E* wg;
   const E* wu;
@@ -230,7 +265,11 @@ struct GateUpProb {
     return (const lm_u32x4*)(base + ((size_t)t.e * I + col) * P);
   }
   LM_DEV const lm_u32x4* b_group(const LmTile& t, int wv, int j) const {
-    return lm_packed_group(j ? wu : wg, (int64_t)t.e * I + t.n0 + wv * 32, P);
+    if constexpr (kMx) return lm_packed_mx_group(j ? wu : wg, (int64_t)t.e * I + t.n0 + wv * 32, P);
+    else return lm_packed_group(j ? wu : wg, (int64_t)t.e * I + t.n0 + wv * 32, P);
+  }
+  LM_DEV const uint32_t* b_scales(const LmTile& t, int wv, int j) const {
+    return lm_packed_mx_scales(j ? su : sg, (int64_t)t.e * I + t.n0 + wv * 32, P);
   }
   LM_DEV int a_ktile(int kt) const { return kt; }
   LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
@@ -255,10 +294,12 @@ struct GateUpProb {
 // -------------------------------------------------------------------- down
 // o = act Wd_e^T for the rows of expert e; writes o (FP32) and per row and
 // n-tile the partial sum of o^2 for the per-expert RMSNorm.
-template <class Cfg_>
+template <class Cfg_, bool MX_ = false>
 struct DownProb {
   using Cfg = Cfg_;
   using E = typename Cfg::E;
+  static constexpr bool kMx = MX_;  // weights in the packed MXFP4 layout
+  const void* sd = nullptr;         // packed scales (MXFP4)
   const E* act;
   const E* wd;
   const int* counts;
@@ -281,7 +322,12 @@ struct DownProb {
     return (const lm_u32x4*)(wd + ((size_t)t.e * P + min(t.n0 + r, P - 1)) * I);
   }
   LM_DEV const lm_u32x4* b_group(const LmTile& t, int wv, int j) const {
-    return lm_packed_group(wd, (int64_t)t.e * P + min(t.n0 + (wv * Cfg::TN + j) * 32, P - 32), I);
+    const int64_t row0 = (int64_t)t.e * P + min(t.n0 + (wv * Cfg::TN + j) * 32, P - 32);
+    if constexpr (kMx) return lm_packed_mx_group(wd, row0, I);
+    else return lm_packed_group(wd, row0, I);
+  }
+  LM_DEV const uint32_t* b_scales(const LmTile& t, int wv, int j) const {
+    return lm_packed_mx_scales(sd, (int64_t)t.e * P + min(t.n0 + (wv * Cfg::TN + j) * 32, P - 32), I);
   }
   LM_DEV int a_ktile(int kt) const { return kt; }
   LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,

@@ -66,7 +66,7 @@ struct Layout {
 };
 
 // Split-K plan for a dense BF16 projection: split only when the output tiles
-// cannot cover the chip; each split a multiple of 4 k-tiles (the streaming
+// cannot cover the chip; each split a multiple of 8 k-tiles (the streaming
 // kernel's unroll).
 void dense_split(int64_t T, int64_t N, int64_t K, int BM, int BN, int& splits, int& kt_per) {
   const int64_t tiles = ceil_div(T, BM) * (int64_t)ceil_div(N, BN);
@@ -75,9 +75,9 @@ void dense_split(int64_t T, int64_t N, int64_t K, int BM, int BN, int& splits, i
   kt_per = ktiles;
   if (tiles >= 256) return;
   int want = ceil_div(512, tiles);
-  if (want > ktiles / 4) want = ktiles / 4;
+  if (want > ktiles / 8) want = ktiles / 8;
   if (want <= 1) return;
-  kt_per = (ceil_div(ktiles, want) + 3) / 4 * 4;
+  kt_per = (ceil_div(ktiles, want) + 7) / 8 * 8;
   splits = ceil_div(ktiles, kt_per);
 }
 
@@ -99,6 +99,9 @@ struct latent_moe {
   const void* pk_gate;
   const void* pk_up;
   const void* pk_down;
+  const void* pk_sgate;  // MXFP4: packed scales
+  const void* pk_sup;
+  const void* pk_sdown;
   bool prof;                       // record stage events in forward
   bool prof_valid;                 // a forward has recorded a full set
   hipEvent_t ev[kStages + 1];      // created by latent_moe_set_profiling
@@ -156,10 +159,9 @@ int validate_config(const latent_moe_config* c) {
   if (!act_ok || !exp_ok) return fail(LMOE_ERR_INVALID_ARG, "unknown dtype code");
   if ((c->act_dtype == LMOE_F32) != (c->expert_dtype == LMOE_F32))
     return fail(LMOE_ERR_UNSUPPORTED, "FP32 experts need FP32 activations and vice versa");
-  if (c->act_dtype == LMOE_BF16 && (c->hidden % 256 || c->pooled % 256 || c->intermediate % 256))
-    return fail(LMOE_ERR_INVALID_ARG, "BF16 layers need hidden, pooled and intermediate to be multiples of 256");
-  if (c->expert_dtype == LMOE_MXFP4)
-    return fail(LMOE_ERR_UNSUPPORTED, "MXFP4 expert weights are not built into this library");
+  if (c->act_dtype == LMOE_BF16 && (c->hidden % 512 || c->pooled % 512 || c->intermediate % 512))
+    return fail(LMOE_ERR_INVALID_ARG,
+                "BF16 layers need hidden, pooled and intermediate to be multiples of 512");
   if ((size_t)c->pooled * c->intermediate * c->experts > ((size_t)1 << 40))
     return fail(LMOE_ERR_INVALID_ARG, "expert tensors too large");
   return LMOE_OK;
@@ -238,7 +240,7 @@ hipError_t launch(const Prob& p, int64_t units, hipStream_t s) {
     if (h->prof) LM_HIP(hipEventRecord(h->ev[(i)], s));  \
   } while (0)
 
-template <typename Et, template <typename> class CW, template <typename> class CR>
+template <typename Et, template <typename> class CW, template <typename> class CR, bool MX = false>
 int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_t s) {
   const latent_moe_config& c = h->cfg;
   const latent_moe_weights& w = h->w;
@@ -371,7 +373,11 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   const int64_t max_tiles = ceil_div(npairs, Cw::BM) + (npairs < E ? npairs : E);
   // 5. gate/up + SwiGLU
   {
-    GateUpProb<Cw> p;
+    GateUpProb<Cw, MX> p;
+    if constexpr (MX) {
+      p.sg = h->pk_sgate;
+      p.su = h->pk_sup;
+    }
     p.pooled = pooled;
     p.wg = (const Et*)Wgate;
     p.wu = (const Et*)Wup;
@@ -384,14 +390,15 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.P = P;
     p.I = I;
     p.Ex = E;
-    p.nt = I / GateUpProb<Cw>::kCols;
+    p.nt = I / GateUpProb<Cw, MX>::kCols;
     LM_HIP(launch(p, max_tiles * p.nt, s));
   }
   LM_MARK(6);
   // 6. down + per-row sum of squares partials
   const int dnt = ceil_div(P, Cw::BN);
   {
-    DownProb<Cw> p;
+    DownProb<Cw, MX> p;
+    if constexpr (MX) p.sd = h->pk_sdown;
     p.act = act;
     p.wd = (const Et*)Wdown;
     p.counts = counts;
@@ -483,6 +490,14 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
   }
   if (w->router_bias && !aligned16(w->router_bias))
     return fail(LMOE_ERR_INVALID_ARG, "router_bias is not 16-byte aligned");
+  if (cfg->expert_dtype == LMOE_MXFP4) {
+    const void* sc[] = {w->s_gate, w->s_up, w->s_down};
+    const char* sn[] = {"s_gate", "s_up", "s_down"};
+    for (int i = 0; i < 3; ++i) {
+      if (!sc[i]) return fail(LMOE_ERR_INVALID_ARG, "MXFP4 scale array %s is NULL", sn[i]);
+      if (!aligned16(sc[i])) return fail(LMOE_ERR_INVALID_ARG, "scale array %s is not 16-byte aligned", sn[i]);
+    }
+  }
 
   int ndev = 0;
   hipError_t he = hipGetDeviceCount(&ndev);
@@ -506,29 +521,38 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
   }
   if (cfg->act_dtype == LMOE_BF16) {
     const size_t E = cfg->experts, H = cfg->hidden, P = cfg->pooled, I = cfg->intermediate;
-    const size_t sz_pool = H * P * 2, sz_exp = E * I * P * 2;
-    h->packed_bytes = 2 * sz_pool + 3 * sz_exp;
+    const bool mx = cfg->expert_dtype == LMOE_MXFP4;
+    const size_t sz_pool = H * P * 2, sz_exp = mx ? E * I * P / 2 : E * I * P * 2;
+    const size_t sz_sc = mx ? E * I * P / 32 : 0;
+    h->packed_bytes = 2 * sz_pool + 3 * sz_exp + 3 * sz_sc;
     he = hipMalloc((void**)&h->packed, h->packed_bytes);
     if (he != hipSuccess) {
       (void)hipGetLastError();
       (void)hipFree(h->ws);
       delete h;
-      return fail(LMOE_ERR_OOM, "hipMalloc of %zu bytes for packed weights failed", 2 * sz_pool + 3 * sz_exp);
+      return fail(LMOE_ERR_OOM, "hipMalloc of %zu bytes for packed weights failed", h->packed_bytes);
     }
     h->pk_pooler = h->packed;
     h->pk_unpooler = h->packed + sz_pool;
     h->pk_gate = h->packed + 2 * sz_pool;
     h->pk_up = h->packed + 2 * sz_pool + sz_exp;
     h->pk_down = h->packed + 2 * sz_pool + 2 * sz_exp;
-    struct Job { const void* src; const void* dst; int64_t rows; int K; };
-    const Job jobs[] = {{w->pooler, h->pk_pooler, (int64_t)P, (int)H},
-                        {w->unpooler, h->pk_unpooler, (int64_t)H, (int)P},
-                        {w->w_gate, h->pk_gate, (int64_t)(E * I), (int)P},
-                        {w->w_up, h->pk_up, (int64_t)(E * I), (int)P},
-                        {w->w_down, h->pk_down, (int64_t)(E * P), (int)I}};
+    h->pk_sgate = h->packed + 2 * sz_pool + 3 * sz_exp;
+    h->pk_sup = h->packed + 2 * sz_pool + 3 * sz_exp + sz_sc;
+    h->pk_sdown = h->packed + 2 * sz_pool + 3 * sz_exp + 2 * sz_sc;
+    struct Job { const void* src; const void* src_s; const void* dst; const void* dst_s; int64_t rows; int K; bool mx; };
+    const Job jobs[] = {{w->pooler, nullptr, h->pk_pooler, nullptr, (int64_t)P, (int)H, false},
+                        {w->unpooler, nullptr, h->pk_unpooler, nullptr, (int64_t)H, (int)P, false},
+                        {w->w_gate, w->s_gate, h->pk_gate, h->pk_sgate, (int64_t)(E * I), (int)P, mx},
+                        {w->w_up, w->s_up, h->pk_up, h->pk_sup, (int64_t)(E * I), (int)P, mx},
+                        {w->w_down, w->s_down, h->pk_down, h->pk_sdown, (int64_t)(E * P), (int)I, mx}};
     for (const Job& j : jobs) {
-      hipLaunchKernelGGL(lm_pack_mfma_kernel, dim3(65536), dim3(256), 0, 0, (const lm_u32x4*)j.src,
-                         (lm_u32x4*)j.dst, j.rows, j.K);
+      if (j.mx)
+        hipLaunchKernelGGL(lm_pack_mx_kernel, dim3(65536), dim3(256), 0, 0, (const lm_u32x4*)j.src,
+                           (const uint8_t*)j.src_s, (lm_u32x4*)j.dst, (uint8_t*)j.dst_s, j.rows, j.K);
+      else
+        hipLaunchKernelGGL(lm_pack_mfma_kernel, dim3(65536), dim3(256), 0, 0, (const lm_u32x4*)j.src,
+                           (lm_u32x4*)j.dst, j.rows, j.K);
     }
     const size_t n = (size_t)cfg->experts * cfg->hidden;
     unsigned blocks = (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
@@ -569,6 +593,9 @@ int latent_moe_forward(latent_moe_t* h, const void* x, int64_t T, float* out, in
   if (h->cfg.act_dtype == LMOE_F32)
     rc = nar ? forward_impl<float, CfgNarrow, CfgRouterNarrow>(h, x, T, out, s)
              : forward_impl<float, CfgWide, CfgRouterWide>(h, x, T, out, s);
+  else if (h->cfg.expert_dtype == LMOE_MXFP4)
+    rc = nar ? forward_impl<uint16_t, CfgNarrow, CfgRouterNarrow, true>(h, x, T, out, s)
+             : forward_impl<uint16_t, CfgWide, CfgRouterWide, true>(h, x, T, out, s);
   else
     rc = nar ? forward_impl<uint16_t, CfgNarrow, CfgRouterNarrow>(h, x, T, out, s)
              : forward_impl<uint16_t, CfgWide, CfgRouterWide>(h, x, T, out, s);

@@ -12,6 +12,7 @@ Workloads (one per layer configuration the method is exercised on):
 * ``decode``   T=64,  H=8192, P=4096, E=256, I=4096, k=8, BF16 x/projections/experts
 * ``prefill``  T=16384, shapes as ``decode``
 * ``mxfp4``    ``prefill`` with the expert weights quantised to MXFP4
+* ``mxfp4_decode`` ``decode`` with the same MXFP4 expert weights
 * ``skew``     5 chunks of 16384 tokens, BF16, with a Zipf(s=1.1) router bias
 
 Value distributions: x ~ N(0,1); every weight ~ N(0, 1/fan_in); RMSNorm gammas
@@ -65,6 +66,7 @@ CONFIGS = {
     "decode": LayerSpec("decode", T=64, **_REAL),
     "prefill": LayerSpec("prefill", T=16384, **_REAL),
     "mxfp4": LayerSpec("mxfp4", T=16384, expert_format="mxfp4", **_REAL),
+    "mxfp4_decode": LayerSpec("mxfp4_decode", T=64, expert_format="mxfp4", **_REAL),
     "skew": LayerSpec("skew", T=16384, router_bias="zipf", chunks=5, **_REAL),
 }
 

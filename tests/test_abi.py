@@ -54,6 +54,9 @@ def test_workspace_bytes_real_shapes():
     (dict(max_tokens=0), B.LMOE_ERR_INVALID_ARG),
     (dict(act_dtype=7), B.LMOE_ERR_INVALID_ARG),
     (dict(act_dtype="f32", expert_dtype="bf16"), B.LMOE_ERR_UNSUPPORTED),
+    (dict(act_dtype="f32", expert_dtype="mxfp4"), B.LMOE_ERR_UNSUPPORTED),
+    (dict(intermediate=4096 + 256), B.LMOE_ERR_INVALID_ARG),  # BF16: multiples of 512
+    (dict(expert_dtype="mxfp4", pooled=4096 + 256), B.LMOE_ERR_INVALID_ARG),
 ])
 def test_bad_configs_rejected(kw, code):
     with pytest.raises(B.LatentMoEError) as ei:
@@ -78,6 +81,23 @@ def test_create_rejects_null_and_misaligned_weights():
     assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
     assert "aligned" in B.latent_moe_last_error()
     assert L.latent_moe_create(None, ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+
+
+def test_mxfp4_accepted_and_scales_required():
+    assert B.latent_moe_workspace_bytes(real_cfg(expert_dtype="mxfp4")) == \
+        B.latent_moe_workspace_bytes(real_cfg())
+    L = B.lib()
+    cfg = real_cfg(expert_dtype="mxfp4")
+    h = ctypes.c_void_p(0)
+    w = B.Weights()
+    for n in ("router", "pooler", "pool_gamma", "w_gate", "w_up", "w_down", "expert_gamma", "unpooler",
+              "s_gate", "s_up"):
+        setattr(w, n, 4096)
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+    assert "s_down" in B.latent_moe_last_error()
+    w.s_down = 4096 + 4
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+    assert "aligned" in B.latent_moe_last_error()
 
 
 @pytest.mark.skipif(_has_device(), reason="checks the no-device error path")

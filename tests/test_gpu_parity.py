@@ -5,9 +5,13 @@ E=256, I=4096, k=8, BF16): routing on every token, outputs and stage
 intermediates on sampled tokens (the layer is token-local, so the oracle on a
 token subset is exact for those rows).
 
+MXFP4 expert weights: the same real shapes, compared with the oracle run on
+the identically decoded weights.
+
 Tolerances: routing ids bit-exact except reported near-ties (< 1e-6 apart in
 the FP64 logits), routing weights within 1e-6; outputs max-abs <= 2e-2 x RMS
-(BF16), <= 1e-4 x RMS for the FP32 layer (its expected error is ~1e-6).
+(BF16), <= 5e-2 x RMS (MXFP4), <= 1e-4 x RMS for the FP32 layer (its expected
+error is ~1e-6).
 """
 import sys
 
@@ -254,3 +258,43 @@ def test_skewed_chunk_parity(torch_dev, tables, real):
     say(f"skew: max expert load {counts.max()} (mean {counts.mean():.0f}), idle experts {(counts == 0).sum()}")
     assert counts.max() > 10 * counts.mean()
     layer.close()
+
+
+# ------------------------------------------------------ MXFP4 expert weights
+
+TOL_MXFP4 = 5e-2  # against the oracle on the identically decoded weights
+
+
+@pytest.fixture(scope="module")
+def mx(torch_dev, tables):
+    spec = synth.CONFIGS["mxfp4"]
+    say("generating real-shape MXFP4 expert weights on the device")
+    wts = device_weights(spec, tables)
+    torch_dev.cuda.synchronize()
+    layer = make_layer(spec, wts, max_tokens=spec.T)
+    host = HostLayer(spec)
+    yield spec, wts, layer, host
+    layer.close()
+
+
+def test_mxfp4_decode_parity(torch_dev, tables, mx):
+    torch = torch_dev
+    spec, _, layer, host = mx
+    dspec = synth.CONFIGS["mxfp4_decode"]
+    say("case: decode, MXFP4 experts, T=64")
+    x = synth.device_tensor(dspec, "x", tables)
+    xh = synth.host(dspec, "x")
+    sample = np.random.default_rng(11).choice(dspec.T, 6, replace=False)
+    _sampled_parity(torch, dspec, layer, host, x, xh, sample, TOL_MXFP4, "mxfp4 decode")
+
+
+@pytest.mark.parametrize("T", [16384, 777])
+def test_mxfp4_prefill_parity(torch_dev, tables, mx, T):
+    torch = torch_dev
+    spec, _, layer, host = mx
+    say(f"case: prefill, MXFP4 experts, T={T}")
+    x = synth.device_tensor(spec, "x", tables)[:T].contiguous()
+    xh = synth.host(spec, "x")[:T]
+    sample = np.sort(np.random.default_rng(T + 1).choice(T, 4, replace=False))
+    sample[-1] = T - 1
+    _sampled_parity(torch, spec, layer, host, x, xh, sample, TOL_MXFP4, f"mxfp4 prefill T={T}")
