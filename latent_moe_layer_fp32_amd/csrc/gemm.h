@@ -21,6 +21,9 @@
 // a_ktile() (k-tile index into A; lets the router reuse x across the three
 // BF16 pieces of its FP32 weights) and epilogue().
 #pragma once
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 
 template <typename E>
@@ -70,6 +73,15 @@ struct LmTile {
   int kt0, kt1;  // k-tile range
   int e;     // expert (grouped problems) or k-split index
 };
+
+// Problems whose epilogue needs one value per tile row (gathered from memory)
+// declare row_value(); it is loaded at the start of the tile, so its latency
+// hides behind the main loop, and handed to the epilogue through LDS.
+template <class P, class = void>
+struct LmHasRowValue : std::false_type {};
+template <class P>
+struct LmHasRowValue<P, std::void_t<decltype(std::declval<const P&>().row_value(std::declval<const LmTile&>(), 0))>>
+    : std::true_type {};
 
 LM_DEV int lm_swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
@@ -126,6 +138,9 @@ __global__ __launch_bounds__(256) void lm_gemm_kernel(const Prob p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
   const int lc = tid & 7, lr = tid >> 3;
+  float rowv = 0.0f;
+  if constexpr (LmHasRowValue<Prob>::value)
+    if (tid < Cfg::BM) rowv = p.row_value(t, tid);
 
   const lm_u32x4* ap[QA];
   const lm_u32x4* bp[QB];
@@ -202,6 +217,10 @@ __global__ __launch_bounds__(256) void lm_gemm_kernel(const Prob p) {
     if (more) sstore(buf ^ 1);
     __syncthreads();
     buf ^= 1;
+  }
+  if constexpr (LmHasRowValue<Prob>::value) {
+    if (tid < Cfg::BM) ((float*)&sm)[tid] = rowv;
+    __syncthreads();
   }
   if constexpr (Cfg::FLUSH)
     p.epilogue_f64(t, acc2, wm, wn, lane);

@@ -52,14 +52,16 @@ void lm_gemm_stream_kernel(const Prob p) {
   static_assert(sizeof(typename Cfg::E) == 2, "BF16 activations");
   constexpr bool kMx = LmIsMx<Prob>::value;
   constexpr int TM = Cfg::TM, TN = Cfg::TN, BM = Cfg::BM;
-  // A (TM = 4): loaded and written to LDS within the iteration, two k-tiles
-  // ahead. A (TM < 4, decode-sized tiles): loaded four k-tiles ahead into a
-  // ring of four; A(kt+2) is written to LDS at iteration kt and, since vmcnt
-  // retires in issue order, that store then waits only on loads issued two
-  // iterations earlier. B: one k-tile ahead in a ring of two for BF16 weights
-  // with TM = 4 (small enough for two workgroups per CU to hide each other's
-  // latency); otherwise (few B registers: narrow tiles, MXFP4 codes) three
-  // ahead in a ring of four.
+  // A (TM = 4): one register slot; A(kt+3) is loaded right after A(kt+2)
+  // has been written to LDS at the end of iteration kt, so it has a whole
+  // iteration in flight, and since vmcnt retires in issue order, the store
+  // that waits for it does not also wait for the B loads issued after it.
+  // A (TM < 4, decode-sized tiles): loaded four k-tiles ahead into a ring of
+  // four; A(kt+2) is written to LDS at iteration kt and waits only on loads
+  // issued two iterations earlier. B: one k-tile ahead in a ring of two for
+  // BF16 weights with TM = 4 (small enough for two workgroups per CU to hide
+  // each other's latency); otherwise (few B registers: narrow tiles, MXFP4
+  // codes) three ahead in a ring of four.
   constexpr bool kLeanA = TM >= 4;
   constexpr bool kLeanB = kLeanA && !kMx;
   constexpr int kRingA = kLeanA ? 2 : 4, kRingB = kLeanB ? 2 : 4;
@@ -74,6 +76,9 @@ void lm_gemm_stream_kernel(const Prob p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, r = lane & 31;
+  float rowv = 0.0f;
+  if constexpr (LmHasRowValue<Prob>::value)
+    if (tid < BM) rowv = p.row_value(t, tid);
   const int lc = tid & 7, lr = tid >> 3;
 
   // A: thread loads chunk lc of tile rows lr + 32 q.
@@ -175,7 +180,7 @@ void lm_gemm_stream_kernel(const Prob p) {
       __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
       if constexpr (decltype(with_vmem)::value)
-        __builtin_amdgcn_sched_group_barrier(0x020, (QA + TN * kBq + TM - 1) / TM, 0);  // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x020, ((kLeanA ? 0 : QA) + TN * kBq + TM - 1) / TM, 0);  // VMEM read
     }
   };
 
@@ -189,20 +194,21 @@ void lm_gemm_stream_kernel(const Prob p) {
   load_scales(0, kt0);
   store_a(0, 0);
   store_a(1, 1);
+  if constexpr (kLeanA) load_a(0, kt0 + 2);
   __syncthreads();
   read_frag(0, 0, 0);
 
   // Iteration kt (q = kt % 8). On entry LDS stage kt&1 holds A(kt), stage
   // (kt+1)&1 holds A(kt+1), fa[0] holds the fragments of (kt, step 0).
   //   step 0: MFMA(kt,0) | LDS reads (kt,1) | global loads of B(kt+kDistB),
-  //           A(kt+kDistA) and, every fourth k-tile, MXFP4 scales
+  //           A(kt+4) (TM < 4) and, every fourth k-tile, MXFP4 scales
   //   step 1: MFMA(kt,1) | LDS reads (kt,2)
   //   step 2: MFMA(kt,2) | LDS reads (kt,3)
   //   barrier: every wave's reads of stage kt&1 are done, and A(kt+1)
   //            (stored in the previous iteration) is visible
   //   step 3: MFMA(kt,3) | LDS reads (kt+1,0) from stage (kt+1)&1
   //   store A(kt+2) into stage kt&1 (published by the next iteration's
-  //   barrier, before its step 3 reads it)
+  //   barrier, before its step 3 reads it); TM = 4: load A(kt+3)
   // One barrier per k-tile, and the matrix pipe never waits for LDS data
   // issued in the same step. The k-tile count is a multiple of 8 and kt0 a
   // multiple of 8 (validated on the host), so ring slots are compile-time;
@@ -214,7 +220,7 @@ void lm_gemm_stream_kernel(const Prob p) {
     read_frag(1, cur, 1);
     load_b((q + kDistB) % kRingB, kt + kDistB);
     if constexpr ((q + kDistB) % 4 == 0) load_scales(((q + kDistB) >> 2) & 1, kt + kDistB);
-    load_a(kLeanA ? 0 : (q + kDistA) % kRingA, kt + kDistA);
+    if constexpr (!kLeanA) load_a((q + kDistA) % kRingA, kt + kDistA);
     mma_step(0, slot, 0, sq, kb);
     pattern(std::true_type{});
     __builtin_amdgcn_sched_barrier(0);
@@ -232,6 +238,8 @@ void lm_gemm_stream_kernel(const Prob p) {
     pattern(std::false_type{});
     __builtin_amdgcn_sched_barrier(0);
     store_a(kLeanA ? 0 : (q + 2) % kRingA, cur);
+    if constexpr (kLeanA) load_a(0, kt + 3);
+    __builtin_amdgcn_sched_barrier(0);
   };
   for (int kt = kt0; kt < kt1; kt += 8) {
     iter(kt, std::integral_constant<int, 0>{});
@@ -244,5 +252,9 @@ void lm_gemm_stream_kernel(const Prob p) {
     iter(kt + 7, std::integral_constant<int, 7>{});
   }
   __syncthreads();
+  if constexpr (LmHasRowValue<Prob>::value) {
+    if (tid < BM) ((float*)sa)[tid] = rowv;
+    __syncthreads();
+  }
   p.epilogue(t, acc, 0, w, lane, (void*)sa);
 }

@@ -272,22 +272,33 @@ struct GateUpProb {
     return lm_packed_mx_scales(j ? su : sg, (int64_t)t.e * I + t.n0 + wv * 32, P);
   }
   LM_DEV int a_ktile(int kt) const { return kt; }
+  // the token's RMSNorm row scale (gathered), one per tile row
+  LM_DEV float row_value(const LmTile& t, int r) const {
+    return row_scale[perm_token[t.m0 + min(r, t.rows - 1)]];
+  }
   LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
-                       int lane, void*) const {
+                       int lane, void* smem) const {
+    const float* rs = (const float*)smem;  // row_value() of each tile row
     const int col = t.n0 + wn * 32 + (lane & 31);
+    auto put = [&](int tm, int i) {
+      const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
+      const float r = rs[row];
+      const float g = r * acc[tm][0][i];
+      const float v = r * acc[tm][1][i];
+      act[(size_t)(t.m0 + row) * I + col] = LmElem<E>::from_f32(lm_silu(g) * v);
+    };
+    if (t.rows == Cfg::BM) {
 #pragma unroll
-    for (int tm = 0; tm < Cfg::TM; ++tm)
+      for (int tm = 0; tm < Cfg::TM; ++tm)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
-        if (row < t.rows) {
-          const int pr = t.m0 + row;
-          const float r = row_scale[perm_token[pr]];
-          const float g = r * acc[tm][0][i];
-          const float v = r * acc[tm][1][i];
-          act[(size_t)pr * I + col] = LmElem<E>::from_f32(lm_silu(g) * v);
-        }
-      }
+        for (int i = 0; i < 16; ++i) put(tm, i);
+    } else {
+#pragma unroll
+      for (int tm = 0; tm < Cfg::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (lm_acc_row<Cfg>(wm, tm, i, lane) < t.rows) put(tm, i);
+    }
   }
 };
 
