@@ -110,7 +110,8 @@ typedef struct {
 /* Create a handle on the current device. Validates cfg and w, allocates the
  * workspace for cfg->max_tokens tokens (never reallocated later) and, for
  * BF16 activations, the repacked weight copies (about the size of the expert
- * weights again), and synchronises the device before returning.
+ * weights again), creates the handle's routing stream (default priority),
+ * and synchronises the device before returning.
  * Errors: INVALID_ARG, UNSUPPORTED, OOM, HIP. On error *out is set to NULL
  * and nothing is leaked. */
 int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const latent_moe_weights* w);
@@ -130,6 +131,10 @@ int latent_moe_workspace_bytes(const latent_moe_config* cfg, size_t* bytes);
  * T = 0 succeeds and enqueues nothing. One forward in flight per handle: the
  * workspace is shared, so overlapping forwards of one handle on different
  * streams race. The forward never allocates or synchronises the host.
+ * Routing (router, top-k, grouping) runs on a stream the handle owns, forked
+ * from `stream` by an event and joined back into it before the expert GEMMs,
+ * so it overlaps the pooler; all work still completes in `stream`'s order
+ * (stage profiling, latent_moe_set_profiling, runs everything on `stream`).
  * Errors: INVALID_ARG (null handle/x/out, misaligned pointer, T < 0),
  * TOO_MANY_TOKENS, HIP (launch failure). */
 int latent_moe_forward(latent_moe_t* h, const void* x, int64_t T, float* out, int32_t* topk_ids,

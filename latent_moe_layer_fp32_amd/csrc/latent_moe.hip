@@ -102,6 +102,8 @@ struct latent_moe {
   const void* pk_sgate;  // MXFP4: packed scales
   const void* pk_sup;
   const void* pk_sdown;
+  hipStream_t side;                // routing (router, top-k, grouping) runs here, beside the pooler
+  hipEvent_t fork, join;           // order the side stream after the caller's and back
   bool prof;                       // record stage events in forward
   bool prof_valid;                 // a forward has recorded a full set
   hipEvent_t ev[kStages + 1];      // created by latent_moe_set_profiling
@@ -275,6 +277,18 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   Et* y = (Et*)(ws + L.y);
 
   LM_MARK(0);
+  // Steps 1-3 (routing) depend only on x, as do the pooler and its norm
+  // statistics (step 4): outside stage profiling, routing runs on the
+  // handle's side stream, forked from and joined back into the caller's
+  // stream, so the two overlap. With stage profiling on, every step runs in
+  // order on the caller's stream so the per-stage times are separable.
+  const bool fork = !h->prof;
+  hipStream_t sr = s;
+  if (fork) {
+    LM_HIP(hipEventRecord(h->fork, s));
+    LM_HIP(hipStreamWaitEvent(h->side, h->fork, 0));
+    sr = h->side;
+  }
   // 1. router: partial logits over k-splits
   {
     int splits, kt_per, mt, nt;
@@ -292,10 +306,10 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.nt = nt;
     p.splits = splits;
     p.kt_per = kt_per;
-    LM_HIP(launch(p, (int64_t)mt * nt * splits, s));
+    LM_HIP(launch(p, (int64_t)mt * nt * splits, sr));
     LM_MARK(1);
     // 2. top-k + softmax + per-expert counts
-    hipLaunchKernelGGL(lm_fill_i32_kernel, dim3(ceil_div(E, 256)), dim3(256), 0, s, counts, E, 0);
+    hipLaunchKernelGGL(lm_fill_i32_kernel, dim3(ceil_div(E, 256)), dim3(256), 0, sr, counts, E, 0);
     // few tokens with many k-splits: one token per workgroup spreads the
     // split sums over all threads; otherwise four tokens per workgroup
     const bool one = splits > 4;
@@ -303,10 +317,10 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
 #define LM_TOPK(NV)                                                                             \
   do {                                                                                          \
     if (one)                                                                                    \
-      hipLaunchKernelGGL((lm_topk_kernel<NV, 1>), g, dim3(256), 0, s, part, splits, (int)T, E, \
+      hipLaunchKernelGGL((lm_topk_kernel<NV, 1>), g, dim3(256), 0, sr, part, splits, (int)T, E, \
                          w.router_bias, k, logits, ids, wts, counts);                           \
     else                                                                                        \
-      hipLaunchKernelGGL((lm_topk_kernel<NV, 4>), g, dim3(256), 0, s, part, splits, (int)T, E, \
+      hipLaunchKernelGGL((lm_topk_kernel<NV, 4>), g, dim3(256), 0, sr, part, splits, (int)T, E, \
                          w.router_bias, k, logits, ids, wts, counts);                           \
   } while (0)
     if (E <= 64) LM_TOPK(1);
@@ -319,9 +333,10 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   }
   LM_MARK(2);
   // 3. grouping by expert
-  hipLaunchKernelGGL(lm_permute_kernel, dim3(E), dim3(256), 0, s, ids, npairs, k, counts, E, Cw::BM,
+  hipLaunchKernelGGL(lm_permute_kernel, dim3(E), dim3(256), 0, sr, ids, npairs, k, counts, E, Cw::BM,
                      offsets, tile_off, perm_token, pair_row);
   LM_HIP(hipGetLastError());
+  if (fork) LM_HIP(hipEventRecord(h->join, sr));
   LM_MARK(3);
   // 4. pooler + norm statistics
   const int pnt = ceil_div(P, Cw::BN);
@@ -370,6 +385,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     LM_HIP(hipGetLastError());
   }
   LM_MARK(5);
+  if (fork) LM_HIP(hipStreamWaitEvent(s, h->join, 0));
   const int64_t max_tiles = ceil_div(npairs, Cw::BM) + (npairs < E ? npairs : E);
   // 5. gate/up + SwiGLU
   {
@@ -567,6 +583,19 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
       return fail(LMOE_ERR_HIP, "weight repack failed: %s", hipGetErrorString(he));
     }
   }
+  // side stream for routing (default priority) and its fork / join events
+  he = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+  if (he == hipSuccess) he = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
+  if (he == hipSuccess) he = hipEventCreateWithFlags(&h->join, hipEventDisableTiming);
+  if (he != hipSuccess) {
+    if (h->join) (void)hipEventDestroy(h->join);
+    if (h->fork) (void)hipEventDestroy(h->fork);
+    if (h->side) (void)hipStreamDestroy(h->side);
+    (void)hipFree(h->ws);
+    if (h->packed) (void)hipFree(h->packed);
+    delete h;
+    return fail(LMOE_ERR_HIP, "stream / event creation failed: %s", hipGetErrorString(he));
+  }
   *out = h;
   return LMOE_OK;
 }
@@ -673,6 +702,9 @@ int latent_moe_destroy(latent_moe_t* h) {
   if (h->packed && e2 == hipSuccess) e2 = hipFree(h->packed);
   for (int i = 0; i <= kStages; ++i)
     if (h->ev[i]) (void)hipEventDestroy(h->ev[i]);
+  (void)hipEventDestroy(h->join);
+  (void)hipEventDestroy(h->fork);
+  (void)hipStreamDestroy(h->side);
   if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
   delete h;
   if (e1 != hipSuccess || e2 != hipSuccess)

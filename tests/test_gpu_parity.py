@@ -160,6 +160,36 @@ def test_tiny_determinism_and_token_equivariance(torch_dev, tiny):
     assert np.array_equal(op, o1[perm])
 
 
+def test_tiny_caller_stream_and_profiled_order(torch_dev, tiny):
+    """Routing forks onto the handle's own stream and joins back: results on a
+    caller-created stream, and with stage profiling (everything in order on
+    the caller's stream), equal the default-stream results bit for bit."""
+    torch = torch_dev
+    from latent_moe_layer_fp32_amd import binding as B
+
+    spec, _, layer, _ = tiny
+    say("case: tiny, caller stream and profiled order")
+    x = synth.device_tensor(spec, "x", synth.DeviceTables("cuda:0"))
+    o1, i1, w1 = run_layer(torch, layer, x)
+    st = torch.cuda.Stream()  # default priority
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        ids = torch.empty((spec.T, spec.k), dtype=torch.int32, device=x.device)
+        w = torch.empty((spec.T, spec.k), dtype=torch.float32, device=x.device)
+        out = layer.forward(x, topk_ids=ids, topk_weights=w, stream=st)
+    st.synchronize()
+    assert np.array_equal(out.cpu().numpy(), o1)
+    assert np.array_equal(ids.cpu().numpy(), i1) and np.array_equal(w.cpu().numpy(), w1)
+    B.latent_moe_set_profiling(layer.handle, True)
+    try:
+        o3, i3, w3 = run_layer(torch, layer, x)
+        times = B.latent_moe_stage_times(layer.handle)
+    finally:
+        B.latent_moe_set_profiling(layer.handle, False)
+    assert np.array_equal(o3, o1) and np.array_equal(i3, i1) and np.array_equal(w3, w1)
+    assert len(times) == len(B.STAGES) and all(v >= 0.0 for v in times.values())
+
+
 def test_tiny_zero_input(torch_dev, tiny):
     torch = torch_dev
     spec, _, layer, _ = tiny
