@@ -17,6 +17,16 @@ def _f32(v: float) -> float:
     return struct.unpack("<f", struct.pack("<f", v))[0]
 
 
+def _bf16(v: float) -> float:
+    """FP32 value -> bfloat16, round to nearest, ties to even."""
+    bits = struct.unpack("<I", struct.pack("<f", v))[0]
+    lower = bits & 0xFFFF
+    upper = bits >> 16
+    if lower > 0x8000 or (lower == 0x8000 and (upper & 1)):
+        upper += 1
+    return struct.unpack("<f", struct.pack("<I", (upper & 0xFFFF) << 16))[0]
+
+
 def _matvec(W, v):
     return [math.fsum(W[r][c] * v[c] for c in range(len(v))) for r in range(len(W))]
 
@@ -28,13 +38,21 @@ def _rmsnorm(v, gamma, eps):
 
 
 def forward(x, router, bias, pooler, pool_gamma, w_gate, w_up, w_down, expert_gamma,
-            unpooler, k, eps):
-    """Returns (out [T][H], ids [T][k], w [T][k]) as Python lists."""
+            unpooler, k, eps, input_gamma=None, bf16_acts=False):
+    """Returns (out [T][H], ids [T][k], w [T][k]) as Python lists.
+
+    input_gamma: x is the pre-norm residual; the router reads its RMSNorm
+    (times input_gamma) rounded to FP32, the pooler the same value rounded
+    on to BF16 when bf16_acts, else the FP32 value."""
     T, E = len(x), len(router)
     outs, all_ids, all_w = [], [], []
     for t in range(T):
         xt = [float(v) for v in x[t]]
-        logit = _matvec(router, xt)
+        xr = xt
+        if input_gamma is not None:
+            xr = [_f32(z) for z in _rmsnorm(xt, [float(g) for g in input_gamma], eps)]
+            xt = [_bf16(z) for z in xr] if bf16_acts else xr
+        logit = _matvec(router, xr)
         if bias is not None:
             logit = [logit[e] + float(bias[e]) for e in range(E)]
         # selection on FP32-rounded logits; ties go to the lower expert index

@@ -3,6 +3,15 @@
 What the layer computes, for each token t (all arithmetic in FP64 on the exact
 input values; BF16/FP32 inputs widen exactly, MXFP4 weights decode exactly):
 
+0. Optional boundary norm, when an input gamma is given ([vllm] "三明治归一化":
+   a block sees the normalised residual, x + post_norm(F(norm(x))); [vllm]
+   "硬件后端 / Nvidia": the router GEMM is driven by the norm's FP32 output;
+   [lmsys] "Fuse normalization and remove routing conversions": the boundary
+   kernel normalises each row in registers): the input is then the pre-norm
+   residual r_t and x_t = r_t / sqrt(mean(r_t^2) + eps) * gamma_in, held in
+   FP32 (nearest). The router reads that FP32 value; the pooler reads it in
+   the activation format (BF16 nearest-even for BF16 inputs, else FP32).
+
 1. Router on the full-width token ([lmsys] "MoE with Pooler, Unpooler and
    Per-Expert Normalization": the router reads the full-width representation;
    [vllm] "硬件后端 / Nvidia": the router GEMM is driven by the norm's FP32
@@ -26,9 +35,10 @@ input values; BF16/FP32 inputs widen exactly, MXFP4 weights decode exactly):
 8. Unpooler back to the model width ([lmsys] same MoE section; [vllm]
    "潜空间 MoE"): out_t = Wun y_t.
 
-Readings where the pages are silent (each listed in the design notes): x is
-already the normed token (the sandwich norm sits outside the layer, [vllm]
-"三明治归一化"); gammas multiply directly; one eps for both norms; no biases
+Readings where the pages are silent (each listed in the design notes): without
+an input gamma, x is already the normed token (the sandwich norm sits outside
+the layer, [vllm] "三明治归一化"); gammas multiply directly; one eps for all
+norms; no biases
 in any linear except an optional router bias, which is part of the logits;
 per-expert gamma has shape [E, P].
 """
@@ -58,6 +68,7 @@ class OracleResult:
     ohat: np.ndarray | None  # [T, k, P] normed expert output per slot
     y: np.ndarray  # [T, P] combined
     near_tie: np.ndarray  # [T] bool: some gap j <= k below NEAR_TIE
+    xn: np.ndarray | None = None  # [T, H] FP32 boundary-norm output (input gamma given)
 
 
 def rms_norm(v: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
@@ -124,7 +135,7 @@ def experts_from_arrays(w_gate, w_up, w_down) -> ExpertFn:
 def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, expert_gamma,
             unpooler, k: int, eps: float, *, force_ids: dict | None = None,
             order: str = "norm_then_sum", keep_pairs: bool = True,
-            round_bf16: Sequence[str] = ()) -> OracleResult:
+            round_bf16: Sequence[str] = (), input_gamma=None) -> OracleResult:
     """Layer forward on tokens x [T, H] (any stored dtype).
 
     force_ids: {token: ids sequence} replaces the selection for those tokens
@@ -133,8 +144,17 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
       combined vector instead (used only to show that the two differ).
     round_bf16: diagnostic emulation; any of "u", "a", "y" rounds that
       intermediate to BF16 (nearest even) the way a BF16 datapath would.
+    input_gamma: [H] gamma of the boundary norm (step 0); x is then the
+      pre-norm residual.
     """
+    act_bf16 = np.asarray(x).dtype == np.uint16
     x = to_f64(x)
+    xn = None
+    x_router = x
+    if input_gamma is not None:
+        xn = rms_norm(x, to_f64(input_gamma), eps).astype(np.float32).astype(np.float64)
+        x_router = xn
+        x = _bf16_round(xn) if act_bf16 else xn
     Wr = to_f64(router)
     b = None if router_bias is None else to_f64(router_bias)
     Wp = to_f64(pooler)
@@ -145,7 +165,7 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
     E = Wr.shape[0]
     P = Wp.shape[0]
 
-    logits = router_logits(x, Wr, b)
+    logits = router_logits(x_router, Wr, b)
     ids, gaps = select_topk(logits, k)
     if force_ids:
         ids = ids.copy()
@@ -193,11 +213,12 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
         y = _bf16_round(y)
     out = y @ Wun.T
     return OracleResult(out=out, ids=ids, w=w, logits=logits, gaps=gaps, h=h, u=u, a=a_all,
-                        o=o_all, ohat=ohat if keep_pairs else None, y=y, near_tie=near)
+                        o=o_all, ohat=ohat if keep_pairs else None, y=y, near_tie=near, xn=xn)
 
 
 def _bf16_round(v: np.ndarray) -> np.ndarray:
-    """FP64 -> FP32 (nearest) -> BF16 (nearest even) -> FP64; diagnostic only."""
+    """FP64 -> FP32 (nearest) -> BF16 (nearest even) -> FP64 (the boundary
+    norm's BF16 output, and the diagnostic emulation)."""
     f = v.astype(np.float32)
     u = f.view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
@@ -209,5 +230,7 @@ def forward_inputs(inp: dict, k: int, eps: float, **kw) -> OracleResult:
     weights: x, router, router_bias, pooler, pool_gamma, w_gate, w_up, w_down,
     expert_gamma, unpooler)."""
     ex = inp.get("experts") or experts_from_arrays(inp["w_gate"], inp["w_up"], inp["w_down"])
+    if inp.get("input_gamma") is not None:
+        kw.setdefault("input_gamma", inp["input_gamma"])
     return forward(inp["x"], inp["router"], inp.get("router_bias"), inp["pooler"], inp["pool_gamma"],
                    ex, inp["expert_gamma"], inp["unpooler"], k, eps, **kw)

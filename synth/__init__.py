@@ -81,6 +81,7 @@ _TENSOR_IDS = {
     "w_down": 7,
     "expert_gamma": 8,
     "unpooler": 9,
+    "input_gamma": 10,
 }
 
 
@@ -97,6 +98,7 @@ def shape(spec: LayerSpec, name: str) -> tuple:
         "w_down": (E, P, I),
         "expert_gamma": (E, P),
         "unpooler": (H, P),
+        "input_gamma": (H,),
     }[name]
 
 
@@ -106,11 +108,11 @@ def _fan_in(spec: LayerSpec, name: str) -> int:
 
 
 def _mode(name: str) -> int:
-    return MODE_GAMMA if name in ("pool_gamma", "expert_gamma") else MODE_SCALED
+    return MODE_GAMMA if name in ("pool_gamma", "expert_gamma", "input_gamma") else MODE_SCALED
 
 
 def kind(spec: LayerSpec, name: str) -> int:
-    if name in ("router", "router_bias", "pool_gamma", "expert_gamma"):
+    if name in ("router", "router_bias", "pool_gamma", "expert_gamma", "input_gamma"):
         return KIND_F32
     if name in ("x", "pooler", "unpooler"):
         return KIND_F32 if spec.act_dtype == "f32" else KIND_BF16

@@ -245,3 +245,74 @@ def test_force_ids_recomputes_weights_from_own_logits():
     assert list(r.ids[1]) == [5, 0]
     lg = r.logits[1, [5, 0]]
     np.testing.assert_allclose(r.w[1], scipy.special.softmax(lg), atol=1e-15)
+
+
+# ------------------------------------------------------- boundary norm (step 0)
+
+
+def _to_bf16_bits(a32: np.ndarray) -> np.ndarray:
+    """float32 -> BF16 bits, nearest even (test-local)."""
+    u = a32.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("bf16_acts", [False, True])
+@pytest.mark.parametrize("seed,k,shape", [
+    (10, 2, dict(T=4, H=8, P=4, E=6, I=4)),
+    (11, 3, dict(T=3, H=6, P=5, E=5, I=3)),
+])
+def test_boundary_norm_matches_brute_force(seed, k, shape, bf16_acts):
+    rng = np.random.default_rng(seed)
+    d = rand_layer(rng, k=k, **shape)
+    d["x"] = (3.0 * d["x"] + 0.5).astype(np.float32)  # a residual stream, not unit-RMS
+    gin = (1 + 0.2 * rng.standard_normal(shape["H"])).astype(np.float32)
+    xs = _to_bf16_bits(d["x"]) if bf16_acts else d["x"]
+    r = orc.forward(xs, d["router"], None, d["pooler"], d["pool_gamma"],
+                    orc.experts_from_arrays(d["w_gate"], d["w_up"], d["w_down"]), d["expert_gamma"],
+                    d["unpooler"], k, 1e-6, input_gamma=gin)
+    f = lambda a: np.asarray(a, np.float64).tolist()
+    xin = (xs.astype(np.uint32) << 16).view(np.float32) if bf16_acts else xs
+    out, ids, w = brute.forward(f(xin), f(d["router"]), None, f(d["pooler"]), f(d["pool_gamma"]),
+                                f(d["w_gate"]), f(d["w_up"]), f(d["w_down"]), f(d["expert_gamma"]),
+                                f(d["unpooler"]), k, 1e-6, input_gamma=f(gin), bf16_acts=bf16_acts)
+    assert np.array_equal(r.ids, np.array(ids))
+    np.testing.assert_allclose(r.w, np.array(w), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(r.out, np.array(out), rtol=0, atol=1e-12)
+
+
+def test_boundary_norm_closed_forms_and_invariance():
+    rng = np.random.default_rng(12)
+    k = 2
+    d = rand_layer(rng, T=6, H=16, P=8, E=5, I=4, k=k)
+    res = (2.5 * d["x"] - 1.0).astype(np.float32)
+    ex = orc.experts_from_arrays(d["w_gate"], d["w_up"], d["w_down"])
+
+    def go(x, gin, eps=0.0):
+        return orc.forward(x, d["router"], None, d["pooler"], d["pool_gamma"], ex, d["expert_gamma"],
+                           d["unpooler"], k, eps, input_gamma=gin)
+
+    ones = np.ones(16, np.float32)
+    r1 = go(res, ones)
+    # unit gamma, eps = 0: every normed row has RMS 1 (to FP32 rounding); gamma c: RMS c
+    np.testing.assert_allclose(np.sqrt((r1.xn ** 2).mean(-1)), 1.0, rtol=2e-7)
+    r3 = go(res, 3 * ones)
+    np.testing.assert_allclose(np.sqrt((r3.xn ** 2).mean(-1)), 3.0, rtol=2e-7)
+    # per-column gamma multiplies column-wise
+    g = np.linspace(0.5, 2.0, 16).astype(np.float32)
+    np.testing.assert_allclose(go(res, g).xn, r1.xn * g, rtol=2e-7)
+    # scale invariance (power-of-two scale, eps = 0: bit-identical)
+    r8 = go((8 * res).astype(np.float32), ones)
+    assert np.array_equal(r8.xn, r1.xn) and np.array_equal(r8.out, r1.out)
+    # FP32 activations: the layer on the residual equals the layer on its FP32 norm
+    plain = orc.forward(r1.xn.astype(np.float32), d["router"], None, d["pooler"], d["pool_gamma"], ex,
+                        d["expert_gamma"], d["unpooler"], k, 0.0)
+    assert np.array_equal(plain.ids, r1.ids)
+    np.testing.assert_allclose(plain.out, r1.out, rtol=0, atol=1e-15)
+    # BF16 activations: the router reads the FP32 norm, the pooler its BF16 rounding
+    rb = go(_to_bf16_bits(res), ones)
+    resb = (_to_bf16_bits(res).astype(np.uint32) << 16).view(np.float32)
+    xn_b = go(resb, ones).xn
+    np.testing.assert_allclose(rb.logits, xn_b @ d["router"].astype(np.float64).T, rtol=1e-13, atol=1e-15)
+    xb = (_to_bf16_bits(xn_b.astype(np.float32)).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert not np.array_equal(xb, xn_b)  # the rounding is visible at these values
+    np.testing.assert_allclose(rb.h, xb @ d["pooler"].astype(np.float64).T, rtol=1e-13, atol=1e-15)
