@@ -5,9 +5,10 @@ One step = one forward of the whole layer (router, top-k, grouping, pooler,
 pre-expert norm, gate/up, down, per-expert norm + weighted sum, unpooler) over
 one batch of seeded synthetic tokens already resident in HBM. Default
 workload: 64-token decode at the real layer shapes (H=8192, P=4096, E=256,
-I=4096, k=8, BF16); the 16384-token prefill chunk on the same weights, and
-the 64-token decode and 16384-token prefill with MXFP4 expert weights, are
-measured in the same run and reported under their workload names.
+I=4096, k=8, BF16); the 16384-token prefill chunk on the same weights, the
+skewed long prompt (five 16384-token chunks, Zipf router bias; one step runs
+all five), and the 64-token decode and 16384-token prefill with MXFP4 expert
+weights are measured in the same run and reported under their workload names.
 
 Prints one JSON line with tokens/s, the roofline of the dominant kernel (the
 gate/up grouped GEMM: HBM-bound at decode, MFMA-bound at prefill; its time
@@ -90,20 +91,28 @@ def layer_flops(spec, T):
     return T * (2 * H * P * 2 + k * 2 * P * 2 * I + k * 2 * I * P)
 
 
-def measure(spec, layer, x, steps, warmup, torch):
+def measure(spec, layer, xs, steps, warmup, torch):
+    """One step = one forward per chunk in xs (a single batch, or the chunks
+    of a long prompt in order). Returns ms per step, wall seconds, per-stage
+    ms summed over the chunks of a step, and the last chunk's expert counts."""
     from latent_moe_layer_fp32_amd import binding as B
 
     stream = torch.cuda.current_stream()
-    T = x.shape[0]
-    out = torch.empty((T, spec.H), dtype=torch.float32, device=x.device)
+    T = xs[0].shape[0]
+    out = torch.empty((T, spec.H), dtype=torch.float32, device=xs[0].device)
+
+    def step():
+        for x in xs:
+            layer.forward(x, out=out)
+
     for _ in range(warmup):
-        layer.forward(x, out=out)
+        step()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     t0 = time.perf_counter()
     for _ in range(steps):
-        layer.forward(x, out=out)
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -112,9 +121,10 @@ def measure(spec, layer, x, steps, warmup, torch):
     B.latent_moe_set_profiling(layer.handle, True)
     acc = None
     for _ in range(steps):
-        layer.forward(x, out=out)
-        st = B.latent_moe_stage_times(layer.handle)
-        acc = st if acc is None else {k: acc[k] + v for k, v in st.items()}
+        for x in xs:
+            layer.forward(x, out=out)
+            st = B.latent_moe_stage_times(layer.handle)
+            acc = st if acc is None else {k: acc[k] + v for k, v in st.items()}
     B.latent_moe_set_profiling(layer.handle, False)
     stages = {k: v / steps for k, v in acc.items()}
     return ms, wall, stages, layer.views(T, names=("counts",))["counts"]
@@ -131,7 +141,9 @@ def cpu_baseline(spec, xh, sample_tokens, budget_s=30.0):
     host = {n: synth.host(spec, n) for n in ("router", "router_bias", "pooler", "pool_gamma",
                                             "expert_gamma", "unpooler")}
     xs = xh[:sample_tokens]
-    lg = orc.router_logits(to_f64(xs), to_f64(host["router"]),
+    gin = synth.host(spec, "input_gamma") if spec.input_norm else None
+    xr = to_f64(xs) if gin is None else orc.rms_norm(to_f64(xs), to_f64(gin), spec.eps).astype(np.float32)
+    lg = orc.router_logits(to_f64(xr), to_f64(host["router"]),
                            None if host["router_bias"] is None else to_f64(host["router_bias"]))
     ids, _ = orc.select_topk(lg, spec.k)
     raw = {int(e): tuple(synth.host(spec, n, experts=(int(e), int(e) + 1)) for n in ("w_gate", "w_up", "w_down"))
@@ -145,7 +157,7 @@ def cpu_baseline(spec, xh, sample_tokens, budget_s=30.0):
 
     t0 = time.perf_counter()
     orc.forward(xs, host["router"], host["router_bias"], host["pooler"], host["pool_gamma"], expert,
-                host["expert_gamma"], host["unpooler"], spec.k, spec.eps, keep_pairs=False)
+                host["expert_gamma"], host["unpooler"], spec.k, spec.eps, keep_pairs=False, input_gamma=gin)
     dt = time.perf_counter() - t0
     return sample_tokens / dt, dt, len(raw)
 
@@ -155,8 +167,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew", "mxfp4", "mxfp4_decode"])
-    ap.add_argument("--also", default="prefill,mxfp4_decode,mxfp4",
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "skew", "mxfp4", "mxfp4_decode", "decode_norm", "prefill_norm"])
+    # skew: five 16384-token chunks of one long prompt (81920 tokens per step)
+    ap.add_argument("--also", default="prefill,skew,decode_norm,prefill_norm,mxfp4_decode,mxfp4",
                     help="extra workloads measured in the same run (comma list)")
     ap.add_argument("--cpu-tokens", type=int, default=48, help="token sample for the CPU oracle (0: skip)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -176,7 +190,8 @@ def main():
     def make_layer(spec, w, max_tokens):
         return LatentMoE(hidden=spec.H, pooled=spec.P, experts=spec.E, intermediate=spec.I,
                          top_k=spec.k, eps=spec.eps, act_dtype=spec.act_dtype,
-                         expert_dtype=spec.expert_format, max_tokens=max_tokens, weights=w)
+                         expert_dtype=spec.expert_format, max_tokens=max_tokens, weights=w,
+                         input_norm=spec.input_norm)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     tables = synth.DeviceTables("cuda:0")
@@ -208,17 +223,19 @@ def main():
     for wl in [args.workload] + [w for w in args.also.split(",") if w and w != args.workload]:
         spec = synth.CONFIGS[wl]
         w = dict(weights_for(spec))
+        if spec.input_norm:
+            w["input_gamma"] = synth.device_tensor(spec, "input_gamma", tables)
         if spec.router_bias != "none":
             w["router_bias"] = synth.device_tensor(spec, "router_bias", tables)
         layer = make_layer(spec, w, max_tokens=spec.T)
-        x = synth.device_tensor(spec, "x", tables)
+        xs = [synth.device_tensor(spec, "x", tables, chunk=c) for c in range(spec.chunks)]
         steps = args.steps if wl == args.workload else max(3, args.steps // 4)
         warm = args.warmup if wl == args.workload else max(1, args.warmup // 2)
-        log(f"{wl}: T={spec.T}, {warm} warmup + {steps} timed steps")
-        ms, wall, stages, counts = measure(spec, layer, x, steps, warm, torch)
+        log(f"{wl}: T={spec.T} x {spec.chunks} chunk(s), {warm} warmup + {steps} timed steps")
+        ms, wall, stages, counts = measure(spec, layer, xs, steps, warm, torch)
         lb, touched = layer_bytes(spec, counts, spec.T)
         r = dict(spec=spec, ms=ms, wall=wall, stages=stages, touched=touched, layer_bytes=lb,
-                 tokens_per_s=spec.T / (ms / 1e3), steps=steps, warmup=warm)
+                 tokens_per_s=spec.T * spec.chunks / (ms / 1e3), steps=steps, warmup=warm)
         gu = stages["gate_up"] / 1e3
         if spec.T * spec.k < 64 * spec.E:  # decode-sized: the expert weights stream once
             ach = gate_up_bytes(spec, counts, spec.T) / gu / 1e9
@@ -229,19 +246,19 @@ def main():
                              "kernel_ms": round(stages["gate_up"], 4)}
             r["layer_frac"] = round(lb / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
         else:
-            fl = 2 * spec.T * spec.k * spec.P * 2 * spec.I
+            fl = 2 * spec.T * spec.chunks * spec.k * spec.P * 2 * spec.I
             ach = fl / gu / 1e12
             r["roofline"] = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
                              "traffic": measured_traffic(wl, "gate_up"),
                              "kernel": "gate_up grouped GEMM + SwiGLU",
                              "kernel_ms": round(stages["gate_up"], 4)}
-            r["layer_frac"] = round(layer_flops(spec, spec.T) / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+            r["layer_frac"] = round(layer_flops(spec, spec.T * spec.chunks) / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)
         log(f"{wl}: {ms:.3f} ms/step, {r['tokens_per_s']:.0f} tok/s, stages "
             + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
         results[wl] = r
         layer.close()
-        del x
+        del xs
 
     main_r = results[args.workload]
     spec = main_r["spec"]
@@ -258,9 +275,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded counter-based N(0,1) inputs, N(0,1/fan_in) weights)",
-        "config": {"workload": f"{args.workload}: {spec.T} tokens, H={spec.H}, P={spec.P}, E={spec.E}, "
+        "config": {"workload": f"{args.workload}: " + (f"{spec.chunks} x " if spec.chunks > 1 else "") + f"{spec.T} tokens, H={spec.H}, P={spec.P}, E={spec.E}, "
                                f"I={spec.I}, top-{spec.k}, {spec.expert_format.upper()} experts, FP32 router",
-                   "global_batch": spec.T, "parallelism": "none (one GPU)"},
+                   "global_batch": spec.T * spec.chunks, "parallelism": "none (one GPU)"},
         "roofline": main_r["roofline"],
         "layer_frac": main_r["layer_frac"],
         "stages_ms": {k: round(v, 4) for k, v in main_r["stages"].items()},
@@ -270,6 +287,7 @@ def main():
         if wl == args.workload:
             continue
         line[wl] = {"value": round(r["tokens_per_s"], 1), "unit": "tokens/s", "ms_per_step": round(r["ms"], 4),
+                    "tokens_per_step": r["spec"].T * r["spec"].chunks,
                     "steps": r["steps"], "roofline": r["roofline"], "layer_frac": r["layer_frac"],
                     "stages_ms": {k: round(v, 4) for k, v in r["stages"].items()}}
     if args.cpu_tokens > 0:

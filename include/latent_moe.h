@@ -72,6 +72,15 @@ typedef struct {
                            BF16 in registers, and the products accumulate in
                            FP32 as for BF16 experts */
   int64_t max_tokens;   /* upper bound on T per forward; sizes the workspace */
+  int32_t input_norm;   /* 0: x is the normed token. 1: x is the pre-norm
+                           residual r; the layer first forms
+                           x = r / sqrt(mean(r^2) + eps) * input_gamma in FP32
+                           (sandwich pre-norm: vLLM Day-0 post, sections on the
+                           sandwich norm and on the FP32 router input; lmsys
+                           post, "Fuse normalization and remove routing
+                           conversions"). The router then reads that FP32
+                           value and the pooler its act_dtype rounding (BF16
+                           nearest-even, or the FP32 value). */
 } latent_moe_config;
 
 /* Layer weights (device pointers), read in place unless stated otherwise; the
@@ -91,7 +100,8 @@ typedef struct {
  *   s_gate, s_up [E, I, P/32], s_down [E, P, I/32]  E8M0 bytes (MXFP4 only,
  *                 else ignored)
  *   expert_gamma [E, P]   F32, one gamma row per expert
- *   unpooler     [H, P]   act_dtype                                         */
+ *   unpooler     [H, P]   act_dtype
+ *   input_gamma  [H]      F32, the boundary norm's gamma (input_norm only)   */
 typedef struct {
   const float* router;
   const float* router_bias;
@@ -105,6 +115,7 @@ typedef struct {
   const uint8_t* s_down;
   const float* expert_gamma;
   const void* unpooler;
+  const float* input_gamma; /* [H] F32 when cfg.input_norm, else ignored */
 } latent_moe_weights;
 
 /* Create a handle on the current device. Validates cfg and w, allocates the
@@ -171,6 +182,10 @@ typedef struct {
   const void* act;
   const float* expert_out;
   const void* combined;
+  const void* x_norm;   /* boundary norm output (input_norm only, else NULL): FP32 layers
+                           [T, H] F32; BF16 layers its exact three-piece BF16 split
+                           [T, 3H] (pieces p1 | p2 | p3 side by side, p1 + p2 + p3 =
+                           the FP32 value, p1 = its BF16 rounding, the pooler's input) */
 } latent_moe_views;
 
 int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v);
@@ -178,14 +193,16 @@ int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v);
 /* Stage timing, for measurement. With profiling enabled, each forward records
  * one HIP event on its stream before the first stage and after each of the
  * LMOE_NUM_STAGES stages (events are created here, never in forward):
- *   0 router GEMM          1 top-k/softmax      2 grouping by expert
- *   3 pooler GEMM          4 pooled row scale   5 gate/up GEMM + SwiGLU
- *   6 down GEMM            7 combine            8 unpooler GEMM
- * latent_moe_stage_times waits for the last recorded event and writes the
- * elapsed milliseconds of each stage of the last forward into ms[0..8].
+ *   0 boundary norm        1 router GEMM        2 top-k/softmax
+ *   3 grouping by expert   4 pooler GEMM        5 pooled row scale
+ *   6 gate/up GEMM+SwiGLU  7 down GEMM          8 combine
+ *   9 unpooler GEMM
+ * (stage 0 is empty unless cfg.input_norm). latent_moe_stage_times waits for
+ * the last recorded event and writes the elapsed milliseconds of each stage
+ * of the last forward into ms[0..9].
  * Errors: INVALID_ARG (NULL handle/ms, n < LMOE_NUM_STAGES, no profiled
  * forward yet), HIP. */
-#define LMOE_NUM_STAGES 9
+#define LMOE_NUM_STAGES 10
 int latent_moe_set_profiling(latent_moe_t* h, int enable);
 int latent_moe_stage_times(latent_moe_t* h, float* ms, int n);
 

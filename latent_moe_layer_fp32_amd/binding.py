@@ -44,19 +44,20 @@ class Config(ctypes.Structure):
         ("act_dtype", ctypes.c_int32),
         ("expert_dtype", ctypes.c_int32),
         ("max_tokens", ctypes.c_int64),
+        ("input_norm", ctypes.c_int32),
     ]
 
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "router", "router_bias", "pooler", "pool_gamma", "w_gate", "w_up", "w_down",
-        "s_gate", "s_up", "s_down", "expert_gamma", "unpooler")]
+        "s_gate", "s_up", "s_down", "expert_gamma", "unpooler", "input_gamma")]
 
 
 class Views(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "ids", "weights", "counts", "offsets", "perm_token", "pair_row", "pooled",
-        "row_scale", "act", "expert_out", "combined")]
+        "row_scale", "act", "expert_out", "combined", "x_norm")]
 
 
 _lib = None
@@ -112,10 +113,10 @@ def _check(rc: int):
 
 
 def make_config(hidden, pooled, experts, intermediate, top_k, eps, act_dtype, expert_dtype,
-                max_tokens) -> Config:
+                max_tokens, input_norm=False) -> Config:
     return Config(hidden, pooled, experts, intermediate, top_k, eps,
                   DTYPE_CODES.get(act_dtype, act_dtype), DTYPE_CODES.get(expert_dtype, expert_dtype),
-                  max_tokens)
+                  max_tokens, int(input_norm))
 
 
 def latent_moe_workspace_bytes(cfg: Config) -> int:
@@ -141,7 +142,8 @@ def latent_moe_debug_views(h: int) -> Views:
     return v
 
 
-STAGES = ("router", "topk", "group", "pooler", "rowscale", "gate_up", "down", "combine", "unpooler")
+STAGES = ("input_norm", "router", "topk", "group", "pooler", "rowscale", "gate_up", "down", "combine",
+          "unpooler")
 
 
 def latent_moe_set_profiling(h: int, enable: bool) -> None:
@@ -170,22 +172,25 @@ class LatentMoE:
 
     weights: dict with router, router_bias (or None), pooler, pool_gamma,
     w_gate, w_up, w_down (MXFP4: (packed, scales) pairs), expert_gamma,
-    unpooler. The tensors are referenced by this object so they outlive the
+    unpooler, and input_gamma when input_norm (x is then the pre-norm
+    residual). The tensors are referenced by this object so they outlive the
     handle.
     """
 
     def __init__(self, *, hidden, pooled, experts, intermediate, top_k, eps, act_dtype,
-                 expert_dtype, max_tokens, weights: dict):
+                 expert_dtype, max_tokens, weights: dict, input_norm: bool = False):
         import torch
 
         self.cfg = make_config(hidden, pooled, experts, intermediate, top_k, eps, act_dtype,
-                               expert_dtype, max_tokens)
+                               expert_dtype, max_tokens, input_norm)
+        self.input_norm = bool(input_norm)
         self.top_k, self.hidden, self.pooled, self.experts = top_k, hidden, pooled, experts
         self.intermediate = intermediate
         self.act_dtype, self.expert_dtype = act_dtype, expert_dtype
         self._keep = dict(weights)
         w = Weights()
-        for name in ("router", "router_bias", "pooler", "pool_gamma", "expert_gamma", "unpooler"):
+        for name in ("router", "router_bias", "pooler", "pool_gamma", "expert_gamma", "unpooler",
+                     "input_gamma"):
             setattr(w, name, _ptr(weights.get(name)))
         for name, sname in (("w_gate", "s_gate"), ("w_up", "s_up"), ("w_down", "s_down")):
             v = weights[name]
@@ -242,6 +247,10 @@ class LatentMoE:
             "expert_out": (v.expert_out, (T * k, P), np.float32),
             "combined": (v.combined, (T, P), act_np),
         }
+        split_norm = bool(v.x_norm) and self.act_dtype != "f32"
+        if v.x_norm:
+            spec["x_norm"] = ((v.x_norm, (T, 3 * self.hidden), np.uint16) if split_norm
+                              else (v.x_norm, (T, self.hidden), np.float32))
         res = {}
         for name, (ptr, shape, dt) in spec.items():
             if names is not None and name not in names:
@@ -249,6 +258,11 @@ class LatentMoE:
             a = np.empty(shape, dt)
             _memcpy_d2h(a.ctypes.data, ptr, a.nbytes)
             res[name] = a
+        if split_norm and "x_norm" in res:  # FP32 value = sum of the three BF16 pieces (exact)
+            H = self.hidden
+            pcs = (res["x_norm"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            res["x_norm_split"] = res["x_norm"]
+            res["x_norm"] = (pcs[:, :H] + pcs[:, H:2 * H] + pcs[:, 2 * H:]).astype(np.float32)
         return res
 
     def close(self):

@@ -37,6 +37,7 @@ struct LmElem<uint16_t> {  // bfloat16 bits
                                                   __builtin_bit_cast(lm_bf16x8, b), acc, 0, 0, 0);
   }
   LM_DEV static uint16_t from_f32(float v) { return lm_f32_to_bf16(v); }
+  LM_DEV static float to_f32(uint16_t v) { return lm_bf16_to_f32(v); }
 };
 
 template <>
@@ -49,6 +50,7 @@ struct LmElem<float> {
                                                  0, 0, 0);
   }
   LM_DEV static float from_f32(float v) { return v; }
+  LM_DEV static float to_f32(float v) { return v; }
 };
 
 // WM x WN waves, each wave TM x TN tiles of 32x32. FLUSH > 0 folds the running
@@ -82,6 +84,18 @@ struct LmHasRowValue : std::false_type {};
 template <class P>
 struct LmHasRowValue<P, std::void_t<decltype(std::declval<const P&>().row_value(std::declval<const LmTile&>(), 0))>>
     : std::true_type {};
+
+// Problems whose B k-tiles are not read in order declare b_ktile() (the
+// router's six-product split); the others read B k-tile kt at step kt.
+template <class P, class = void>
+struct LmHasBKtile : std::false_type {};
+template <class P>
+struct LmHasBKtile<P, std::void_t<decltype(std::declval<const P&>().b_ktile(0))>> : std::true_type {};
+template <class P>
+LM_DEV int lm_b_ktile(const P& p, int kt) {
+  if constexpr (LmHasBKtile<P>::value) return p.b_ktile(kt);
+  else return kt;
+}
 
 LM_DEV int lm_swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
@@ -171,8 +185,9 @@ __global__ __launch_bounds__(256) void lm_gemm_kernel(const Prob p) {
     const int ka = p.a_ktile(kt);
 #pragma unroll
     for (int q = 0; q < QA; ++q) ra[q] = ap[q][ka * 8 + lc];
+    const int kb = lm_b_ktile(p, kt);
 #pragma unroll
-    for (int q = 0; q < QB; ++q) rb[q] = bp[q][kt * 8 + lc];
+    for (int q = 0; q < QB; ++q) rb[q] = bp[q][kb * 8 + lc];
   };
   auto sstore = [&](int buf) {
 #pragma unroll

@@ -2,6 +2,7 @@
 //
 // Step order (web page "SGLang and Miles Add Day-0 Support for Muse Spark
 // Open", section "MoE with Pooler, Unpooler and Per-Expert Normalization"):
+//   optional boundary RMSNorm of the residual     lm_input_norm_kernel
 //   router logits (FP32)  -> top-k + softmax      lm_topk_kernel
 //   grouping by expert    (LDS histogram per block, then a stable scatter:
 //                          the "LDS kernel" replacing an atomic-add expert
@@ -15,6 +16,96 @@
 //   unpooler GEMM                                 UnpoolerProb
 #pragma once
 #include "gemm.h"
+
+// ------------------------------------------------------------ boundary norm
+// Exact three-piece BF16 split of an FP32 value: f = b1 + b2 + b3 with each
+// piece the nearest-even BF16 of what remains (exact for normal floats: 8
+// significant bits per piece, and each remainder is exact in FP32).
+LM_DEV void lm_split3(float f, uint16_t& b1, uint16_t& b2, uint16_t& b3) {
+  b1 = lm_f32_to_bf16(f);
+  const float r1 = f - lm_bf16_to_f32(b1);
+  b2 = lm_f32_to_bf16(r1);
+  const float r2 = r1 - lm_bf16_to_f32(b2);
+  b3 = lm_f32_to_bf16(r2);
+}
+
+// One token row per workgroup: x = r * (1 / sqrt(mean(r^2) + eps)) * gamma
+// (the block's sandwich pre-norm; the router reads its FP32 output), with the
+// sum of squares, the root and each product in FP64 and one rounding to FP32
+// per element. FP32 layers write x to xn [T, H]. BF16 layers write its exact
+// three-piece BF16 split to xs [T, 3H] (pieces side by side): the first piece
+// is x's nearest-even BF16 rounding, the pooler's input, and the router forms
+// the FP32 products from the pieces on the matrix cores. Each thread owns
+// 8-element chunks (H % 64 == 0); sum order: per-thread chunk partials, wave
+// butterfly, then the four waves in order. The second pass re-reads the row
+// (16 KB at H = 8192, from L2).
+template <typename Et>
+__global__ __launch_bounds__(256) void lm_input_norm_kernel(const Et* r, int H, const float* gamma,
+                                                            float eps, float* xn, uint16_t* xs) {
+  __shared__ double red[4];
+  // 8 elements = one 16-byte load (BF16) or two (FP32)
+  const lm_u32x4* row = (const lm_u32x4*)(r + (size_t)blockIdx.x * H);
+  const int nch = H / 8;
+  auto elems = [&](int c, float (&v)[8]) {
+    if constexpr (sizeof(Et) == 2) {
+      const lm_u32x4 q = row[c];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(q[j] << 16);
+        v[2 * j + 1] = __uint_as_float(q[j] & 0xffff0000u);
+      }
+    } else {
+      const lm_u32x4 q0 = row[2 * c], q1 = row[2 * c + 1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = __uint_as_float(q0[j]);
+        v[4 + j] = __uint_as_float(q1[j]);
+      }
+    }
+  };
+  double s = 0.0;
+  for (int c = threadIdx.x; c < nch; c += 256) {
+    float v[8];
+    elems(c, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += (double)v[j] * (double)v[j];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  const double inv = 1.0 / sqrt((((red[0] + red[1]) + red[2]) + red[3]) / H + (double)eps);
+  for (int c = threadIdx.x; c < nch; c += 256) {
+    float v[8];
+    elems(c, v);
+    const float4 g0 = ((const float4*)gamma)[2 * c], g1 = ((const float4*)gamma)[2 * c + 1];
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = (float)((double)v[j] * inv * (double)g[j]);
+    if (xn) {
+      float4* dst = (float4*)(xn + (size_t)blockIdx.x * H) + 2 * c;
+      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+    }
+    if (xs) {
+      lm_u32x4 p[3];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint16_t a1, a2, a3, b1, b2, b3;
+        lm_split3(o[2 * j], a1, a2, a3);
+        lm_split3(o[2 * j + 1], b1, b2, b3);
+        p[0][j] = (uint32_t)a1 | ((uint32_t)b1 << 16);
+        p[1][j] = (uint32_t)a2 | ((uint32_t)b2 << 16);
+        p[2][j] = (uint32_t)a3 | ((uint32_t)b3 << 16);
+      }
+      lm_u32x4* dst = (lm_u32x4*)(xs + (size_t)blockIdx.x * 3 * H);
+      dst[c] = p[0];
+      dst[nch + c] = p[1];
+      dst[2 * nch + c] = p[2];
+    }
+  }
+}
 
 // --------------------------------------------------- matrix-core B layout
 // Weights read by the streaming kernel are repacked once (at create) so that
@@ -80,9 +171,16 @@ __global__ void lm_pack_mx_kernel(const lm_u32x4* src, const uint8_t* src_scales
 // ----------------------------------------------------------------- router
 // Partial logits over k-splits: part[s][t][e] = sum over split s of x[t,k] W[e,k],
 // accumulated as FP64 sums of per-k-tile FP32 matrix-core chains.
-// BF16 activations: W is [E, 3H] holding an exact three-piece BF16 split of
-// the FP32 router, and x is read three times (a_ktile wraps), so the matrix
-// cores see exact products and FP32 accumulation.
+// FP32 layers: x and W FP32, one k-tile per 32 columns.
+// BF16 activations: W is [E, 3H] holding the exact three-piece BF16 split
+// W1|W2|W3 of the FP32 router. x BF16 (pieces = 1): x is read three times
+// (a_ktile wraps), so the matrix cores see exact products x*Wj. x given as
+// its own three-piece split X1|X2|X3 [T, 3H] (pieces = 3, the boundary norm's
+// FP32 output): the logical K runs over six segments X1W1, X1W2, X1W3, X2W1,
+// X2W2, X3W1, every product exact. The dropped cross terms X2W3, X3W2 and
+// X3W3 are each at most 2^-24 of |x||W| (X2, W2 within 2^-8 and X3, W3 within
+// 2^-16 of the whole), about 2^-26 on average, and of random sign, so their
+// sum over a row stays far below the FP32 rounding of the logit.
 template <class Cfg_>
 struct RouterProb {
   using Cfg = Cfg_;
@@ -91,7 +189,10 @@ struct RouterProb {
   const E* w;
   double* part;
   int T, Ew, H, Kw, kta, mt, nt, splits, kt_per;
+  int lda = 0;     // row stride of x in elements (0: H)
+  int pieces = 1;  // BF16: pieces of x (1 or 3)
 
+  LM_DEV int ktot() const { return pieces == 3 ? 6 * kta : Kw / Cfg::KT; }
   LM_DEV bool tile(int bid, LmTile& t) const {
     int L;
     if (!lm_xcd_map(bid, mt * nt * splits, L)) return false;
@@ -104,16 +205,26 @@ struct RouterProb {
     t.nt = n;
     t.e = s;
     t.kt0 = s * kt_per;
-    t.kt1 = min(Kw / Cfg::KT, t.kt0 + kt_per);
+    t.kt1 = min(ktot(), t.kt0 + kt_per);
     return true;
   }
   LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
-    return (const lm_u32x4*)(x + (size_t)(t.m0 + min(r, t.rows - 1)) * H);
+    return (const lm_u32x4*)(x + (size_t)(t.m0 + min(r, t.rows - 1)) * (lda ? lda : H));
   }
   LM_DEV const lm_u32x4* b_row(const LmTile& t, int r) const {
     return (const lm_u32x4*)(w + (size_t)min(t.n0 + r, Ew - 1) * Kw);
   }
-  LM_DEV int a_ktile(int kt) const { return kt % kta; }
+  // segment g of the six-product K: x piece (0,0,0,1,1,2), W piece (0,1,2,0,1,0)
+  LM_DEV int a_ktile(int kt) const {
+    if (pieces != 3) return kt % kta;
+    const int g = kt / kta;
+    return (g < 3 ? 0 : g < 5 ? 1 : 2) * kta + kt % kta;
+  }
+  LM_DEV int b_ktile(int kt) const {
+    if (pieces != 3) return kt;
+    const int g = kt / kta;
+    return (g < 3 ? g : g - 3 - (g == 5 ? 2 : 0)) * kta + kt % kta;
+  }
   LM_DEV void epilogue_f64(const LmTile& t, const double (&acc)[Cfg::TM][Cfg::TN][16], int wm,
                            int wn, int lane) const {
     double* dst = part + ((size_t)t.e * T + t.m0) * Ew + t.n0;
@@ -159,8 +270,9 @@ struct PoolerProb {
     t.kt1 = H / Cfg::KT;
     return true;
   }
+  int lda = 0;  // row stride of x in elements (0: H)
   LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
-    return (const lm_u32x4*)(x + (size_t)(t.m0 + min(r, t.rows - 1)) * H);
+    return (const lm_u32x4*)(x + (size_t)(t.m0 + min(r, t.rows - 1)) * (lda ? lda : H));
   }
   LM_DEV const lm_u32x4* b_row(const LmTile& t, int r) const {
     return (const lm_u32x4*)(w + (size_t)min(t.n0 + r, P - 1) * H);
@@ -441,8 +553,9 @@ struct DenseSplitProb {
     t.kt1 = min(K / Cfg::KT, t.kt0 + kt_per);
     return true;
   }
+  int lda = 0;  // row stride of a in elements (0: K)
   LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
-    return (const lm_u32x4*)(a + (size_t)(t.m0 + min(r, t.rows - 1)) * K);
+    return (const lm_u32x4*)(a + (size_t)(t.m0 + min(r, t.rows - 1)) * (lda ? lda : K));
   }
   LM_DEV const lm_u32x4* b_group(const LmTile& t, int wv, int j) const {
     return lm_packed_group(w, min(t.n0 + (wv * Cfg::TN + j) * 32, N - 32), K);
@@ -516,12 +629,8 @@ __global__ void lm_split_router_kernel(const float* w, uint16_t* w3, int E, int 
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x) {
     const size_t e = i / H, h = i - e * H;
-    const float f = w[i];
-    const uint16_t b1 = lm_f32_to_bf16(f);
-    const float r1 = f - lm_bf16_to_f32(b1);
-    const uint16_t b2 = lm_f32_to_bf16(r1);
-    const float r2 = r1 - lm_bf16_to_f32(b2);
-    const uint16_t b3 = lm_f32_to_bf16(r2);
+    uint16_t b1, b2, b3;
+    lm_split3(w[i], b1, b2, b3);
     uint16_t* row = w3 + e * 3 * (size_t)H;
     row[h] = b1;
     row[H + h] = b2;

@@ -62,7 +62,7 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 struct Layout {
   size_t part, logits, ids, wts, counts, offsets, tile_off, perm_token, pair_row, pooled, pssq,
-      row_scale, act, O, ossq, y, wr3, kpart, total;
+      row_scale, act, O, ossq, y, wr3, kpart, xn, xna, total;
 };
 
 // Split-K plan for a dense BF16 projection: split only when the output tiles
@@ -119,14 +119,16 @@ bool narrow_for(const latent_moe_config& c, int64_t T) {
 }
 
 // Router k-splits: enough blocks to cover the chip, each split at least 4
-// k-tiles, all splits non-empty.
+// k-tiles, all splits non-empty. FP32 layers: K = H in 32-column k-tiles.
+// BF16 layers: x against the three-piece BF16 split of the router (K = 3H),
+// or, with the boundary norm, the six exact piece products (K = 6H).
 void router_split(const latent_moe_config& c, int64_t T, int& splits, int& kt_per, int& mt,
                   int& nt) {
   const bool f32 = c.act_dtype == LMOE_F32;
   const bool nar = narrow_for(c, T);
   const int BM = nar ? 32 : 64, BN = nar ? 256 : 128;  // router tile shapes
   const int KT = f32 ? 32 : 64;
-  const int64_t Kw = f32 ? c.hidden : 3 * c.hidden;
+  const int64_t Kw = f32 ? c.hidden : (c.input_norm ? 6 : 3) * c.hidden;
   const int ktot = (int)(Kw / KT);
   mt = ceil_div(T, BM);
   nt = ceil_div(c.experts, BN);
@@ -164,6 +166,8 @@ int validate_config(const latent_moe_config* c) {
   if (c->act_dtype == LMOE_BF16 && (c->hidden % 512 || c->pooled % 512 || c->intermediate % 512))
     return fail(LMOE_ERR_INVALID_ARG,
                 "BF16 layers need hidden, pooled and intermediate to be multiples of 512");
+  if (c->input_norm != 0 && c->input_norm != 1)
+    return fail(LMOE_ERR_INVALID_ARG, "input_norm must be 0 or 1");
   if ((size_t)c->pooled * c->intermediate * c->experts > ((size_t)1 << 40))
     return fail(LMOE_ERR_INVALID_ARG, "expert tensors too large");
   return LMOE_OK;
@@ -222,6 +226,8 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
     }
   }
   L.kpart = take(kp * 4);
+  L.xn = take(c.input_norm && c.act_dtype == LMOE_F32 ? (size_t)Tm * c.hidden * 4 : 0);
+  L.xna = take(c.input_norm && c.act_dtype == LMOE_BF16 ? (size_t)Tm * 3 * c.hidden * 2 : 0);
   L.total = o;
   return L;
 }
@@ -277,6 +283,24 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   Et* y = (Et*)(ws + L.y);
 
   LM_MARK(0);
+  // 0. boundary norm (optional): x is the pre-norm residual. FP32 layers: the
+  // router and pooler read the FP32 norm. BF16 layers: its exact three-piece
+  // BF16 split [T, 3H]; the router forms the FP32 products from the pieces,
+  // the pooler reads the first piece (the BF16 rounding) at row stride 3H.
+  const Et* xp = (const Et*)x;  // pooler input
+  int xp_ld = 0;                // its row stride (0: H)
+  const void* xr = x;           // router input
+  if (c.input_norm) {
+    float* xn = sizeof(Et) == 4 ? (float*)(ws + L.xn) : nullptr;
+    uint16_t* xs = sizeof(Et) == 2 ? (uint16_t*)(ws + L.xna) : nullptr;
+    hipLaunchKernelGGL(lm_input_norm_kernel<Et>, dim3((unsigned)T), dim3(256), 0, s, (const Et*)x, H,
+                       w.input_gamma, c.eps, xn, xs);
+    LM_HIP(hipGetLastError());
+    xr = sizeof(Et) == 4 ? (const void*)xn : (const void*)xs;
+    xp = (const Et*)xr;
+    xp_ld = sizeof(Et) == 4 ? 0 : 3 * H;
+  }
+  LM_MARK(1);
   // Steps 1-3 (routing) depend only on x, as do the pooler and its norm
   // statistics (step 4): outside stage profiling, routing runs on the
   // handle's side stream, forked from and joined back into the caller's
@@ -294,7 +318,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     int splits, kt_per, mt, nt;
     router_split(c, T, splits, kt_per, mt, nt);
     RouterProb<Cr> p;
-    p.x = (const Et*)x;
+    p.x = (const Et*)xr;
     p.w = sizeof(Et) == 2 ? (const Et*)(ws + L.wr3) : (const Et*)w.router;
     p.part = part;
     p.T = (int)T;
@@ -306,8 +330,12 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.nt = nt;
     p.splits = splits;
     p.kt_per = kt_per;
+    if (sizeof(Et) == 2 && c.input_norm) {
+      p.lda = 3 * H;
+      p.pieces = 3;
+    }
     LM_HIP(launch(p, (int64_t)mt * nt * splits, sr));
-    LM_MARK(1);
+    LM_MARK(2);
     // 2. top-k + softmax + per-expert counts
     hipLaunchKernelGGL(lm_fill_i32_kernel, dim3(ceil_div(E, 256)), dim3(256), 0, sr, counts, E, 0);
     // few tokens with many k-splits: one token per workgroup spreads the
@@ -331,13 +359,13 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
 #undef LM_TOPK
     LM_HIP(hipGetLastError());
   }
-  LM_MARK(2);
+  LM_MARK(3);
   // 3. grouping by expert
   hipLaunchKernelGGL(lm_permute_kernel, dim3(E), dim3(256), 0, sr, ids, npairs, k, counts, E, Cw::BM,
                      offsets, tile_off, perm_token, pair_row);
   LM_HIP(hipGetLastError());
   if (fork) LM_HIP(hipEventRecord(h->join, sr));
-  LM_MARK(3);
+  LM_MARK(4);
   // 4. pooler + norm statistics
   const int pnt = ceil_div(P, Cw::BN);
   int psplits = 1, pkt = 0;
@@ -345,7 +373,8 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   if (psplits > 1) {
     if constexpr (sizeof(Et) == 2) {
     DenseSplitProb<Cw> p;
-    p.a = (const Et*)x;
+    p.a = xp;
+    p.lda = xp_ld;
     p.w = (const Et*)Wpool;
     p.part = (float*)(ws + L.kpart);
     p.T = (int)T;
@@ -356,7 +385,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.splits = psplits;
     p.kt_per = pkt;
     LM_HIP(launch(p, (int64_t)p.mt * p.nt * psplits, s));
-    LM_MARK(4);
+    LM_MARK(5);
     const int chunks = ceil_div(P, 256);
     hipLaunchKernelGGL(lm_pool_finish_kernel, dim3((unsigned)T, (unsigned)chunks), dim3(256), 0, s,
                        (const float*)(ws + L.kpart), psplits, (int)T, P, w.pool_gamma,
@@ -368,7 +397,8 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     }
   } else {
     PoolerProb<Cw> p;
-    p.x = (const Et*)x;
+    p.x = xp;
+    p.lda = xp_ld;
     p.w = (const Et*)Wpool;
     p.gamma = w.pool_gamma;
     p.pooled = pooled;
@@ -379,12 +409,12 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.mt = ceil_div(T, Cw::BM);
     p.nt = pnt;
     LM_HIP(launch(p, (int64_t)p.mt * p.nt, s));
-    LM_MARK(4);
+    LM_MARK(5);
     hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, pssq, pnt,
                        (int)T, P, c.eps, row_scale);
     LM_HIP(hipGetLastError());
   }
-  LM_MARK(5);
+  LM_MARK(6);
   if (fork) LM_HIP(hipStreamWaitEvent(s, h->join, 0));
   const int64_t max_tiles = ceil_div(npairs, Cw::BM) + (npairs < E ? npairs : E);
   // 5. gate/up + SwiGLU
@@ -409,7 +439,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.nt = I / GateUpProb<Cw, MX>::kCols;
     LM_HIP(launch(p, max_tiles * p.nt, s));
   }
-  LM_MARK(6);
+  LM_MARK(7);
   // 6. down + per-row sum of squares partials
   const int dnt = ceil_div(P, Cw::BN);
   {
@@ -428,12 +458,12 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.nt = dnt;
     LM_HIP(launch(p, max_tiles * p.nt, s));
   }
-  LM_MARK(7);
+  LM_MARK(8);
   // 7. per-expert norm, routing weight, FP32 sum
   hipLaunchKernelGGL(lm_combine_kernel<Et>, dim3((unsigned)T), dim3(256), 0, s, O, ossq, dnt, pair_row,
                      ids, wts, w.expert_gamma, k, P, c.eps, y);
   LM_HIP(hipGetLastError());
-  LM_MARK(8);
+  LM_MARK(9);
   // 8. unpooler
   int usplits = 1, ukt = 0;
   if (packed) dense_split(T, H, P, Cw::BM, Cw::BN, usplits, ukt);
@@ -468,7 +498,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.nt = ceil_div(H, Cw::BN);
     LM_HIP(launch(p, (int64_t)p.mt * p.nt, s));
   }
-  LM_MARK(9);
+  LM_MARK(10);
   if (h->prof) h->prof_valid = true;
   return LMOE_OK;
 }
@@ -506,6 +536,10 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
   }
   if (w->router_bias && !aligned16(w->router_bias))
     return fail(LMOE_ERR_INVALID_ARG, "router_bias is not 16-byte aligned");
+  if (cfg->input_norm && !w->input_gamma)
+    return fail(LMOE_ERR_INVALID_ARG, "input_norm needs input_gamma");
+  if (cfg->input_norm && !aligned16(w->input_gamma))
+    return fail(LMOE_ERR_INVALID_ARG, "input_gamma is not 16-byte aligned");
   if (cfg->expert_dtype == LMOE_MXFP4) {
     const void* sc[] = {w->s_gate, w->s_up, w->s_down};
     const char* sn[] = {"s_gate", "s_up", "s_down"};
@@ -658,6 +692,8 @@ int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v) {
   v->act = ws + L.act;
   v->expert_out = (const float*)(ws + L.O);
   v->combined = ws + L.y;
+  v->x_norm = !h->cfg.input_norm ? nullptr
+              : h->cfg.act_dtype == LMOE_F32 ? (const void*)(ws + L.xn) : (const void*)(ws + L.xna);
   return LMOE_OK;
 }
 

@@ -13,6 +13,8 @@ Workloads (one per layer configuration the method is exercised on):
 * ``prefill``  T=16384, shapes as ``decode``
 * ``mxfp4``    ``prefill`` with the expert weights quantised to MXFP4
 * ``mxfp4_decode`` ``decode`` with the same MXFP4 expert weights
+* ``decode_norm``, ``prefill_norm``: ``decode`` / ``prefill`` with x taken as the
+  pre-norm residual (the layer applies its boundary norm, gamma ``input_gamma``)
 * ``skew``     5 chunks of 16384 tokens, BF16, with a Zipf(s=1.1) router bias
 
 Value distributions: x ~ N(0,1); every weight ~ N(0, 1/fan_in); RMSNorm gammas
@@ -55,6 +57,7 @@ class LayerSpec:
     zipf_s: float = 1.1
     chunks: int = 1
     seed: int = 0
+    input_norm: bool = False  # x is the pre-norm residual; the layer applies its boundary norm
 
     def with_(self, **kw) -> "LayerSpec":
         return replace(self, **kw)
@@ -67,6 +70,8 @@ CONFIGS = {
     "prefill": LayerSpec("prefill", T=16384, **_REAL),
     "mxfp4": LayerSpec("mxfp4", T=16384, expert_format="mxfp4", **_REAL),
     "mxfp4_decode": LayerSpec("mxfp4_decode", T=64, expert_format="mxfp4", **_REAL),
+    "decode_norm": LayerSpec("decode_norm", T=64, input_norm=True, **_REAL),
+    "prefill_norm": LayerSpec("prefill_norm", T=16384, input_norm=True, **_REAL),
     "skew": LayerSpec("skew", T=16384, router_bias="zipf", chunks=5, **_REAL),
 }
 

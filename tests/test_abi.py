@@ -18,7 +18,7 @@ def _has_device() -> bool:
 
 def real_cfg(**kw):
     d = dict(hidden=8192, pooled=4096, experts=256, intermediate=4096, top_k=8, eps=1e-6,
-             act_dtype="bf16", expert_dtype="bf16", max_tokens=16384)
+             act_dtype="bf16", expert_dtype="bf16", max_tokens=16384, input_norm=0)
     d.update(kw)
     return B.make_config(**d)
 
@@ -57,6 +57,7 @@ def test_workspace_bytes_real_shapes():
     (dict(act_dtype="f32", expert_dtype="mxfp4"), B.LMOE_ERR_UNSUPPORTED),
     (dict(intermediate=4096 + 256), B.LMOE_ERR_INVALID_ARG),  # BF16: multiples of 512
     (dict(expert_dtype="mxfp4", pooled=4096 + 256), B.LMOE_ERR_INVALID_ARG),
+    (dict(input_norm=2), B.LMOE_ERR_INVALID_ARG),
 ])
 def test_bad_configs_rejected(kw, code):
     with pytest.raises(B.LatentMoEError) as ei:
@@ -81,6 +82,24 @@ def test_create_rejects_null_and_misaligned_weights():
     assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
     assert "aligned" in B.latent_moe_last_error()
     assert L.latent_moe_create(None, ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+
+
+def test_input_norm_needs_gamma_and_sizes_workspace():
+    base = B.latent_moe_workspace_bytes(real_cfg())
+    withn = B.latent_moe_workspace_bytes(real_cfg(input_norm=1))
+    T, H = 16384, 8192
+    assert withn >= base + T * H * (4 + 2)  # FP32 norm output + its BF16 copy
+    L = B.lib()
+    cfg = real_cfg(input_norm=1)
+    h = ctypes.c_void_p(0)
+    w = B.Weights()
+    for n in ("router", "pooler", "pool_gamma", "w_gate", "w_up", "w_down", "expert_gamma", "unpooler"):
+        setattr(w, n, 4096)
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+    assert "input_gamma" in B.latent_moe_last_error()
+    w.input_gamma = 4096 + 4
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+    assert "aligned" in B.latent_moe_last_error()
 
 
 def test_mxfp4_accepted_and_scales_required():
