@@ -173,6 +173,8 @@ def main():
     ap.add_argument("--also", default="prefill,skew,decode_norm,prefill_norm,mxfp4_decode,mxfp4",
                     help="extra workloads measured in the same run (comma list)")
     ap.add_argument("--cpu-tokens", type=int, default=48, help="token sample for the CPU oracle (0: skip)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="also time torch's BF16 batched GEMM (hipBLASLt) on the gate/up shape, for reference")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run a plain device copy of this many bytes (calibrates profiler byte counters)")
     args = ap.parse_args()
@@ -290,6 +292,23 @@ def main():
                     "tokens_per_step": r["spec"].T * r["spec"].chunks,
                     "steps": r["steps"], "roofline": r["roofline"], "layer_frac": r["layer_frac"],
                     "stages_ms": {k: round(v, 4) for k, v in r["stages"].items()}}
+    if args.vendor_gemm:
+        # 256 experts x 512 rows (uniform routing), K = P, N = 2I; contiguous operands, no gather
+        E_, M_, K_, N_ = 256, 512, 4096, 8192
+        a = torch.randn(E_, M_, K_, device="cuda:0", dtype=torch.bfloat16)
+        b = torch.randn(E_, K_, N_, device="cuda:0", dtype=torch.bfloat16)
+        torch.bmm(a, b)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(10):
+            torch.bmm(a, b)
+        ev1.record()
+        torch.cuda.synchronize()
+        vms = ev0.elapsed_time(ev1) / 10
+        line["vendor_bf16_gemm"] = {"shape": f"bmm {E_} x [{M_} x {K_}] x [{K_} x {N_}]", "ms": round(vms, 4),
+                                    "TFLOP/s": round(2 * E_ * M_ * K_ * N_ / vms / 1e9, 1)}
+        del a, b
     if args.cpu_tokens > 0:
         xh = synth.host(spec, "x")
         log(f"cpu oracle on {args.cpu_tokens} tokens")

@@ -168,7 +168,9 @@ int latent_moe_forward(latent_moe_t* h, const void* x, int64_t T, float* out, in
  *   act      [T*k, I] (F32 if expert_dtype is F32, else BF16): SwiGLU
  *            output, grouped order
  *   expert_out [T*k, P] F32: o (before the per-expert norm), grouped order
- *   combined [T, P] (F32 or BF16 per act_dtype): y                          */
+ *   combined y: FP32 layers [T, P] F32; BF16 layers the BF16 pair [T, 2P]
+ *            (hi | lo, hi = BF16 rounding of y, lo = that of the remainder;
+ *            the unpooler reads both)                                     */
 typedef struct {
   const float* logits;
   const int32_t* ids;

@@ -245,7 +245,8 @@ class LatentMoE:
             "row_scale": (v.row_scale, (T,), np.float32),
             "act": (v.act, (T * k, I), exp_np),
             "expert_out": (v.expert_out, (T * k, P), np.float32),
-            "combined": (v.combined, (T, P), act_np),
+            "combined": (v.combined, (T, P), np.float32) if self.act_dtype == "f32"
+            else (v.combined, (T, 2 * P), np.uint16),
         }
         split_norm = bool(v.x_norm) and self.act_dtype != "f32"
         if v.x_norm:
@@ -258,6 +259,9 @@ class LatentMoE:
             a = np.empty(shape, dt)
             _memcpy_d2h(a.ctypes.data, ptr, a.nbytes)
             res[name] = a
+        if self.act_dtype != "f32" and "combined" in res:  # BF16 pair -> y = hi + lo (exact in FP32)
+            pr = (res["combined"].astype(np.uint32) << 16).view(np.float32)
+            res["combined"] = pr[:, :P] + pr[:, P:]
         if split_norm and "x_norm" in res:  # FP32 value = sum of the three BF16 pieces (exact)
             H = self.hidden
             pcs = (res["x_norm"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -113,7 +113,7 @@ void lm_gemm_stream_kernel(const Prob p) {
     for (int q = 0; q < QA; ++q) sa[buf * kStage + lm_swz(lr + 32 * q, lc)] = ra[slot][q];
   };
   auto load_b = [&](int slot, int kt) {
-    const int kc = min(kt, klast);
+    const int kc = lm_b_ktile(p, min(kt, klast));
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       if constexpr (kMx) {

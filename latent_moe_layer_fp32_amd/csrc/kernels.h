@@ -483,6 +483,7 @@ struct UnpoolerProb {
   const E* w;
   float* out;  // [T, H]
   int T, H, P, mt, nt;
+  int pieces = 1;  // 2: y is the BF16 pair [T, 2P], K runs over hi and lo k-tiles in turn
 
   LM_DEV bool tile(int bid, LmTile& t) const {
     int L;
@@ -495,11 +496,11 @@ struct UnpoolerProb {
     t.nt = n;
     t.e = 0;
     t.kt0 = 0;
-    t.kt1 = P / Cfg::KT;
+    t.kt1 = pieces * P / Cfg::KT;
     return true;
   }
   LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
-    return (const lm_u32x4*)(y + (size_t)(t.m0 + min(r, t.rows - 1)) * P);
+    return (const lm_u32x4*)(y + (size_t)(t.m0 + min(r, t.rows - 1)) * pieces * P);
   }
   LM_DEV const lm_u32x4* b_row(const LmTile& t, int r) const {
     return (const lm_u32x4*)(w + (size_t)min(t.n0 + r, H - 1) * P);
@@ -507,7 +508,9 @@ struct UnpoolerProb {
   LM_DEV const lm_u32x4* b_group(const LmTile& t, int wv, int j) const {
     return lm_packed_group(w, min(t.n0 + (wv * Cfg::TN + j) * 32, H - 32), P);
   }
-  LM_DEV int a_ktile(int kt) const { return kt; }
+  // pair: logical k-tile 2m + i reads piece i of y's k-tile m and W's k-tile m
+  LM_DEV int a_ktile(int kt) const { return pieces == 2 ? (kt & 1) * (P / Cfg::KT) + (kt >> 1) : kt; }
+  LM_DEV int b_ktile(int kt) const { return pieces == 2 ? kt >> 1 : kt; }
   LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
                        int lane, void*) const {
 #pragma unroll
@@ -533,10 +536,11 @@ template <class Cfg_>
 struct DenseSplitProb {
   using Cfg = Cfg_;
   using E = typename Cfg::E;
-  const E* a;   // [T, K]
+  const E* a;   // [T, K] (pieces 2: [T, 2K], hi | lo)
   const E* w;   // packed [N, K]
   float* part;  // [splits, T, N]
   int T, N, K, mt, nt, splits, kt_per;
+  int pieces = 1;  // 2: a is a BF16 pair, K runs over hi and lo k-tiles in turn
 
   LM_DEV bool tile(int bid, LmTile& t) const {
     int L;
@@ -550,17 +554,18 @@ struct DenseSplitProb {
     t.nt = n;
     t.e = s;
     t.kt0 = s * kt_per;
-    t.kt1 = min(K / Cfg::KT, t.kt0 + kt_per);
+    t.kt1 = min(pieces * K / Cfg::KT, t.kt0 + kt_per);
     return true;
   }
-  int lda = 0;  // row stride of a in elements (0: K)
+  int lda = 0;  // row stride of a in elements (0: pieces * K)
   LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
-    return (const lm_u32x4*)(a + (size_t)(t.m0 + min(r, t.rows - 1)) * (lda ? lda : K));
+    return (const lm_u32x4*)(a + (size_t)(t.m0 + min(r, t.rows - 1)) * (lda ? lda : pieces * K));
   }
   LM_DEV const lm_u32x4* b_group(const LmTile& t, int wv, int j) const {
     return lm_packed_group(w, min(t.n0 + (wv * Cfg::TN + j) * 32, N - 32), K);
   }
-  LM_DEV int a_ktile(int kt) const { return kt; }
+  LM_DEV int a_ktile(int kt) const { return pieces == 2 ? (kt & 1) * (K / Cfg::KT) + (kt >> 1) : kt; }
+  LM_DEV int b_ktile(int kt) const { return pieces == 2 ? kt >> 1 : kt; }
   LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
                        int lane, void*) const {
     float* dst = part + ((size_t)t.e * T + t.m0) * N;
@@ -837,7 +842,10 @@ __global__ void lm_rowscale_kernel(const float* ssq, int nparts, int T, int P, f
 }
 
 // One workgroup per token: y = sum over slots j (in order) of
-// w_j / sqrt(mean(o_j^2) + eps) * gamma_{e_j} * o_j, in FP32.
+// w_j / sqrt(mean(o_j^2) + eps) * gamma_{e_j} * o_j, in FP32. FP32 layers
+// store y [T, P]; BF16 layers store it as a BF16 pair [T, 2P] (hi | lo), which
+// the unpooler reads as a K of 2P (one BF16 rounding of y alone would be a
+// third of the layer's output error).
 template <typename Y>
 __global__ __launch_bounds__(256) void lm_combine_kernel(const float* O, const float* ossq,
                                                          int nparts, const int* pair_row,
@@ -866,10 +874,22 @@ __global__ __launch_bounds__(256) void lm_combine_kernel(const float* O, const f
     if constexpr (sizeof(Y) == 4) {
       *(lm_f32x4*)((float*)y + (size_t)t * P + c) = acc;
     } else {
-      lm_u32x2 v;
-      v[0] = (uint32_t)lm_f32_to_bf16(acc[0]) | ((uint32_t)lm_f32_to_bf16(acc[1]) << 16);
-      v[1] = (uint32_t)lm_f32_to_bf16(acc[2]) | ((uint32_t)lm_f32_to_bf16(acc[3]) << 16);
-      *(lm_u32x2*)((uint16_t*)y + (size_t)t * P + c) = v;
+      // BF16 pair y = hi + lo (hi the nearest-even BF16 of y, lo that of the
+      // exact FP32 remainder): 16 significant bits into the unpooler
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        hi[q] = lm_f32_to_bf16(acc[q]);
+        lo[q] = lm_f32_to_bf16(acc[q] - lm_bf16_to_f32(hi[q]));
+      }
+      uint16_t* row = (uint16_t*)y + (size_t)t * 2 * P;
+      lm_u32x2 vh, vl;
+      vh[0] = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
+      vh[1] = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
+      vl[0] = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
+      vl[1] = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
+      *(lm_u32x2*)(row + c) = vh;
+      *(lm_u32x2*)(row + P + c) = vl;
     }
   }
 }

@@ -211,7 +211,7 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
   L.act = take((size_t)Mp * I * esize_exp(c));
   L.O = take((size_t)Mp * P * 4);
   L.ossq = take((size_t)Mp * parts * 4);
-  L.y = take((size_t)Tm * P * esize_act(c));
+  L.y = take((size_t)Tm * P * 4);  // FP32 [T, P], or the BF16 pair [T, 2P]
   L.wr3 = take(c.act_dtype == LMOE_BF16 ? (size_t)E * 3 * c.hidden * 2 : 0);
   size_t kp = 0;
   if (c.act_dtype == LMOE_BF16) {
@@ -221,7 +221,7 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
       int sp, kpt;
       dense_split(T, P, c.hidden, BM, BN, sp, kpt);
       if (sp > 1 && (size_t)sp * T * P > kp) kp = (size_t)sp * T * P;
-      dense_split(T, c.hidden, P, BM, BN, sp, kpt);
+      dense_split(T, c.hidden, 2 * P, BM, BN, sp, kpt);
       if (sp > 1 && (size_t)sp * T * c.hidden > kp) kp = (size_t)sp * T * c.hidden;
     }
   }
@@ -464,9 +464,10 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
                      ids, wts, w.expert_gamma, k, P, c.eps, y);
   LM_HIP(hipGetLastError());
   LM_MARK(9);
-  // 8. unpooler
+  // 8. unpooler (BF16 layers: y as its BF16 pair, K = 2P)
+  const int ypieces = sizeof(Et) == 2 ? 2 : 1;
   int usplits = 1, ukt = 0;
-  if (packed) dense_split(T, H, P, Cw::BM, Cw::BN, usplits, ukt);
+  if (packed) dense_split(T, H, ypieces * P, Cw::BM, Cw::BN, usplits, ukt);
   if (usplits > 1) {
     if constexpr (sizeof(Et) == 2) {
     DenseSplitProb<Cw> p;
@@ -476,6 +477,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.T = (int)T;
     p.N = H;
     p.K = P;
+    p.pieces = ypieces;
     p.mt = ceil_div(T, Cw::BM);
     p.nt = ceil_div(H, Cw::BN);
     p.splits = usplits;
@@ -494,6 +496,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.T = (int)T;
     p.H = H;
     p.P = P;
+    p.pieces = ypieces;
     p.mt = ceil_div(T, Cw::BM);
     p.nt = ceil_div(H, Cw::BN);
     LM_HIP(launch(p, (int64_t)p.mt * p.nt, s));
