@@ -27,6 +27,36 @@ def _bf16(v: float) -> float:
     return struct.unpack("<f", struct.pack("<I", (upper & 0xFFFF) << 16))[0]
 
 
+def _e4m3_value(code: int) -> float:
+    e, m = (code >> 3) & 15, code & 7
+    mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -mag if code & 0x80 else mag
+
+
+def _mxfp8(v):
+    """MX FP8 (E4M3) quantisation of a list, blocks of 32: scale 2^(floor(log2
+    amax) - 8), each element the nearest finite E4M3 value (ties to the even
+    code), saturating at 448. Returns the dequantised list."""
+    out = []
+    for b0 in range(0, len(v), 32):
+        blk = v[b0:b0 + 32]
+        amax = max(abs(z) for z in blk)
+        if amax == 0.0:
+            out.extend(0.0 for _ in blk)
+            continue
+        m, ex = math.frexp(amax)  # amax = m * 2^ex, 0.5 <= m < 1
+        scale = 2.0 ** (ex - 1 - 8)
+        for z in blk:
+            q = min(abs(z) / scale, 448.0)
+            best, best_d = 0, None
+            for code in range(0x7F):  # +0 .. 448
+                d = abs(_e4m3_value(code) - q)
+                if best_d is None or d < best_d or (d == best_d and code % 2 == 0):
+                    best, best_d = code, d
+            out.append(math.copysign(_e4m3_value(best) * scale, z) if best else 0.0)
+    return out
+
+
 def _matvec(W, v):
     return [math.fsum(W[r][c] * v[c] for c in range(len(v))) for r in range(len(W))]
 
@@ -38,12 +68,13 @@ def _rmsnorm(v, gamma, eps):
 
 
 def forward(x, router, bias, pooler, pool_gamma, w_gate, w_up, w_down, expert_gamma,
-            unpooler, k, eps, input_gamma=None, bf16_acts=False):
+            unpooler, k, eps, input_gamma=None, bf16_acts=False, mxfp8_acts=False):
     """Returns (out [T][H], ids [T][k], w [T][k]) as Python lists.
 
     input_gamma: x is the pre-norm residual; the router reads its RMSNorm
     (times input_gamma) rounded to FP32, the pooler the same value rounded
-    on to BF16 when bf16_acts, else the FP32 value."""
+    on to BF16 when bf16_acts, else the FP32 value. mxfp8_acts: the expert
+    GEMMs read u and a MX-quantised to FP8 E4M3."""
     T, E = len(x), len(router)
     outs, all_ids, all_w = [], [], []
     for t in range(T):
@@ -71,12 +102,16 @@ def forward(x, router, bias, pooler, pool_gamma, w_gate, w_up, w_down, expert_ga
         wt = [v / s for v in ex]
 
         u = _rmsnorm(_matvec(pooler, xt), pool_gamma, eps)
+        if mxfp8_acts:
+            u = _mxfp8(u)
         P = len(u)
         y = [0.0] * P
         for j, e in enumerate(chosen):
             g = _matvec(w_gate[e], u)
             v = _matvec(w_up[e], u)
             a = [g[i] / (1.0 + math.exp(-g[i])) * v[i] for i in range(len(g))]
+            if mxfp8_acts:
+                a = _mxfp8(a)
             o = _matvec(w_down[e], a)
             oh = _rmsnorm(o, expert_gamma[e], eps)
             y = [y[p] + wt[j] * oh[p] for p in range(P)]

@@ -8,10 +8,23 @@
   element is FP4 E2M1. Stored as two elements per byte, element 2i in the low
   nibble. Value = scale * element, exact in FP64.
 
-Tables written from the OCP MX v1.0 definitions:
+* MXFP8 activations (the "fp8 x fp4" MMA kind, [lmsys] "NVFP4 as a third MMA
+  kind"; the quantiser that takes the pre-expert norm in [lmsys] "Fuse
+  normalization and remove routing conversions"): blocks of 32 consecutive
+  elements along the reduction axis share one E8M0 scale; elements are OCP
+  FP8 E4M3.
+
+Tables written from the OCP definitions (OCP 8-bit floating point v1.0, OCP MX v1.0):
   E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0; exponent 0 is
         subnormal (0 or 0.5). Magnitudes by code 0..7: 0, .5, 1, 1.5, 2, 3, 4, 6.
+  E4M3: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0; exponent 0
+        is subnormal (m/8 * 2^-6); no infinities; S.1111.111 is NaN, so the
+        largest magnitude is 1.75 * 2^8 = 448.
   E8M0: unsigned exponent, value 2^(code-127); code 255 is NaN.
+MX quantisation of a block (OCP MX v1.0): X = 2^(floor(log2(amax)) - emax) with
+emax the element format's largest exponent (2 for E2M1, 8 for E4M3), each
+element v/X rounded to the nearest representable element (ties to the even
+code), saturating at the largest magnitude; an all-zero block takes X = 2^-127.
 """
 from __future__ import annotations
 
@@ -33,6 +46,59 @@ def _e2m1_table() -> np.ndarray:
 
 
 E2M1 = _e2m1_table()
+
+
+def _e4m3_table() -> np.ndarray:
+    """Value of each of the 256 E4M3 codes (NaN for the two NaN codes)."""
+    vals = np.empty(256, np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 15
+        m = code & 7
+        if e == 15 and m == 7:
+            vals[code] = np.nan
+        elif e == 0:
+            vals[code] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            vals[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+E4M3 = _e4m3_table()
+E4M3_MAX = 448.0
+
+
+def _nearest_even(mag: np.ndarray, grid: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    """Round non-negative magnitudes to the nearest value of an ascending grid
+    (codes give each grid value's code; ties go to the even code)."""
+    i = np.clip(np.searchsorted(grid, mag), 1, len(grid) - 1)
+    lo, hi = grid[i - 1], grid[i]
+    dlo, dhi = mag - lo, hi - mag
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (codes[i] % 2 == 0))
+    return np.where(pick_hi, hi, lo)
+
+
+def quantize_mx(v: np.ndarray, fmt: str) -> tuple[np.ndarray, np.ndarray]:
+    """MX-quantise v [..., K] (K % 32 == 0) in blocks of 32 along the last axis.
+    Returns (dequantised values, scale exponents e with X = 2^e), FP64."""
+    if fmt == "mxfp8":
+        table, emax, vmax = E4M3[:0x7F], 8, E4M3_MAX  # codes 0..126: +0 .. 448
+    elif fmt == "mxfp4":
+        table, emax, vmax = E2M1[:8], 2, 6.0
+    else:
+        raise ValueError(fmt)
+    K = v.shape[-1]
+    b = v.reshape(v.shape[:-1] + (K // 32, 32))
+    amax = np.abs(b).max(-1)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - emax, -127.0)
+    e = np.clip(e, -127.0, 127.0)
+    X = np.ldexp(1.0, e.astype(np.int64))[..., None]
+    q = b / X
+    codes = np.arange(len(table))
+    mag = _nearest_even(np.minimum(np.abs(q), vmax), table, codes)
+    out = (np.sign(q) * mag * X).reshape(v.shape)
+    return out, e
 
 
 def e8m0_to_f64(codes: np.ndarray) -> np.ndarray:

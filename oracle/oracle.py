@@ -26,7 +26,11 @@ input values; BF16/FP32 inputs widen exactly, MXFP4 weights decode exactly):
    h_t = Wp x_t,  u_t = h_t / sqrt(mean(h_t^2) + eps) * gamma_p.
 5. Each selected SwiGLU expert e ([lmsys] same section, "routed SwiGLU experts"):
    g = Wg_e u_t, v = Wu_e u_t, a = silu(g) * v with silu(z) = z / (1 + e^-z),
-   o = Wd_e a.
+   o = Wd_e a. Optional MX activations (act_quant="mxfp8"; the "fp8 x fp4" MMA
+   kind of [lmsys] "NVFP4 as a third MMA kind", with the pre-expert norm folded
+   into the quantiser as in [lmsys] "Fuse normalization and remove routing
+   conversions"): the expert GEMMs read u and a MX-quantised to FP8 E4M3 in
+   blocks of 32 along their reduction axis (oracle/mx.py).
 6. Per-expert RMSNorm before the routing weight ([lmsys] same section, and
    "The Fused Post-per-expert Norm"):  o^ = o / sqrt(mean(o^2) + eps) * gamma_e.
 7. Routing-weighted sum ([lmsys] "Trainable Muse Spark Open Backend": each
@@ -49,7 +53,7 @@ from typing import Callable, Sequence
 
 import numpy as np
 
-from .mx import to_f64
+from .mx import quantize_mx, to_f64
 
 NEAR_TIE = 1e-6
 
@@ -135,7 +139,8 @@ def experts_from_arrays(w_gate, w_up, w_down) -> ExpertFn:
 def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, expert_gamma,
             unpooler, k: int, eps: float, *, force_ids: dict | None = None,
             order: str = "norm_then_sum", keep_pairs: bool = True,
-            round_bf16: Sequence[str] = (), input_gamma=None) -> OracleResult:
+            round_bf16: Sequence[str] = (), input_gamma=None,
+            act_quant: str | None = None) -> OracleResult:
     """Layer forward on tokens x [T, H] (any stored dtype).
 
     force_ids: {token: ids sequence} replaces the selection for those tokens
@@ -146,6 +151,7 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
       intermediate to BF16 (nearest even) the way a BF16 datapath would.
     input_gamma: [H] gamma of the boundary norm (step 0); x is then the
       pre-norm residual.
+    act_quant: None, or "mxfp8": the expert GEMMs read u and a MX-quantised.
     """
     act_bf16 = np.asarray(x).dtype == np.uint16
     x = to_f64(x)
@@ -178,6 +184,8 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
     u = rms_norm(h, gp, eps)
     if "u" in round_bf16:
         u = _bf16_round(u)
+    if act_quant:
+        u = quantize_mx(u, act_quant)[0]
 
     I = None
     ohat = np.zeros((T, k, P))
@@ -195,6 +203,8 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
         a = silu(g) * v
         if "a" in round_bf16:
             a = _bf16_round(a)
+        if act_quant:
+            a = quantize_mx(a, act_quant)[0]
         o = a @ Wd.T
         if keep_pairs:
             a_all[tt, jj] = a

@@ -2,6 +2,7 @@
 OCP Microscaling v1.0 definitions and to their own invariants."""
 import numpy as np
 import pytest
+import torch
 
 import synth
 from oracle import mx
@@ -118,3 +119,87 @@ def test_zipf_bias():
     r = np.sort(w)[::-1]
     ranks = np.arange(1, 257)
     np.testing.assert_allclose(r / r[0], ranks ** -1.1, rtol=1e-5)
+
+
+# ------------------------------------------------------------ MXFP8 activations
+
+
+def test_e4m3_table_matches_ocp_definition():
+    t = mx.E4M3
+    assert t[0x38] == 1.0 and t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x08] == 2.0 ** -6 and t[0x01] == 2.0 ** -9 and t[0x00] == 0.0
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    pos = t[:0x7F]
+    assert (np.diff(pos) > 0).all()
+    # the same values as torch's float8_e4m3fn (finite OCP E4M3) for every finite code
+    codes = torch.arange(256, dtype=torch.uint8)
+    tv = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    fin = ~np.isnan(t)
+    np.testing.assert_array_equal(tv[fin], t[fin])
+
+
+def test_mx_quantiser_reproduces_generated_mxfp4_weights():
+    # the generator (synth, C) and the oracle's quantiser (numpy) share no code
+    s = synth.CONFIGS["mxfp4"].with_(E=2, I=64, P=128, H=256)
+    f = synth.host(s.with_(expert_format="f32"), "w_up").astype(np.float64)
+    packed, scales = synth.host(s, "w_up")
+    q, e = mx.quantize_mx(f, "mxfp4")
+    np.testing.assert_array_equal(q, mx.mxfp4_to_f64(packed, scales))
+    np.testing.assert_array_equal(e, scales.astype(np.int64) - 127)
+
+
+def test_mxfp8_quantiser_definition_ties_saturation_and_library_rounding():
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((64, 128)) * np.exp(rng.uniform(-6, 6, (64, 1)))
+    q, e = mx.quantize_mx(v, "mxfp8")
+    b = v.reshape(-1, 32)
+    amax = np.abs(b).max(-1)
+    np.testing.assert_array_equal(e.reshape(-1), np.floor(np.log2(amax)) - 8)
+    X = 2.0 ** e.reshape(-1, 1)
+    r = b / X
+    # in range (|r| <= 448), element rounding equals torch's FP8 E4M3 cast (nearest even)
+    ok = np.abs(r) <= 448
+    tq = torch.from_numpy(r[ok]).to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    # the FP32 step is exact here: r has at most 53-bit significands but torch needs FP32 input,
+    # so only compare values that FP32 holds exactly
+    exact32 = r[ok].astype(np.float32).astype(np.float64) == r[ok]
+    np.testing.assert_array_equal((q.reshape(-1, 32) / X)[ok][exact32], tq[exact32])
+    # saturation above 448, ties to even, power-of-two equivariance, idempotence
+    sat, _ = mx.quantize_mx(np.array([[480.0, 500.0, -511.0] + [1.0] * 29]), "mxfp8")
+    assert sat[0, 0] == 448.0 and sat[0, 1] == 448.0 and sat[0, 2] == -448.0
+    tie, _ = mx.quantize_mx(np.array([[256.0, 1.0625, 1.1875, 3 * 2.0 ** -10] + [0.0] * 28]), "mxfp8")
+    assert tie[0, 1] == 1.0 and tie[0, 2] == 1.25 and tie[0, 3] == 2.0 ** -8
+    q2, _ = mx.quantize_mx(v * 2.0 ** 5, "mxfp8")
+    np.testing.assert_array_equal(q2, q * 2.0 ** 5)
+    q3, _ = mx.quantize_mx(q, "mxfp8")
+    np.testing.assert_array_equal(q3, q)
+    z, ez = mx.quantize_mx(np.zeros((1, 32)), "mxfp8")
+    assert not z.any() and ez[0, 0] == -127
+
+
+def test_oracle_mxfp8_activations_match_brute_force():
+    from oracle import brute
+    from oracle import oracle as orc
+
+    rng = np.random.default_rng(21)
+    T, H, P, E, I, k = 3, 8, 32, 4, 32, 2
+
+    def nrm(*shape, fan=1):
+        return (rng.standard_normal(shape) / np.sqrt(fan)).astype(np.float32)
+
+    d = dict(x=nrm(T, H), router=nrm(E, H, fan=H), pooler=nrm(P, H, fan=H),
+             pool_gamma=(1 + 0.1 * rng.standard_normal(P)).astype(np.float32),
+             w_gate=nrm(E, I, P, fan=P), w_up=nrm(E, I, P, fan=P), w_down=nrm(E, P, I, fan=I),
+             expert_gamma=(1 + 0.1 * rng.standard_normal((E, P))).astype(np.float32),
+             unpooler=nrm(H, P, fan=P))
+    r = orc.forward_inputs(d, k, 1e-6, act_quant="mxfp8")
+    plain = orc.forward_inputs(d, k, 1e-6)
+    f = lambda a: np.asarray(a, np.float64).tolist()
+    out, ids, w = brute.forward(f(d["x"]), f(d["router"]), None, f(d["pooler"]), f(d["pool_gamma"]),
+                                f(d["w_gate"]), f(d["w_up"]), f(d["w_down"]), f(d["expert_gamma"]),
+                                f(d["unpooler"]), k, 1e-6, mxfp8_acts=True)
+    assert np.array_equal(r.ids, np.array(ids))
+    np.testing.assert_allclose(r.out, np.array(out), rtol=0, atol=1e-12)
+    # the quantisation is visible, and of the size FP8 predicts (a few percent)
+    rel = np.abs(r.out - plain.out).max() / np.sqrt(np.mean(plain.out ** 2))
+    assert 1e-3 < rel < 0.2
