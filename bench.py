@@ -157,7 +157,8 @@ def cpu_baseline(spec, xh, sample_tokens, budget_s=30.0):
 
     t0 = time.perf_counter()
     orc.forward(xs, host["router"], host["router_bias"], host["pooler"], host["pool_gamma"], expert,
-                host["expert_gamma"], host["unpooler"], spec.k, spec.eps, keep_pairs=False, input_gamma=gin)
+                host["expert_gamma"], host["unpooler"], spec.k, spec.eps, keep_pairs=False, input_gamma=gin,
+                act_quant=spec.expert_act)
     dt = time.perf_counter() - t0
     return sample_tokens / dt, dt, len(raw)
 
@@ -168,9 +169,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "skew", "mxfp4", "mxfp4_decode", "decode_norm", "prefill_norm"])
+                    choices=["decode", "prefill", "skew", "mxfp4", "mxfp4_decode", "mxfp8", "mxfp8_decode",
+                             "decode_norm", "prefill_norm"])
     # skew: five 16384-token chunks of one long prompt (81920 tokens per step)
-    ap.add_argument("--also", default="prefill,skew,decode_norm,prefill_norm,mxfp4_decode,mxfp4",
+    ap.add_argument("--also", default="prefill,skew,decode_norm,prefill_norm,mxfp4_decode,mxfp4,mxfp8_decode,mxfp8",
                     help="extra workloads measured in the same run (comma list)")
     ap.add_argument("--cpu-tokens", type=int, default=48, help="token sample for the CPU oracle (0: skip)")
     ap.add_argument("--vendor-gemm", action="store_true",
@@ -193,7 +195,7 @@ def main():
         return LatentMoE(hidden=spec.H, pooled=spec.P, experts=spec.E, intermediate=spec.I,
                          top_k=spec.k, eps=spec.eps, act_dtype=spec.act_dtype,
                          expert_dtype=spec.expert_format, max_tokens=max_tokens, weights=w,
-                         input_norm=spec.input_norm)
+                         input_norm=spec.input_norm, expert_act=spec.expert_act)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     tables = synth.DeviceTables("cuda:0")
@@ -278,7 +280,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded counter-based N(0,1) inputs, N(0,1/fan_in) weights)",
         "config": {"workload": f"{args.workload}: " + (f"{spec.chunks} x " if spec.chunks > 1 else "") + f"{spec.T} tokens, H={spec.H}, P={spec.P}, E={spec.E}, "
-                               f"I={spec.I}, top-{spec.k}, {spec.expert_format.upper()} experts, FP32 router",
+                               f"I={spec.I}, top-{spec.k}, {spec.expert_format.upper()} experts"
+                               + (f", {spec.expert_act.upper()} expert inputs" if spec.expert_act else "")
+                               + ", FP32 router",
                    "global_batch": spec.T * spec.chunks, "parallelism": "none (one GPU)"},
         "roofline": main_r["roofline"],
         "layer_frac": main_r["layer_frac"],

@@ -54,6 +54,8 @@ extern "C" {
 #define LMOE_MXFP4 2 /* OCP MX FP4: E2M1 elements, two per byte (element 2i in the
                         low nibble), plus one E8M0 scale byte per 32 consecutive
                         elements along the input (K) axis */
+#define LMOE_MXFP8 3 /* OCP MX FP8: E4M3 elements, one per byte, plus one E8M0
+                        scale byte per 32 consecutive elements along K */
 
 typedef struct latent_moe latent_moe_t;
 
@@ -81,6 +83,16 @@ typedef struct {
                            conversions"). The router then reads that FP32
                            value and the pooler its act_dtype rounding (BF16
                            nearest-even, or the FP32 value). */
+  int32_t expert_act;   /* 0: the expert GEMMs read u and a in act_dtype (BF16).
+                           LMOE_MXFP8: they read them as MX FP8 (E4M3, one E8M0
+                           scale per 32 along K), quantised with nearest-even
+                           rounding and saturation at 448, on the scaled matrix
+                           cores against MXFP4 weights ("fp8 x fp4" MMA kind,
+                           lmsys post, "NVFP4 as a third MMA kind"; the
+                           pre-expert norm is applied by the quantiser, section
+                           "Fuse normalization and remove routing conversions").
+                           Needs expert_dtype LMOE_MXFP4 and act_dtype LMOE_BF16;
+                           changes the numerics (a few percent of RMS). */
 } latent_moe_config;
 
 /* Layer weights (device pointers), read in place unless stated otherwise; the
@@ -163,7 +175,8 @@ int latent_moe_forward(latent_moe_t* h, const void* x, int64_t T, float* out, in
  *            (stable in (t, j) order within an expert)
  *   pair_row [T*k] int32: for pair (t, j) at index t*k+j, its row in the
  *            grouped order
- *   pooled   [T, P] act_dtype: gamma_p * (Wp x_t), before the row scale
+ *   pooled   [T, P] act_dtype (F32 in MXFP8 mode): gamma_p * (Wp x_t), before
+ *            the row scale
  *   row_scale [T] F32: 1/sqrt(mean((Wp x_t)^2) + eps)
  *   act      [T*k, I] (F32 if expert_dtype is F32, else BF16): SwiGLU
  *            output, grouped order
@@ -184,6 +197,10 @@ typedef struct {
   const void* act;
   const float* expert_out;
   const void* combined;
+  const uint8_t* expert_in;        /* MXFP8 mode: u codes [T, P] E4M3, else NULL */
+  const uint8_t* expert_in_scales; /* MXFP8 mode: u scales [T, P/32] E8M0, else NULL */
+  const uint8_t* act_scales;       /* MXFP8 mode: act scales [T*k, I/32] E8M0 (act then
+                                      holds E4M3 codes [T*k, I]), else NULL */
   const void* x_norm;   /* boundary norm output (input_norm only, else NULL): FP32 layers
                            [T, H] F32; BF16 layers its exact three-piece BF16 split
                            [T, 3H] (pieces p1 | p2 | p3 side by side, p1 + p2 + p3 =

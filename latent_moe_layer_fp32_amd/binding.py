@@ -23,8 +23,8 @@ LMOE_ERR_UNSUPPORTED = -2
 LMOE_ERR_OOM = -3
 LMOE_ERR_HIP = -4
 LMOE_ERR_TOO_MANY_TOKENS = -5
-LMOE_F32, LMOE_BF16, LMOE_MXFP4 = 0, 1, 2
-DTYPE_CODES = {"f32": LMOE_F32, "bf16": LMOE_BF16, "mxfp4": LMOE_MXFP4}
+LMOE_F32, LMOE_BF16, LMOE_MXFP4, LMOE_MXFP8 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": LMOE_F32, "bf16": LMOE_BF16, "mxfp4": LMOE_MXFP4, "mxfp8": LMOE_MXFP8}
 
 
 class LatentMoEError(RuntimeError):
@@ -45,6 +45,7 @@ class Config(ctypes.Structure):
         ("expert_dtype", ctypes.c_int32),
         ("max_tokens", ctypes.c_int64),
         ("input_norm", ctypes.c_int32),
+        ("expert_act", ctypes.c_int32),
     ]
 
 
@@ -57,7 +58,8 @@ class Weights(ctypes.Structure):
 class Views(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "ids", "weights", "counts", "offsets", "perm_token", "pair_row", "pooled",
-        "row_scale", "act", "expert_out", "combined", "x_norm")]
+        "row_scale", "act", "expert_out", "combined", "expert_in", "expert_in_scales", "act_scales",
+        "x_norm")]
 
 
 _lib = None
@@ -113,10 +115,10 @@ def _check(rc: int):
 
 
 def make_config(hidden, pooled, experts, intermediate, top_k, eps, act_dtype, expert_dtype,
-                max_tokens, input_norm=False) -> Config:
+                max_tokens, input_norm=False, expert_act=0) -> Config:
     return Config(hidden, pooled, experts, intermediate, top_k, eps,
                   DTYPE_CODES.get(act_dtype, act_dtype), DTYPE_CODES.get(expert_dtype, expert_dtype),
-                  max_tokens, int(input_norm))
+                  max_tokens, int(input_norm), DTYPE_CODES.get(expert_act, expert_act) if expert_act else 0)
 
 
 def latent_moe_workspace_bytes(cfg: Config) -> int:
@@ -173,17 +175,20 @@ class LatentMoE:
     weights: dict with router, router_bias (or None), pooler, pool_gamma,
     w_gate, w_up, w_down (MXFP4: (packed, scales) pairs), expert_gamma,
     unpooler, and input_gamma when input_norm (x is then the pre-norm
-    residual). The tensors are referenced by this object so they outlive the
-    handle.
+    residual). expert_act="mxfp8" runs the expert GEMMs on MX FP8 activations
+    (MXFP4 experts only). The tensors are referenced by this object so they
+    outlive the handle.
     """
 
     def __init__(self, *, hidden, pooled, experts, intermediate, top_k, eps, act_dtype,
-                 expert_dtype, max_tokens, weights: dict, input_norm: bool = False):
+                 expert_dtype, max_tokens, weights: dict, input_norm: bool = False,
+                 expert_act=None):
         import torch
 
         self.cfg = make_config(hidden, pooled, experts, intermediate, top_k, eps, act_dtype,
-                               expert_dtype, max_tokens, input_norm)
+                               expert_dtype, max_tokens, input_norm, expert_act or 0)
         self.input_norm = bool(input_norm)
+        self.expert_act = expert_act
         self.top_k, self.hidden, self.pooled, self.experts = top_k, hidden, pooled, experts
         self.intermediate = intermediate
         self.act_dtype, self.expert_dtype = act_dtype, expert_dtype
@@ -231,8 +236,9 @@ class LatentMoE:
         torch.cuda.synchronize(self.device)
         v = latent_moe_debug_views(self.handle)
         k, E, P, I = self.top_k, self.experts, self.pooled, self.intermediate
+        f8 = self.expert_act == "mxfp8"
         act_np = np.float32 if self.act_dtype == "f32" else np.uint16
-        exp_np = np.float32 if self.expert_dtype == "f32" else np.uint16
+        exp_np = np.float32 if self.expert_dtype == "f32" else (np.uint8 if f8 else np.uint16)
         spec = {
             "logits": (v.logits, (T, E), np.float32),
             "ids": (v.ids, (T, k), np.int32),
@@ -241,13 +247,17 @@ class LatentMoE:
             "offsets": (v.offsets, (E + 1,), np.int32),
             "perm_token": (v.perm_token, (T * k,), np.int32),
             "pair_row": (v.pair_row, (T * k,), np.int32),
-            "pooled": (v.pooled, (T, P), act_np),
+            "pooled": (v.pooled, (T, P), np.float32 if f8 else act_np),
             "row_scale": (v.row_scale, (T,), np.float32),
             "act": (v.act, (T * k, I), exp_np),
             "expert_out": (v.expert_out, (T * k, P), np.float32),
             "combined": (v.combined, (T, P), np.float32) if self.act_dtype == "f32"
             else (v.combined, (T, 2 * P), np.uint16),
         }
+        if f8:  # MX FP8 codes and E8M0 scales, as stored
+            spec["expert_in"] = (v.expert_in, (T, P), np.uint8)
+            spec["expert_in_scales"] = (v.expert_in_scales, (T, P // 32), np.uint8)
+            spec["act_scales"] = (v.act_scales, (T * k, I // 32), np.uint8)
         split_norm = bool(v.x_norm) and self.act_dtype != "f32"
         if v.x_norm:
             spec["x_norm"] = ((v.x_norm, (T, 3 * self.hidden), np.uint16) if split_norm

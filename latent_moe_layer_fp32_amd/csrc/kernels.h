@@ -255,6 +255,7 @@ struct PoolerProb {
   E* pooled;
   float* ssq;  // [T, nt]
   int T, H, P, mt, nt;
+  float* pooled32 = nullptr;  // if set, gamma_p * h is written here in FP32 instead
 
   LM_DEV bool tile(int bid, LmTile& t) const {
     int L;
@@ -297,8 +298,11 @@ struct PoolerProb {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
-          if (row < t.rows)
-            pooled[(size_t)(t.m0 + row) * P + col] = LmElem<E>::from_f32(acc[tm][tn][i] * g);
+          if (row < t.rows) {
+            const float v = acc[tm][tn][i] * g;
+            if (pooled32) pooled32[(size_t)(t.m0 + row) * P + col] = v;
+            else pooled[(size_t)(t.m0 + row) * P + col] = LmElem<E>::from_f32(v);
+          }
         }
     }
   }
@@ -590,14 +594,16 @@ struct DenseSplitProb {
 // lm_rowscale_kernel forms the row scale exactly as on the unsplit path.
 __global__ __launch_bounds__(256) void lm_pool_finish_kernel(const float* part, int splits, int T,
                                                              int P, const float* gamma,
-                                                             uint16_t* pooled, float* ssq) {
+                                                             uint16_t* pooled, float* ssq,
+                                                             float* pooled32) {
   __shared__ float red[256];
   const int t = blockIdx.x, chunk = blockIdx.y, tid = threadIdx.x;
   const int c = chunk * 256 + tid;
   float h = 0.0f;
   if (c < P) {
     for (int sp = 0; sp < splits; ++sp) h += part[((size_t)sp * T + t) * P + c];
-    pooled[(size_t)t * P + c] = lm_f32_to_bf16(h * gamma[c]);
+    if (pooled32) pooled32[(size_t)t * P + c] = h * gamma[c];
+    else pooled[(size_t)t * P + c] = lm_f32_to_bf16(h * gamma[c]);
   }
   red[tid] = h * h;
   __syncthreads();

@@ -18,6 +18,7 @@
 #include "../../include/latent_moe.h"
 #include "gemm_stream.h"
 #include "kernels.h"
+#include "mx_act.h"
 
 namespace {
 
@@ -62,7 +63,7 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 struct Layout {
   size_t part, logits, ids, wts, counts, offsets, tile_off, perm_token, pair_row, pooled, pssq,
-      row_scale, act, O, ossq, y, wr3, kpart, xn, xna, total;
+      row_scale, act, O, ossq, y, wr3, kpart, xn, xna, uq, us, acts, total;
 };
 
 // Split-K plan for a dense BF16 projection: split only when the output tiles
@@ -168,6 +169,10 @@ int validate_config(const latent_moe_config* c) {
                 "BF16 layers need hidden, pooled and intermediate to be multiples of 512");
   if (c->input_norm != 0 && c->input_norm != 1)
     return fail(LMOE_ERR_INVALID_ARG, "input_norm must be 0 or 1");
+  if (c->expert_act != 0 && c->expert_act != LMOE_MXFP8)
+    return fail(LMOE_ERR_INVALID_ARG, "expert_act must be 0 or LMOE_MXFP8");
+  if (c->expert_act == LMOE_MXFP8 && (c->expert_dtype != LMOE_MXFP4 || c->act_dtype != LMOE_BF16))
+    return fail(LMOE_ERR_UNSUPPORTED, "MXFP8 expert activations need MXFP4 experts and BF16 activations");
   if ((size_t)c->pooled * c->intermediate * c->experts > ((size_t)1 << 40))
     return fail(LMOE_ERR_INVALID_ARG, "expert tensors too large");
   return LMOE_OK;
@@ -205,7 +210,8 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
   L.tile_off = take((size_t)(E + 1) * 4);
   L.perm_token = take((size_t)Mp * 4);
   L.pair_row = take((size_t)Mp * 4);
-  L.pooled = take((size_t)Tm * P * esize_act(c));
+  const bool f8 = c.expert_act == LMOE_MXFP8;
+  L.pooled = take((size_t)Tm * P * (f8 ? 4 : esize_act(c)));  // MXFP8: FP32 gamma_p * h
   L.pssq = take((size_t)Tm * parts * 4);
   L.row_scale = take((size_t)Tm * 4);
   L.act = take((size_t)Mp * I * esize_exp(c));
@@ -226,6 +232,9 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
     }
   }
   L.kpart = take(kp * 4);
+  L.uq = take(f8 ? (size_t)Tm * P : 0);          // MX FP8 u codes
+  L.us = take(f8 ? (size_t)Tm * P / 32 : 0);     // and E8M0 scales
+  L.acts = take(f8 ? (size_t)Mp * I / 32 : 0);   // E8M0 scales of the FP8 act codes (in act)
   L.xn = take(c.input_norm && c.act_dtype == LMOE_F32 ? (size_t)Tm * c.hidden * 4 : 0);
   L.xna = take(c.input_norm && c.act_dtype == LMOE_BF16 ? (size_t)Tm * 3 * c.hidden * 2 : 0);
   L.total = o;
@@ -248,7 +257,16 @@ hipError_t launch(const Prob& p, int64_t units, hipStream_t s) {
     if (h->prof) LM_HIP(hipEventRecord(h->ev[(i)], s));  \
   } while (0)
 
-template <typename Et, template <typename> class CW, template <typename> class CR, bool MX = false>
+template <class Prob>
+hipError_t launch_f8(const Prob& p, int64_t units, hipStream_t s) {
+  if (units <= 0) return hipSuccess;
+  const int64_t g = (units + 7) / 8 * 8;
+  hipLaunchKernelGGL(lm_gemm_stream_f8_kernel<Prob>, dim3((unsigned)g), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename Et, template <typename> class CW, template <typename> class CR, bool MX = false,
+          bool F8 = false>
 int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_t s) {
   const latent_moe_config& c = h->cfg;
   const latent_moe_weights& w = h->w;
@@ -389,7 +407,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     const int chunks = ceil_div(P, 256);
     hipLaunchKernelGGL(lm_pool_finish_kernel, dim3((unsigned)T, (unsigned)chunks), dim3(256), 0, s,
                        (const float*)(ws + L.kpart), psplits, (int)T, P, w.pool_gamma,
-                       (uint16_t*)pooled, pssq);
+                       (uint16_t*)pooled, pssq, F8 ? (float*)pooled : nullptr);
     LM_HIP(hipGetLastError());
     hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, pssq, chunks,
                        (int)T, P, c.eps, row_scale);
@@ -397,6 +415,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     }
   } else {
     PoolerProb<Cw> p;
+    if (F8) p.pooled32 = (float*)pooled;
     p.x = xp;
     p.lda = xp_ld;
     p.w = (const Et*)Wpool;
@@ -414,11 +433,40 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
                        (int)T, P, c.eps, row_scale);
     LM_HIP(hipGetLastError());
   }
+  if constexpr (F8) {  // u = r * gamma_p * h quantised to MX FP8 for the expert GEMMs
+    const int64_t nthr = T * (int64_t)(P / 32) * 8;
+    hipLaunchKernelGGL(lm_quant_u_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s,
+                       (const float*)pooled, row_scale, (int)T, P, (uint8_t*)(ws + L.uq),
+                       (uint8_t*)(ws + L.us));
+    LM_HIP(hipGetLastError());
+  }
   LM_MARK(6);
   if (fork) LM_HIP(hipStreamWaitEvent(s, h->join, 0));
   const int64_t max_tiles = ceil_div(npairs, Cw::BM) + (npairs < E ? npairs : E);
   // 5. gate/up + SwiGLU
-  {
+  if constexpr (F8) {
+    GateUpF8Prob<Cw> p;
+    p.sg = h->pk_sgate;
+    p.su = h->pk_sup;
+    p.pooled = pooled;
+    p.wg = (const Et*)Wgate;
+    p.wu = (const Et*)Wup;
+    p.row_scale = row_scale;
+    p.perm_token = perm_token;
+    p.counts = counts;
+    p.offsets = offsets;
+    p.tile_off = tile_off;
+    p.act = act;
+    p.P = P;
+    p.I = I;
+    p.Ex = E;
+    p.nt = I / GateUpF8Prob<Cw>::kCols;
+    p.uq = (const uint8_t*)(ws + L.uq);
+    p.us = (const uint8_t*)(ws + L.us);
+    p.aq = (uint8_t*)act;
+    p.as = (uint8_t*)(ws + L.acts);
+    LM_HIP(launch_f8(p, max_tiles * p.nt, s));
+  } else {
     GateUpProb<Cw, MX> p;
     if constexpr (MX) {
       p.sg = h->pk_sgate;
@@ -442,7 +490,24 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   LM_MARK(7);
   // 6. down + per-row sum of squares partials
   const int dnt = ceil_div(P, Cw::BN);
-  {
+  if constexpr (F8) {
+    DownF8Prob<Cw> p;
+    p.sd = h->pk_sdown;
+    p.act = act;
+    p.wd = (const Et*)Wdown;
+    p.counts = counts;
+    p.offsets = offsets;
+    p.tile_off = tile_off;
+    p.out = O;
+    p.ssq = ossq;
+    p.P = P;
+    p.I = I;
+    p.Ex = E;
+    p.nt = dnt;
+    p.aq = (const uint8_t*)act;
+    p.as = (const uint8_t*)(ws + L.acts);
+    LM_HIP(launch_f8(p, max_tiles * p.nt, s));
+  } else {
     DownProb<Cw, MX> p;
     if constexpr (MX) p.sd = h->pk_sdown;
     p.act = act;
@@ -659,6 +724,9 @@ int latent_moe_forward(latent_moe_t* h, const void* x, int64_t T, float* out, in
   if (h->cfg.act_dtype == LMOE_F32)
     rc = nar ? forward_impl<float, CfgNarrow, CfgRouterNarrow>(h, x, T, out, s)
              : forward_impl<float, CfgWide, CfgRouterWide>(h, x, T, out, s);
+  else if (h->cfg.expert_dtype == LMOE_MXFP4 && h->cfg.expert_act == LMOE_MXFP8)
+    rc = nar ? forward_impl<uint16_t, CfgNarrow, CfgRouterNarrow, true, true>(h, x, T, out, s)
+             : forward_impl<uint16_t, CfgWide, CfgRouterWide, true, true>(h, x, T, out, s);
   else if (h->cfg.expert_dtype == LMOE_MXFP4)
     rc = nar ? forward_impl<uint16_t, CfgNarrow, CfgRouterNarrow, true>(h, x, T, out, s)
              : forward_impl<uint16_t, CfgWide, CfgRouterWide, true>(h, x, T, out, s);
@@ -695,6 +763,10 @@ int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v) {
   v->act = ws + L.act;
   v->expert_out = (const float*)(ws + L.O);
   v->combined = ws + L.y;
+  const bool f8 = h->cfg.expert_act == LMOE_MXFP8;
+  v->expert_in = f8 ? (const uint8_t*)(ws + L.uq) : nullptr;
+  v->expert_in_scales = f8 ? (const uint8_t*)(ws + L.us) : nullptr;
+  v->act_scales = f8 ? (const uint8_t*)(ws + L.acts) : nullptr;
   v->x_norm = !h->cfg.input_norm ? nullptr
               : h->cfg.act_dtype == LMOE_F32 ? (const void*)(ws + L.xn) : (const void*)(ws + L.xna);
   return LMOE_OK;

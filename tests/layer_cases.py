@@ -58,7 +58,7 @@ def make_layer(spec: synth.LayerSpec, weights: dict, max_tokens: int):
 
     return LatentMoE(hidden=spec.H, pooled=spec.P, experts=spec.E, intermediate=spec.I, top_k=spec.k,
                      eps=spec.eps, act_dtype=spec.act_dtype, expert_dtype=spec.expert_format,
-                     max_tokens=max_tokens, weights=weights)
+                     max_tokens=max_tokens, weights=weights, expert_act=spec.expert_act)
 
 
 def check_routing(gpu_ids: np.ndarray, gpu_w: np.ndarray, logits64: np.ndarray, k: int,

@@ -327,3 +327,33 @@ def test_mxfp4_prefill_parity(torch_dev, tables, mx, T):
     sample = np.sort(np.random.default_rng(T + 1).choice(T, 4, replace=False))
     sample[-1] = T - 1
     _sampled_parity(torch, spec, layer, host, x, xh, sample, TOL_MXFP4, f"mxfp4 prefill T={T}")
+
+
+# ------------------------------------ MX FP8 activations against MXFP4 weights
+
+
+def test_mxfp8_activations_real_shapes(torch_dev, tables, mx):
+    """The MXFP4 layer with the expert GEMMs on MX FP8 activations (scaled
+    matrix cores), against the oracle quantising u and a identically: every
+    token of the decode batch and sampled tokens of the 16384-token batch,
+    output max-abs <= 5e-2 x RMS."""
+    torch = torch_dev
+    spec, wts, _, _ = mx
+    for wl, T in (("mxfp8_decode", 64), ("mxfp8", 16384)):
+        s8 = synth.CONFIGS[wl]
+        say(f"case: {wl}, T={T}")
+        layer = make_layer(s8, wts, max_tokens=T)
+        host = HostLayer(s8)
+        try:
+            x = synth.device_tensor(s8, "x", tables)
+            xh = synth.host(s8, "x")
+            out, ids, w = run_layer(torch, layer, x)
+            near, _ = check_routing(ids, w, host.logits(xh), s8.k)
+            sample = np.arange(T) if T <= 64 else np.sort(np.random.default_rng(8).choice(T, 4, replace=False))
+            force = {i: ids[t] for i, t in enumerate(sample) if t in near}
+            r = host.oracle(xh[sample], act_quant="mxfp8", force_ids=force or None)
+            assert np.array_equal(ids[sample], r.ids)
+            e = check_output(out[sample], r.out, 5e-2)
+            say(f"{wl}: out max-abs {e:.3g} x RMS on {len(sample)} tokens")
+        finally:
+            layer.close()

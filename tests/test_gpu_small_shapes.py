@@ -95,3 +95,62 @@ def test_small_full_parity(torch_dev, tables, name, over, T):
         say(f"{name}: out max-abs {e:.3g} x RMS over all {T} tokens")
     finally:
         layer.close()
+
+
+# ------------------------------------------- MX FP8 activations (fp8 x fp4 MMA)
+
+F8_CASES = [("mxfp8 wide", 300), ("mxfp8 narrow", 37)]
+
+
+def _decode_mx8(codes, scales):
+    from oracle import mx
+
+    v = mx.E4M3[codes.astype(np.int64)]
+    s = mx.e8m0_to_f64(scales)
+    K = codes.shape[-1]
+    return (v.reshape(codes.shape[:-1] + (K // 32, 32)) * s[..., None]).reshape(codes.shape)
+
+
+@pytest.mark.parametrize("name,T", F8_CASES, ids=[c[0] for c in F8_CASES])
+def test_small_mxfp8_activations_parity(torch_dev, tables, name, T):
+    """Against the oracle with u and a MX-quantised to FP8 at the same points:
+    quantised u equal code for code except rare rounding-boundary flips (the
+    GPU forms u in FP32, the oracle in FP64), output max-abs <= 5e-2 x RMS."""
+    torch = torch_dev
+    from latent_moe_layer_fp32_amd import LatentMoE
+
+    spec = synth.CONFIGS["decode"].with_(name="small", T=T, E=16, k=4, expert_format="mxfp4", **SMALL)
+    say(f"case: {name}, T={T}")
+    wts = device_weights(spec, tables)
+    layer = LatentMoE(hidden=spec.H, pooled=spec.P, experts=spec.E, intermediate=spec.I, top_k=spec.k,
+                      eps=spec.eps, act_dtype=spec.act_dtype, expert_dtype=spec.expert_format,
+                      max_tokens=512, weights=wts, expert_act="mxfp8")
+    try:
+        x = synth.device_tensor(spec, "x", tables)
+        ids_d = torch.empty((T, spec.k), dtype=torch.int32, device=x.device)
+        w_d = torch.empty((T, spec.k), dtype=torch.float32, device=x.device)
+        out = layer.forward(x, topk_ids=ids_d, topk_weights=w_d)
+        torch.cuda.synchronize()
+        out, ids, w = out.cpu().numpy(), ids_d.cpu().numpy(), w_d.cpu().numpy()
+        v = layer.views(T)
+        host = HostLayer(spec)
+        xh = host.x()
+        r0 = host.oracle(xh, keep_pairs=False, act_quant="mxfp8")
+        near, _ = check_routing(ids, w, r0.logits, spec.k)
+        force = {int(t): ids[t] for t in near}
+        r = host.oracle(xh, act_quant="mxfp8", force_ids=force or None)
+        assert np.array_equal(ids, r.ids)
+        # the quantised expert input: same codes but for rare boundary flips
+        uq = _decode_mx8(v["expert_in"], v["expert_in_scales"])
+        diff = uq != r.u
+        frac = diff.mean()
+        rel = np.abs(uq - r.u)[diff] / np.abs(r.u)[diff] if diff.any() else np.zeros(1)
+        assert frac < 1e-3 and rel.max() <= 0.14, f"u: {frac:.3g} of elements differ, max rel {rel.max():.3g}"
+        pr = v["pair_row"].reshape(T, spec.k)
+        aq = _decode_mx8(v["act"], v["act_scales"])[pr]
+        check_rel_l2(aq, r.a, 1e-2, "act (MX FP8)")
+        check_rel_l2(v["expert_out"][pr], r.o, 1e-2, "expert out")
+        e = check_output(out, r.out, 5e-2)
+        say(f"{name}: u flips {frac:.2e}; out max-abs {e:.3g} x RMS over all {T} tokens")
+    finally:
+        layer.close()
