@@ -18,7 +18,7 @@ def _has_device() -> bool:
 
 def real_cfg(**kw):
     d = dict(hidden=8192, pooled=4096, experts=256, intermediate=4096, top_k=8, eps=1e-6,
-             act_dtype="bf16", expert_dtype="bf16", max_tokens=16384, input_norm=0)
+             act_dtype="bf16", expert_dtype="bf16", max_tokens=16384, input_norm=0, expert_act=0)
     d.update(kw)
     return B.make_config(**d)
 
@@ -58,6 +58,9 @@ def test_workspace_bytes_real_shapes():
     (dict(intermediate=4096 + 256), B.LMOE_ERR_INVALID_ARG),  # BF16: multiples of 512
     (dict(expert_dtype="mxfp4", pooled=4096 + 256), B.LMOE_ERR_INVALID_ARG),
     (dict(input_norm=2), B.LMOE_ERR_INVALID_ARG),
+    (dict(expert_act=5), B.LMOE_ERR_INVALID_ARG),
+    (dict(expert_act="mxfp8"), B.LMOE_ERR_UNSUPPORTED),  # BF16 experts
+    (dict(expert_act="mxfp8", expert_dtype="mxfp4", act_dtype="f32"), B.LMOE_ERR_UNSUPPORTED),
 ])
 def test_bad_configs_rejected(kw, code):
     with pytest.raises(B.LatentMoEError) as ei:
@@ -82,6 +85,14 @@ def test_create_rejects_null_and_misaligned_weights():
     assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
     assert "aligned" in B.latent_moe_last_error()
     assert L.latent_moe_create(None, ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+
+
+def test_mxfp8_activations_accepted_with_mxfp4_experts():
+    base = B.latent_moe_workspace_bytes(real_cfg(expert_dtype="mxfp4"))
+    f8 = B.latent_moe_workspace_bytes(real_cfg(expert_dtype="mxfp4", expert_act="mxfp8"))
+    T, P, I, k = 16384, 4096, 4096, 8
+    # FP32 pooled rows instead of BF16, plus FP8 u codes and the E8M0 scales
+    assert f8 >= base + T * P * 2 + T * P + T * P // 32 + T * k * I // 32
 
 
 def test_input_norm_needs_gamma_and_sizes_workspace():
