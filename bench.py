@@ -28,6 +28,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
+# dense matrix peaks of the scaled (MX) instructions: an fp8 x fp4 product runs at the
+# FP8 rate, fp4 x fp4 at the FP4 rate
+MX_PEAK_TFLOPS = {"mxfp8": 5000.0, "mxfp4": 10100.0}
 
 
 def log(*a):
@@ -170,9 +173,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "skew", "mxfp4", "mxfp4_decode", "mxfp8", "mxfp8_decode",
-                             "decode_norm", "prefill_norm"])
+                             "mxfp4act", "mxfp4act_decode", "decode_norm", "prefill_norm"])
     # skew: five 16384-token chunks of one long prompt (81920 tokens per step)
-    ap.add_argument("--also", default="prefill,skew,decode_norm,prefill_norm,mxfp4_decode,mxfp4,mxfp8_decode,mxfp8",
+    ap.add_argument("--also", default="prefill,skew,decode_norm,prefill_norm,mxfp4_decode,mxfp4,mxfp8_decode,mxfp8,"
+                                      "mxfp4act_decode,mxfp4act",
                     help="extra workloads measured in the same run (comma list)")
     ap.add_argument("--cpu-tokens", type=int, default=48, help="token sample for the CPU oracle (0: skip)")
     ap.add_argument("--vendor-gemm", action="store_true",
@@ -252,8 +256,10 @@ def main():
         else:
             fl = 2 * spec.T * spec.chunks * spec.k * spec.P * 2 * spec.I
             ach = fl / gu / 1e12
-            r["roofline"] = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+            peak = MX_PEAK_TFLOPS.get(spec.expert_act, BF16_PEAK_TFLOPS)
+            r["roofline"] = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak,
+                             "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                             "peak_dtype": spec.expert_act or "bf16",
                              "traffic": measured_traffic(wl, "gate_up"),
                              "kernel": "gate_up grouped GEMM + SwiGLU",
                              "kernel_ms": round(stages["gate_up"], 4)}

@@ -91,8 +91,11 @@ typedef struct {
                            lmsys post, "NVFP4 as a third MMA kind"; the
                            pre-expert norm is applied by the quantiser, section
                            "Fuse normalization and remove routing conversions").
-                           Needs expert_dtype LMOE_MXFP4 and act_dtype LMOE_BF16;
-                           changes the numerics (a few percent of RMS). */
+                           LMOE_MXFP4: MX FP4 (E2M1, two per byte, one E8M0
+                           scale per 32 along K), nearest-even rounding,
+                           saturation at 6 ("mxfp4 x mxfp4" MMA kind, same
+                           section). Both need expert_dtype LMOE_MXFP4 and
+                           act_dtype LMOE_BF16 and change the numerics. */
 } latent_moe_config;
 
 /* Layer weights (device pointers), read in place unless stated otherwise; the
@@ -175,7 +178,7 @@ int latent_moe_forward(latent_moe_t* h, const void* x, int64_t T, float* out, in
  *            (stable in (t, j) order within an expert)
  *   pair_row [T*k] int32: for pair (t, j) at index t*k+j, its row in the
  *            grouped order
- *   pooled   [T, P] act_dtype (F32 in MXFP8 mode): gamma_p * (Wp x_t), before
+ *   pooled   [T, P] act_dtype (F32 with MX expert inputs): gamma_p * (Wp x_t), before
  *            the row scale
  *   row_scale [T] F32: 1/sqrt(mean((Wp x_t)^2) + eps)
  *   act      [T*k, I] (F32 if expert_dtype is F32, else BF16): SwiGLU
@@ -197,10 +200,14 @@ typedef struct {
   const void* act;
   const float* expert_out;
   const void* combined;
-  const uint8_t* expert_in;        /* MXFP8 mode: u codes [T, P] E4M3, else NULL */
-  const uint8_t* expert_in_scales; /* MXFP8 mode: u scales [T, P/32] E8M0, else NULL */
-  const uint8_t* act_scales;       /* MXFP8 mode: act scales [T*k, I/32] E8M0 (act then
-                                      holds E4M3 codes [T*k, I]), else NULL */
+  const uint8_t* expert_in;        /* MX expert inputs: u codes, [T, P] E4M3 bytes
+                                      (MXFP8) or [T, P/2] packed E2M1 (MXFP4);
+                                      else NULL */
+  const uint8_t* expert_in_scales; /* MX expert inputs: u scales [T, P/32] E8M0,
+                                      else NULL */
+  const uint8_t* act_scales;       /* MX expert inputs: act scales [T*k, I/32] E8M0
+                                      (act then holds the codes, [T*k, I] E4M3 or
+                                      [T*k, I/2] packed E2M1), else NULL */
   const void* x_norm;   /* boundary norm output (input_norm only, else NULL): FP32 layers
                            [T, H] F32; BF16 layers its exact three-piece BF16 split
                            [T, 3H] (pieces p1 | p2 | p3 side by side, p1 + p2 + p3 =

@@ -175,8 +175,8 @@ class LatentMoE:
     weights: dict with router, router_bias (or None), pooler, pool_gamma,
     w_gate, w_up, w_down (MXFP4: (packed, scales) pairs), expert_gamma,
     unpooler, and input_gamma when input_norm (x is then the pre-norm
-    residual). expert_act="mxfp8" runs the expert GEMMs on MX FP8 activations
-    (MXFP4 experts only). The tensors are referenced by this object so they
+    residual). expert_act="mxfp8" or "mxfp4" runs the expert GEMMs on MX FP8 or
+    MX FP4 activations (MXFP4 experts only). The tensors are referenced by this object so they
     outlive the handle.
     """
 
@@ -236,9 +236,10 @@ class LatentMoE:
         torch.cuda.synchronize(self.device)
         v = latent_moe_debug_views(self.handle)
         k, E, P, I = self.top_k, self.experts, self.pooled, self.intermediate
-        f8 = self.expert_act == "mxfp8"
+        mxa = self.expert_act in ("mxfp8", "mxfp4")
+        cb = 2 if self.expert_act == "mxfp4" else 1  # elements per code byte
         act_np = np.float32 if self.act_dtype == "f32" else np.uint16
-        exp_np = np.float32 if self.expert_dtype == "f32" else (np.uint8 if f8 else np.uint16)
+        exp_np = np.float32 if self.expert_dtype == "f32" else (np.uint8 if mxa else np.uint16)
         spec = {
             "logits": (v.logits, (T, E), np.float32),
             "ids": (v.ids, (T, k), np.int32),
@@ -247,15 +248,15 @@ class LatentMoE:
             "offsets": (v.offsets, (E + 1,), np.int32),
             "perm_token": (v.perm_token, (T * k,), np.int32),
             "pair_row": (v.pair_row, (T * k,), np.int32),
-            "pooled": (v.pooled, (T, P), np.float32 if f8 else act_np),
+            "pooled": (v.pooled, (T, P), np.float32 if mxa else act_np),
             "row_scale": (v.row_scale, (T,), np.float32),
-            "act": (v.act, (T * k, I), exp_np),
+            "act": (v.act, (T * k, I // cb), exp_np),
             "expert_out": (v.expert_out, (T * k, P), np.float32),
             "combined": (v.combined, (T, P), np.float32) if self.act_dtype == "f32"
             else (v.combined, (T, 2 * P), np.uint16),
         }
-        if f8:  # MX FP8 codes and E8M0 scales, as stored
-            spec["expert_in"] = (v.expert_in, (T, P), np.uint8)
+        if mxa:  # MX codes (FP4: two per byte) and E8M0 scales, as stored
+            spec["expert_in"] = (v.expert_in, (T, P // cb), np.uint8)
             spec["expert_in_scales"] = (v.expert_in_scales, (T, P // 32), np.uint8)
             spec["act_scales"] = (v.act_scales, (T * k, I // 32), np.uint8)
         split_norm = bool(v.x_norm) and self.act_dtype != "f32"

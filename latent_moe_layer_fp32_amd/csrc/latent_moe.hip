@@ -169,10 +169,10 @@ int validate_config(const latent_moe_config* c) {
                 "BF16 layers need hidden, pooled and intermediate to be multiples of 512");
   if (c->input_norm != 0 && c->input_norm != 1)
     return fail(LMOE_ERR_INVALID_ARG, "input_norm must be 0 or 1");
-  if (c->expert_act != 0 && c->expert_act != LMOE_MXFP8)
-    return fail(LMOE_ERR_INVALID_ARG, "expert_act must be 0 or LMOE_MXFP8");
-  if (c->expert_act == LMOE_MXFP8 && (c->expert_dtype != LMOE_MXFP4 || c->act_dtype != LMOE_BF16))
-    return fail(LMOE_ERR_UNSUPPORTED, "MXFP8 expert activations need MXFP4 experts and BF16 activations");
+  if (c->expert_act != 0 && c->expert_act != LMOE_MXFP8 && c->expert_act != LMOE_MXFP4)
+    return fail(LMOE_ERR_INVALID_ARG, "expert_act must be 0, LMOE_MXFP8 or LMOE_MXFP4");
+  if (c->expert_act != 0 && (c->expert_dtype != LMOE_MXFP4 || c->act_dtype != LMOE_BF16))
+    return fail(LMOE_ERR_UNSUPPORTED, "MX expert activations need MXFP4 experts and BF16 activations");
   if ((size_t)c->pooled * c->intermediate * c->experts > ((size_t)1 << 40))
     return fail(LMOE_ERR_INVALID_ARG, "expert tensors too large");
   return LMOE_OK;
@@ -210,8 +210,9 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
   L.tile_off = take((size_t)(E + 1) * 4);
   L.perm_token = take((size_t)Mp * 4);
   L.pair_row = take((size_t)Mp * 4);
-  const bool f8 = c.expert_act == LMOE_MXFP8;
-  L.pooled = take((size_t)Tm * P * (f8 ? 4 : esize_act(c)));  // MXFP8: FP32 gamma_p * h
+  const bool mxa = c.expert_act != 0;
+  const size_t abits = c.expert_act == LMOE_MXFP8 ? 8 : 4;
+  L.pooled = take((size_t)Tm * P * (mxa ? 4 : esize_act(c)));  // MX acts: FP32 gamma_p * h
   L.pssq = take((size_t)Tm * parts * 4);
   L.row_scale = take((size_t)Tm * 4);
   L.act = take((size_t)Mp * I * esize_exp(c));
@@ -232,9 +233,9 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
     }
   }
   L.kpart = take(kp * 4);
-  L.uq = take(f8 ? (size_t)Tm * P : 0);          // MX FP8 u codes
-  L.us = take(f8 ? (size_t)Tm * P / 32 : 0);     // and E8M0 scales
-  L.acts = take(f8 ? (size_t)Mp * I / 32 : 0);   // E8M0 scales of the FP8 act codes (in act)
+  L.uq = take(mxa ? (size_t)Tm * P * abits / 8 : 0);  // MX u codes
+  L.us = take(mxa ? (size_t)Tm * P / 32 : 0);          // and E8M0 scales
+  L.acts = take(mxa ? (size_t)Mp * I / 32 : 0);        // E8M0 scales of the MX act codes (in act)
   L.xn = take(c.input_norm && c.act_dtype == LMOE_F32 ? (size_t)Tm * c.hidden * 4 : 0);
   L.xna = take(c.input_norm && c.act_dtype == LMOE_BF16 ? (size_t)Tm * 3 * c.hidden * 2 : 0);
   L.total = o;
@@ -258,16 +259,19 @@ hipError_t launch(const Prob& p, int64_t units, hipStream_t s) {
   } while (0)
 
 template <class Prob>
-hipError_t launch_f8(const Prob& p, int64_t units, hipStream_t s) {
+hipError_t launch_mxa(const Prob& p, int64_t units, hipStream_t s) {
   if (units <= 0) return hipSuccess;
   const int64_t g = (units + 7) / 8 * 8;
-  hipLaunchKernelGGL(lm_gemm_stream_f8_kernel<Prob>, dim3((unsigned)g), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(lm_gemm_stream_mxa_kernel<Prob>, dim3((unsigned)g), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
+// MX: MXFP4 expert weights; AB: expert GEMM inputs as MX FP8 (8) or MX FP4
+// (4) codes, or in the activation type (0).
 template <typename Et, template <typename> class CW, template <typename> class CR, bool MX = false,
-          bool F8 = false>
+          int AB = 0>
 int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_t s) {
+  constexpr bool MXA = AB != 0;
   const latent_moe_config& c = h->cfg;
   const latent_moe_weights& w = h->w;
   const Layout& L = h->lay;
@@ -407,7 +411,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     const int chunks = ceil_div(P, 256);
     hipLaunchKernelGGL(lm_pool_finish_kernel, dim3((unsigned)T, (unsigned)chunks), dim3(256), 0, s,
                        (const float*)(ws + L.kpart), psplits, (int)T, P, w.pool_gamma,
-                       (uint16_t*)pooled, pssq, F8 ? (float*)pooled : nullptr);
+                       (uint16_t*)pooled, pssq, MXA ? (float*)pooled : nullptr);
     LM_HIP(hipGetLastError());
     hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, pssq, chunks,
                        (int)T, P, c.eps, row_scale);
@@ -415,7 +419,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     }
   } else {
     PoolerProb<Cw> p;
-    if (F8) p.pooled32 = (float*)pooled;
+    if (MXA) p.pooled32 = (float*)pooled;
     p.x = xp;
     p.lda = xp_ld;
     p.w = (const Et*)Wpool;
@@ -433,9 +437,9 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
                        (int)T, P, c.eps, row_scale);
     LM_HIP(hipGetLastError());
   }
-  if constexpr (F8) {  // u = r * gamma_p * h quantised to MX FP8 for the expert GEMMs
+  if constexpr (MXA) {  // u = r * gamma_p * h MX-quantised for the expert GEMMs
     const int64_t nthr = T * (int64_t)(P / 32) * 8;
-    hipLaunchKernelGGL(lm_quant_u_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(lm_quant_u_kernel<AB>, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s,
                        (const float*)pooled, row_scale, (int)T, P, (uint8_t*)(ws + L.uq),
                        (uint8_t*)(ws + L.us));
     LM_HIP(hipGetLastError());
@@ -444,8 +448,8 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   if (fork) LM_HIP(hipStreamWaitEvent(s, h->join, 0));
   const int64_t max_tiles = ceil_div(npairs, Cw::BM) + (npairs < E ? npairs : E);
   // 5. gate/up + SwiGLU
-  if constexpr (F8) {
-    GateUpF8Prob<Cw> p;
+  if constexpr (MXA) {
+    GateUpMxaProb<Cw, AB> p;
     p.sg = h->pk_sgate;
     p.su = h->pk_sup;
     p.pooled = pooled;
@@ -460,12 +464,12 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.P = P;
     p.I = I;
     p.Ex = E;
-    p.nt = I / GateUpF8Prob<Cw>::kCols;
+    p.nt = I / GateUpMxaProb<Cw, AB>::kCols;
     p.uq = (const uint8_t*)(ws + L.uq);
     p.us = (const uint8_t*)(ws + L.us);
     p.aq = (uint8_t*)act;
     p.as = (uint8_t*)(ws + L.acts);
-    LM_HIP(launch_f8(p, max_tiles * p.nt, s));
+    LM_HIP(launch_mxa(p, max_tiles * p.nt, s));
   } else {
     GateUpProb<Cw, MX> p;
     if constexpr (MX) {
@@ -490,8 +494,8 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   LM_MARK(7);
   // 6. down + per-row sum of squares partials
   const int dnt = ceil_div(P, Cw::BN);
-  if constexpr (F8) {
-    DownF8Prob<Cw> p;
+  if constexpr (MXA) {
+    DownMxaProb<Cw, AB> p;
     p.sd = h->pk_sdown;
     p.act = act;
     p.wd = (const Et*)Wdown;
@@ -506,7 +510,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.nt = dnt;
     p.aq = (const uint8_t*)act;
     p.as = (const uint8_t*)(ws + L.acts);
-    LM_HIP(launch_f8(p, max_tiles * p.nt, s));
+    LM_HIP(launch_mxa(p, max_tiles * p.nt, s));
   } else {
     DownProb<Cw, MX> p;
     if constexpr (MX) p.sd = h->pk_sdown;
@@ -725,8 +729,11 @@ int latent_moe_forward(latent_moe_t* h, const void* x, int64_t T, float* out, in
     rc = nar ? forward_impl<float, CfgNarrow, CfgRouterNarrow>(h, x, T, out, s)
              : forward_impl<float, CfgWide, CfgRouterWide>(h, x, T, out, s);
   else if (h->cfg.expert_dtype == LMOE_MXFP4 && h->cfg.expert_act == LMOE_MXFP8)
-    rc = nar ? forward_impl<uint16_t, CfgNarrow, CfgRouterNarrow, true, true>(h, x, T, out, s)
-             : forward_impl<uint16_t, CfgWide, CfgRouterWide, true, true>(h, x, T, out, s);
+    rc = nar ? forward_impl<uint16_t, CfgNarrow, CfgRouterNarrow, true, 8>(h, x, T, out, s)
+             : forward_impl<uint16_t, CfgWide, CfgRouterWide, true, 8>(h, x, T, out, s);
+  else if (h->cfg.expert_dtype == LMOE_MXFP4 && h->cfg.expert_act == LMOE_MXFP4)
+    rc = nar ? forward_impl<uint16_t, CfgNarrow, CfgRouterNarrow, true, 4>(h, x, T, out, s)
+             : forward_impl<uint16_t, CfgWide, CfgRouterWide, true, 4>(h, x, T, out, s);
   else if (h->cfg.expert_dtype == LMOE_MXFP4)
     rc = nar ? forward_impl<uint16_t, CfgNarrow, CfgRouterNarrow, true>(h, x, T, out, s)
              : forward_impl<uint16_t, CfgWide, CfgRouterWide, true>(h, x, T, out, s);
@@ -763,10 +770,10 @@ int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v) {
   v->act = ws + L.act;
   v->expert_out = (const float*)(ws + L.O);
   v->combined = ws + L.y;
-  const bool f8 = h->cfg.expert_act == LMOE_MXFP8;
-  v->expert_in = f8 ? (const uint8_t*)(ws + L.uq) : nullptr;
-  v->expert_in_scales = f8 ? (const uint8_t*)(ws + L.us) : nullptr;
-  v->act_scales = f8 ? (const uint8_t*)(ws + L.acts) : nullptr;
+  const bool mxa = h->cfg.expert_act != 0;
+  v->expert_in = mxa ? (const uint8_t*)(ws + L.uq) : nullptr;
+  v->expert_in_scales = mxa ? (const uint8_t*)(ws + L.us) : nullptr;
+  v->act_scales = mxa ? (const uint8_t*)(ws + L.acts) : nullptr;
   v->x_norm = !h->cfg.input_norm ? nullptr
               : h->cfg.act_dtype == LMOE_F32 ? (const void*)(ws + L.xn) : (const void*)(ws + L.xna);
   return LMOE_OK;

@@ -1,9 +1,10 @@
-// MX FP8 activations for the expert GEMMs (gfx950 scaled matrix cores).
+// MX activations for the expert GEMMs (gfx950 scaled matrix cores).
 //
-// The "fp8 x fp4" MMA kind (web page "SGLang and Miles Add Day-0 Support for
-// Muse Spark Open", section "NVFP4 as a third MMA kind"): the expert GEMMs
-// read their activations as OCP MX FP8 (E4M3 elements, one E8M0 scale per 32
-// consecutive elements along the reduction axis) against MXFP4 weights, on
+// The "fp8 x fp4" and "mxfp4 x mxfp4" MMA kinds (web page "SGLang and Miles
+// Add Day-0 Support for Muse Spark Open", section "NVFP4 as a third MMA
+// kind"): the expert GEMMs read their activations as OCP MX FP8 (E4M3
+// elements) or MX FP4 (E2M1 elements, two per byte), one E8M0 scale per 32
+// consecutive elements along the reduction axis, against MXFP4 weights, on
 // v_mfma_scale_f32_32x32x64_f8f6f4. The pre-expert norm is applied by the
 // quantiser (section "Fuse normalization and remove routing conversions"):
 // u = r * (gamma_p * h) is formed in FP32 and quantised; a = silu(g) * v is
@@ -11,28 +12,45 @@
 //
 // Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 on gfx950 (measured with
 // one-hot probes): with K split into two 32-element blocks g = 0, 1,
-//   B (FP4, 16 bytes per lane): lane 32g + n holds column n, block g, element
-//     p in nibble p (low nibble first), and supplies that block's scale;
-//   A (FP8, 32 bytes per lane): lane 32h + m holds row m, bytes 16g .. 16g+15
+//   FP4 operand (B, or A with cbsz = 4; 16 bytes per lane): lane 32g + n
+//     holds row / column n, block g, element p in nibble p (low nibble
+//     first), and supplies that block's scale;
+//   FP8 A (32 bytes per lane): lane 32h + m holds row m, bytes 16g .. 16g+15
 //     = block g, elements 16h .. 16h+15; the scale of (row m, block g) comes
 //     from lane 32g + m whatever lane holds the data.
 // The scale operands are dwords; an immediate selects the byte.
 // The MXFP4 weight layout (lm_packed_mx_group) already gives each lane one
-// 32-element block per 64-wide k-tile; A is staged through LDS in 128-byte
-// row segments (128 FP8 = two MFMA steps), so lane half h reads the 16-byte
-// chunks 4s + h and 4s + 2 + h for step s.
+// 32-element block per 64-wide k-tile; A is staged through LDS in row
+// segments of one 128-element k-tile (two MFMA steps): 128 bytes of FP8, of
+// which lane half h reads the 16-byte chunks 4s + h and 4s + 2 + h for step s,
+// or 64 bytes of FP4, of which it reads chunk 2s + h. Either way lane half h
+// supplies the scale of block 2s + h: byte 2s + h of its row's scale dword.
 #pragma once
 #include "kernels.h"
 
-// ----------------------------------------------------------- MX FP8 codec
-// E8M0 exponent of a block: floor(log2(amax)) - 8 (E4M3's largest exponent),
-// clamped to [-127, 127]; an all-zero block takes -127.
-LM_DEV int lm_mx8_scale_exp(float amax) {
+// ------------------------------------------------------------- MX codecs
+// E8M0 exponent of a block: floor(log2(amax)) - emax (the element format's
+// largest exponent: 8 for E4M3, 2 for E2M1), clamped to [-127, 127]; an
+// all-zero block takes -127.
+template <int EMAX>
+LM_DEV int lm_mx_scale_exp(float amax) {
   if (!(amax > 0.0f)) return -127;
   int e;
   (void)frexpf(amax, &e);  // amax = m * 2^e, m in [0.5, 1)
-  const int s = e - 1 - 8;
+  const int s = e - 1 - EMAX;
   return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// E2M1 code (sign in bit 3) of q (already divided by the block scale): the
+// nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code, saturating
+// at 6. Each magnitude code is the count of midpoints below |q|; a midpoint
+// between an odd and an even code goes to the even one.
+LM_DEV uint32_t lm_e2m1_rne(float q) {
+  const float a = fabsf(q);
+  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return ((__float_as_uint(q) >> 28) & 0x8u) | m;
 }
 
 // E4M3 code of q (already divided by the block scale): nearest value, ties to
@@ -66,9 +84,11 @@ LM_DEV float lm_half_max(float v) {
   return v;
 }
 
-// u = r_t * u'_t (u' = gamma_p * Wp x, FP32 [T, P]) quantised to MX FP8:
-// codes [T, P] bytes, scales [T, P/32] E8M0 bytes. Eight threads per block of
-// 32, four elements each.
+// u = r_t * u'_t (u' = gamma_p * Wp x, FP32 [T, P]) quantised to MX FP8
+// (BITS = 8: codes [T, P] bytes) or MX FP4 (BITS = 4: codes [T, P/2] bytes,
+// element 2i in the low nibble), scales [T, P/32] E8M0 bytes. Eight threads
+// per block of 32, four elements each.
+template <int BITS>
 __global__ __launch_bounds__(256) void lm_quant_u_kernel(const float* pooled, const float* row_scale,
                                                          int T, int P, uint8_t* uq, uint8_t* us) {
   const int64_t nblk = (int64_t)T * (P / 32);
@@ -84,29 +104,34 @@ __global__ __launch_bounds__(256) void lm_quant_u_kernel(const float* pooled, co
   float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 #pragma unroll
   for (int o = 1; o < 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
-  const int se = lm_mx8_scale_exp(amax);
+  const int se = lm_mx_scale_exp<BITS == 8 ? 8 : 2>(amax);
   uint32_t w = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) w |= lm_e4m3_rne(ldexpf(v[q], -se)) << (8 * q);
+  for (int q = 0; q < 4; ++q) {
+    if constexpr (BITS == 8) w |= lm_e4m3_rne(ldexpf(v[q], -se)) << (8 * q);
+    else w |= lm_e2m1_rne(ldexpf(v[q], -se)) << (4 * q);
+  }
   if (live) {
-    *(uint32_t*)(uq + bb * 32 + sub * 4) = w;
+    if constexpr (BITS == 8) *(uint32_t*)(uq + bb * 32 + sub * 4) = w;
+    else *(uint16_t*)(uq + bb * 16 + sub * 2) = (uint16_t)w;
     if (sub == 0) us[bb] = (uint8_t)(se + 127);
   }
 }
 
 // ------------------------------------------------------------ GEMM problems
-// Gate/up on MX FP8 u (gathered rows) against MXFP4 weights; the epilogue
-// forms a = silu(g) * v in FP32 and writes it MX FP8 (codes [pairs, I],
-// scales [pairs, I/32]): the 32 columns of one block are the 32 lanes of a
+// Gate/up on MX u (gathered rows; BITS 8: E4M3 codes [T, P], 4: E2M1 codes
+// [T, P/2]) against MXFP4 weights; the epilogue forms a = silu(g) * v in FP32
+// and writes it in the same format (codes [pairs, I * BITS / 8], scales
+// [pairs, I/32]): the 32 columns of one block are the 32 lanes of a
 // half-wave, so the block maximum is a half-wave reduction.
-template <class Cfg_>
-struct GateUpF8Prob : GateUpProb<Cfg_, true> {
+template <class Cfg_, int BITS>
+struct GateUpMxaProb : GateUpProb<Cfg_, true> {
   using Base = GateUpProb<Cfg_, true>;
   using Cfg = Cfg_;
-  static constexpr bool kF8 = true;
-  const uint8_t* uq = nullptr;  // [T, P] E4M3
+  static constexpr int kBits = BITS;
+  const uint8_t* uq = nullptr;  // [T, P * BITS / 8]
   const uint8_t* us = nullptr;  // [T, P/32] E8M0
-  uint8_t* aq = nullptr;        // [pairs, I] E4M3
+  uint8_t* aq = nullptr;        // [pairs, I * BITS / 8]
   uint8_t* as = nullptr;        // [pairs, I/32] E8M0
 
   LM_DEV bool tile(int bid, LmTile& t) const {
@@ -116,9 +141,9 @@ struct GateUpF8Prob : GateUpProb<Cfg_, true> {
   }
   LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
     const int tok = this->perm_token[t.m0 + min(r, t.rows - 1)];
-    return (const lm_u32x4*)(uq + (size_t)tok * this->P);
+    return (const lm_u32x4*)(uq + (size_t)tok * this->P * BITS / 8);
   }
-  // scales sit at 1/32 of the data offset: row tok's at us + tok * P / 32
+  // a row's scales sit at 1 / (4 BITS) of its code offset from the bases
   LM_DEV const uint8_t* a_base() const { return uq; }
   LM_DEV const uint8_t* a_scale_base() const { return us; }
   LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
@@ -131,24 +156,29 @@ struct GateUpF8Prob : GateUpProb<Cfg_, true> {
       for (int i = 0; i < 16; ++i) {
         const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
         const float a = lm_silu(acc[tm][0][i]) * acc[tm][1][i];
-        const int se = lm_mx8_scale_exp(lm_half_max(fabsf(a)));
-        const uint32_t code = lm_e4m3_rne(ldexpf(a, -se));
-        if (row < t.rows) {
-          const size_t pr = (size_t)(t.m0 + row);
-          aq[pr * I + col] = (uint8_t)code;
-          if ((lane & 31) == 0) as[pr * (I / 32) + (col >> 5)] = (uint8_t)(se + 127);
+        const int se = lm_mx_scale_exp<BITS == 8 ? 8 : 2>(lm_half_max(fabsf(a)));
+        const size_t pr = (size_t)(t.m0 + row);
+        if constexpr (BITS == 8) {
+          const uint32_t code = lm_e4m3_rne(ldexpf(a, -se));
+          if (row < t.rows) aq[pr * I + col] = (uint8_t)code;
+        } else {
+          // columns 2c and 2c+1 (neighbouring lanes) share a byte
+          const uint32_t code = lm_e2m1_rne(ldexpf(a, -se));
+          const uint32_t hi = (uint32_t)__shfl_xor((int)code, 1, kWave);
+          if (row < t.rows && (lane & 1) == 0) aq[pr * (I / 2) + (col >> 1)] = (uint8_t)(code | (hi << 4));
         }
+        if (row < t.rows && (lane & 31) == 0) as[pr * (I / 32) + (col >> 5)] = (uint8_t)(se + 127);
       }
   }
 };
 
-// Down on MX FP8 act (grouped rows) against MXFP4 weights; epilogue as DownProb.
-template <class Cfg_>
-struct DownF8Prob : DownProb<Cfg_, true> {
+// Down on MX act (grouped rows) against MXFP4 weights; epilogue as DownProb.
+template <class Cfg_, int BITS>
+struct DownMxaProb : DownProb<Cfg_, true> {
   using Base = DownProb<Cfg_, true>;
   using Cfg = Cfg_;
-  static constexpr bool kF8 = true;
-  const uint8_t* aq = nullptr;  // [pairs, I] E4M3
+  static constexpr int kBits = BITS;
+  const uint8_t* aq = nullptr;  // [pairs, I * BITS / 8]
   const uint8_t* as = nullptr;  // [pairs, I/32] E8M0
 
   LM_DEV bool tile(int bid, LmTile& t) const {
@@ -157,18 +187,19 @@ struct DownF8Prob : DownProb<Cfg_, true> {
     return true;
   }
   LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
-    return (const lm_u32x4*)(aq + (size_t)(t.m0 + min(r, t.rows - 1)) * this->I);
+    return (const lm_u32x4*)(aq + (size_t)(t.m0 + min(r, t.rows - 1)) * this->I * BITS / 8);
   }
   LM_DEV const uint8_t* a_base() const { return aq; }
   LM_DEV const uint8_t* a_scale_base() const { return as; }
 };
 
 // ------------------------------------------------------------------ kernel
-// Streaming-B GEMM with MX FP8 A and MXFP4 B, four waves side by side along
-// N as in lm_gemm_stream_kernel. A k-tile is 128 elements: 128 bytes per A row
-// (LDS, double buffered, with each row's E8M0 scale dword of the k-tile next
-// to it) and two 64-wide MXFP4 k-tiles of B per wave group (1 KB each, loaded
-// straight into the MFMA registers); two scaled MFMA steps of K = 64.
+// Streaming-B GEMM with MX FP8 or FP4 A and MXFP4 B, four waves side by side
+// along N as in lm_gemm_stream_kernel. A k-tile is 128 elements: 128 (FP8) or
+// 64 (FP4) bytes per A row (LDS, double buffered, with each row's E8M0 scale
+// dword of the k-tile next to it) and two 64-wide MXFP4 k-tiles of B per wave
+// group (1 KB each, loaded straight into the MFMA registers); two scaled MFMA
+// steps of K = 64.
 // Iteration kt:
 //   step 0: MFMA(kt,0), each A fragment re-read for step 1 right after its
 //           MFMAs | global loads of B(kt+kDistB)
@@ -181,17 +212,21 @@ struct DownF8Prob : DownProb<Cfg_, true> {
 // slots and scale byte selectors are compile-time.
 template <class Prob>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LM_WAVES_MAX, LM_WAVES_MAX)))
-void lm_gemm_stream_f8_kernel(const Prob p) {
+void lm_gemm_stream_mxa_kernel(const Prob p) {
   using Cfg = typename Prob::Cfg;
   static_assert(Cfg::WM == 1 && Cfg::WN == 4, "streaming-B layout: four waves along N");
   constexpr int TM = Cfg::TM, TN = Cfg::TN, BM = Cfg::BM;
+  constexpr bool kA4 = Prob::kBits == 4;
+  constexpr int kCh = kA4 ? 4 : 8;     // 16-byte A chunks per row and k-tile
+  constexpr int kRows = 256 / kCh;     // A rows covered by one load pass
   // B one k-tile ahead (ring of two) for TM = 4; three ahead (ring of four)
   // for decode-sized tiles, whose time goes to streaming the weights.
   constexpr bool kLean = TM >= 4;
   constexpr int kRingB = kLean ? 2 : 4, kDistB = kLean ? 1 : 3;
-  constexpr int kStage = BM * 8;    // 16-byte chunks per A stage
-  constexpr int QA = BM * 8 / 256;  // A chunks per thread per k-tile
-  static_assert(QA >= 1, "at least 32 rows");
+  constexpr int kStage = BM * kCh;  // 16-byte chunks per A stage
+  // A chunks per thread per k-tile; with fewer rows than one pass covers
+  // (FP4, 32-row tiles) two threads load and store the same chunk
+  constexpr int QA = BM >= kRows ? BM / kRows : 1;
   __shared__ lm_u32x4 sa[2 * kStage];
   __shared__ uint32_t ssc[2 * BM];
 
@@ -200,13 +235,21 @@ void lm_gemm_stream_f8_kernel(const Prob p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, r = lane & 31;
-  const int lc = tid & 7, lr = tid >> 3;
+  const int lc = tid % kCh, lr = tid / kCh;
+  auto arow = [&](int q) { return (lr + kRows * q) % BM; };
+  // LDS row of kCh 16-byte chunks, chunk index XORed so that 16 consecutive
+  // rows read at one logical chunk (and the stores of one load pass) fall in
+  // 16 distinct 16-byte bank groups
+  auto swz = [](int row, int c) {
+    if constexpr (kA4) return row * 4 + (c ^ ((row >> 2) & 3));
+    else return lm_swz(row, c);
+  };
 
-  // A rows; a row's E8M0 scales sit at 1/32 of its data offset from the
-  // scale base (K bytes of codes, K/32 of scales per row)
+  // A rows; a row's E8M0 scales sit at 1 / (4 BITS) of its code offset from
+  // the scale base (K * BITS / 8 bytes of codes, K/32 of scales per row)
   const lm_u32x4* asrc[QA];
 #pragma unroll
-  for (int q = 0; q < QA; ++q) asrc[q] = p.a_row(t, lr + 32 * q);
+  for (int q = 0; q < QA; ++q) asrc[q] = p.a_row(t, arow(q));
   const uint8_t* const abase = p.a_base();
   const uint8_t* const asbase = p.a_scale_base();
   const lm_u32x4* bsrc[TN];
@@ -226,19 +269,19 @@ void lm_gemm_stream_f8_kernel(const Prob p) {
     const int ka = min(kt, klast);
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
-      ra[q] = asrc[q][ka * 8 + lc];
-      const size_t off = (size_t)((const uint8_t*)asrc[q] - abase) >> 5;
+      ra[q] = asrc[q][ka * kCh + lc];
+      const size_t off = (size_t)((const uint8_t*)asrc[q] - abase) >> (kA4 ? 4 : 5);
       rsa[q] = ((const uint32_t*)(asbase + off))[ka];
     }
   };
   auto store_a = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
-      sa[buf * kStage + lm_swz(lr + 32 * q, lc)] = ra[q];
-      // the eight threads of a row hold the same dword: an unconditional store
+      sa[buf * kStage + swz(arow(q), lc)] = ra[q];
+      // the threads of a row hold the same dword: an unconditional store
       // keeps the loop free of branches (which would let the compiler move
       // MFMAs across iterations)
-      ssc[buf * BM + lr + 32 * q] = rsa[q];
+      ssc[buf * BM + arow(q)] = rsa[q];
     }
   };
   auto load_b = [&](int slot, int kt) __attribute__((always_inline)) {
@@ -260,13 +303,20 @@ void lm_gemm_stream_f8_kernel(const Prob p) {
   // (s, i) run (ping-pong on i over the whole k-tile sequence); the A scale
   // dwords of the current and next k-tile.
   typedef __attribute__((ext_vector_type(8))) int v8i;
-  v8i fa[2];  // 32 bytes: block 0 elements 16h.., block 1 elements 16h..
+  // FP8: 32 bytes, block 0 elements 16h.., block 1 elements 16h..;
+  // FP4: 16 bytes, block h (upper half unused)
+  v8i fa[2];
   uint32_t asd[2][TM];
   auto read_frag = [&](int fb, int i, int buf, int s) __attribute__((always_inline)) {
     const lm_u32x4* st = sa + buf * kStage;
-    const lm_u32x4 c0 = st[lm_swz(i * 32 + r, 4 * s + h)];
-    const lm_u32x4 c1 = st[lm_swz(i * 32 + r, 4 * s + 2 + h)];
-    fa[fb] = __builtin_bit_cast(v8i, __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7));
+    if constexpr (kA4) {
+      const lm_u32x4 c = st[swz(i * 32 + r, 2 * s + h)];
+      fa[fb] = __builtin_bit_cast(v8i, __builtin_shufflevector(c, c, 0, 1, 2, 3, -1, -1, -1, -1));
+    } else {
+      const lm_u32x4 c0 = st[swz(i * 32 + r, 4 * s + h)];
+      const lm_u32x4 c1 = st[swz(i * 32 + r, 4 * s + 2 + h)];
+      fa[fb] = __builtin_bit_cast(v8i, __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
   };
   auto read_scales = [&](int sb, int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -286,7 +336,7 @@ void lm_gemm_stream_f8_kernel(const Prob p) {
     constexpr int opb = decltype(ob)::value;
     const lm_u32x4 b4 = rb[slot][j][s];
     const v8i bv = __builtin_bit_cast(v8i, __builtin_shufflevector(b4, b4, 0, 1, 2, 3, -1, -1, -1, -1));
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[fb], bv, acc[i][j], 0, 4, 2 * s,
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[fb], bv, acc[i][j], kA4 ? 4 : 0, 4, 2 * s,
                                                                 (int)asd[asl][i], opb,
                                                                 (int)rsb[sbsl][j]);
   };
@@ -323,8 +373,8 @@ void lm_gemm_stream_f8_kernel(const Prob p) {
         mma(std::integral_constant<int, 0>{}, std::integral_constant<int, ob0>{}, fb, i, j, slot, sbs, cur);
       if (i + 1 < TM) read_frag(fb ^ 1, i + 1, cur, 0);
       else read_frag(fb ^ 1, 0, cur, 1);
-      __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);            // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, kA4 ? 1 : 2, 0);   // DS read
       __builtin_amdgcn_sched_group_barrier(0x020, (TN * 2 + TM - 1) / TM, 0);  // VMEM read
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -345,7 +395,7 @@ void lm_gemm_stream_f8_kernel(const Prob p) {
       if (i + 1 < TM) read_frag(fb ^ 1, i + 1, cur, 1);
       else read_frag(fb ^ 1, 0, nxt, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kA4 ? 1 : 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     store_a(cur);

@@ -57,6 +57,33 @@ def _mxfp8(v):
     return out
 
 
+_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _mxfp4(v):
+    """MX FP4 (E2M1) quantisation of a list, blocks of 32: scale 2^(floor(log2
+    amax) - 2), each element the nearest of the eight E2M1 magnitudes (ties to
+    the even code), saturating at 6. Returns the dequantised list."""
+    out = []
+    for b0 in range(0, len(v), 32):
+        blk = v[b0:b0 + 32]
+        amax = max(abs(z) for z in blk)
+        if amax == 0.0:
+            out.extend(0.0 for _ in blk)
+            continue
+        m, ex = math.frexp(amax)
+        scale = 2.0 ** (ex - 1 - 2)
+        for z in blk:
+            q = min(abs(z) / scale, 6.0)
+            best, best_d = 0, None
+            for code, val in enumerate(_E2M1):
+                d = abs(val - q)
+                if best_d is None or d < best_d or (d == best_d and code % 2 == 0):
+                    best, best_d = code, d
+            out.append(math.copysign(_E2M1[best] * scale, z) if best else 0.0)
+    return out
+
+
 def _matvec(W, v):
     return [math.fsum(W[r][c] * v[c] for c in range(len(v))) for r in range(len(W))]
 
@@ -68,13 +95,14 @@ def _rmsnorm(v, gamma, eps):
 
 
 def forward(x, router, bias, pooler, pool_gamma, w_gate, w_up, w_down, expert_gamma,
-            unpooler, k, eps, input_gamma=None, bf16_acts=False, mxfp8_acts=False):
+            unpooler, k, eps, input_gamma=None, bf16_acts=False, mxfp8_acts=False,
+            mxfp4_acts=False):
     """Returns (out [T][H], ids [T][k], w [T][k]) as Python lists.
 
     input_gamma: x is the pre-norm residual; the router reads its RMSNorm
     (times input_gamma) rounded to FP32, the pooler the same value rounded
-    on to BF16 when bf16_acts, else the FP32 value. mxfp8_acts: the expert
-    GEMMs read u and a MX-quantised to FP8 E4M3."""
+    on to BF16 when bf16_acts, else the FP32 value. mxfp8_acts / mxfp4_acts:
+    the expert GEMMs read u and a MX-quantised to FP8 E4M3 / FP4 E2M1."""
     T, E = len(x), len(router)
     outs, all_ids, all_w = [], [], []
     for t in range(T):
@@ -104,6 +132,8 @@ def forward(x, router, bias, pooler, pool_gamma, w_gate, w_up, w_down, expert_ga
         u = _rmsnorm(_matvec(pooler, xt), pool_gamma, eps)
         if mxfp8_acts:
             u = _mxfp8(u)
+        if mxfp4_acts:
+            u = _mxfp4(u)
         P = len(u)
         y = [0.0] * P
         for j, e in enumerate(chosen):
@@ -112,6 +142,8 @@ def forward(x, router, bias, pooler, pool_gamma, w_gate, w_up, w_down, expert_ga
             a = [g[i] / (1.0 + math.exp(-g[i])) * v[i] for i in range(len(g))]
             if mxfp8_acts:
                 a = _mxfp8(a)
+            if mxfp4_acts:
+                a = _mxfp4(a)
             o = _matvec(w_down[e], a)
             oh = _rmsnorm(o, expert_gamma[e], eps)
             y = [y[p] + wt[j] * oh[p] for p in range(P)]

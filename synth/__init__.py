@@ -15,6 +15,7 @@ Workloads (one per layer configuration the method is exercised on):
 * ``mxfp4_decode`` ``decode`` with the same MXFP4 expert weights
 * ``mxfp8``, ``mxfp8_decode``: the MXFP4 layer with the expert GEMMs reading
   MX FP8 activations (quantised inside the layer; no extra input)
+* ``mxfp4act``, ``mxfp4act_decode``: the same with MX FP4 activations
 * ``decode_norm``, ``prefill_norm``: ``decode`` / ``prefill`` with x taken as the
   pre-norm residual (the layer applies its boundary norm, gamma ``input_gamma``)
 * ``skew``     5 chunks of 16384 tokens, BF16, with a Zipf(s=1.1) router bias
@@ -60,7 +61,7 @@ class LayerSpec:
     chunks: int = 1
     seed: int = 0
     input_norm: bool = False  # x is the pre-norm residual; the layer applies its boundary norm
-    expert_act: str | None = None  # None: BF16 activations into the experts; 'mxfp8': MX FP8
+    expert_act: str | None = None  # None: BF16 activations into the experts; 'mxfp8' / 'mxfp4': MX
 
     def with_(self, **kw) -> "LayerSpec":
         return replace(self, **kw)
@@ -75,6 +76,9 @@ CONFIGS = {
     "mxfp4_decode": LayerSpec("mxfp4_decode", T=64, expert_format="mxfp4", **_REAL),
     "mxfp8": LayerSpec("mxfp8", T=16384, expert_format="mxfp4", expert_act="mxfp8", **_REAL),
     "mxfp8_decode": LayerSpec("mxfp8_decode", T=64, expert_format="mxfp4", expert_act="mxfp8", **_REAL),
+    "mxfp4act": LayerSpec("mxfp4act", T=16384, expert_format="mxfp4", expert_act="mxfp4", **_REAL),
+    "mxfp4act_decode": LayerSpec("mxfp4act_decode", T=64, expert_format="mxfp4", expert_act="mxfp4",
+                                 **_REAL),
     "decode_norm": LayerSpec("decode_norm", T=64, input_norm=True, **_REAL),
     "prefill_norm": LayerSpec("prefill_norm", T=16384, input_norm=True, **_REAL),
     "skew": LayerSpec("skew", T=16384, router_bias="zipf", chunks=5, **_REAL),

@@ -61,6 +61,8 @@ def test_workspace_bytes_real_shapes():
     (dict(expert_act=5), B.LMOE_ERR_INVALID_ARG),
     (dict(expert_act="mxfp8"), B.LMOE_ERR_UNSUPPORTED),  # BF16 experts
     (dict(expert_act="mxfp8", expert_dtype="mxfp4", act_dtype="f32"), B.LMOE_ERR_UNSUPPORTED),
+    (dict(expert_act="mxfp4"), B.LMOE_ERR_UNSUPPORTED),  # BF16 experts
+    (dict(expert_act="mxfp4", expert_dtype="mxfp4", act_dtype="f32"), B.LMOE_ERR_UNSUPPORTED),
 ])
 def test_bad_configs_rejected(kw, code):
     with pytest.raises(B.LatentMoEError) as ei:
@@ -87,12 +89,15 @@ def test_create_rejects_null_and_misaligned_weights():
     assert L.latent_moe_create(None, ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
 
 
-def test_mxfp8_activations_accepted_with_mxfp4_experts():
+def test_mx_activations_accepted_with_mxfp4_experts():
     base = B.latent_moe_workspace_bytes(real_cfg(expert_dtype="mxfp4"))
     f8 = B.latent_moe_workspace_bytes(real_cfg(expert_dtype="mxfp4", expert_act="mxfp8"))
     T, P, I, k = 16384, 4096, 4096, 8
     # FP32 pooled rows instead of BF16, plus FP8 u codes and the E8M0 scales
     assert f8 >= base + T * P * 2 + T * P + T * P // 32 + T * k * I // 32
+    f4 = B.latent_moe_workspace_bytes(real_cfg(expert_dtype="mxfp4", expert_act="mxfp4"))
+    # FP4 u codes are half the size of FP8 ones
+    assert base + T * P * 2 + T * P // 2 + T * P // 32 + T * k * I // 32 <= f4 < f8
 
 
 def test_input_norm_needs_gamma_and_sizes_workspace():

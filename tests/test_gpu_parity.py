@@ -329,17 +329,19 @@ def test_mxfp4_prefill_parity(torch_dev, tables, mx, T):
     _sampled_parity(torch, spec, layer, host, x, xh, sample, TOL_MXFP4, f"mxfp4 prefill T={T}")
 
 
-# ------------------------------------ MX FP8 activations against MXFP4 weights
+# ------------------------------ MX FP8 / FP4 activations against MXFP4 weights
 
 
-def test_mxfp8_activations_real_shapes(torch_dev, tables, mx):
-    """The MXFP4 layer with the expert GEMMs on MX FP8 activations (scaled
-    matrix cores), against the oracle quantising u and a identically: every
-    token of the decode batch and sampled tokens of the 16384-token batch,
-    output max-abs <= 5e-2 x RMS."""
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_mx_activations_real_shapes(torch_dev, tables, mx, fmt):
+    """The MXFP4 layer with the expert GEMMs on MX FP8 or FP4 activations
+    (scaled matrix cores), against the oracle quantising u and a identically:
+    every token of the decode batch and sampled tokens of the 16384-token
+    batch, output max-abs <= 5e-2 x RMS."""
     torch = torch_dev
     spec, wts, _, _ = mx
-    for wl, T in (("mxfp8_decode", 64), ("mxfp8", 16384)):
+    pre = "mxfp8" if fmt == "mxfp8" else "mxfp4act"
+    for wl, T in ((pre + "_decode", 64), (pre, 16384)):
         s8 = synth.CONFIGS[wl]
         say(f"case: {wl}, T={T}")
         layer = make_layer(s8, wts, max_tokens=T)
@@ -351,7 +353,7 @@ def test_mxfp8_activations_real_shapes(torch_dev, tables, mx):
             near, _ = check_routing(ids, w, host.logits(xh), s8.k)
             sample = np.arange(T) if T <= 64 else np.sort(np.random.default_rng(8).choice(T, 4, replace=False))
             force = {i: ids[t] for i, t in enumerate(sample) if t in near}
-            r = host.oracle(xh[sample], act_quant="mxfp8", force_ids=force or None)
+            r = host.oracle(xh[sample], act_quant=fmt, force_ids=force or None)
             assert np.array_equal(ids[sample], r.ids)
             e = check_output(out[sample], r.out, 5e-2)
             say(f"{wl}: out max-abs {e:.3g} x RMS on {len(sample)} tokens")

@@ -97,25 +97,29 @@ def test_small_full_parity(torch_dev, tables, name, over, T):
         layer.close()
 
 
-# ------------------------------------------- MX FP8 activations (fp8 x fp4 MMA)
+# ------------------- MX FP8 / FP4 activations (fp8 x fp4, mxfp4 x mxfp4 MMA)
 
-F8_CASES = [("mxfp8 wide", 300), ("mxfp8 narrow", 37)]
+MXA_CASES = [("mxfp8 wide", "mxfp8", 300), ("mxfp8 narrow", "mxfp8", 37),
+             ("mxfp4 wide", "mxfp4", 300), ("mxfp4 narrow", "mxfp4", 37)]
 
 
-def _decode_mx8(codes, scales):
+def _decode_mx(codes, scales, fmt):
     from oracle import mx
 
+    if fmt == "mxfp4":
+        return mx.mxfp4_to_f64(codes, scales)
     v = mx.E4M3[codes.astype(np.int64)]
     s = mx.e8m0_to_f64(scales)
     K = codes.shape[-1]
     return (v.reshape(codes.shape[:-1] + (K // 32, 32)) * s[..., None]).reshape(codes.shape)
 
 
-@pytest.mark.parametrize("name,T", F8_CASES, ids=[c[0] for c in F8_CASES])
-def test_small_mxfp8_activations_parity(torch_dev, tables, name, T):
-    """Against the oracle with u and a MX-quantised to FP8 at the same points:
-    quantised u equal code for code except rare rounding-boundary flips (the
-    GPU forms u in FP32, the oracle in FP64), output max-abs <= 5e-2 x RMS."""
+@pytest.mark.parametrize("name,fmt,T", MXA_CASES, ids=[c[0] for c in MXA_CASES])
+def test_small_mx_activations_parity(torch_dev, tables, name, fmt, T):
+    """Against the oracle with u and a MX-quantised (FP8 or FP4) at the same
+    points: quantised u equal code for code except rare rounding-boundary flips
+    to a neighbouring code (the GPU forms u in FP32, the oracle in FP64),
+    output max-abs <= 5e-2 x RMS."""
     torch = torch_dev
     from latent_moe_layer_fp32_amd import LatentMoE
 
@@ -124,7 +128,7 @@ def test_small_mxfp8_activations_parity(torch_dev, tables, name, T):
     wts = device_weights(spec, tables)
     layer = LatentMoE(hidden=spec.H, pooled=spec.P, experts=spec.E, intermediate=spec.I, top_k=spec.k,
                       eps=spec.eps, act_dtype=spec.act_dtype, expert_dtype=spec.expert_format,
-                      max_tokens=512, weights=wts, expert_act="mxfp8")
+                      max_tokens=512, weights=wts, expert_act=fmt)
     try:
         x = synth.device_tensor(spec, "x", tables)
         ids_d = torch.empty((T, spec.k), dtype=torch.int32, device=x.device)
@@ -135,20 +139,27 @@ def test_small_mxfp8_activations_parity(torch_dev, tables, name, T):
         v = layer.views(T)
         host = HostLayer(spec)
         xh = host.x()
-        r0 = host.oracle(xh, keep_pairs=False, act_quant="mxfp8")
+        r0 = host.oracle(xh, keep_pairs=False, act_quant=fmt)
         near, _ = check_routing(ids, w, r0.logits, spec.k)
         force = {int(t): ids[t] for t in near}
-        r = host.oracle(xh, act_quant="mxfp8", force_ids=force or None)
+        r = host.oracle(xh, act_quant=fmt, force_ids=force or None)
         assert np.array_equal(ids, r.ids)
         # the quantised expert input: same codes but for rare boundary flips
-        uq = _decode_mx8(v["expert_in"], v["expert_in_scales"])
+        uq = _decode_mx(v["expert_in"], v["expert_in_scales"], fmt)
         diff = uq != r.u
         frac = diff.mean()
-        rel = np.abs(uq - r.u)[diff] / np.abs(r.u)[diff] if diff.any() else np.zeros(1)
-        assert frac < 1e-3 and rel.max() <= 0.14, f"u: {frac:.3g} of elements differ, max rel {rel.max():.3g}"
+        # a flip moves one element to a neighbouring code: at most 1/8 of its value for
+        # E4M3 (3 mantissa bits), at most one E2M1 step (<= 2 x the block scale) for FP4
+        step = np.abs(uq - r.u)[diff]
+        if fmt == "mxfp8":
+            bound = 0.14 * np.abs(r.u)[diff]
+        else:
+            blk = np.repeat(np.abs(r.u).reshape(T, -1, 32).max(-1), 32, axis=-1)
+            bound = 2.0 * 2.0 ** (np.floor(np.log2(np.maximum(blk, 1e-300))) - 2)[diff]
+        assert frac < 1e-3 and (step <= bound).all(), f"u: {frac:.3g} of elements differ"
         pr = v["pair_row"].reshape(T, spec.k)
-        aq = _decode_mx8(v["act"], v["act_scales"])[pr]
-        check_rel_l2(aq, r.a, 1e-2, "act (MX FP8)")
+        aq = _decode_mx(v["act"], v["act_scales"], fmt)[pr]
+        check_rel_l2(aq, r.a, 1e-2, f"act ({fmt})")
         check_rel_l2(v["expert_out"][pr], r.o, 1e-2, "expert out")
         e = check_output(out, r.out, 5e-2)
         say(f"{name}: u flips {frac:.2e}; out max-abs {e:.3g} x RMS over all {T} tokens")

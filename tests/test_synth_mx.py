@@ -203,3 +203,48 @@ def test_oracle_mxfp8_activations_match_brute_force():
     # the quantisation is visible, and of the size FP8 predicts (a few percent)
     rel = np.abs(r.out - plain.out).max() / np.sqrt(np.mean(plain.out ** 2))
     assert 1e-3 < rel < 0.2
+
+
+def test_mxfp4_quantiser_ties_saturation_and_scale():
+    # amax 7 -> scale 2^(floor(log2 7) - 2) = 1, so the block shows the element rule directly:
+    # midpoints 0.25, 1.25, 2.5, 5 go down to the even code, 0.75, 1.75, 3.5 up; 7 saturates to 6
+    blk = [7.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.75, 0.3, -6.5, 0.2]
+    q, e = mx.quantize_mx(np.array([blk + [0.0] * (32 - len(blk))]), "mxfp4")
+    assert e[0, 0] == 0
+    np.testing.assert_array_equal(q[0, :len(blk)],
+                                  [6.0, 0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, -1.0, 0.5, -6.0, 0.0])
+    # power-of-two equivariance and idempotence on random data
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((16, 64)) * np.exp(rng.uniform(-4, 4, (16, 1)))
+    q1, _ = mx.quantize_mx(v, "mxfp4")
+    q2, _ = mx.quantize_mx(v * 2.0 ** -7, "mxfp4")
+    np.testing.assert_array_equal(q2, q1 * 2.0 ** -7)
+    np.testing.assert_array_equal(mx.quantize_mx(q1, "mxfp4")[0], q1)
+
+
+def test_oracle_mxfp4_activations_match_brute_force():
+    from oracle import brute
+    from oracle import oracle as orc
+
+    rng = np.random.default_rng(22)
+    T, H, P, E, I, k = 3, 8, 32, 4, 32, 2
+
+    def nrm(*shape, fan=1):
+        return (rng.standard_normal(shape) / np.sqrt(fan)).astype(np.float32)
+
+    d = dict(x=nrm(T, H), router=nrm(E, H, fan=H), pooler=nrm(P, H, fan=H),
+             pool_gamma=(1 + 0.1 * rng.standard_normal(P)).astype(np.float32),
+             w_gate=nrm(E, I, P, fan=P), w_up=nrm(E, I, P, fan=P), w_down=nrm(E, P, I, fan=I),
+             expert_gamma=(1 + 0.1 * rng.standard_normal((E, P))).astype(np.float32),
+             unpooler=nrm(H, P, fan=P))
+    r = orc.forward_inputs(d, k, 1e-6, act_quant="mxfp4")
+    plain = orc.forward_inputs(d, k, 1e-6)
+    f = lambda a: np.asarray(a, np.float64).tolist()
+    out, ids, w = brute.forward(f(d["x"]), f(d["router"]), None, f(d["pooler"]), f(d["pool_gamma"]),
+                                f(d["w_gate"]), f(d["w_up"]), f(d["w_down"]), f(d["expert_gamma"]),
+                                f(d["unpooler"]), k, 1e-6, mxfp4_acts=True)
+    assert np.array_equal(r.ids, np.array(ids))
+    np.testing.assert_allclose(r.out, np.array(out), rtol=0, atol=1e-12)
+    # FP4 activations move the output by far more than FP8 ones (one mantissa bit)
+    rel = np.abs(r.out - plain.out).max() / np.sqrt(np.mean(plain.out ** 2))
+    assert 2e-2 < rel < 1.0
