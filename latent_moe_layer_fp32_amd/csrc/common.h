@@ -23,7 +23,9 @@ LM_DEV uint16_t lm_f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-LM_DEV float lm_silu(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g * sigma(g), with the hardware reciprocal (about one ulp) in
+// place of an IEEE division: the result is rounded to BF16 or an MX code.
+LM_DEV float lm_silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // Deterministic wave-wide sums (fixed butterfly order).
 LM_DEV float lm_wave_sum(float v) {

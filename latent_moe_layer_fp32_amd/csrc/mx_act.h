@@ -27,6 +27,12 @@
 // supplies the scale of block 2s + h: byte 2s + h of its row's scale dword.
 #pragma once
 #include "kernels.h"
+#ifndef LM_MXA_DEEPB_GU
+#define LM_MXA_DEEPB_GU 0
+#endif
+#ifndef LM_MXA_DEEPB_DN
+#define LM_MXA_DEEPB_DN 1
+#endif
 
 // ------------------------------------------------------------- MX codecs
 // E8M0 exponent of a block: floor(log2(amax)) - emax (the element format's
@@ -39,18 +45,6 @@ LM_DEV int lm_mx_scale_exp(float amax) {
   (void)frexpf(amax, &e);  // amax = m * 2^e, m in [0.5, 1)
   const int s = e - 1 - EMAX;
   return s < -127 ? -127 : (s > 127 ? 127 : s);
-}
-
-// E2M1 code (sign in bit 3) of q (already divided by the block scale): the
-// nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code, saturating
-// at 6. Each magnitude code is the count of midpoints below |q|; a midpoint
-// between an odd and an even code goes to the even one.
-LM_DEV uint32_t lm_e2m1_rne(float q) {
-  const float a = fabsf(q);
-  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                     (uint32_t)(a > 5.0f);
-  return ((__float_as_uint(q) >> 28) & 0x8u) | m;
 }
 
 // E4M3 code of q (already divided by the block scale): nearest value, ties to
@@ -77,11 +71,46 @@ LM_DEV uint32_t lm_e4m3_rne(float q) {
   return sgn | code;
 }
 
-// Max over the 32 lanes sharing bit 5 of the lane id.
+// E2M1 code (sign in bit 3) of q (already divided by the block scale): the
+// nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code, saturating
+// at 6. Below 1 the grid is the multiples of 0.5 (codes 0, 1, 2: nearest-even
+// rounding of 2|q|); from 1 up it is every FP32 value with one mantissa bit,
+// so the FP32 bits are rounded to one mantissa bit (nearest, ties to even:
+// add just under half a unit, plus the kept bit), clamped at 6.0, and the
+// code is the exponent (1 -> 1, 2 -> 2, 4 -> 3) and that bit. No compares:
+// a compare's mask feeding a select costs wait states on this chip.
+LM_DEV uint32_t lm_e2m1_rne(float q) {
+  const float a = fabsf(q);
+  const uint32_t lo = (uint32_t)rintf(a * 2.0f);
+  uint32_t b = __float_as_uint(a);
+  b = (b + 0x1FFFFFu + ((b >> 22) & 1u)) & ~0x3FFFFFu;
+  b = min(b, 0x40C00000u);
+  const uint32_t hi = (((b >> 23) - 126u) << 1) | ((b >> 22) & 1u);
+  return ((__float_as_uint(q) >> 28) & 0x8u) | (a < 1.0f ? lo : hi);
+}
+
+// v from the lane that a DPP control word names (quad_perm, row mirrors).
+template <int CTRL>
+LM_DEV float lm_dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// v from lane xor 16 within each group of 32 (ds_swizzle, bit mode: and
+// mask 0x1F, xor mask 0x10; no memory access).
+LM_DEV float lm_xor16(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+
+// Max over the 32 lanes sharing bit 5 of the lane id: lanes xor 1 and xor 2
+// (DPP quad_perm), then the mirrored partner in the group of 8 and of 16
+// (DPP row mirrors; each group already holds its maximum in every lane), then
+// lane xor 16.
 LM_DEV float lm_half_max(float v) {
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, lm_dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, lm_dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, lm_dpp<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, lm_dpp<0x140>(v));  // row_mirror
+  return fmaxf(v, lm_xor16(v));
 }
 
 // u = r_t * u'_t (u' = gamma_p * Wp x, FP32 [T, P]) quantised to MX FP8
@@ -129,6 +158,7 @@ struct GateUpMxaProb : GateUpProb<Cfg_, true> {
   using Base = GateUpProb<Cfg_, true>;
   using Cfg = Cfg_;
   static constexpr int kBits = BITS;
+  static constexpr bool kDeepB = LM_MXA_DEEPB_GU;
   const uint8_t* uq = nullptr;  // [T, P * BITS / 8]
   const uint8_t* us = nullptr;  // [T, P/32] E8M0
   uint8_t* aq = nullptr;        // [pairs, I * BITS / 8]
@@ -150,25 +180,56 @@ struct GateUpMxaProb : GateUpProb<Cfg_, true> {
                        int lane, void*) const {
     const int I = this->I;
     const int col = t.n0 + wn * 32 + (lane & 31);
+    // One row block (16 values per lane) at a time, each step applied to all
+    // 16 values before the next: the cross-lane moves of one value are then
+    // 16 instructions apart, with no wait states between them.
+    auto block = [&](int tm, bool full) __attribute__((always_inline)) {
+      float a[16], m[16];
 #pragma unroll
-    for (int tm = 0; tm < Cfg::TM; ++tm)
+      for (int i = 0; i < 16; ++i) {
+        a[i] = lm_silu(acc[tm][0][i]) * acc[tm][1][i];
+        m[i] = fabsf(a[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m[i] = fmaxf(m[i], lm_dpp<0xB1>(m[i]));   // quad_perm [1,0,3,2]
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m[i] = fmaxf(m[i], lm_dpp<0x4E>(m[i]));   // quad_perm [2,3,0,1]
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m[i] = fmaxf(m[i], lm_dpp<0x141>(m[i]));  // row_half_mirror
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m[i] = fmaxf(m[i], lm_dpp<0x140>(m[i]));  // row_mirror
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m[i] = fmaxf(m[i], lm_xor16(m[i]));      // lane xor 16
+      uint32_t code[16];
+      int se[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        se[i] = lm_mx_scale_exp<BITS == 8 ? 8 : 2>(m[i]);
+        code[i] = BITS == 8 ? lm_e4m3_rne(ldexpf(a[i], -se[i])) : lm_e2m1_rne(ldexpf(a[i], -se[i]));
+      }
+      if constexpr (BITS == 4) {  // columns 2c and 2c+1 (neighbouring lanes) share a byte
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          code[i] |= __builtin_bit_cast(uint32_t, lm_dpp<0xB1>(__builtin_bit_cast(float, code[i]))) << 4;
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
-        const float a = lm_silu(acc[tm][0][i]) * acc[tm][1][i];
-        const int se = lm_mx_scale_exp<BITS == 8 ? 8 : 2>(lm_half_max(fabsf(a)));
+        if (!full && row >= t.rows) continue;
         const size_t pr = (size_t)(t.m0 + row);
-        if constexpr (BITS == 8) {
-          const uint32_t code = lm_e4m3_rne(ldexpf(a, -se));
-          if (row < t.rows) aq[pr * I + col] = (uint8_t)code;
-        } else {
-          // columns 2c and 2c+1 (neighbouring lanes) share a byte
-          const uint32_t code = lm_e2m1_rne(ldexpf(a, -se));
-          const uint32_t hi = (uint32_t)__shfl_xor((int)code, 1, kWave);
-          if (row < t.rows && (lane & 1) == 0) aq[pr * (I / 2) + (col >> 1)] = (uint8_t)(code | (hi << 4));
-        }
-        if (row < t.rows && (lane & 31) == 0) as[pr * (I / 32) + (col >> 5)] = (uint8_t)(se + 127);
+        if constexpr (BITS == 8) aq[pr * I + col] = (uint8_t)code[i];
+        else if ((lane & 1) == 0) aq[pr * (I / 2) + (col >> 1)] = (uint8_t)code[i];
+        if ((lane & 31) == 0) as[pr * (I / 32) + (col >> 5)] = (uint8_t)(se[i] + 127);
       }
+    };
+    // full tiles store without a row test
+    if (t.rows == Cfg::BM) {
+#pragma unroll
+      for (int tm = 0; tm < Cfg::TM; ++tm) block(tm, true);
+    } else {
+#pragma unroll
+      for (int tm = 0; tm < Cfg::TM; ++tm) block(tm, false);
+    }
   }
 };
 
@@ -178,6 +239,7 @@ struct DownMxaProb : DownProb<Cfg_, true> {
   using Base = DownProb<Cfg_, true>;
   using Cfg = Cfg_;
   static constexpr int kBits = BITS;
+  static constexpr bool kDeepB = LM_MXA_DEEPB_DN;
   const uint8_t* aq = nullptr;  // [pairs, I * BITS / 8]
   const uint8_t* as = nullptr;  // [pairs, I/32] E8M0
 
@@ -221,8 +283,12 @@ void lm_gemm_stream_mxa_kernel(const Prob p) {
   constexpr int kRows = 256 / kCh;     // A rows covered by one load pass
   // B one k-tile ahead (ring of two) for TM = 4; three ahead (ring of four)
   // for decode-sized tiles, whose time goes to streaming the weights.
-  constexpr bool kLean = TM >= 4;
+  // With FP4 A a k-tile holds half the matrix work of an FP8 one, too little
+  // to cover a load's latency in one iteration: B then runs three k-tiles
+  // ahead and A two iterations ahead of its LDS store (a ring of two slots).
+  constexpr bool kLean = TM >= 4 && !(kA4 && Prob::kDeepB);
   constexpr int kRingB = kLean ? 2 : 4, kDistB = kLean ? 1 : 3;
+  constexpr int kRingA = 1;
   constexpr int kStage = BM * kCh;  // 16-byte chunks per A stage
   // A chunks per thread per k-tile; with fewer rows than one pass covers
   // (FP4, 32-row tiles) two threads load and store the same chunk
@@ -261,27 +327,27 @@ void lm_gemm_stream_mxa_kernel(const Prob p) {
   }
 
   const int kt0 = t.kt0, kt1 = t.kt1, klast = kt1 - 1;
-  lm_u32x4 ra[QA];
-  uint32_t rsa[QA];
+  lm_u32x4 ra[kRingA][QA];
+  uint32_t rsa[kRingA][QA];
   lm_u32x4 rb[kRingB][TN][2];
   uint32_t rsb[2][TN];
-  auto load_a = [&](int kt) __attribute__((always_inline)) {
+  auto load_a = [&](int aslot, int kt) __attribute__((always_inline)) {
     const int ka = min(kt, klast);
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
-      ra[q] = asrc[q][ka * kCh + lc];
+      ra[aslot][q] = asrc[q][ka * kCh + lc];
       const size_t off = (size_t)((const uint8_t*)asrc[q] - abase) >> (kA4 ? 4 : 5);
-      rsa[q] = ((const uint32_t*)(asbase + off))[ka];
+      rsa[aslot][q] = ((const uint32_t*)(asbase + off))[ka];
     }
   };
-  auto store_a = [&](int buf) __attribute__((always_inline)) {
+  auto store_a = [&](int aslot, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
-      sa[buf * kStage + swz(arow(q), lc)] = ra[q];
+      sa[buf * kStage + swz(arow(q), lc)] = ra[aslot][q];
       // the threads of a row hold the same dword: an unconditional store
       // keeps the loop free of branches (which would let the compiler move
       // MFMAs across iterations)
-      ssc[buf * BM + arow(q)] = rsa[q];
+      ssc[buf * BM + arow(q)] = rsa[aslot][q];
     }
   };
   auto load_b = [&](int slot, int kt) __attribute__((always_inline)) {
@@ -318,6 +384,15 @@ void lm_gemm_stream_mxa_kernel(const Prob p) {
       fa[fb] = __builtin_bit_cast(v8i, __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
+  // FP4 A: the TM fragments of a whole step are read one step ahead (an FP4
+  // step's MFMAs take half the time of an FP8 one, too short to cover an LDS
+  // read issued one fragment ahead): f4[step parity][i].
+  lm_u32x4 f4[kA4 ? 2 : 1][TM];
+  auto read_step4 = [&](int fs, int buf, int s) __attribute__((always_inline)) {
+    const lm_u32x4* st = sa + buf * kStage;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) f4[fs][i] = st[swz(i * 32 + r, 2 * s + h)];
+  };
   auto read_scales = [&](int sb, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) asd[sb][i] = ssc[buf * BM + i * 32 + r] >> (8 * h);
@@ -336,24 +411,31 @@ void lm_gemm_stream_mxa_kernel(const Prob p) {
     constexpr int opb = decltype(ob)::value;
     const lm_u32x4 b4 = rb[slot][j][s];
     const v8i bv = __builtin_bit_cast(v8i, __builtin_shufflevector(b4, b4, 0, 1, 2, 3, -1, -1, -1, -1));
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[fb], bv, acc[i][j], kA4 ? 4 : 0, 4, 2 * s,
+    v8i av;
+    if constexpr (kA4)
+      av = __builtin_bit_cast(v8i, __builtin_shufflevector(f4[fb][i], f4[fb][i], 0, 1, 2, 3, -1, -1, -1, -1));
+    else
+      av = fa[fb];
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], kA4 ? 4 : 0, 4, 2 * s,
                                                                 (int)asd[asl][i], opb,
                                                                 (int)rsb[sbsl][j]);
   };
 
   // Prologue: A(kt0), A(kt0+1) in the two stages, B in flight, fragments and
   // scales of (kt0, 0) in registers.
-  load_a(kt0);
+  load_a(0, kt0);
 #pragma unroll
   for (int d = 0; d < kDistB; ++d) load_b(d, kt0 + d);
   load_bs(0, kt0);
   if (kDistB >= 2) load_bs(1, kt0 + 2);
-  store_a(0);
-  load_a(kt0 + 1);
-  store_a(1);
-  load_a(kt0 + 2);
+  store_a(0, 0);
+  load_a(0, kt0 + 1);
+  store_a(0, 1);
+  load_a(0, kt0 + 2);
+  if constexpr (kRingA == 2) load_a(1, kt0 + 3);
   __syncthreads();
-  read_frag(0, 0, 0, 0);
+  if constexpr (kA4) read_step4(0, 0, 0);
+  else read_frag(0, 0, 0, 0);
   read_scales(0, 0);
 
   // Fragment (s, i) of k-tile kt sits in fa[(2 * TM * kt + s * TM + i) & 1];
@@ -364,6 +446,34 @@ void lm_gemm_stream_mxa_kernel(const Prob p) {
     constexpr int sbs = (q >> 1) & 1;        // B scale slot of this k-tile
     constexpr int ob0 = 2 * (q & 1), ob1 = ob0 + 1;  // B scale bytes of steps 0, 1
     load_b((q + kDistB) % kRingB, kt + kDistB);
+    if constexpr (kA4) {
+      // step 0: MFMAs of step 0 (f4[0]) while step 1 is read from this stage
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          mma(std::integral_constant<int, 0>{}, std::integral_constant<int, ob0>{}, 0, i, j, slot, sbs, cur);
+        f4[1][i] = sa[cur * kStage + swz(i * 32 + r, 2 + h)];
+        __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x020, (TN * 2 + TM - 1) / TM, 0);  // VMEM read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // barrier: every wave has read this stage (it is overwritten below) and
+      // the next stage, stored in the previous iteration, is visible
+      __syncthreads();
+      read_scales(nxt, nxt);
+      // step 1: MFMAs of step 1 (f4[1]) while step 0 of kt+1 is read
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          mma(std::integral_constant<int, 1>{}, std::integral_constant<int, ob1>{}, 1, i, j, slot, sbs, cur);
+        f4[0][i] = sa[nxt * kStage + swz(i * 32 + r, h)];
+        __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    } else {
     // step 0: MFMAs of (0, i) while (0, i+1), then (1, 0), are read
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -397,9 +507,12 @@ void lm_gemm_stream_mxa_kernel(const Prob p) {
       __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, kA4 ? 1 : 2, 0);
     }
+    }
     __builtin_amdgcn_sched_barrier(0);
-    store_a(cur);
-    load_a(kt + 3);
+    // A(kt+2) (slot cur with a ring of two) into the stage just consumed; the
+    // next load into that slot is A(kt + 2 + kRingA)
+    store_a(kRingA == 2 ? cur : 0, cur);
+    load_a(kRingA == 2 ? cur : 0, kt + 2 + kRingA);
     // B scales of the pair starting at k-tile kt+kDistB; its slot's previous
     // pair (k-tiles up to kt) is done with
     if constexpr (((q + kDistB) & 1) == 0) load_bs(((q + kDistB) >> 1) & 1, kt + kDistB);

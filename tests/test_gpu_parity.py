@@ -259,6 +259,19 @@ def test_decode_parity(torch_dev, tables, real):
     _sampled_parity(torch, dspec, layer, host, x, xh, np.arange(dspec.T), TOL_BF16, "decode")
 
 
+def test_single_token_parity(torch_dev, tables, real, mx):
+    """T = 1 at real shapes: split-K projections over one row, eight experts of
+    one row each (every expert tile ragged), BF16 and MXFP4 experts."""
+    torch = torch_dev
+    for fx, wl, tol in ((real, "decode", TOL_BF16), (mx, "mxfp4_decode", TOL_MXFP4)):
+        spec, _, layer, host = fx
+        dspec = synth.CONFIGS[wl]
+        say(f"case: {wl}, T=1")
+        x = synth.device_tensor(dspec, "x", tables)[5:6].contiguous()
+        xh = synth.host(dspec, "x")[5:6]
+        _sampled_parity(torch, dspec, layer, host, x, xh, np.arange(1), tol, f"{wl} T=1")
+
+
 @pytest.mark.parametrize("T", [16384, 4097, 1000])
 def test_prefill_parity(torch_dev, tables, real, T):
     torch = torch_dev
