@@ -33,9 +33,35 @@ LM_DEV float lm_wave_sum(float v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
-// Sum over the 32 lanes sharing bit 5 of the lane id (lanes 0-31 / 32-63).
-LM_DEV float lm_half_sum(float v) {
+// v from the lane that a DPP control word names (quad_perm, row mirrors).
+template <int CTRL>
+LM_DEV float lm_dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// v from lane xor 16 within each group of 32 (ds_swizzle, bit mode: and
+// mask 0x1F, xor mask 0x10; no memory access).
+LM_DEV float lm_xor16(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+
+// Reduction over the 32 lanes sharing bit 5 of the lane id of N values per
+// lane at once, each step applied to all N before the next (so a value's
+// cross-lane moves are N instructions apart, with no wait states): lanes
+// xor 1 and xor 2 (DPP quad_perm), then the mirrored partner in the group of
+// 8 and of 16 (DPP row mirrors; each group already holds its result in every
+// lane), then lane xor 16. Every lane ends with the same result: each step
+// combines a lane with one partner, and max and + commute.
+template <int N, class Op>
+LM_DEV void lm_half_reduce(float (&v)[N], Op op) {
 #pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  for (int i = 0; i < N; ++i) v[i] = op(v[i], lm_dpp<0xB1>(v[i]));   // quad_perm [1,0,3,2]
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = op(v[i], lm_dpp<0x4E>(v[i]));   // quad_perm [2,3,0,1]
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = op(v[i], lm_dpp<0x141>(v[i]));  // row_half_mirror
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = op(v[i], lm_dpp<0x140>(v[i]));  // row_mirror
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = op(v[i], lm_xor16(v[i]));       // lane xor 16
 }

@@ -252,18 +252,21 @@ LM_DEV void lm_tile_row_ssq(const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, in
                             int ncols_valid, float* red, F value) {
 #pragma unroll
   for (int tm = 0; tm < Cfg::TM; ++tm) {
+    float s[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float s = 0.0f;
+      s[i] = 0.0f;
 #pragma unroll
       for (int tn = 0; tn < Cfg::TN; ++tn) {
         const int col = lm_acc_col<Cfg>(wn, tn, lane);
         const float v = value(acc[tm][tn][i], tn, col);
-        s += col < ncols_valid ? v * v : 0.0f;
+        s[i] += col < ncols_valid ? v * v : 0.0f;
       }
-      s = lm_half_sum(s);
-      if ((lane & 31) == 0) red[wn * Cfg::BM + lm_acc_row<Cfg>(wm, tm, i, lane)] = s;
     }
+    lm_half_reduce(s, [](float x, float y) { return x + y; });
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((lane & 31) == 0) red[wn * Cfg::BM + lm_acc_row<Cfg>(wm, tm, i, lane)] = s[i];
   }
   __syncthreads();
   if (threadIdx.x < Cfg::BM) {

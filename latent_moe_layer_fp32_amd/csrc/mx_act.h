@@ -89,28 +89,11 @@ LM_DEV uint32_t lm_e2m1_rne(float q) {
   return ((__float_as_uint(q) >> 28) & 0x8u) | (a < 1.0f ? lo : hi);
 }
 
-// v from the lane that a DPP control word names (quad_perm, row mirrors).
-template <int CTRL>
-LM_DEV float lm_dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-
-// v from lane xor 16 within each group of 32 (ds_swizzle, bit mode: and
-// mask 0x1F, xor mask 0x10; no memory access).
-LM_DEV float lm_xor16(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
-}
-
-// Max over the 32 lanes sharing bit 5 of the lane id: lanes xor 1 and xor 2
-// (DPP quad_perm), then the mirrored partner in the group of 8 and of 16
-// (DPP row mirrors; each group already holds its maximum in every lane), then
-// lane xor 16.
+// Max over the 32 lanes sharing bit 5 of the lane id.
 LM_DEV float lm_half_max(float v) {
-  v = fmaxf(v, lm_dpp<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = fmaxf(v, lm_dpp<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = fmaxf(v, lm_dpp<0x141>(v));  // row_half_mirror
-  v = fmaxf(v, lm_dpp<0x140>(v));  // row_mirror
-  return fmaxf(v, lm_xor16(v));
+  float a[1] = {v};
+  lm_half_reduce(a, [](float x, float y) { return fmaxf(x, y); });
+  return a[0];
 }
 
 // u = r_t * u'_t (u' = gamma_p * Wp x, FP32 [T, P]) quantised to MX FP8
@@ -181,8 +164,7 @@ struct GateUpMxaProb : GateUpProb<Cfg_, true> {
     const int I = this->I;
     const int col = t.n0 + wn * 32 + (lane & 31);
     // One row block (16 values per lane) at a time, each step applied to all
-    // 16 values before the next: the cross-lane moves of one value are then
-    // 16 instructions apart, with no wait states between them.
+    // 16 values before the next.
     auto block = [&](int tm, bool full) __attribute__((always_inline)) {
       float a[16], m[16];
 #pragma unroll
@@ -190,16 +172,7 @@ struct GateUpMxaProb : GateUpProb<Cfg_, true> {
         a[i] = lm_silu(acc[tm][0][i]) * acc[tm][1][i];
         m[i] = fabsf(a[i]);
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m[i] = fmaxf(m[i], lm_dpp<0xB1>(m[i]));   // quad_perm [1,0,3,2]
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m[i] = fmaxf(m[i], lm_dpp<0x4E>(m[i]));   // quad_perm [2,3,0,1]
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m[i] = fmaxf(m[i], lm_dpp<0x141>(m[i]));  // row_half_mirror
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m[i] = fmaxf(m[i], lm_dpp<0x140>(m[i]));  // row_mirror
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m[i] = fmaxf(m[i], lm_xor16(m[i]));      // lane xor 16
+      lm_half_reduce(m, [](float x, float y) { return fmaxf(x, y); });
       uint32_t code[16];
       int se[16];
 #pragma unroll
