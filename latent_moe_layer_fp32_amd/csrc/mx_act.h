@@ -27,12 +27,6 @@
 // supplies the scale of block 2s + h: byte 2s + h of its row's scale dword.
 #pragma once
 #include "kernels.h"
-#ifndef LM_MXA_DEEPB_GU
-#define LM_MXA_DEEPB_GU 0
-#endif
-#ifndef LM_MXA_DEEPB_DN
-#define LM_MXA_DEEPB_DN 1
-#endif
 
 // ------------------------------------------------------------- MX codecs
 // E8M0 exponent of a block: floor(log2(amax)) - emax (the element format's
@@ -141,7 +135,9 @@ struct GateUpMxaProb : GateUpProb<Cfg_, true> {
   using Base = GateUpProb<Cfg_, true>;
   using Cfg = Cfg_;
   static constexpr int kBits = BITS;
-  static constexpr bool kDeepB = LM_MXA_DEEPB_GU;
+  // FP4 A, 128-row tiles: B one k-tile ahead (the step-ahead A fragments
+  // leave no registers for more); see lm_gemm_stream_mxa_kernel
+  static constexpr bool kDeepB = false;
   const uint8_t* uq = nullptr;  // [T, P * BITS / 8]
   const uint8_t* us = nullptr;  // [T, P/32] E8M0
   uint8_t* aq = nullptr;        // [pairs, I * BITS / 8]
@@ -212,7 +208,8 @@ struct DownMxaProb : DownProb<Cfg_, true> {
   using Base = DownProb<Cfg_, true>;
   using Cfg = Cfg_;
   static constexpr int kBits = BITS;
-  static constexpr bool kDeepB = LM_MXA_DEEPB_DN;
+  // FP4 A, 128-row tiles: B three k-tiles ahead (measured 10% faster)
+  static constexpr bool kDeepB = true;
   const uint8_t* aq = nullptr;  // [pairs, I * BITS / 8]
   const uint8_t* as = nullptr;  // [pairs, I/32] E8M0
 

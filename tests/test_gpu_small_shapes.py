@@ -75,6 +75,8 @@ def test_small_full_parity(torch_dev, tables, name, over, T):
         torch.cuda.synchronize()
         out, ids, w = out.cpu().numpy(), ids_d.cpu().numpy(), w_d.cpu().numpy()
         v = layer.views(T)
+        # run to run, bit for bit (fixed reduction orders, no atomics)
+        assert np.array_equal(layer.forward(x).cpu().numpy(), out), "second forward differs"
         host = HostLayer(spec)
         xh = host.x()
         r0 = host.oracle(xh, input_gamma=gin, keep_pairs=False)
@@ -137,6 +139,7 @@ def test_small_mx_activations_parity(torch_dev, tables, name, fmt, T):
         torch.cuda.synchronize()
         out, ids, w = out.cpu().numpy(), ids_d.cpu().numpy(), w_d.cpu().numpy()
         v = layer.views(T)
+        assert np.array_equal(layer.forward(x).cpu().numpy(), out), "second forward differs"
         host = HostLayer(spec)
         xh = host.x()
         r0 = host.oracle(xh, keep_pairs=False, act_quant=fmt)
