@@ -73,6 +73,7 @@ class OracleResult:
     y: np.ndarray  # [T, P] combined
     near_tie: np.ndarray  # [T] bool: some gap j <= k below NEAR_TIE
     xn: np.ndarray | None = None  # [T, H] FP32 boundary-norm output (input gamma given)
+    u_pre: np.ndarray | None = None  # [T, P] MX activations: u before its quantisation
 
 
 def rms_norm(v: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
@@ -140,7 +141,7 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
             unpooler, k: int, eps: float, *, force_ids: dict | None = None,
             order: str = "norm_then_sum", keep_pairs: bool = True,
             round_bf16: Sequence[str] = (), input_gamma=None,
-            act_quant: str | None = None) -> OracleResult:
+            act_quant: str | None = None, force_u: dict | None = None) -> OracleResult:
     """Layer forward on tokens x [T, H] (any stored dtype).
 
     force_ids: {token: ids sequence} replaces the selection for those tokens
@@ -151,7 +152,12 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
       intermediate to BF16 (nearest even) the way a BF16 datapath would.
     input_gamma: [H] gamma of the boundary norm (step 0); x is then the
       pre-norm residual.
-    act_quant: None, or "mxfp8": the expert GEMMs read u and a MX-quantised.
+    act_quant: None, "mxfp8" or "mxfp4": the expert GEMMs read u and a
+      MX-quantised.
+    force_u: {token: quantised u row} replaces the quantised u of those tokens
+      (an element whose value sits on the midpoint between two codes may be
+      rounded either way by a kernel that forms it in lower precision; the
+      caller checks that the rows differ from this oracle's only there).
     """
     act_bf16 = np.asarray(x).dtype == np.uint16
     x = to_f64(x)
@@ -184,8 +190,14 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
     u = rms_norm(h, gp, eps)
     if "u" in round_bf16:
         u = _bf16_round(u)
+    u_pre = None
     if act_quant:
+        u_pre = u
         u = quantize_mx(u, act_quant)[0]
+        if force_u:
+            u = u.copy()
+            for t, row in force_u.items():
+                u[t] = row
 
     I = None
     ohat = np.zeros((T, k, P))
@@ -223,7 +235,8 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
         y = _bf16_round(y)
     out = y @ Wun.T
     return OracleResult(out=out, ids=ids, w=w, logits=logits, gaps=gaps, h=h, u=u, a=a_all,
-                        o=o_all, ohat=ohat if keep_pairs else None, y=y, near_tie=near, xn=xn)
+                        o=o_all, ohat=ohat if keep_pairs else None, y=y, near_tie=near, xn=xn,
+                        u_pre=u_pre)
 
 
 def _bf16_round(v: np.ndarray) -> np.ndarray:

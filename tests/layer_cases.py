@@ -102,3 +102,26 @@ def check_rel_l2(gpu: np.ndarray, ref: np.ndarray, c: float, what: str):
 
 def bf16_to_f64(a):
     return to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def mx_rounding_ties(uq_gpu: np.ndarray, r, fmt: str, rel: float = 1e-4) -> dict:
+    """MX-quantised u from the kernel against the oracle's: where they differ,
+    check that the oracle's unquantised value lies on the midpoint between the
+    two codes (within rel of the block scale: the kernel forms u in FP32, the
+    oracle in FP64, so exactly there either rounding is right), or that the
+    block maximum lies on a power of two (the scale itself a tie). Returns
+    {token: kernel row} to pass to the oracle as force_u."""
+    from oracle import mx
+
+    diff = uq_gpu != r.u
+    if not diff.any():
+        return {}
+    _, e = mx.quantize_mx(r.u_pre, fmt)
+    X = np.repeat(np.ldexp(1.0, e.astype(np.int64)), 32, axis=-1)
+    amax = np.repeat(np.abs(r.u_pre).reshape(r.u_pre.shape[0], -1, 32).max(-1), 32, axis=-1)
+    scale_tie = np.abs(np.log2(amax) - np.round(np.log2(amax))) <= rel
+    q, g, o = r.u_pre / X, uq_gpu / X, r.u / X
+    code_tie = np.abs(q - 0.5 * (g + o)) <= rel * np.maximum(np.abs(q), 1.0)
+    bad = diff & ~(code_tie | scale_tie)
+    assert not bad.any(), f"u differs from the oracle away from a rounding tie at {np.argwhere(bad)[:5]}"
+    return {int(t): uq_gpu[t] for t in np.unique(np.nonzero(diff)[0])}

@@ -21,7 +21,8 @@ import pytest
 
 import synth
 from layer_cases import (HostLayer, bf16_to_f64, check_output, check_rel_l2, check_routing,
-                         device_weights, make_layer)
+                         device_weights, make_layer, mx_rounding_ties)
+from oracle import mx as mx_mod
 from oracle import oracle as orc
 
 pytestmark = pytest.mark.gpu
@@ -368,6 +369,14 @@ def test_mx_activations_real_shapes(torch_dev, tables, mx, fmt):
             force = {i: ids[t] for i, t in enumerate(sample) if t in near}
             r = host.oracle(xh[sample], act_quant=fmt, force_ids=force or None)
             assert np.array_equal(ids[sample], r.ids)
+            v = layer.views(T, names=("expert_in", "expert_in_scales"))
+            uq = (mx_mod.mxfp4_to_f64(v["expert_in"][sample], v["expert_in_scales"][sample]) if fmt == "mxfp4"
+                  else mx_mod.E4M3[v["expert_in"][sample].astype(np.int64)].reshape(len(sample), -1, 32)
+                  * mx_mod.e8m0_to_f64(v["expert_in_scales"][sample])[..., None]).reshape(len(sample), -1)
+            ties = mx_rounding_ties(uq, r, fmt)
+            if ties:  # the oracle takes the kernel's rounding where u sits on a midpoint
+                say(f"{wl}: u rounding ties at sampled tokens {sorted(ties)}")
+                r = host.oracle(xh[sample], act_quant=fmt, force_ids=force or None, force_u=ties)
             e = check_output(out[sample], r.out, 5e-2)
             say(f"{wl}: out max-abs {e:.3g} x RMS on {len(sample)} tokens")
         finally:

@@ -15,7 +15,8 @@ import numpy as np
 import pytest
 
 import synth
-from layer_cases import HostLayer, bf16_to_f64, check_output, check_rel_l2, check_routing, device_weights
+from layer_cases import (HostLayer, bf16_to_f64, check_output, check_rel_l2, check_routing, device_weights,
+                         mx_rounding_ties)
 
 pytestmark = pytest.mark.gpu
 
@@ -101,8 +102,9 @@ def test_small_full_parity(torch_dev, tables, name, over, T):
 
 # ------------------- MX FP8 / FP4 activations (fp8 x fp4, mxfp4 x mxfp4 MMA)
 
-MXA_CASES = [("mxfp8 wide", "mxfp8", 300), ("mxfp8 narrow", "mxfp8", 37),
-             ("mxfp4 wide", "mxfp4", 300), ("mxfp4 narrow", "mxfp4", 37)]
+MXA_CASES = [("mxfp8 wide", "mxfp8", 300, False), ("mxfp8 narrow", "mxfp8", 37, False),
+             ("mxfp4 wide", "mxfp4", 300, False), ("mxfp4 narrow", "mxfp4", 37, False),
+             ("mxfp8 boundary norm", "mxfp8", 64, True), ("mxfp4 boundary norm", "mxfp4", 300, True)]
 
 
 def _decode_mx(codes, scales, fmt):
@@ -116,8 +118,8 @@ def _decode_mx(codes, scales, fmt):
     return (v.reshape(codes.shape[:-1] + (K // 32, 32)) * s[..., None]).reshape(codes.shape)
 
 
-@pytest.mark.parametrize("name,fmt,T", MXA_CASES, ids=[c[0] for c in MXA_CASES])
-def test_small_mx_activations_parity(torch_dev, tables, name, fmt, T):
+@pytest.mark.parametrize("name,fmt,T,norm", MXA_CASES, ids=[c[0] for c in MXA_CASES])
+def test_small_mx_activations_parity(torch_dev, tables, name, fmt, T, norm):
     """Against the oracle with u and a MX-quantised (FP8 or FP4) at the same
     points: quantised u equal code for code except rare rounding-boundary flips
     to a neighbouring code (the GPU forms u in FP32, the oracle in FP64),
@@ -125,12 +127,17 @@ def test_small_mx_activations_parity(torch_dev, tables, name, fmt, T):
     torch = torch_dev
     from latent_moe_layer_fp32_amd import LatentMoE
 
-    spec = synth.CONFIGS["decode"].with_(name="small", T=T, E=16, k=4, expert_format="mxfp4", **SMALL)
+    spec = synth.CONFIGS["decode"].with_(name="small", T=T, E=16, k=4, expert_format="mxfp4",
+                                         input_norm=norm, **SMALL)
     say(f"case: {name}, T={T}")
     wts = device_weights(spec, tables)
+    gin = None
+    if norm:  # x is the pre-norm residual
+        wts["input_gamma"] = synth.device_tensor(spec, "input_gamma", tables)
+        gin = synth.host(spec, "input_gamma")
     layer = LatentMoE(hidden=spec.H, pooled=spec.P, experts=spec.E, intermediate=spec.I, top_k=spec.k,
                       eps=spec.eps, act_dtype=spec.act_dtype, expert_dtype=spec.expert_format,
-                      max_tokens=512, weights=wts, expert_act=fmt)
+                      max_tokens=512, weights=wts, expert_act=fmt, input_norm=norm)
     try:
         x = synth.device_tensor(spec, "x", tables)
         ids_d = torch.empty((T, spec.k), dtype=torch.int32, device=x.device)
@@ -142,10 +149,10 @@ def test_small_mx_activations_parity(torch_dev, tables, name, fmt, T):
         assert np.array_equal(layer.forward(x).cpu().numpy(), out), "second forward differs"
         host = HostLayer(spec)
         xh = host.x()
-        r0 = host.oracle(xh, keep_pairs=False, act_quant=fmt)
+        r0 = host.oracle(xh, keep_pairs=False, act_quant=fmt, input_gamma=gin)
         near, _ = check_routing(ids, w, r0.logits, spec.k)
         force = {int(t): ids[t] for t in near}
-        r = host.oracle(xh, act_quant=fmt, force_ids=force or None)
+        r = host.oracle(xh, act_quant=fmt, input_gamma=gin, force_ids=force or None)
         assert np.array_equal(ids, r.ids)
         # the quantised expert input: same codes but for rare boundary flips
         uq = _decode_mx(v["expert_in"], v["expert_in_scales"], fmt)
@@ -160,6 +167,10 @@ def test_small_mx_activations_parity(torch_dev, tables, name, fmt, T):
             blk = np.repeat(np.abs(r.u).reshape(T, -1, 32).max(-1), 32, axis=-1)
             bound = 2.0 * 2.0 ** (np.floor(np.log2(np.maximum(blk, 1e-300))) - 2)[diff]
         assert frac < 1e-3 and (step <= bound).all(), f"u: {frac:.3g} of elements differ"
+        ties = mx_rounding_ties(uq, r, fmt)
+        if ties:  # the oracle takes the kernel's rounding where u sits on a midpoint
+            say(f"{name}: u rounding ties at tokens {sorted(ties)}")
+            r = host.oracle(xh, act_quant=fmt, input_gamma=gin, force_ids=force or None, force_u=ties)
         pr = v["pair_row"].reshape(T, spec.k)
         aq = _decode_mx(v["act"], v["act_scales"], fmt)[pr]
         check_rel_l2(aq, r.a, 1e-2, f"act ({fmt})")
