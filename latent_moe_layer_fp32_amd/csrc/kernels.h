@@ -311,9 +311,11 @@ struct PoolerProb {
 // ------------------------------------------------------ grouped tile lookup
 // Tiles of all experts form one list: expert e owns tiles
 // [tile_off[e], tile_off[e+1]) (ceil(count_e / BM) of them), each walked over
-// all nt column tiles. Logical index L -> (expert, m-tile, n-tile) with the
-// m-tiles of one expert and one n-tile adjacent, so they share the weight
-// tile in L2.
+// all nt column tiles. Logical index L -> (expert, m-tile, n-tile): within an
+// expert, groups of up to 8 m-tiles walk all n-tiles together, the m-tiles of
+// a group adjacent, so they share each weight tile in L2 while the group's
+// rows are reused across the n-tiles (an expert of a few m-tiles is one
+// group; a hot expert's rows are not streamed again for every n-tile).
 LM_DEV bool lm_group_tile(const int* tile_off, const int* offsets, const int* counts, int E, int BM,
                           int nt, int cols, int bid, LmTile& t) {
   const int total = tile_off[E] * nt;
@@ -327,8 +329,8 @@ LM_DEV bool lm_group_tile(const int* tile_off, const int* offsets, const int* co
   }
   const int e = lo;
   const int mte = tile_off[e + 1] - tile_off[e];
-  const int local = L - tile_off[e] * nt;
-  const int n = local / mte, mi = local - n * mte;
+  int mi, n;
+  lm_dense_order(L - tile_off[e] * nt, mte, nt, 8, mi, n);
   t.e = e;
   t.m0 = offsets[e] + mi * BM;
   t.rows = min(BM, counts[e] - mi * BM);
