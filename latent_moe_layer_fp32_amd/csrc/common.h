@@ -27,12 +27,6 @@ LM_DEV uint16_t lm_f32_to_bf16(float f) {
 // place of an IEEE division: the result is rounded to BF16 or an MX code.
 LM_DEV float lm_silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
-// Deterministic wave-wide sums (fixed butterfly order).
-LM_DEV float lm_wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
 // v from the lane that a DPP control word names (quad_perm, row mirrors).
 template <int CTRL>
 LM_DEV float lm_dpp(float v) {

@@ -83,13 +83,6 @@ LM_DEV uint32_t lm_e2m1_rne(float q) {
   return ((__float_as_uint(q) >> 28) & 0x8u) | (a < 1.0f ? lo : hi);
 }
 
-// Max over the 32 lanes sharing bit 5 of the lane id.
-LM_DEV float lm_half_max(float v) {
-  float a[1] = {v};
-  lm_half_reduce(a, [](float x, float y) { return fmaxf(x, y); });
-  return a[0];
-}
-
 // u = r_t * u'_t (u' = gamma_p * Wp x, FP32 [T, P]) quantised to MX FP8
 // (BITS = 8: codes [T, P] bytes) or MX FP4 (BITS = 4: codes [T, P/2] bytes,
 // element 2i in the low nibble), scales [T, P/32] E8M0 bytes. Eight threads
