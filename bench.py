@@ -185,8 +185,8 @@ def main():
                     help="also run a plain device copy of this many bytes (calibrates profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the layer runs unsharded on a single MI355X; "
-              "multi-GPU runs are not part of this build", file=sys.stderr)
+        print("bench.py measures one GPU: the layer runs unsharded on a single MI355X "
+              "(sharding across GPUs is designed, not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
