@@ -67,6 +67,7 @@ void lm_gemm_stream_kernel(const Prob p) {
   constexpr int kRingA = kLeanA ? 2 : 4, kRingB = kLeanB ? 2 : 4;
   constexpr int kDistB = kLeanB ? 1 : 3, kDistA = kLeanA ? 2 : 4;
   constexpr int kBq = kMx ? 1 : 4;  // 16-byte B loads per 32-row group and k-tile
+  constexpr bool kNT = TM == 1 && LmWeightsOnce<Prob>::value;  // streaming weight loads
   constexpr int kStage = BM * 8;    // 16-byte chunks per A stage
   constexpr int QA = BM * 8 / 256;  // A chunks per thread per k-tile (= TM)
   __shared__ lm_u32x4 sa[2 * kStage];
@@ -117,10 +118,10 @@ void lm_gemm_stream_kernel(const Prob p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       if constexpr (kMx) {
-        rb[slot][j][0] = bsrc[j][kc * 64];
+        rb[slot][j][0] = lm_wload<kNT>(&bsrc[j][kc * 64]);
       } else {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) rb[slot][j][s] = bsrc[j][(kc * 4 + s) * 64];
+        for (int s = 0; s < 4; ++s) rb[slot][j][s] = lm_wload<kNT>(&bsrc[j][(kc * 4 + s) * 64]);
       }
     }
   };
@@ -128,7 +129,7 @@ void lm_gemm_stream_kernel(const Prob p) {
     if constexpr (kMx) {
       const int kc4 = min(kt, klast) >> 2;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) rsc[sslot][j] = ssrc[j][kc4 * 64];
+      for (int j = 0; j < TN; ++j) rsc[sslot][j] = lm_wload<kNT>(&ssrc[j][kc4 * 64]);
     }
   };
   // A fragments of one MFMA step, double-buffered across steps.

@@ -353,6 +353,7 @@ struct GateUpProb {
   static_assert(Cfg::TN == 2, "gate/up pairs");
   static constexpr int kCols = Cfg::WN * 32;
   static constexpr bool kMx = MX_;  // weights in the packed MXFP4 layout
+  static constexpr bool kWeightsOnce = true;
   const void* sg = nullptr;  // packed scales (MXFP4)
   const void* su = nullptr;
   const E* pooled;
@@ -428,6 +429,7 @@ struct DownProb {
   using Cfg = Cfg_;
   using E = typename Cfg::E;
   static constexpr bool kMx = MX_;  // weights in the packed MXFP4 layout
+  static constexpr bool kWeightsOnce = true;
   const void* sd = nullptr;         // packed scales (MXFP4)
   const E* act;
   const E* wd;

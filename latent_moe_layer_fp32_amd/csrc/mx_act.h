@@ -251,6 +251,7 @@ void lm_gemm_stream_mxa_kernel(const Prob p) {
   // ahead and A two iterations ahead of its LDS store (a ring of two slots).
   constexpr bool kLean = TM >= 4 && !(kA4 && Prob::kDeepB);
   constexpr int kRingB = kLean ? 2 : 4, kDistB = kLean ? 1 : 3;
+  constexpr bool kNT = TM == 1 && LmWeightsOnce<Prob>::value;  // streaming weight loads
   constexpr int kRingA = 1;
   constexpr int kStage = BM * kCh;  // 16-byte chunks per A stage
   // A chunks per thread per k-tile; with fewer rows than one pass covers
@@ -317,15 +318,15 @@ void lm_gemm_stream_mxa_kernel(const Prob p) {
     const int kc = min(kt, klast);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      rb[slot][j][0] = bsrc[j][(2 * kc) * 64];
-      rb[slot][j][1] = bsrc[j][(2 * kc + 1) * 64];
+      rb[slot][j][0] = lm_wload<kNT>(&bsrc[j][(2 * kc) * 64]);
+      rb[slot][j][1] = lm_wload<kNT>(&bsrc[j][(2 * kc + 1) * 64]);
     }
   };
   // B scale dword of 64-wide k-tiles 4m .. 4m+3 = 128-wide k-tiles 2m, 2m+1
   auto load_bs = [&](int sslot, int kt) __attribute__((always_inline)) {
     const int kc = min(kt, klast);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) rsb[sslot][j] = bscl[j][(kc >> 1) * 64];
+    for (int j = 0; j < TN; ++j) rsb[sslot][j] = lm_wload<kNT>(&bscl[j][(kc >> 1) * 64]);
   };
 
   // A fragments, two in flight: fragment (s, i+1) is read while the MFMAs of
