@@ -877,7 +877,8 @@ __global__ __launch_bounds__(256) void lm_combine_kernel(const float* O, const f
   for (int c = tid * 4; c < P; c += 1024) {
     lm_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int j = 0; j < k; ++j) {
-      const lm_f32x4 o = *(const lm_f32x4*)(O + (size_t)s_row[j] * P + c);
+      // each expert-output row is read once: streaming (non-temporal) load
+      const lm_f32x4 o = __builtin_nontemporal_load((const lm_f32x4*)(O + (size_t)s_row[j] * P + c));
       const lm_f32x4 g = *(const lm_f32x4*)(gamma + (size_t)s_e[j] * P + c);
       acc += s_coef[j] * (g * o);
     }
