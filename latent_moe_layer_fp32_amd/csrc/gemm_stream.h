@@ -37,6 +37,14 @@ struct LmIsMx : std::false_type {};
 template <class P>
 struct LmIsMx<P, std::void_t<decltype(P::kMx)>> : std::integral_constant<bool, P::kMx> {};
 
+// Problems whose k-tiles come in pairs that share one B k-tile (the
+// unpooler's BF16 hi/lo pair of y: k-tiles 2m and 2m+1 both read W's k-tile
+// m) declare kPairB = true: B is then loaded once per pair.
+template <class P, class = void>
+struct LmPairB : std::false_type {};
+template <class P>
+struct LmPairB<P, std::void_t<decltype(P::kPairB)>> : std::integral_constant<bool, P::kPairB> {};
+
 // E8M0 scale code -> FP32 2^(code-127) (code 0 is the subnormal 2^-127,
 // code 255 is NaN).
 LM_DEV float lm_e8m0_to_f32(uint32_t code) {
@@ -66,6 +74,11 @@ void lm_gemm_stream_kernel(const Prob p) {
   constexpr bool kLeanB = kLeanA && !kMx;
   constexpr int kRingA = kLeanA ? 2 : 4, kRingB = kLeanB ? 2 : 4;
   constexpr int kDistB = kLeanB ? 1 : 3, kDistA = kLeanA ? 2 : 4;
+  // Paired B (k-tiles 2m, 2m+1 share B k-tile m): the ring holds pairs, loaded
+  // once per pair at its even k-tile, one pair (two k-tiles) ahead in a ring of
+  // two, or two pairs ahead in a ring of four.
+  constexpr bool kPair = LmPairB<Prob>::value && !kMx;
+  constexpr int kDistP = kLeanB ? 1 : 2;
   constexpr int kBq = kMx ? 1 : 4;  // 16-byte B loads per 32-row group and k-tile
   constexpr bool kNT = TM == 1 && LmWeightsOnce<Prob>::value;  // streaming weight loads
   constexpr int kStage = BM * 8;    // 16-byte chunks per A stage
@@ -189,7 +202,11 @@ void lm_gemm_stream_kernel(const Prob p) {
   // stages, step 0 of kt0 in registers.
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    if (d < kDistB) load_b(d, kt0 + d);
+    if constexpr (kPair) {
+      if (d < kDistP) load_b(d, kt0 + 2 * d);
+    } else {
+      if (d < kDistB) load_b(d, kt0 + d);
+    }
     if (d < (kLeanA ? 2 : kDistA)) load_a(d, kt0 + d);
   }
   load_scales(0, kt0);
@@ -216,10 +233,14 @@ void lm_gemm_stream_kernel(const Prob p) {
   // indices past the end are clamped: those loads are issued but unused.
   auto iter = [&](int kt, auto qc) {
     constexpr int q = decltype(qc)::value;
-    constexpr int cur = q & 1, nxt = cur ^ 1, slot = q % kRingB;
+    constexpr int cur = q & 1, nxt = cur ^ 1, slot = kPair ? (q >> 1) % kRingB : q % kRingB;
     constexpr int sq = (q >> 2) & 1, kb = q & 3;
     read_frag(1, cur, 1);
-    load_b((q + kDistB) % kRingB, kt + kDistB);
+    if constexpr (kPair) {
+      if constexpr ((q & 1) == 0) load_b(((q >> 1) + kDistP) % kRingB, kt + 2 * kDistP);
+    } else {
+      load_b((q + kDistB) % kRingB, kt + kDistB);
+    }
     if constexpr ((q + kDistB) % 4 == 0) load_scales(((q + kDistB) >> 2) & 1, kt + kDistB);
     if constexpr (!kLeanA) load_a((q + kDistA) % kRingA, kt + kDistA);
     mma_step(0, slot, 0, sq, kb);

@@ -483,10 +483,13 @@ struct DownProb {
 };
 
 // ---------------------------------------------------------------- unpooler
-template <class Cfg_>
+// PAIR: y is the BF16 pair (pieces = 2, set by the host): consecutive
+// k-tiles share one W k-tile, which the streaming kernel then loads once.
+template <class Cfg_, bool PAIR = false>
 struct UnpoolerProb {
   using Cfg = Cfg_;
   using E = typename Cfg::E;
+  static constexpr bool kPairB = PAIR;
   const E* y;
   const E* w;
   float* out;  // [T, H]
@@ -540,10 +543,11 @@ struct UnpoolerProb {
 // For few tokens the pooler / unpooler have too few output tiles to keep the
 // chip streaming weights, so K is split and each split writes FP32 partial
 // sums part[s][row][col]; a finish kernel adds them in split order.
-template <class Cfg_>
+template <class Cfg_, bool PAIR = false>  // PAIR as for UnpoolerProb
 struct DenseSplitProb {
   using Cfg = Cfg_;
   using E = typename Cfg::E;
+  static constexpr bool kPairB = PAIR;
   const E* a;   // [T, K] (pieces 2: [T, 2K], hi | lo)
   const E* w;   // packed [N, K]
   float* part;  // [splits, T, N]

@@ -539,7 +539,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   if (packed) dense_split(T, H, ypieces * P, Cw::BM, Cw::BN, usplits, ukt);
   if (usplits > 1) {
     if constexpr (sizeof(Et) == 2) {
-    DenseSplitProb<Cw> p;
+    DenseSplitProb<Cw, true> p;  // the BF16 pair: W k-tiles shared by hi and lo
     p.a = y;
     p.w = (const Et*)Wunpool;
     p.part = (float*)(ws + L.kpart);
@@ -558,7 +558,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     LM_HIP(hipGetLastError());
     }
   } else {
-    UnpoolerProb<Cw> p;
+    UnpoolerProb<Cw, sizeof(Et) == 2> p;  // BF16 layers: y is the pair
     p.y = y;
     p.w = (const Et*)Wunpool;
     p.out = out;
