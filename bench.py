@@ -27,7 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 (and FP16) matrix peak
 # dense matrix peaks of the scaled (MX) instructions: an fp8 x fp4 product runs at the
 # FP8 rate, fp4 x fp4 at the FP4 rate
 MX_PEAK_TFLOPS = {"mxfp8": 5000.0, "mxfp4": 10100.0}
@@ -259,7 +259,7 @@ def main():
             peak = MX_PEAK_TFLOPS.get(spec.expert_act, BF16_PEAK_TFLOPS)
             r["roofline"] = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak,
                              "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                             "peak_dtype": spec.expert_act or "bf16",
+                             "peak_dtype": spec.expert_act or "f16",
                              "traffic": measured_traffic(wl, "gate_up"),
                              "kernel": "gate_up grouped GEMM + SwiGLU",
                              "kernel_ms": round(stages["gate_up"], 4)}
@@ -283,7 +283,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16/f16",
         "data": "synthetic (seeded counter-based N(0,1) inputs, N(0,1/fan_in) weights)",
         "config": {"workload": f"{args.workload}: " + (f"{spec.chunks} x " if spec.chunks > 1 else "") + f"{spec.T} tokens, H={spec.H}, P={spec.P}, E={spec.E}, "
                                f"I={spec.I}, top-{spec.k}, {spec.expert_format.upper()} experts"

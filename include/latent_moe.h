@@ -66,13 +66,28 @@ typedef struct {
   int64_t intermediate; /* I: SwiGLU intermediate width per expert */
   int32_t top_k;        /* k: experts per token, 1 <= k <= min(E, 16) */
   float eps;            /* RMSNorm epsilon for both norms, finite, >= 0 */
-  int32_t act_dtype;    /* x, pooler and unpooler: LMOE_F32 or LMOE_BF16 */
+  int32_t act_dtype;    /* x, pooler and unpooler: LMOE_F32 or LMOE_BF16.
+                           LMOE_BF16: the pooler multiplies BF16 x by BF16 Wp;
+                           the expert and unpooler GEMMs then run on FP16
+                           operands: u, the SwiGLU output a and y are rounded
+                           to FP16 (nearest even; a saturates at +-65504; u
+                           and y are bounded by sqrt(P) max|gamma|), and the
+                           weights are used as FP16 copies made at create,
+                           each weight row times a power of two 2^s that puts
+                           its largest magnitude in [2^14, 2^15), undone in
+                           FP32 after the product. Every BF16 weight within
+                           2^31 of its row's largest is exact in that copy.
+                           FP16 carries three more significand bits than BF16
+                           at the same matrix rate; products accumulate in
+                           FP32 */
   int32_t expert_dtype; /* gate/up/down: LMOE_F32, LMOE_BF16 or LMOE_MXFP4.
                            LMOE_F32 requires act_dtype LMOE_F32 and vice versa;
                            LMOE_MXFP4 runs with BF16 activations: each element
-                           is decoded exactly (code value x 2^(scale-127)) to
-                           BF16 in registers, and the products accumulate in
-                           FP32 as for BF16 experts */
+                           is decoded in registers to FP16, times its row's
+                           2^s (code value x 2^(scale-127+s), exact for every
+                           block whose scale is within 2^35 of the row's
+                           largest), and the products accumulate in FP32 as
+                           for BF16 experts */
   int64_t max_tokens;   /* upper bound on T per forward; sizes the workspace */
   int32_t input_norm;   /* 0: x is the normed token. 1: x is the pre-norm
                            residual r; the layer first forms
@@ -83,7 +98,7 @@ typedef struct {
                            conversions"). The router then reads that FP32
                            value and the pooler its act_dtype rounding (BF16
                            nearest-even, or the FP32 value). */
-  int32_t expert_act;   /* 0: the expert GEMMs read u and a in act_dtype (BF16).
+  int32_t expert_act;   /* 0: the expert GEMMs read u and a in FP16 (above).
                            LMOE_MXFP8: they read them as MX FP8 (E4M3, one E8M0
                            scale per 32 along K), quantised with nearest-even
                            rounding and saturation at 448, on the scaled matrix
@@ -178,15 +193,12 @@ int latent_moe_forward(latent_moe_t* h, const void* x, int64_t T, float* out, in
  *            (stable in (t, j) order within an expert)
  *   pair_row [T*k] int32: for pair (t, j) at index t*k+j, its row in the
  *            grouped order
- *   pooled   [T, P] act_dtype (F32 with MX expert inputs): gamma_p * (Wp x_t), before
- *            the row scale
+ *   pooled   [T, P] F32: gamma_p * (Wp x_t), before the row scale
  *   row_scale [T] F32: 1/sqrt(mean((Wp x_t)^2) + eps)
- *   act      [T*k, I] (F32 if expert_dtype is F32, else BF16): SwiGLU
+ *   act      [T*k, I] (F32 if expert_dtype is F32, else FP16): SwiGLU
  *            output, grouped order
  *   expert_out [T*k, P] F32: o (before the per-expert norm), grouped order
- *   combined y: FP32 layers [T, P] F32; BF16 layers the BF16 pair [T, 2P]
- *            (hi | lo, hi = BF16 rounding of y, lo = that of the remainder;
- *            the unpooler reads both)                                     */
+ *   combined y [T, P]: F32 in FP32 layers, FP16 in BF16 layers          */
 typedef struct {
   const float* logits;
   const int32_t* ids;
@@ -200,9 +212,11 @@ typedef struct {
   const void* act;
   const float* expert_out;
   const void* combined;
-  const uint8_t* expert_in;        /* MX expert inputs: u codes, [T, P] E4M3 bytes
+  const uint8_t* expert_in;        /* the expert GEMMs' input u as they read it:
+                                      MX expert inputs: codes, [T, P] E4M3 bytes
                                       (MXFP8) or [T, P/2] packed E2M1 (MXFP4);
-                                      else NULL */
+                                      other BF16 layers: [T, P] FP16 (row_scale
+                                      times pooled, rounded); FP32 layers: NULL */
   const uint8_t* expert_in_scales; /* MX expert inputs: u scales [T, P/32] E8M0,
                                       else NULL */
   const uint8_t* act_scales;       /* MX expert inputs: act scales [T*k, I/32] E8M0

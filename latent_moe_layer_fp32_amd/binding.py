@@ -238,8 +238,8 @@ class LatentMoE:
         k, E, P, I = self.top_k, self.experts, self.pooled, self.intermediate
         mxa = self.expert_act in ("mxfp8", "mxfp4")
         cb = 2 if self.expert_act == "mxfp4" else 1  # elements per code byte
-        act_np = np.float32 if self.act_dtype == "f32" else np.uint16
-        exp_np = np.float32 if self.expert_dtype == "f32" else (np.uint8 if mxa else np.uint16)
+        f32 = self.act_dtype == "f32"
+        exp_np = np.float32 if f32 else (np.uint8 if mxa else np.float16)
         spec = {
             "logits": (v.logits, (T, E), np.float32),
             "ids": (v.ids, (T, k), np.int32),
@@ -248,13 +248,14 @@ class LatentMoE:
             "offsets": (v.offsets, (E + 1,), np.int32),
             "perm_token": (v.perm_token, (T * k,), np.int32),
             "pair_row": (v.pair_row, (T * k,), np.int32),
-            "pooled": (v.pooled, (T, P), np.float32 if mxa else act_np),
+            "pooled": (v.pooled, (T, P), np.float32),
             "row_scale": (v.row_scale, (T,), np.float32),
             "act": (v.act, (T * k, I // cb), exp_np),
             "expert_out": (v.expert_out, (T * k, P), np.float32),
-            "combined": (v.combined, (T, P), np.float32) if self.act_dtype == "f32"
-            else (v.combined, (T, 2 * P), np.uint16),
+            "combined": (v.combined, (T, P), np.float32 if f32 else np.float16),
         }
+        if not f32 and not mxa:  # the FP16 u the expert GEMMs read
+            spec["expert_in"] = (v.expert_in, (T, P), np.float16)
         if mxa:  # MX codes (FP4: two per byte) and E8M0 scales, as stored
             spec["expert_in"] = (v.expert_in, (T, P // cb), np.uint8)
             spec["expert_in_scales"] = (v.expert_in_scales, (T, P // 32), np.uint8)
@@ -270,9 +271,6 @@ class LatentMoE:
             a = np.empty(shape, dt)
             _memcpy_d2h(a.ctypes.data, ptr, a.nbytes)
             res[name] = a
-        if self.act_dtype != "f32" and "combined" in res:  # BF16 pair -> y = hi + lo (exact in FP32)
-            pr = (res["combined"].astype(np.uint32) << 16).view(np.float32)
-            res["combined"] = pr[:, :P] + pr[:, P:]
         if split_norm and "x_norm" in res:  # FP32 value = sum of the three BF16 pieces (exact)
             H = self.hidden
             pcs = (res["x_norm"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 typedef __attribute__((ext_vector_type(8))) __bf16 lm_bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 lm_f16x8;
 typedef __attribute__((ext_vector_type(16))) float lm_f32x16;
 typedef __attribute__((ext_vector_type(4))) float lm_f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t lm_u32x4;
@@ -23,8 +24,19 @@ LM_DEV uint16_t lm_f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Nearest-even FP16, saturating at the largest finite value (65504); NaN
+// stays NaN.
+LM_DEV _Float16 lm_f32_to_f16_sat(float f) {
+  return (_Float16)(fabsf(f) > 65504.0f ? copysignf(65504.0f, f) : f);
+}
+
+// Power of two 2^s (|s| <= 126) and the shift s of such a power, by their
+// exponent bits.
+LM_DEV float lm_pow2(int s) { return __uint_as_float((uint32_t)(127 + s) << 23); }
+LM_DEV int lm_log2_of_pow2(float p) { return (int)(__float_as_uint(p) >> 23) - 127; }
+
 // silu(g) = g * sigma(g), with the hardware reciprocal (about one ulp) in
-// place of an IEEE division: the result is rounded to BF16 or an MX code.
+// place of an IEEE division: the result is rounded to FP16 or an MX code.
 LM_DEV float lm_silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // v from the lane that a DPP control word names (quad_perm, row mirrors).

@@ -11,8 +11,8 @@
 // distinct 16-byte bank groups. (XOR by row % 8 leaves rows r and r+8 on
 // the same banks: a measured 2-way conflict on the operand reads.)
 //
-// Matrix instructions: BF16 uses v_mfma_f32_32x32x16_bf16, FP32 uses
-// v_mfma_f32_32x32x2_f32. A lane reads one 16-byte chunk of its A row and its
+// Matrix instructions: BF16 uses v_mfma_f32_32x32x16_bf16, FP16
+// v_mfma_f32_32x32x16_f16, FP32 v_mfma_f32_32x32x2_f32. A lane reads one 16-byte chunk of its A row and its
 // B row per step; any assignment of k to (lane, step) is valid as long as A
 // and B use the same one, which lets every lane read whole chunks.
 //
@@ -38,6 +38,17 @@ struct LmElem<uint16_t> {  // bfloat16 bits
   }
   LM_DEV static uint16_t from_f32(float v) { return lm_f32_to_bf16(v); }
   LM_DEV static float to_f32(uint16_t v) { return lm_bf16_to_f32(v); }
+};
+
+template <>
+struct LmElem<_Float16> {  // IEEE half: same matrix rate as BF16, three more mantissa bits
+  static constexpr int kPerChunk = 8;
+  LM_DEV static void mma(lm_f32x16& acc, lm_u32x4 a, lm_u32x4 b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(lm_f16x8, a),
+                                                 __builtin_bit_cast(lm_f16x8, b), acc, 0, 0, 0);
+  }
+  LM_DEV static _Float16 from_f32(float v) { return lm_f32_to_f16_sat(v); }
+  LM_DEV static float to_f32(_Float16 v) { return (float)v; }
 };
 
 template <>
@@ -77,13 +88,18 @@ struct LmTile {
 };
 
 // Problems whose epilogue needs one value per tile row (gathered from memory)
-// declare row_value(); it is loaded at the start of the tile, so its latency
-// hides behind the main loop, and handed to the epilogue through LDS.
+// declare row_value() (and may switch it off with kRowValue = false); it is
+// loaded at the start of the tile, so its latency hides behind the main loop,
+// and handed to the epilogue through LDS.
+template <class P, class = void>
+struct LmRowValueOn : std::true_type {};
+template <class P>
+struct LmRowValueOn<P, std::void_t<decltype(P::kRowValue)>> : std::integral_constant<bool, P::kRowValue> {};
 template <class P, class = void>
 struct LmHasRowValue : std::false_type {};
 template <class P>
 struct LmHasRowValue<P, std::void_t<decltype(std::declval<const P&>().row_value(std::declval<const LmTile&>(), 0))>>
-    : std::true_type {};
+    : LmRowValueOn<P> {};
 
 // Problems whose B k-tiles are not read in order declare b_ktile() (the
 // router's six-product split); the others read B k-tile kt at step kt.

@@ -1,4 +1,5 @@
-// Streaming-B matrix-core GEMM for gfx950 (BF16 operands, FP32 accumulation).
+// Streaming-B matrix-core GEMM for gfx950 (BF16 or FP16 operands, FP32
+// accumulation).
 //
 // Same problem interface and accumulator layout as lm_gemm_kernel, with all
 // four wavefronts side by side along N (WM = 1): every wave needs the whole
@@ -13,8 +14,11 @@
 //     per wave: loading the row-major layout straight into MFMA registers
 //     would touch 32 cache lines per instruction and throttle the vector
 //     memory path. MXFP4 weights arrive as E2M1 codes plus E8M0 scales and
-//     are decoded exactly to BF16 in registers right before their MFMA.
-// Per 64-wide k-tile a wave issues TM*TN*4 v_mfma_f32_32x32x16_bf16 and reads
+//     are decoded exactly to FP16 in registers right before their MFMA, each
+//     weight row times its power of two 2^s (chosen at create so that the
+//     row's largest value lands in [2^14, 2^15)); the epilogue multiplies
+//     the row's output column by 2^-s.
+// Per 64-wide k-tile a wave issues TM*TN*4 32x32x16 MFMAs and reads
 // only A from LDS: with TM = 4 that is about 64 B/clk/CU of LDS reads at full
 // matrix rate, against ~135 B/clk measured on MI355X, where a 64x64 wave tile
 // reading both operands from LDS needs twice that and becomes LDS-bound.
@@ -37,18 +41,12 @@ struct LmIsMx : std::false_type {};
 template <class P>
 struct LmIsMx<P, std::void_t<decltype(P::kMx)>> : std::integral_constant<bool, P::kMx> {};
 
-// Problems whose k-tiles come in pairs that share one B k-tile (the
-// unpooler's BF16 hi/lo pair of y: k-tiles 2m and 2m+1 both read W's k-tile
-// m) declare kPairB = true: B is then loaded once per pair.
-template <class P, class = void>
-struct LmPairB : std::false_type {};
-template <class P>
-struct LmPairB<P, std::void_t<decltype(P::kPairB)>> : std::integral_constant<bool, P::kPairB> {};
-
-// E8M0 scale code -> FP32 2^(code-127) (code 0 is the subnormal 2^-127,
-// code 255 is NaN).
-LM_DEV float lm_e8m0_to_f32(uint32_t code) {
-  return __uint_as_float(code == 0 ? 0x00400000u : code == 255 ? 0x7fc00000u : code << 23);
+// E8M0 scale code times 2^s as FP32: 2^(code - 127 + s) (code 0 is 2^-127,
+// code 255 is NaN). The callers keep code + s <= 254; below the normal range
+// the scale is 0 (such a block is over 2^100 below its row's largest).
+LM_DEV float lm_e8m0_shifted(uint32_t code, int s) {
+  const int ex = (int)code + s;
+  return code == 255 ? __uint_as_float(0x7fc00000u) : ex >= 1 ? __uint_as_float((uint32_t)ex << 23) : 0.0f;
 }
 
 // The register budget allows two workgroups per CU (see kLeanA, kLeanB below).
@@ -57,8 +55,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LM_WAVES_MA
 void lm_gemm_stream_kernel(const Prob p) {
   using Cfg = typename Prob::Cfg;
   static_assert(Cfg::WM == 1 && Cfg::WN == 4, "streaming-B layout: four waves along N");
-  static_assert(sizeof(typename Cfg::E) == 2, "BF16 activations");
+  static_assert(sizeof(typename Cfg::E) == 2, "16-bit operands");
   constexpr bool kMx = LmIsMx<Prob>::value;
+  static_assert(!kMx || std::is_same_v<typename Cfg::E, _Float16>, "MXFP4 weights decode to FP16");
   constexpr int TM = Cfg::TM, TN = Cfg::TN, BM = Cfg::BM;
   // A (TM = 4): one register slot; A(kt+3) is loaded right after A(kt+2)
   // has been written to LDS at the end of iteration kt, so it has a whole
@@ -74,11 +73,6 @@ void lm_gemm_stream_kernel(const Prob p) {
   constexpr bool kLeanB = kLeanA && !kMx;
   constexpr int kRingA = kLeanA ? 2 : 4, kRingB = kLeanB ? 2 : 4;
   constexpr int kDistB = kLeanB ? 1 : 3, kDistA = kLeanA ? 2 : 4;
-  // Paired B (k-tiles 2m, 2m+1 share B k-tile m): the ring holds pairs, loaded
-  // once per pair at its even k-tile, one pair (two k-tiles) ahead in a ring of
-  // two, or two pairs ahead in a ring of four.
-  constexpr bool kPair = LmPairB<Prob>::value && !kMx;
-  constexpr int kDistP = kLeanB ? 1 : 2;
   constexpr int kBq = kMx ? 1 : 4;  // 16-byte B loads per 32-row group and k-tile
   constexpr bool kNT = TM == 1 && LmWeightsOnce<Prob>::value;  // streaming weight loads
   constexpr int kStage = BM * 8;    // 16-byte chunks per A stage
@@ -105,10 +99,14 @@ void lm_gemm_stream_kernel(const Prob p) {
   // four k-tiles.
   const lm_u32x4* bsrc[TN];
   const uint32_t* ssrc[TN];
+  int bsh[TN];  // MXFP4: the shift s of the lane's weight row (from its 2^-s)
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     bsrc[j] = p.b_group(t, w, j) + lane;
-    if constexpr (kMx) ssrc[j] = p.b_scales(t, w, j) + lane;
+    if constexpr (kMx) {
+      ssrc[j] = p.b_scales(t, w, j) + lane;
+      bsh[j] = -lm_log2_of_pow2(p.b_descale(t, w, j)[lane & 31]);
+    }
   }
 
   const int kt0 = t.kt0, kt1 = t.kt1, klast = kt1 - 1;
@@ -161,17 +159,19 @@ void lm_gemm_stream_kernel(const Prob p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // B fragment of step s: BF16 straight from the ring; MXFP4 decoded here,
-  // exactly, four codes pairs at a time (v_cvt_scalef32_pk_bf16_fp4).
+  // B fragment of step s: 16-bit weights straight from the ring; MXFP4
+  // decoded here to FP16, exactly (every E2M1 value x 2^(e - 127 + s) is an
+  // FP16 number unless the block's scale is over 2^35 below the row's
+  // largest), one code pair per conversion (v_cvt_scalef32_pk_f16_fp4).
   auto b_frag = [&](int slot, int j, int s, int sq, int kb) -> lm_u32x4 {
     if constexpr (kMx) {
       const uint32_t codes = rb[slot][j][0][s];
-      const float scale = lm_e8m0_to_f32((rsc[sq][j] >> (8 * kb)) & 0xffu);
+      const float scale = lm_e8m0_shifted((rsc[sq][j] >> (8 * kb)) & 0xffu, bsh[j]);
       lm_u32x4 f;
-      f[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
-      f[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
-      f[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
-      f[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
+      f[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 0));
+      f[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 1));
+      f[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 2));
+      f[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 3));
       return f;
     } else {
       return rb[slot][j][s];
@@ -182,7 +182,7 @@ void lm_gemm_stream_kernel(const Prob p) {
     for (int j = 0; j < TN; ++j) {
       const lm_u32x4 bf = b_frag(slot, j, s, sq, kb);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) LmElem<uint16_t>::mma(acc[i][j], fa[fb][i], bf);
+      for (int i = 0; i < TM; ++i) LmElem<typename Cfg::E>::mma(acc[i][j], fa[fb][i], bf);
     }
   };
   // Interleave within a step: the step's TM*TN MFMAs with the TM LDS reads
@@ -202,11 +202,7 @@ void lm_gemm_stream_kernel(const Prob p) {
   // stages, step 0 of kt0 in registers.
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    if constexpr (kPair) {
-      if (d < kDistP) load_b(d, kt0 + 2 * d);
-    } else {
-      if (d < kDistB) load_b(d, kt0 + d);
-    }
+    if (d < kDistB) load_b(d, kt0 + d);
     if (d < (kLeanA ? 2 : kDistA)) load_a(d, kt0 + d);
   }
   load_scales(0, kt0);
@@ -233,14 +229,10 @@ void lm_gemm_stream_kernel(const Prob p) {
   // indices past the end are clamped: those loads are issued but unused.
   auto iter = [&](int kt, auto qc) {
     constexpr int q = decltype(qc)::value;
-    constexpr int cur = q & 1, nxt = cur ^ 1, slot = kPair ? (q >> 1) % kRingB : q % kRingB;
+    constexpr int cur = q & 1, nxt = cur ^ 1, slot = q % kRingB;
     constexpr int sq = (q >> 2) & 1, kb = q & 3;
     read_frag(1, cur, 1);
-    if constexpr (kPair) {
-      if constexpr ((q & 1) == 0) load_b(((q >> 1) + kDistP) % kRingB, kt + 2 * kDistP);
-    } else {
-      load_b((q + kDistB) % kRingB, kt + kDistB);
-    }
+    load_b((q + kDistB) % kRingB, kt + kDistB);
     if constexpr ((q + kDistB) % 4 == 0) load_scales(((q + kDistB) >> 2) & 1, kt + kDistB);
     if constexpr (!kLeanA) load_a((q + kDistA) % kRingA, kt + kDistA);
     mma_step(0, slot, 0, sq, kb);

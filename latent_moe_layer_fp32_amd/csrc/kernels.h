@@ -115,13 +115,16 @@ __global__ __launch_bounds__(256) void lm_input_norm_kernel(const Et* r, int H, 
 // K % 64 == 0), 16-byte chunk c of row n lands at chunk index
 //   ((n/32 * K/64 + c/8) * 4 + (c%8)%4) * 64 + ((c%8)/4) * 32 + n%32
 // i.e. blocks of 32 rows x 64 columns, ordered by MFMA step s = (c%8)%4, then
-// by lane (h = (c%8)/4, r = n%32).
+// by lane (h = (c%8)/4, r = n%32). The same layout holds FP16 matrices.
 template <typename E>
 LM_DEV const lm_u32x4* lm_packed_group(const E* base, int64_t row0, int K) {
   return (const lm_u32x4*)base + (row0 / 32) * (int64_t)(K / 64) * 256;
 }
 
-__global__ void lm_pack_mfma_kernel(const lm_u32x4* src, lm_u32x4* dst, int64_t rows, int K) {
+// ds == nullptr: BF16 copied as is. Otherwise the BF16 source is written as
+// FP16, each row times 2^s, with 2^-s = ds[row] from lm_row_descale_bf16_kernel.
+__global__ void lm_pack_mfma_kernel(const lm_u32x4* src, lm_u32x4* dst, int64_t rows, int K,
+                                    const float* ds) {
   const int64_t n = rows * (K / 8);
   const int ktiles = K / 64;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -132,7 +135,66 @@ __global__ void lm_pack_mfma_kernel(const lm_u32x4* src, lm_u32x4* dst, int64_t 
     const int64_t g = blk / ktiles;
     const int kt = (int)(blk - g * ktiles);
     const int64_t row = g * 32 + (lane & 31);
-    dst[i] = src[row * (K / 8) + kt * 8 + 4 * (lane >> 5) + s];
+    lm_u32x4 v = src[row * (K / 8) + kt * 8 + 4 * (lane >> 5) + s];
+    if (ds) {
+      const float m = lm_pow2(-lm_log2_of_pow2(ds[row]));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const _Float16 lo = (_Float16)(lm_bf16_to_f32((uint16_t)(v[q] & 0xffffu)) * m);
+        const _Float16 hi = (_Float16)(lm_bf16_to_f32((uint16_t)(v[q] >> 16)) * m);
+        v[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+    }
+    dst[i] = v;
+  }
+}
+
+// FP16 copies of BF16 weights: each weight row (an output column of its
+// GEMM) is scaled by a power of two 2^s before the conversion, so that its
+// largest magnitude lands in [2^14, 2^15): s = 141 - the biased exponent of
+// that magnitude. A BF16 value has 8 significant bits and FP16 reaches down
+// to multiples of 2^-24, so every value of the row within 2^31 of the
+// largest converts exactly (a smaller one rounds, by at most 2^-39 of the
+// largest). The epilogue multiplies the output
+// column by ds[row] = 2^-s (exact). s is clamped to [-100, 100] (an all-zero
+// row gets 2^-100). One wavefront per row.
+__global__ __launch_bounds__(256) void lm_row_descale_bf16_kernel(const uint16_t* w, int64_t rows,
+                                                                  int K, float* ds) {
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += waves) {
+    const lm_u32x4* row = (const lm_u32x4*)(w + r * K);
+    uint32_t m = 0;
+    for (int c = lane; c < K / 8; c += 64) {
+      const lm_u32x4 q = row[c];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = max(m, max(q[j] & 0x7fffu, (q[j] >> 16) & 0x7fffu));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
+    if (lane == 0) ds[r] = lm_pow2(-min(max(141 - (int)(m >> 7), -100), 100));
+  }
+}
+
+// The same for MXFP4 weights, from their E8M0 scales [rows, K/32]: with emax
+// the row's largest scale code (255, NaN, ignored), s = 139 - emax puts the
+// row's largest decoded magnitude (at most 6 x 2^(emax - 127)) in [2^14,
+// 24576]; every E2M1 value of a block whose scale is within 2^35 of emax is
+// then an FP16 number. One thread per row.
+__global__ void lm_row_descale_mx_kernel(const uint8_t* sc, int64_t rows, int K, float* ds) {
+  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < rows;
+       r += (int64_t)gridDim.x * blockDim.x) {
+    const lm_u32x4* row = (const lm_u32x4*)(sc + r * (K / 32));
+    int m = 0;
+    for (int c = 0; c < K / 512; ++c) {
+      const lm_u32x4 q = row[c];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int b = (int)((q[j >> 2] >> (8 * (j & 3))) & 0xffu);
+        m = b != 255 ? max(m, b) : m;
+      }
+    }
+    ds[r] = lm_pow2(-min(max(139 - m, -100), 100));
   }
 }
 
@@ -243,8 +305,9 @@ struct RouterProb {
 };
 
 // ----------------------------------------------------------------- pooler
-// h = x Wp^T. Writes pooled = gamma_p * h (activation dtype) and, per row and
-// n-tile, the partial sum of h^2 used by the pre-expert RMSNorm.
+// h = x Wp^T. Writes gamma_p * h (FP32 layers: to pooled; BF16 layers: in
+// FP32 to pooled32) and, per row and n-tile, the partial sum of h^2 used by
+// the pre-expert RMSNorm.
 template <class Cfg_>
 struct PoolerProb {
   using Cfg = Cfg_;
@@ -340,9 +403,12 @@ LM_DEV bool lm_group_tile(const int* tile_off, const int* offsets, const int* co
 }
 
 // --------------------------------------------------------------- gate / up
-// For the rows (routed pairs) of expert e: g = r * (pooled Wg_e^T),
-// v = r * (pooled Wu_e^T), act = silu(g) * v, with r the token's RMSNorm row
-// scale (the norm is linear in its input, so it is applied after the GEMM).
+// For the rows (routed pairs) of expert e: g = u Wg_e^T, v = u Wu_e^T,
+// act = silu(g) * v. FP16 operands: u is the normed FP16 row and the weights
+// the FP16 copies scaled per row by 2^s, so g and v are the accumulators
+// times the rows' 2^-s. FP32 layers: pooled holds gamma_p * h and the token's
+// RMSNorm row scale r multiplies the accumulators (the norm is linear in its
+// input, so it is applied after the GEMM).
 // B tile rows: wave column wn owns rows [64 wn, 64 wn + 64): the first 32 are
 // gate rows, the next 32 the up rows of the same 32 output columns, so each
 // lane holds g and v of the same element.
@@ -354,9 +420,13 @@ struct GateUpProb {
   static constexpr int kCols = Cfg::WN * 32;
   static constexpr bool kMx = MX_;  // weights in the packed MXFP4 layout
   static constexpr bool kWeightsOnce = true;
+  static constexpr bool kScaledW = std::is_same_v<E, _Float16>;  // per-row 2^s weight copies
+  static constexpr bool kRowValue = !kScaledW;                    // r applied in the epilogue
   const void* sg = nullptr;  // packed scales (MXFP4)
   const void* su = nullptr;
-  const E* pooled;
+  const float* dsg = nullptr;  // FP16 operands: 2^-s per gate / up weight row [E*I]
+  const float* dsu = nullptr;
+  const E* pooled;  // FP16 operands: the normed u [T, P]; FP32 layers: gamma_p * h
   const E* wg;
   const E* wu;
   const float* row_scale;
@@ -390,6 +460,9 @@ struct GateUpProb {
   LM_DEV const uint32_t* b_scales(const LmTile& t, int wv, int j) const {
     return lm_packed_mx_scales(j ? su : sg, (int64_t)t.e * I + t.n0 + wv * 32, P);
   }
+  LM_DEV const float* b_descale(const LmTile& t, int wv, int j) const {
+    return (j ? dsu : dsg) + (int64_t)t.e * I + t.n0 + wv * 32;
+  }
   LM_DEV int a_ktile(int kt) const { return kt; }
   // the token's RMSNorm row scale (gathered), one per tile row
   LM_DEV float row_value(const LmTile& t, int r) const {
@@ -399,11 +472,21 @@ struct GateUpProb {
                        int lane, void* smem) const {
     const float* rs = (const float*)smem;  // row_value() of each tile row
     const int col = t.n0 + wn * 32 + (lane & 31);
+    float dg = 1.0f, du = 1.0f;
+    if constexpr (kScaledW) {
+      dg = dsg[(size_t)t.e * I + col];
+      du = dsu[(size_t)t.e * I + col];
+    }
     auto put = [&](int tm, int i) {
       const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
-      const float r = rs[row];
-      const float g = r * acc[tm][0][i];
-      const float v = r * acc[tm][1][i];
+      float g, v;
+      if constexpr (kScaledW) {
+        g = acc[tm][0][i] * dg;
+        v = acc[tm][1][i] * du;
+      } else {
+        g = rs[row] * acc[tm][0][i];
+        v = rs[row] * acc[tm][1][i];
+      }
       act[(size_t)(t.m0 + row) * I + col] = LmElem<E>::from_f32(lm_silu(g) * v);
     };
     if (t.rows == Cfg::BM) {
@@ -423,14 +506,17 @@ struct GateUpProb {
 
 // -------------------------------------------------------------------- down
 // o = act Wd_e^T for the rows of expert e; writes o (FP32) and per row and
-// n-tile the partial sum of o^2 for the per-expert RMSNorm.
+// n-tile the partial sum of o^2 for the per-expert RMSNorm. FP16 operands:
+// o is the accumulator times the weight row's 2^-s.
 template <class Cfg_, bool MX_ = false>
 struct DownProb {
   using Cfg = Cfg_;
   using E = typename Cfg::E;
   static constexpr bool kMx = MX_;  // weights in the packed MXFP4 layout
   static constexpr bool kWeightsOnce = true;
+  static constexpr bool kScaledW = std::is_same_v<E, _Float16>;
   const void* sd = nullptr;         // packed scales (MXFP4)
+  const float* dsd = nullptr;       // FP16 operands: 2^-s per down weight row [E*P]
   const E* act;
   const E* wd;
   const int* counts;
@@ -460,11 +546,18 @@ struct DownProb {
   LM_DEV const uint32_t* b_scales(const LmTile& t, int wv, int j) const {
     return lm_packed_mx_scales(sd, (int64_t)t.e * P + min(t.n0 + (wv * Cfg::TN + j) * 32, P - 32), I);
   }
+  LM_DEV const float* b_descale(const LmTile& t, int wv, int j) const {
+    return dsd + (int64_t)t.e * P + min(t.n0 + (wv * Cfg::TN + j) * 32, P - 32);
+  }
   LM_DEV int a_ktile(int kt) const { return kt; }
   LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
                        int lane, void* smem) const {
     float* red = (float*)smem;
-    lm_tile_row_ssq<Cfg>(acc, wm, wn, lane, P - t.n0, red, [](float v, int, int) { return v; });
+    float dd[Cfg::TN];
+#pragma unroll
+    for (int tn = 0; tn < Cfg::TN; ++tn)
+      dd[tn] = kScaledW ? dsd[(size_t)t.e * P + min(t.n0 + lm_acc_col<Cfg>(wn, tn, lane), P - 1)] : 1.0f;
+    lm_tile_row_ssq<Cfg>(acc, wm, wn, lane, P - t.n0, red, [&](float v, int tn, int) { return v * dd[tn]; });
     if ((int)threadIdx.x < t.rows)
       ssq[(size_t)(t.m0 + threadIdx.x) * nt + t.nt] = red[Cfg::WN * Cfg::BM + threadIdx.x];
 #pragma unroll
@@ -476,25 +569,24 @@ struct DownProb {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
-          if (row < t.rows) out[(size_t)(t.m0 + row) * P + col] = acc[tm][tn][i];
+          if (row < t.rows) out[(size_t)(t.m0 + row) * P + col] = acc[tm][tn][i] * dd[tn];
         }
     }
   }
 };
 
 // ---------------------------------------------------------------- unpooler
-// PAIR: y is the BF16 pair (pieces = 2, set by the host): consecutive
-// k-tiles share one W k-tile, which the streaming kernel then loads once.
-template <class Cfg_, bool PAIR = false>
+// out = y Wun^T. FP16 operands (ds set): W is the FP16 copy scaled per row by
+// 2^s and out the accumulator times ds[col] = 2^-s.
+template <class Cfg_>
 struct UnpoolerProb {
   using Cfg = Cfg_;
   using E = typename Cfg::E;
-  static constexpr bool kPairB = PAIR;
   const E* y;
   const E* w;
+  const float* ds = nullptr;  // [H] or none
   float* out;  // [T, H]
   int T, H, P, mt, nt;
-  int pieces = 1;  // 2: y is the BF16 pair [T, 2P], K runs over hi and lo k-tiles in turn
 
   LM_DEV bool tile(int bid, LmTile& t) const {
     int L;
@@ -507,11 +599,11 @@ struct UnpoolerProb {
     t.nt = n;
     t.e = 0;
     t.kt0 = 0;
-    t.kt1 = pieces * P / Cfg::KT;
+    t.kt1 = P / Cfg::KT;
     return true;
   }
   LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
-    return (const lm_u32x4*)(y + (size_t)(t.m0 + min(r, t.rows - 1)) * pieces * P);
+    return (const lm_u32x4*)(y + (size_t)(t.m0 + min(r, t.rows - 1)) * P);
   }
   LM_DEV const lm_u32x4* b_row(const LmTile& t, int r) const {
     return (const lm_u32x4*)(w + (size_t)min(t.n0 + r, H - 1) * P);
@@ -519,21 +611,20 @@ struct UnpoolerProb {
   LM_DEV const lm_u32x4* b_group(const LmTile& t, int wv, int j) const {
     return lm_packed_group(w, min(t.n0 + (wv * Cfg::TN + j) * 32, H - 32), P);
   }
-  // pair: logical k-tile 2m + i reads piece i of y's k-tile m and W's k-tile m
-  LM_DEV int a_ktile(int kt) const { return pieces == 2 ? (kt & 1) * (P / Cfg::KT) + (kt >> 1) : kt; }
-  LM_DEV int b_ktile(int kt) const { return pieces == 2 ? kt >> 1 : kt; }
+  LM_DEV int a_ktile(int kt) const { return kt; }
   LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
                        int lane, void*) const {
 #pragma unroll
     for (int tn = 0; tn < Cfg::TN; ++tn) {
       const int col = t.n0 + lm_acc_col<Cfg>(wn, tn, lane);
       if (col >= H) continue;
+      const float d = ds ? ds[col] : 1.0f;
 #pragma unroll
       for (int tm = 0; tm < Cfg::TM; ++tm)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
-          if (row < t.rows) out[(size_t)(t.m0 + row) * H + col] = acc[tm][tn][i];
+          if (row < t.rows) out[(size_t)(t.m0 + row) * H + col] = acc[tm][tn][i] * d;
         }
     }
   }
@@ -542,17 +633,17 @@ struct UnpoolerProb {
 // ------------------------------------------- split-K dense projections
 // For few tokens the pooler / unpooler have too few output tiles to keep the
 // chip streaming weights, so K is split and each split writes FP32 partial
-// sums part[s][row][col]; a finish kernel adds them in split order.
-template <class Cfg_, bool PAIR = false>  // PAIR as for UnpoolerProb
+// sums part[s][row][col] (times ds[col] where the weights are a per-row
+// scaled FP16 copy); a finish kernel adds them in split order.
+template <class Cfg_>
 struct DenseSplitProb {
   using Cfg = Cfg_;
   using E = typename Cfg::E;
-  static constexpr bool kPairB = PAIR;
-  const E* a;   // [T, K] (pieces 2: [T, 2K], hi | lo)
+  const E* a;   // [T, K]
   const E* w;   // packed [N, K]
+  const float* ds = nullptr;  // [N] or none
   float* part;  // [splits, T, N]
   int T, N, K, mt, nt, splits, kt_per;
-  int pieces = 1;  // 2: a is a BF16 pair, K runs over hi and lo k-tiles in turn
 
   LM_DEV bool tile(int bid, LmTile& t) const {
     int L;
@@ -566,18 +657,17 @@ struct DenseSplitProb {
     t.nt = n;
     t.e = s;
     t.kt0 = s * kt_per;
-    t.kt1 = min(pieces * K / Cfg::KT, t.kt0 + kt_per);
+    t.kt1 = min(K / Cfg::KT, t.kt0 + kt_per);
     return true;
   }
-  int lda = 0;  // row stride of a in elements (0: pieces * K)
+  int lda = 0;  // row stride of a in elements (0: K)
   LM_DEV const lm_u32x4* a_row(const LmTile& t, int r) const {
-    return (const lm_u32x4*)(a + (size_t)(t.m0 + min(r, t.rows - 1)) * (lda ? lda : pieces * K));
+    return (const lm_u32x4*)(a + (size_t)(t.m0 + min(r, t.rows - 1)) * (lda ? lda : K));
   }
   LM_DEV const lm_u32x4* b_group(const LmTile& t, int wv, int j) const {
     return lm_packed_group(w, min(t.n0 + (wv * Cfg::TN + j) * 32, N - 32), K);
   }
-  LM_DEV int a_ktile(int kt) const { return pieces == 2 ? (kt & 1) * (K / Cfg::KT) + (kt >> 1) : kt; }
-  LM_DEV int b_ktile(int kt) const { return pieces == 2 ? kt >> 1 : kt; }
+  LM_DEV int a_ktile(int kt) const { return kt; }
   LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
                        int lane, void*) const {
     float* dst = part + ((size_t)t.e * T + t.m0) * N;
@@ -585,24 +675,24 @@ struct DenseSplitProb {
     for (int tn = 0; tn < Cfg::TN; ++tn) {
       const int col = t.n0 + lm_acc_col<Cfg>(wn, tn, lane);
       if (col >= N) continue;
+      const float d = ds ? ds[col] : 1.0f;
 #pragma unroll
       for (int tm = 0; tm < Cfg::TM; ++tm)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
-          if (row < t.rows) dst[(size_t)row * N + col] = acc[tm][tn][i];
+          if (row < t.rows) dst[(size_t)row * N + col] = acc[tm][tn][i] * d;
         }
     }
   }
 };
 
 // Pooler finish, one workgroup per (token, 256 columns): h = sum of the
-// split partials in split order; pooled = BF16(gamma_p * h); the chunk's sum
-// of h^2 (fixed tree over the workgroup) goes to ssq[t][chunk], from which
-// lm_rowscale_kernel forms the row scale exactly as on the unsplit path.
+// split partials in split order; pooled32 = gamma_p * h (FP32); the chunk's
+// sum of h^2 (fixed tree over the workgroup) goes to ssq[t][chunk], from
+// which the row scale is formed exactly as on the unsplit path.
 __global__ __launch_bounds__(256) void lm_pool_finish_kernel(const float* part, int splits, int T,
-                                                             int P, const float* gamma,
-                                                             uint16_t* pooled, float* ssq,
+                                                             int P, const float* gamma, float* ssq,
                                                              float* pooled32) {
   __shared__ float red[256];
   const int t = blockIdx.x, chunk = blockIdx.y, tid = threadIdx.x;
@@ -610,8 +700,7 @@ __global__ __launch_bounds__(256) void lm_pool_finish_kernel(const float* part, 
   float h = 0.0f;
   if (c < P) {
     for (int sp = 0; sp < splits; ++sp) h += part[((size_t)sp * T + t) * P + c];
-    if (pooled32) pooled32[(size_t)t * P + c] = h * gamma[c];
-    else pooled[(size_t)t * P + c] = lm_f32_to_bf16(h * gamma[c]);
+    pooled32[(size_t)t * P + c] = h * gamma[c];
   }
   red[tid] = h * h;
   __syncthreads();
@@ -846,20 +935,53 @@ __global__ __launch_bounds__(256) void lm_permute_kernel(const int* ids, int npa
 }
 
 // r_t = 1 / sqrt(sum of the row's pooled partial sums of squares / P + eps).
+LM_DEV float lm_row_rms_scale(const float* ssq, int nparts, int t, int P, float eps) {
+  float s = 0.0f;
+  for (int i = 0; i < nparts; ++i) s += ssq[(size_t)t * nparts + i];
+  return 1.0f / sqrtf(s / (float)P + eps);
+}
 __global__ void lm_rowscale_kernel(const float* ssq, int nparts, int T, int P, float eps,
                                    float* rs) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
-  float s = 0.0f;
-  for (int i = 0; i < nparts; ++i) s += ssq[(size_t)t * nparts + i];
-  rs[t] = 1.0f / sqrtf(s / (float)P + eps);
+  rs[t] = lm_row_rms_scale(ssq, nparts, t, P, eps);
+}
+
+// Pre-expert RMSNorm for FP16 expert inputs, one token row per workgroup: the
+// row scale r_t as above, then u = FP16(r_t * pooled32), pooled32 = gamma_p * h
+// in FP32 (|u| <= sqrt(P) max|gamma_p|: within FP16's range).
+__global__ __launch_bounds__(256) void lm_norm_u_kernel(const float* pooled32, const float* ssq,
+                                                        int nparts, int P, float eps, float* rs,
+                                                        _Float16* u) {
+  __shared__ float sr;
+  const int t = blockIdx.x;
+  if (threadIdx.x == 0) {
+    const float r = lm_row_rms_scale(ssq, nparts, t, P, eps);
+    sr = r;
+    rs[t] = r;
+  }
+  __syncthreads();
+  const float r = sr;
+  const float* src = pooled32 + (size_t)t * P;
+  for (int c = threadIdx.x * 8; c < P; c += 256 * 8) {
+    const lm_f32x4 a = *(const lm_f32x4*)(src + c) * r;
+    const lm_f32x4 b = *(const lm_f32x4*)(src + c + 4) * r;
+    lm_u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(a[2 * q])) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(a[2 * q + 1])) << 16);
+      o[2 + q] = (uint32_t)__builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(b[2 * q])) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(b[2 * q + 1])) << 16);
+    }
+    *(lm_u32x4*)(u + (size_t)t * P + c) = o;
+  }
 }
 
 // One workgroup per token: y = sum over slots j (in order) of
 // w_j / sqrt(mean(o_j^2) + eps) * gamma_{e_j} * o_j, in FP32. FP32 layers
-// store y [T, P]; BF16 layers store it as a BF16 pair [T, 2P] (hi | lo), which
-// the unpooler reads as a K of 2P (one BF16 rounding of y alone would be a
-// third of the layer's output error).
+// store y [T, P] in FP32, BF16 layers its nearest-even FP16 rounding, the
+// unpooler's operand (|y| <= sqrt(P) max|gamma_e|: within FP16's range).
 template <typename Y>
 __global__ __launch_bounds__(256) void lm_combine_kernel(const float* O, const float* ossq,
                                                          int nparts, const int* pair_row,
@@ -889,22 +1011,14 @@ __global__ __launch_bounds__(256) void lm_combine_kernel(const float* O, const f
     if constexpr (sizeof(Y) == 4) {
       *(lm_f32x4*)((float*)y + (size_t)t * P + c) = acc;
     } else {
-      // BF16 pair y = hi + lo (hi the nearest-even BF16 of y, lo that of the
-      // exact FP32 remainder): 16 significant bits into the unpooler
-      uint16_t hi[4], lo[4];
+      static_assert(std::is_same_v<Y, _Float16>, "FP32 or FP16 y");
+      uint16_t hv[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        hi[q] = lm_f32_to_bf16(acc[q]);
-        lo[q] = lm_f32_to_bf16(acc[q] - lm_bf16_to_f32(hi[q]));
-      }
-      uint16_t* row = (uint16_t*)y + (size_t)t * 2 * P;
-      lm_u32x2 vh, vl;
-      vh[0] = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
-      vh[1] = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
-      vl[0] = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
-      vl[1] = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
-      *(lm_u32x2*)(row + c) = vh;
-      *(lm_u32x2*)(row + P + c) = vl;
+      for (int q = 0; q < 4; ++q) hv[q] = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[q]));
+      lm_u32x2 v;
+      v[0] = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+      v[1] = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+      *(lm_u32x2*)((uint16_t*)y + (size_t)t * P + c) = v;
     }
   }
 }

@@ -1,7 +1,11 @@
 // Host runtime and C ABI of the latent-MoE layer forward (see include/latent_moe.h).
 //
 // create(): validate, allocate one workspace sized by max_tokens, split the
-// FP32 router into three BF16 pieces (BF16 activations). forward(): enqueue
+// FP32 router into three BF16 pieces and repack the weights into the
+// matrix-core layout (BF16 activations: the pooler in BF16, the expert and
+// unpooler weights as FP16 copies scaled per row by a power of two, or
+// MXFP4 codes with that power of two per row, so that the expert and
+// unpooler GEMMs run on FP16 operands u, a and y). forward(): enqueue
 // the kernel sequence on the caller's stream with no host synchronisation and
 // no allocation; per-expert tile counts stay on the device and the grouped
 // GEMMs are launched with upper-bound grids whose surplus blocks exit.
@@ -63,7 +67,7 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 struct Layout {
   size_t part, logits, ids, wts, counts, offsets, tile_off, perm_token, pair_row, pooled, pssq,
-      row_scale, act, O, ossq, y, wr3, kpart, xn, xna, uq, us, acts, total;
+      row_scale, act, O, ossq, y, wr3, kpart, xn, xna, uq, us, acts, u16, total;
 };
 
 // Split-K plan for a dense BF16 projection: split only when the output tiles
@@ -103,6 +107,10 @@ struct latent_moe {
   const void* pk_sgate;  // MXFP4: packed scales
   const void* pk_sup;
   const void* pk_sdown;
+  const float* ds_gate;  // 2^-s per weight row of the FP16 / MXFP4 copies
+  const float* ds_up;
+  const float* ds_down;
+  const float* ds_unpooler;
   hipStream_t side;                // routing (router, top-k, grouping) runs here, beside the pooler
   hipEvent_t fork, join;           // order the side stream after the caller's and back
   bool prof;                       // record stage events in forward
@@ -212,13 +220,13 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
   L.pair_row = take((size_t)Mp * 4);
   const bool mxa = c.expert_act != 0;
   const size_t abits = c.expert_act == LMOE_MXFP8 ? 8 : 4;
-  L.pooled = take((size_t)Tm * P * (mxa ? 4 : esize_act(c)));  // MX acts: FP32 gamma_p * h
+  L.pooled = take((size_t)Tm * P * 4);  // gamma_p * h, FP32
   L.pssq = take((size_t)Tm * parts * 4);
   L.row_scale = take((size_t)Tm * 4);
   L.act = take((size_t)Mp * I * esize_exp(c));
   L.O = take((size_t)Mp * P * 4);
   L.ossq = take((size_t)Mp * parts * 4);
-  L.y = take((size_t)Tm * P * 4);  // FP32 [T, P], or the BF16 pair [T, 2P]
+  L.y = take((size_t)Tm * P * esize_act(c));  // FP32 or FP16 [T, P]
   L.wr3 = take(c.act_dtype == LMOE_BF16 ? (size_t)E * 3 * c.hidden * 2 : 0);
   size_t kp = 0;
   if (c.act_dtype == LMOE_BF16) {
@@ -228,7 +236,7 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
       int sp, kpt;
       dense_split(T, P, c.hidden, BM, BN, sp, kpt);
       if (sp > 1 && (size_t)sp * T * P > kp) kp = (size_t)sp * T * P;
-      dense_split(T, c.hidden, 2 * P, BM, BN, sp, kpt);
+      dense_split(T, c.hidden, P, BM, BN, sp, kpt);
       if (sp > 1 && (size_t)sp * T * c.hidden > kp) kp = (size_t)sp * T * c.hidden;
     }
   }
@@ -238,6 +246,7 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
   L.acts = take(mxa ? (size_t)Mp * I / 32 : 0);        // E8M0 scales of the MX act codes (in act)
   L.xn = take(c.input_norm && c.act_dtype == LMOE_F32 ? (size_t)Tm * c.hidden * 4 : 0);
   L.xna = take(c.input_norm && c.act_dtype == LMOE_BF16 ? (size_t)Tm * 3 * c.hidden * 2 : 0);
+  L.u16 = take(c.act_dtype == LMOE_BF16 && !mxa ? (size_t)Tm * P * 2 : 0);  // FP16 u
   L.total = o;
   return L;
 }
@@ -287,6 +296,10 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   const void* Wdown = packed ? h->pk_down : w.w_down;
   using Cw = CW<Et>;
   using Cr = CR<Et>;
+  // expert and unpooler operands: FP16 in BF16 layers, FP32 in FP32 layers
+  constexpr bool F16 = sizeof(Et) == 2;
+  using Eh = std::conditional_t<F16, _Float16, Et>;
+  using Ch = CW<Eh>;
   double* part = (double*)(ws + L.part);
   float* logits = (float*)(ws + L.logits);
   int* ids = (int*)(ws + L.ids);
@@ -296,13 +309,15 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   int* tile_off = (int*)(ws + L.tile_off);
   int* perm_token = (int*)(ws + L.perm_token);
   int* pair_row = (int*)(ws + L.pair_row);
-  Et* pooled = (Et*)(ws + L.pooled);
+  Et* pooled = (Et*)(ws + L.pooled);  // FP32 layers: gamma_p * h; BF16 layers: unused
+  float* pooled32 = (float*)(ws + L.pooled);  // BF16 layers: gamma_p * h in FP32
   float* pssq = (float*)(ws + L.pssq);
   float* row_scale = (float*)(ws + L.row_scale);
-  Et* act = (Et*)(ws + L.act);
+  Eh* u16 = (Eh*)(ws + L.u16);  // BF16 layers without MX inputs: the FP16 u
+  Eh* act = (Eh*)(ws + L.act);
   float* O = (float*)(ws + L.O);
   float* ossq = (float*)(ws + L.ossq);
-  Et* y = (Et*)(ws + L.y);
+  Eh* y = (Eh*)(ws + L.y);
 
   LM_MARK(0);
   // 0. boundary norm (optional): x is the pre-norm residual. FP32 layers: the
@@ -410,16 +425,20 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     LM_MARK(5);
     const int chunks = ceil_div(P, 256);
     hipLaunchKernelGGL(lm_pool_finish_kernel, dim3((unsigned)T, (unsigned)chunks), dim3(256), 0, s,
-                       (const float*)(ws + L.kpart), psplits, (int)T, P, w.pool_gamma,
-                       (uint16_t*)pooled, pssq, MXA ? (float*)pooled : nullptr);
+                       (const float*)(ws + L.kpart), psplits, (int)T, P, w.pool_gamma, pssq, pooled32);
     LM_HIP(hipGetLastError());
-    hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, pssq, chunks,
-                       (int)T, P, c.eps, row_scale);
+    if (MXA) {
+      hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, pssq, chunks,
+                         (int)T, P, c.eps, row_scale);
+    } else {
+      hipLaunchKernelGGL(lm_norm_u_kernel, dim3((unsigned)T), dim3(256), 0, s, pooled32, pssq, chunks,
+                         P, c.eps, row_scale, (_Float16*)u16);
+    }
     LM_HIP(hipGetLastError());
     }
   } else {
     PoolerProb<Cw> p;
-    if (MXA) p.pooled32 = (float*)pooled;
+    if (F16) p.pooled32 = pooled32;
     p.x = xp;
     p.lda = xp_ld;
     p.w = (const Et*)Wpool;
@@ -433,14 +452,20 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.nt = pnt;
     LM_HIP(launch(p, (int64_t)p.mt * p.nt, s));
     LM_MARK(5);
-    hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, pssq, pnt,
-                       (int)T, P, c.eps, row_scale);
+    if (F16 && !MXA) {
+      if constexpr (F16)
+        hipLaunchKernelGGL(lm_norm_u_kernel, dim3((unsigned)T), dim3(256), 0, s, pooled32, pssq, pnt,
+                           P, c.eps, row_scale, u16);
+    } else {
+      hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, pssq, pnt,
+                         (int)T, P, c.eps, row_scale);
+    }
     LM_HIP(hipGetLastError());
   }
   if constexpr (MXA) {  // u = r * gamma_p * h MX-quantised for the expert GEMMs
     const int64_t nthr = T * (int64_t)(P / 32) * 8;
     hipLaunchKernelGGL(lm_quant_u_kernel<AB>, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s,
-                       (const float*)pooled, row_scale, (int)T, P, (uint8_t*)(ws + L.uq),
+                       pooled32, row_scale, (int)T, P, (uint8_t*)(ws + L.uq),
                        (uint8_t*)(ws + L.us));
     LM_HIP(hipGetLastError());
   }
@@ -452,7 +477,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     GateUpMxaProb<Cw, AB> p;
     p.sg = h->pk_sgate;
     p.su = h->pk_sup;
-    p.pooled = pooled;
+    p.pooled = (const Et*)pooled32;
     p.wg = (const Et*)Wgate;
     p.wu = (const Et*)Wup;
     p.row_scale = row_scale;
@@ -460,7 +485,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.counts = counts;
     p.offsets = offsets;
     p.tile_off = tile_off;
-    p.act = act;
+    p.act = (Et*)act;
     p.P = P;
     p.I = I;
     p.Ex = E;
@@ -471,14 +496,20 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.as = (uint8_t*)(ws + L.acts);
     LM_HIP(launch_mxa(p, max_tiles * p.nt, s));
   } else {
-    GateUpProb<Cw, MX> p;
+    GateUpProb<Ch, MX> p;
     if constexpr (MX) {
       p.sg = h->pk_sgate;
       p.su = h->pk_sup;
     }
-    p.pooled = pooled;
-    p.wg = (const Et*)Wgate;
-    p.wu = (const Et*)Wup;
+    if constexpr (F16) {
+      p.dsg = h->ds_gate;
+      p.dsu = h->ds_up;
+      p.pooled = u16;
+    } else {
+      p.pooled = (const Eh*)pooled;
+    }
+    p.wg = (const Eh*)Wgate;
+    p.wu = (const Eh*)Wup;
     p.row_scale = row_scale;
     p.perm_token = perm_token;
     p.counts = counts;
@@ -488,7 +519,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.P = P;
     p.I = I;
     p.Ex = E;
-    p.nt = I / GateUpProb<Cw, MX>::kCols;
+    p.nt = I / GateUpProb<Ch, MX>::kCols;
     LM_HIP(launch(p, max_tiles * p.nt, s));
   }
   LM_MARK(7);
@@ -497,7 +528,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   if constexpr (MXA) {
     DownMxaProb<Cw, AB> p;
     p.sd = h->pk_sdown;
-    p.act = act;
+    p.act = (const Et*)act;
     p.wd = (const Et*)Wdown;
     p.counts = counts;
     p.offsets = offsets;
@@ -512,10 +543,11 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.as = (const uint8_t*)(ws + L.acts);
     LM_HIP(launch_mxa(p, max_tiles * p.nt, s));
   } else {
-    DownProb<Cw, MX> p;
+    DownProb<Ch, MX> p;
     if constexpr (MX) p.sd = h->pk_sdown;
+    if constexpr (F16) p.dsd = h->ds_down;
     p.act = act;
-    p.wd = (const Et*)Wdown;
+    p.wd = (const Eh*)Wdown;
     p.counts = counts;
     p.offsets = offsets;
     p.tile_off = tile_off;
@@ -529,24 +561,23 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   }
   LM_MARK(8);
   // 7. per-expert norm, routing weight, FP32 sum
-  hipLaunchKernelGGL(lm_combine_kernel<Et>, dim3((unsigned)T), dim3(256), 0, s, O, ossq, dnt, pair_row,
+  hipLaunchKernelGGL(lm_combine_kernel<Eh>, dim3((unsigned)T), dim3(256), 0, s, O, ossq, dnt, pair_row,
                      ids, wts, w.expert_gamma, k, P, c.eps, y);
   LM_HIP(hipGetLastError());
   LM_MARK(9);
-  // 8. unpooler (BF16 layers: y as its BF16 pair, K = 2P)
-  const int ypieces = sizeof(Et) == 2 ? 2 : 1;
+  // 8. unpooler (BF16 layers: FP16 y against the per-row scaled FP16 copy of W)
   int usplits = 1, ukt = 0;
-  if (packed) dense_split(T, H, ypieces * P, Cw::BM, Cw::BN, usplits, ukt);
+  if (packed) dense_split(T, H, P, Cw::BM, Cw::BN, usplits, ukt);
   if (usplits > 1) {
-    if constexpr (sizeof(Et) == 2) {
-    DenseSplitProb<Cw, true> p;  // the BF16 pair: W k-tiles shared by hi and lo
+    if constexpr (F16) {
+    DenseSplitProb<Ch> p;
     p.a = y;
-    p.w = (const Et*)Wunpool;
+    p.w = (const Eh*)Wunpool;
+    p.ds = h->ds_unpooler;
     p.part = (float*)(ws + L.kpart);
     p.T = (int)T;
     p.N = H;
     p.K = P;
-    p.pieces = ypieces;
     p.mt = ceil_div(T, Cw::BM);
     p.nt = ceil_div(H, Cw::BN);
     p.splits = usplits;
@@ -558,14 +589,14 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     LM_HIP(hipGetLastError());
     }
   } else {
-    UnpoolerProb<Cw, sizeof(Et) == 2> p;  // BF16 layers: y is the pair
+    UnpoolerProb<Ch> p;
     p.y = y;
-    p.w = (const Et*)Wunpool;
+    p.w = (const Eh*)Wunpool;
+    if constexpr (F16) p.ds = h->ds_unpooler;
     p.out = out;
     p.T = (int)T;
     p.H = H;
     p.P = P;
-    p.pieces = ypieces;
     p.mt = ceil_div(T, Cw::BM);
     p.nt = ceil_div(H, Cw::BN);
     LM_HIP(launch(p, (int64_t)p.mt * p.nt, s));
@@ -646,7 +677,9 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
     const bool mx = cfg->expert_dtype == LMOE_MXFP4;
     const size_t sz_pool = H * P * 2, sz_exp = mx ? E * I * P / 2 : E * I * P * 2;
     const size_t sz_sc = mx ? E * I * P / 32 : 0;
-    h->packed_bytes = 2 * sz_pool + 3 * sz_exp + 3 * sz_sc;
+    // per weight row 2^-s: gate, up [E*I], down [E*P], unpooler [H] (FP32)
+    const size_t n_ds = 2 * E * I + E * P + H;
+    h->packed_bytes = 2 * sz_pool + 3 * sz_exp + 3 * sz_sc + n_ds * 4;
     he = hipMalloc((void**)&h->packed, h->packed_bytes);
     if (he != hipSuccess) {
       (void)hipGetLastError();
@@ -662,19 +695,35 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
     h->pk_sgate = h->packed + 2 * sz_pool + 3 * sz_exp;
     h->pk_sup = h->packed + 2 * sz_pool + 3 * sz_exp + sz_sc;
     h->pk_sdown = h->packed + 2 * sz_pool + 3 * sz_exp + 2 * sz_sc;
-    struct Job { const void* src; const void* src_s; const void* dst; const void* dst_s; int64_t rows; int K; bool mx; };
-    const Job jobs[] = {{w->pooler, nullptr, h->pk_pooler, nullptr, (int64_t)P, (int)H, false},
-                        {w->unpooler, nullptr, h->pk_unpooler, nullptr, (int64_t)H, (int)P, false},
-                        {w->w_gate, w->s_gate, h->pk_gate, h->pk_sgate, (int64_t)(E * I), (int)P, mx},
-                        {w->w_up, w->s_up, h->pk_up, h->pk_sup, (int64_t)(E * I), (int)P, mx},
-                        {w->w_down, w->s_down, h->pk_down, h->pk_sdown, (int64_t)(E * P), (int)I, mx}};
+    float* ds = (float*)(h->packed + 2 * sz_pool + 3 * sz_exp + 3 * sz_sc);
+    h->ds_gate = ds;
+    h->ds_up = ds + E * I;
+    h->ds_down = ds + 2 * E * I;
+    h->ds_unpooler = ds + 2 * E * I + E * P;
+    // The pooler stays BF16 (x is BF16). The unpooler and BF16 experts become
+    // FP16 copies scaled per row by 2^s; MXFP4 experts keep their codes and
+    // get the per-row 2^s applied when they are decoded.
+    struct Job { const void* src; const void* src_s; const void* dst; const void* dst_s; int64_t rows; int K;
+                 bool mx; const float* ds; };
+    const Job jobs[] = {
+        {w->pooler, nullptr, h->pk_pooler, nullptr, (int64_t)P, (int)H, false, nullptr},
+        {w->unpooler, nullptr, h->pk_unpooler, nullptr, (int64_t)H, (int)P, false, h->ds_unpooler},
+        {w->w_gate, w->s_gate, h->pk_gate, h->pk_sgate, (int64_t)(E * I), (int)P, mx, h->ds_gate},
+        {w->w_up, w->s_up, h->pk_up, h->pk_sup, (int64_t)(E * I), (int)P, mx, h->ds_up},
+        {w->w_down, w->s_down, h->pk_down, h->pk_sdown, (int64_t)(E * P), (int)I, mx, h->ds_down}};
     for (const Job& j : jobs) {
-      if (j.mx)
+      if (j.mx) {
+        hipLaunchKernelGGL(lm_row_descale_mx_kernel, dim3((unsigned)((j.rows + 255) / 256)), dim3(256), 0, 0,
+                           (const uint8_t*)j.src_s, j.rows, j.K, (float*)j.ds);
         hipLaunchKernelGGL(lm_pack_mx_kernel, dim3(65536), dim3(256), 0, 0, (const lm_u32x4*)j.src,
                            (const uint8_t*)j.src_s, (lm_u32x4*)j.dst, (uint8_t*)j.dst_s, j.rows, j.K);
-      else
+      } else {
+        if (j.ds)
+          hipLaunchKernelGGL(lm_row_descale_bf16_kernel, dim3((unsigned)((j.rows + 3) / 4 < 65536 ? (j.rows + 3) / 4 : 65536)),
+                             dim3(256), 0, 0, (const uint16_t*)j.src, j.rows, j.K, (float*)j.ds);
         hipLaunchKernelGGL(lm_pack_mfma_kernel, dim3(65536), dim3(256), 0, 0, (const lm_u32x4*)j.src,
-                           (lm_u32x4*)j.dst, j.rows, j.K);
+                           (lm_u32x4*)j.dst, j.rows, j.K, j.ds);
+      }
     }
     const size_t n = (size_t)cfg->experts * cfg->hidden;
     unsigned blocks = (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
@@ -771,7 +820,8 @@ int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v) {
   v->expert_out = (const float*)(ws + L.O);
   v->combined = ws + L.y;
   const bool mxa = h->cfg.expert_act != 0;
-  v->expert_in = mxa ? (const uint8_t*)(ws + L.uq) : nullptr;
+  v->expert_in = mxa ? (const uint8_t*)(ws + L.uq)
+                 : h->cfg.act_dtype == LMOE_BF16 ? (const uint8_t*)(ws + L.u16) : nullptr;
   v->expert_in_scales = mxa ? (const uint8_t*)(ws + L.us) : nullptr;
   v->act_scales = mxa ? (const uint8_t*)(ws + L.acts) : nullptr;
   v->x_norm = !h->cfg.input_norm ? nullptr

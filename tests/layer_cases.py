@@ -104,6 +104,20 @@ def bf16_to_f64(a):
     return to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
 
 
+def check_expert_input(v: dict, rows, ref_u: np.ndarray) -> float:
+    """BF16 layers: the pooler's FP32 gamma_p * h times the row scale equals
+    the oracle's u to FP32 accumulation error, and the FP16 u the expert
+    GEMMs read is its nearest FP16 value (relative error <= 2^-11, plus the
+    same absolute slack). Returns the largest relative error of the FP16 u."""
+    u32 = v["pooled"][rows].astype(np.float64) * v["row_scale"][rows, None]
+    d32 = np.abs(u32 - ref_u)
+    assert np.all(d32 <= 2.0 ** -20 * np.abs(ref_u) + 2e-5), f"pooled * row_scale: max abs error {d32.max():.3g}"
+    u16 = v["expert_in"][rows].astype(np.float64)
+    d16 = np.abs(u16 - ref_u)
+    assert np.all(d16 <= 2.0 ** -10 * np.abs(ref_u) + 2e-5), f"FP16 u: max abs error {d16.max():.3g}"
+    return float((d16 / (np.abs(ref_u) + 1e-30)).max())
+
+
 def mx_rounding_ties(uq_gpu: np.ndarray, r, fmt: str, rel: float = 1e-4) -> dict:
     """MX-quantised u from the kernel against the oracle's: where they differ,
     check that the oracle's unquantised value lies on the midpoint between the

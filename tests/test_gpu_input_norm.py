@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 
 import synth
-from layer_cases import HostLayer, bf16_to_f64, check_output, check_rel_l2, check_routing, device_weights
+from layer_cases import (HostLayer, bf16_to_f64, check_expert_input, check_output, check_rel_l2, check_routing,
+                         device_weights)
 from oracle import oracle as orc
 from oracle.mx import to_f64
 
@@ -159,8 +160,7 @@ def test_real_input_norm_sampled_parity(torch_dev, tables, real_norm, wl, T):
     ref = host.oracle(rh[sample], input_gamma=gin, force_ids=force or None)
     assert np.array_equal(ids[sample], ref.ids)
     pr = v["pair_row"].reshape(T, spec.k)[sample]
-    u = bf16_to_f64(v["pooled"][sample]) * v["row_scale"][sample, None]
-    assert np.all(np.abs(u - ref.u) <= 2.0 ** -8 * np.abs(ref.u) + 1e-5)
+    check_expert_input(v, sample, ref.u)
     check_rel_l2(bf16_to_f64(v["act"][pr]), ref.a, 1e-2, "act")
     e = check_output(out[sample], ref.out, 2e-2)
     say(f"{wl} norm: x_norm {nd} elements 1 ulp off; max |logit err| {dl.max():.3g}; "

@@ -4,7 +4,8 @@ Tiny FP32 layer: every token, every stage. Real shapes (H=8192, P=4096,
 E=256, I=4096, k=8, BF16): routing on every token; outputs and stage
 intermediates on every token of the 64-token decode batches and on sampled
 tokens of the prefill batches (the layer is token-local, so the oracle on a
-token subset is exact for those rows).
+token subset is exact for those rows), and once every token of the 16384-token
+batch.
 
 MXFP4 expert weights: the same real shapes, compared with the oracle run on
 the identically decoded weights.
@@ -20,16 +21,17 @@ import numpy as np
 import pytest
 
 import synth
-from layer_cases import (HostLayer, bf16_to_f64, check_output, check_rel_l2, check_routing,
-                         device_weights, make_layer, mx_rounding_ties)
+from layer_cases import (HostLayer, bf16_to_f64, check_expert_input, check_output, check_rel_l2,
+                         check_routing, device_weights, make_layer, mx_rounding_ties)
 from oracle import mx as mx_mod
 from oracle import oracle as orc
+from oracle.mx import to_f64
 
 pytestmark = pytest.mark.gpu
 
 TOL_BF16 = 2e-2
 TOL_F32 = 1e-4
-STAGE_L2 = 1e-2  # relative L2 bound for BF16 intermediates (expected ~1e-3)
+STAGE_L2 = 1e-2  # relative L2 bound for FP16 intermediates (expected ~1e-4)
 
 
 def say(*a):
@@ -237,10 +239,7 @@ def _sampled_parity(torch, spec, layer, host, x_dev, xh, sample, tol, chunk_labe
     r = host.oracle(xh[sample], force_ids=force or None)
     assert np.array_equal(ids[sample], r.ids)
     pr = v["pair_row"].reshape(T, spec.k)[sample]
-    u = bf16_to_f64(v["pooled"][sample]) * v["row_scale"][sample, None]
-    # one BF16 rounding of gamma_p * h: relative error <= 2^-9 per element
-    eu = float((np.abs(u - r.u) / (np.abs(r.u) + 1e-30)).max())
-    assert np.all(np.abs(u - r.u) <= 2.0 ** -8 * np.abs(r.u) + 1e-5), f"u: max relative error {eu:.3g}"
+    eu = check_expert_input(v, sample, r.u)
     ea = check_rel_l2(bf16_to_f64(v["act"][pr]), r.a, STAGE_L2, "act")
     eo = check_rel_l2(v["expert_out"][pr], r.o, STAGE_L2, "expert out")
     ey = check_rel_l2(bf16_to_f64(v["combined"][sample]), r.y, STAGE_L2, "y")
@@ -283,6 +282,41 @@ def test_prefill_parity(torch_dev, tables, real, T):
     sample = np.sort(np.random.default_rng(T).choice(T, 4, replace=False))
     sample[-1] = T - 1  # ragged tail
     _sampled_parity(torch, spec, layer, host, x, xh, sample, TOL_BF16, f"prefill T={T}")
+
+
+def test_prefill_every_token(torch_dev, tables, real):
+    """The whole 16384-token batch against the oracle, every token and every
+    output element: max-abs error <= 2e-2 x RMS over all of them (with FP16
+    expert operands the largest is expected near 5e-3). The oracle reads the
+    seeded expert weights from their device copies, which equal the host
+    generator's bit for bit (test_device_generator_matches_host)."""
+    torch = torch_dev
+    spec, wts, layer, host = real
+    T = spec.T
+    say(f"case: prefill BF16, T={T}, every token")
+    x = synth.device_tensor(spec, "x", tables)
+    out, ids, w = run_layer(torch, layer, x)
+    xh = synth.host(spec, "x")
+    near, _ = check_routing(ids, w, host.logits(xh), spec.k)
+
+    def bits(t):
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def expert(e):
+        return tuple(to_f64(bits(wts[n][e])) for n in ("w_gate", "w_up", "w_down"))
+
+    force = {int(t): ids[t] for t in near}
+    hw = host.w
+    r = orc.forward(xh, hw["router"], hw["router_bias"], hw["pooler"], hw["pool_gamma"], expert,
+                    hw["expert_gamma"], hw["unpooler"], spec.k, spec.eps, force_ids=force or None,
+                    keep_pairs=False)
+    assert np.array_equal(ids, r.ids)
+    rms = float(np.sqrt(np.mean(r.out ** 2)))
+    per_tok = np.abs(out.astype(np.float64) - r.out).max(axis=1) / rms
+    q = np.quantile(per_tok, [0.5, 0.99, 0.999])
+    say(f"prefill every token: per-token max-abs / RMS median {q[0]:.3g}, p99 {q[1]:.3g}, "
+        f"p99.9 {q[2]:.3g}, max {per_tok.max():.3g} (token {int(per_tok.argmax())}); near-ties {near}")
+    assert per_tok.max() <= TOL_BF16
 
 
 def test_skewed_chunk_parity(torch_dev, tables, real):
