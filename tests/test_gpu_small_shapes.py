@@ -179,3 +179,74 @@ def test_small_mx_activations_parity(torch_dev, tables, name, fmt, T, norm):
         say(f"{name}: u flips {frac:.2e}; out max-abs {e:.3g} x RMS over all {T} tokens")
     finally:
         layer.close()
+
+
+# ------------------------------- weight rows of very different magnitudes
+
+ROW_CASES = [("bf16 wide", "bf16", 300), ("bf16 narrow", "bf16", 100), ("mxfp4 wide", "mxfp4", 300)]
+
+
+@pytest.mark.parametrize("name,fmt,T", ROW_CASES, ids=[c[0] for c in ROW_CASES])
+def test_small_row_magnitudes(torch_dev, tables, name, fmt, T):
+    """Every weight row of the expert and unpooler matrices scaled by its own
+    power of two 2^k (gate/up rows k in [-8, 3], down rows [-10, 10], unpooler
+    rows [-30, 30]; exact in BF16 and, for MXFP4, an offset of the row's E8M0
+    codes). The FP16 copies take each row's own 2^s, so the layer matches the
+    oracle on the scaled weights: routing exact, every output element within
+    2e-2 x RMS after dividing each unpooler column by its 2^k (so the rows of
+    2^-30 are checked as tightly as those of 2^30). Gate/up rows stay at most
+    2^3 up: the SwiGLU output a is an FP16 operand and saturates at 65504
+    (here |a| stays below ~2e3)."""
+    torch = torch_dev
+    from latent_moe_layer_fp32_amd import LatentMoE
+    from oracle import oracle as orc
+    from oracle.mx import to_f64
+
+    spec = synth.CONFIGS["decode"].with_(name="small", T=T, E=16, k=4, expert_format=fmt, **SMALL)
+    E, H, P, I = spec.E, spec.H, spec.P, spec.I
+    say(f"case: row magnitudes, {name}, T={T}")
+    rng = np.random.default_rng(21)
+    kexp = {"w_gate": rng.integers(-8, 4, size=(E, I)), "w_up": rng.integers(-8, 4, size=(E, I)),
+            "w_down": rng.integers(-10, 11, size=(E, P))}
+    kun = rng.integers(-30, 31, size=H)
+    wts = device_weights(spec, tables)
+    dev = wts["pooler"].device
+    for n, k in kexp.items():
+        if fmt == "mxfp4":  # 2^k on a row = k added to each of its E8M0 scale codes
+            codes, sc = wts[n]
+            wts[n] = (codes, (sc.int() + torch.from_numpy(k).to(dev)[..., None].int()).to(torch.uint8))
+        else:
+            f = torch.from_numpy(np.ldexp(1.0, k).astype(np.float32)).to(dev)
+            wts[n] = (wts[n].float() * f[..., None]).to(torch.bfloat16)
+    fu = torch.from_numpy(np.ldexp(1.0, kun).astype(np.float32)).to(dev)
+    wts["unpooler"] = (wts["unpooler"].float() * fu[:, None]).to(torch.bfloat16)
+    layer = LatentMoE(hidden=H, pooled=P, experts=E, intermediate=I, top_k=spec.k, eps=spec.eps,
+                      act_dtype=spec.act_dtype, expert_dtype=fmt, max_tokens=512, weights=wts)
+    try:
+        x = synth.device_tensor(spec, "x", tables)
+        ids_d = torch.empty((T, spec.k), dtype=torch.int32, device=x.device)
+        w_d = torch.empty((T, spec.k), dtype=torch.float32, device=x.device)
+        out = layer.forward(x, topk_ids=ids_d, topk_weights=w_d)
+        torch.cuda.synchronize()
+        out, ids, w = out.cpu().numpy(), ids_d.cpu().numpy(), w_d.cpu().numpy()
+    finally:
+        layer.close()
+    host = HostLayer(spec)
+
+    def expert(e):
+        return tuple(to_f64(_first(synth.host(spec, n, experts=(e, e + 1)))) * np.ldexp(1.0, kexp[n][e])[:, None]
+                     for n in ("w_gate", "w_up", "w_down"))
+
+    xh = host.x()
+    hw = host.w
+    near, _ = check_routing(ids, w, host.logits(xh), spec.k)
+    force = {int(t): ids[t] for t in near}
+    r = orc.forward(xh, hw["router"], None, hw["pooler"], hw["pool_gamma"], expert, hw["expert_gamma"],
+                    hw["unpooler"], spec.k, spec.eps, force_ids=force or None, keep_pairs=False)
+    assert np.array_equal(ids, r.ids)
+    e = check_output(np.ldexp(out.astype(np.float64), -kun[None, :]), r.out, 2e-2)
+    say(f"row magnitudes, {name}: out max-abs {e:.3g} x RMS over all {T} tokens (columns divided by 2^k)")
+
+
+def _first(a):
+    return (a[0][0], a[1][0]) if isinstance(a, tuple) else a[0]
