@@ -75,7 +75,7 @@ struct LmGemmCfg {
   static constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   static constexpr int FLUSH = FLUSH_;
   static constexpr int KT = 8 * LmElem<E>::kPerChunk;  // elements per k-tile
-  static_assert(WM * WN == 4, "four wavefronts per workgroup");
+  static_assert(WM * WN == 4 || (WM == 1 && WN == 8), "four wavefronts per workgroup, or eight along N");
 };
 
 struct LmTile {
@@ -176,6 +176,7 @@ LM_DEV void lm_dense_order(int L, int mt, int nt, int GM, int& m, int& n) {
 template <class Prob>
 __global__ __launch_bounds__(256) void lm_gemm_kernel(const Prob p) {
   using Cfg = typename Prob::Cfg;
+  static_assert(Cfg::WM * Cfg::WN == 4, "four wavefronts");
   using El = LmElem<typename Cfg::E>;
   constexpr int TM = Cfg::TM, TN = Cfg::TN;
   constexpr int QA = Cfg::BM / 32, QB = Cfg::BN / 32;

@@ -2,8 +2,8 @@
 // accumulation).
 //
 // Same problem interface and accumulator layout as lm_gemm_kernel, with all
-// four wavefronts side by side along N (WM = 1): every wave needs the whole
-// A tile and its own 32*TN rows of B, so
+// four (or eight) wavefronts side by side along N (WM = 1): every wave needs
+// the whole A tile and its own 32*TN rows of B, so
 //   * A (activations) is staged through LDS: loaded into registers four
 //     k-tiles ahead, written to the LDS double buffer two k-tiles ahead, and
 //     read into fragment registers one MFMA step ahead;
@@ -21,7 +21,9 @@
 // Per 64-wide k-tile a wave issues TM*TN*4 32x32x16 MFMAs and reads
 // only A from LDS: with TM = 4 that is about 64 B/clk/CU of LDS reads at full
 // matrix rate, against ~135 B/clk measured on MI355X, where a 64x64 wave tile
-// reading both operands from LDS needs twice that and becomes LDS-bound.
+// reading both operands from LDS needs twice that and becomes LDS-bound. Eight
+// waves along N share each A tile twice as widely: the same LDS reads per
+// MFMA, half the A loads per MFMA.
 //
 // The K bijection: lane half h (lane / 32) at step s consumes the 16-byte
 // chunk 4h + s of the 128-byte k-tile row, for A and B alike, so each lane
@@ -49,12 +51,13 @@ LM_DEV float lm_e8m0_shifted(uint32_t code, int s) {
   return code == 255 ? __uint_as_float(0x7fc00000u) : ex >= 1 ? __uint_as_float((uint32_t)ex << 23) : 0.0f;
 }
 
-// The register budget allows two workgroups per CU (see kLeanA, kLeanB below).
+// The register budget allows two waves per SIMD: two four-wave workgroups
+// per CU, or one eight-wave workgroup (see kLeanA, kLeanB below).
 template <class Prob>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LM_WAVES_MAX, LM_WAVES_MAX)))
+__global__ __launch_bounds__(64 * Prob::Cfg::WN) __attribute__((amdgpu_waves_per_eu(LM_WAVES_MAX, LM_WAVES_MAX)))
 void lm_gemm_stream_kernel(const Prob p) {
   using Cfg = typename Prob::Cfg;
-  static_assert(Cfg::WM == 1 && Cfg::WN == 4, "streaming-B layout: four waves along N");
+  static_assert(Cfg::WM == 1 && (Cfg::WN == 4 || Cfg::WN == 8), "streaming-B layout: four or eight waves along N");
   static_assert(sizeof(typename Cfg::E) == 2, "16-bit operands");
   constexpr bool kMx = LmIsMx<Prob>::value;
   static_assert(!kMx || std::is_same_v<typename Cfg::E, _Float16>, "MXFP4 weights decode to FP16");
@@ -75,8 +78,10 @@ void lm_gemm_stream_kernel(const Prob p) {
   constexpr int kDistB = kLeanB ? 1 : 3, kDistA = kLeanA ? 2 : 4;
   constexpr int kBq = kMx ? 1 : 4;  // 16-byte B loads per 32-row group and k-tile
   constexpr bool kNT = TM == 1 && LmWeightsOnce<Prob>::value;  // streaming weight loads
+  constexpr int NT = 64 * Cfg::WN;  // threads
+  constexpr int RS = NT / 8;        // A rows per pass of the workgroup (8 chunks per row)
   constexpr int kStage = BM * 8;    // 16-byte chunks per A stage
-  constexpr int QA = BM * 8 / 256;  // A chunks per thread per k-tile (= TM)
+  constexpr int QA = BM * 8 / NT;   // A chunks per thread per k-tile
   __shared__ lm_u32x4 sa[2 * kStage];
 
   LmTile t;
@@ -89,10 +94,10 @@ void lm_gemm_stream_kernel(const Prob p) {
     if (tid < BM) rowv = p.row_value(t, tid);
   const int lc = tid & 7, lr = tid >> 3;
 
-  // A: thread loads chunk lc of tile rows lr + 32 q.
+  // A: thread loads chunk lc of tile rows lr + RS q.
   const lm_u32x4* asrc[QA];
 #pragma unroll
-  for (int q = 0; q < QA; ++q) asrc[q] = p.a_row(t, lr + 32 * q);
+  for (int q = 0; q < QA; ++q) asrc[q] = p.a_row(t, lr + RS * q);
   // B: wave w's j-th 32-row group in the packed layout. BF16: the fragment
   // of step s of k-tile kt is 1 KB at (kt*4 + s)*64 chunks. MXFP4: all four
   // steps of k-tile kt are 1 KB at kt*64 chunks, scales a dword per lane per
@@ -122,7 +127,7 @@ void lm_gemm_stream_kernel(const Prob p) {
   };
   auto store_a = [&](int slot, int buf) {
 #pragma unroll
-    for (int q = 0; q < QA; ++q) sa[buf * kStage + lm_swz(lr + 32 * q, lc)] = ra[slot][q];
+    for (int q = 0; q < QA; ++q) sa[buf * kStage + lm_swz(lr + RS * q, lc)] = ra[slot][q];
   };
   auto load_b = [&](int slot, int kt) {
     const int kc = lm_b_ktile(p, min(kt, klast));

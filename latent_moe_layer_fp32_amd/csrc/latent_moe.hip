@@ -47,14 +47,23 @@ int fail(int code, const char* fmt, ...) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Tile configurations: "wide" for many rows per expert (prefill-sized),
-// "narrow" for few (decode-sized). BF16 runs the streaming-B kernel (four
-// waves along N, BN = 256); FP32 runs the LDS-staged kernel.
+// "narrow" for few (decode-sized). 16-bit operands run the streaming-B kernel
+// (four or eight waves along N, 64 output columns each); FP32 runs the
+// LDS-staged kernel.
 #ifndef LM_WIDE_TM
 #define LM_WIDE_TM 4
 #endif
+#ifndef LM_EXPERT_WN
+#define LM_EXPERT_WN 8
+#endif
+// FP16 operands (expert and unpooler GEMMs), prefill-sized: one workgroup of
+// LM_EXPERT_WN waves along N per CU (128 x 512 tiles: each gathered A row is
+// read once per 256 output columns of gate/up instead of per 128, and the
+// L2 bytes per MFMA drop by a sixth against two 128 x 256 workgroups).
 template <typename E>
-using CfgWide =
-    std::conditional_t<sizeof(E) == 2, LmGemmCfg<E, 1, 4, LM_WIDE_TM, 2>, LmGemmCfg<E, 2, 2, 2, 2>>;
+using CfgWide = std::conditional_t<
+    std::is_same_v<E, _Float16>, LmGemmCfg<E, 1, LM_EXPERT_WN, LM_WIDE_TM, 2>,
+    std::conditional_t<sizeof(E) == 2, LmGemmCfg<E, 1, 4, LM_WIDE_TM, 2>, LmGemmCfg<E, 2, 2, 2, 2>>>;
 template <typename E> using CfgNarrow = LmGemmCfg<E, 1, 4, 1, 2>;
 // Router: FP32 chains of one k-tile (64 BF16 products per lane pair), FP64 beyond.
 template <typename E> using CfgRouterWide = LmGemmCfg<E, 2, 2, 1, 2, 1>;
@@ -231,12 +240,15 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
   size_t kp = 0;
   if (c.act_dtype == LMOE_BF16) {
     for (int64_t T = 1; T <= (Tm < 65536 ? Tm : 65536); ++T) {
+      // the tile shapes forward uses: pooler on BF16, unpooler on FP16 operands
       const bool nar = narrow_for(c, T);
-      const int BM = nar ? 32 : 32 * LM_WIDE_TM, BN = 256;
+      const int BM = nar ? CfgNarrow<uint16_t>::BM : CfgWide<uint16_t>::BM;
+      const int BNp = nar ? CfgNarrow<uint16_t>::BN : CfgWide<uint16_t>::BN;
+      const int BNu = nar ? CfgNarrow<_Float16>::BN : CfgWide<_Float16>::BN;
       int sp, kpt;
-      dense_split(T, P, c.hidden, BM, BN, sp, kpt);
+      dense_split(T, P, c.hidden, BM, BNp, sp, kpt);
       if (sp > 1 && (size_t)sp * T * P > kp) kp = (size_t)sp * T * P;
-      dense_split(T, c.hidden, P, BM, BN, sp, kpt);
+      dense_split(T, c.hidden, P, BM, BNu, sp, kpt);
       if (sp > 1 && (size_t)sp * T * c.hidden > kp) kp = (size_t)sp * T * c.hidden;
     }
   }
@@ -256,7 +268,7 @@ hipError_t launch(const Prob& p, int64_t units, hipStream_t s) {
   if (units <= 0) return hipSuccess;
   const int64_t g = (units + 7) / 8 * 8;
   if constexpr (sizeof(typename Prob::Cfg::E) == 2 && Prob::Cfg::WM == 1 && !Prob::Cfg::FLUSH)
-    hipLaunchKernelGGL(lm_gemm_stream_kernel<Prob>, dim3((unsigned)g), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(lm_gemm_stream_kernel<Prob>, dim3((unsigned)g), dim3(64 * Prob::Cfg::WN), 0, s, p);
   else
     hipLaunchKernelGGL(lm_gemm_kernel<Prob>, dim3((unsigned)g), dim3(256), 0, s, p);
   return hipGetLastError();
@@ -524,7 +536,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   }
   LM_MARK(7);
   // 6. down + per-row sum of squares partials
-  const int dnt = ceil_div(P, Cw::BN);
+  const int dnt = ceil_div(P, MXA ? Cw::BN : Ch::BN);
   if constexpr (MXA) {
     DownMxaProb<Cw, AB> p;
     p.sd = h->pk_sdown;
@@ -567,7 +579,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   LM_MARK(9);
   // 8. unpooler (BF16 layers: FP16 y against the per-row scaled FP16 copy of W)
   int usplits = 1, ukt = 0;
-  if (packed) dense_split(T, H, P, Cw::BM, Cw::BN, usplits, ukt);
+  if (packed) dense_split(T, H, P, Ch::BM, Ch::BN, usplits, ukt);
   if (usplits > 1) {
     if constexpr (F16) {
     DenseSplitProb<Ch> p;
@@ -578,8 +590,8 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.T = (int)T;
     p.N = H;
     p.K = P;
-    p.mt = ceil_div(T, Cw::BM);
-    p.nt = ceil_div(H, Cw::BN);
+    p.mt = ceil_div(T, Ch::BM);
+    p.nt = ceil_div(H, Ch::BN);
     p.splits = usplits;
     p.kt_per = ukt;
     LM_HIP(launch(p, (int64_t)p.mt * p.nt * usplits, s));
@@ -597,8 +609,8 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.T = (int)T;
     p.H = H;
     p.P = P;
-    p.mt = ceil_div(T, Cw::BM);
-    p.nt = ceil_div(H, Cw::BN);
+    p.mt = ceil_div(T, Ch::BM);
+    p.nt = ceil_div(H, Ch::BN);
     LM_HIP(launch(p, (int64_t)p.mt * p.nt, s));
   }
   LM_MARK(10);
