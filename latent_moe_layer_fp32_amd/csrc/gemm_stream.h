@@ -69,7 +69,7 @@ void lm_gemm_stream_kernel(const Prob p) {
   // A (TM < 4, decode-sized tiles): loaded four k-tiles ahead into a ring of
   // four; A(kt+2) is written to LDS at iteration kt and waits only on loads
   // issued two iterations earlier. B: one k-tile ahead in a ring of two for
-  // BF16 weights with TM = 4 (small enough for two workgroups per CU to hide
+  // 16-bit weights with TM = 4 (small enough for two waves per SIMD to hide
   // each other's latency); otherwise (few B registers: narrow tiles, MXFP4
   // codes) three ahead in a ring of four.
   constexpr bool kLeanA = TM >= 4;
