@@ -115,6 +115,10 @@ LM_DEV int lm_b_ktile(const P& p, int kt) {
 
 LM_DEV int lm_swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
+// Row groups of 32 rows interleaved per k-tile in the packed weight layout
+// (lm_packed_group).
+constexpr int kLmPackGroups = 8;
+
 // Weight loads. NT: a non-temporal load, for weights read once and never
 // again (the streaming hint measured 7.07 against 6.34 TB/s for plain
 // 16-byte loads on MI355X); otherwise a plain load, where other m-tiles reuse

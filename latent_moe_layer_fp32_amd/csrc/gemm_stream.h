@@ -98,8 +98,9 @@ void lm_gemm_stream_kernel(const Prob p) {
   const lm_u32x4* asrc[QA];
 #pragma unroll
   for (int q = 0; q < QA; ++q) asrc[q] = p.a_row(t, lr + RS * q);
-  // B: wave w's j-th 32-row group in the packed layout. BF16: the fragment
-  // of step s of k-tile kt is 1 KB at (kt*4 + s)*64 chunks. MXFP4: all four
+  // B: wave w's j-th 32-row group in the packed layout. 16-bit weights: the
+  // fragment of step s of k-tile kt is 1 KB at (kt*4*8 + s)*64 chunks (eight
+  // groups interleaved per k-tile). MXFP4: all four
   // steps of k-tile kt are 1 KB at kt*64 chunks, scales a dword per lane per
   // four k-tiles.
   const lm_u32x4* bsrc[TN];
@@ -137,7 +138,8 @@ void lm_gemm_stream_kernel(const Prob p) {
         rb[slot][j][0] = lm_wload<kNT>(&bsrc[j][kc * 64]);
       } else {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) rb[slot][j][s] = lm_wload<kNT>(&bsrc[j][(kc * 4 + s) * 64]);
+        for (int s = 0; s < 4; ++s)
+          rb[slot][j][s] = lm_wload<kNT>(&bsrc[j][(kc * 4 * kLmPackGroups + s) * 64]);
       }
     }
   };

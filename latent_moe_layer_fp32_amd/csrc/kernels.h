@@ -109,16 +109,22 @@ __global__ __launch_bounds__(256) void lm_input_norm_kernel(const Et* r, int H, 
 
 // --------------------------------------------------- matrix-core B layout
 // Weights read by the streaming kernel are repacked once (at create) so that
-// one 16-byte load per lane fetches exactly the B fragment of a
-// v_mfma_f32_32x32x16_bf16 step, and the 64 lanes of that load read 1 KB of
-// contiguous memory. For a row-major [R, K] BF16 matrix (R % 32 == 0,
-// K % 64 == 0), 16-byte chunk c of row n lands at chunk index
-//   ((n/32 * K/64 + c/8) * 4 + (c%8)%4) * 64 + ((c%8)/4) * 32 + n%32
-// i.e. blocks of 32 rows x 64 columns, ordered by MFMA step s = (c%8)%4, then
-// by lane (h = (c%8)/4, r = n%32). The same layout holds FP16 matrices.
+// one 16-byte load per lane fetches exactly the B fragment of a 32x32x16
+// MFMA step, and the 64 lanes of that load read 1 KB of contiguous memory.
+// For a row-major [R, K] matrix of 16-bit elements (R % 256 == 0, K % 64 ==
+// 0), 16-byte chunk c of row n, in row group g = n/32 (block gb = g/8, gi =
+// g%8) and k-tile kt = c/8, lands at chunk index
+//   (((gb * K/64 + kt) * 8 + gi) * 4 + s) * 64 + h * 32 + n%32
+// with MFMA step s = (c%8)%4 and lane half h = (c%8)/4: 4 KB per group and
+// k-tile, the eight groups of a block side by side for each k-tile. A
+// workgroup reading 4 or 8 consecutive groups (its waves' weight rows) thus
+// reads 16 or 32 KB of contiguous memory per k-tile and tensor, not 4 KB
+// pieces 256 KB apart.
 template <typename E>
 LM_DEV const lm_u32x4* lm_packed_group(const E* base, int64_t row0, int K) {
-  return (const lm_u32x4*)base + (row0 / 32) * (int64_t)(K / 64) * 256;
+  const int64_t g = row0 / 32;
+  return (const lm_u32x4*)base +
+         ((g / kLmPackGroups) * (int64_t)(K / 64) * kLmPackGroups + g % kLmPackGroups) * 256;
 }
 
 // ds == nullptr: BF16 copied as is. Otherwise the BF16 source is written as
@@ -129,12 +135,12 @@ __global__ void lm_pack_mfma_kernel(const lm_u32x4* src, lm_u32x4* dst, int64_t 
   const int ktiles = K / 64;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t blk = i >> 8;
-    const int within = (int)(i & 255);
-    const int s = within >> 6, lane = within & 63;
-    const int64_t g = blk / ktiles;
-    const int kt = (int)(blk - g * ktiles);
-    const int64_t row = g * 32 + (lane & 31);
+    const int lane = (int)(i & 63), s = (int)((i >> 6) & 3);
+    const int gi = (int)((i >> 8) % kLmPackGroups);
+    const int64_t rest = (i >> 8) / kLmPackGroups;  // gb * K/64 + kt
+    const int64_t gb = rest / ktiles;
+    const int kt = (int)(rest - gb * ktiles);
+    const int64_t row = (gb * kLmPackGroups + gi) * 32 + (lane & 31);
     lm_u32x4 v = src[row * (K / 8) + kt * 8 + 4 * (lane >> 5) + s];
     if (ds) {
       const float m = lm_pow2(-lm_log2_of_pow2(ds[row]));
