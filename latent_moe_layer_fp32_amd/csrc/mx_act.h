@@ -219,8 +219,8 @@ struct DownMxaProb : DownProb<Cfg_, true> {
 };
 
 // ------------------------------------------------------------------ kernel
-// Streaming-B GEMM with MX FP8 or FP4 A and MXFP4 B, four waves side by side
-// along N as in lm_gemm_stream_kernel. A k-tile is 128 elements: 128 (FP8) or
+// Streaming-B GEMM with MX FP8 or FP4 A and MXFP4 B, four or eight waves side
+// by side along N as in lm_gemm_stream_kernel. A k-tile is 128 elements: 128 (FP8) or
 // 64 (FP4) bytes per A row (LDS, double buffered, with each row's E8M0 scale
 // dword of the k-tile next to it) and two 64-wide MXFP4 k-tiles of B per wave
 // group (1 KB each, loaded straight into the MFMA registers); two scaled MFMA
@@ -236,14 +236,14 @@ struct DownMxaProb : DownProb<Cfg_, true> {
 // The k-tile count is a multiple of 4 (validated on the host) so the ring
 // slots and scale byte selectors are compile-time.
 template <class Prob>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LM_WAVES_MAX, LM_WAVES_MAX)))
+__global__ __launch_bounds__(64 * Prob::Cfg::WN) __attribute__((amdgpu_waves_per_eu(LM_WAVES_MAX, LM_WAVES_MAX)))
 void lm_gemm_stream_mxa_kernel(const Prob p) {
   using Cfg = typename Prob::Cfg;
-  static_assert(Cfg::WM == 1 && Cfg::WN == 4, "streaming-B layout: four waves along N");
+  static_assert(Cfg::WM == 1 && (Cfg::WN == 4 || Cfg::WN == 8), "streaming-B layout: four or eight waves along N");
   constexpr int TM = Cfg::TM, TN = Cfg::TN, BM = Cfg::BM;
   constexpr bool kA4 = Prob::kBits == 4;
   constexpr int kCh = kA4 ? 4 : 8;     // 16-byte A chunks per row and k-tile
-  constexpr int kRows = 256 / kCh;     // A rows covered by one load pass
+  constexpr int kRows = 64 * Cfg::WN / kCh;  // A rows covered by one load pass
   // B one k-tile ahead (ring of two) for TM = 4; three ahead (ring of four)
   // for decode-sized tiles, whose time goes to streaming the weights.
   // With FP4 A a k-tile holds half the matrix work of an FP8 one, too little
