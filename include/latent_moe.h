@@ -71,7 +71,10 @@ typedef struct {
                            the expert and unpooler GEMMs then run on FP16
                            operands: u, the SwiGLU output a and y are rounded
                            to FP16 (nearest even; a saturates at +-65504; u
-                           and y are bounded by sqrt(P) max|gamma|), and the
+                           and y, bounded by sqrt(P) max|gamma|, are stored
+                           times a power of two that keeps that bound within
+                           2^15, 1 for ordinary gammas, so they never
+                           saturate), and the
                            weights are used as FP16 copies made at create,
                            each weight row times a power of two 2^s that puts
                            its largest magnitude in [2^14, 2^15), undone in
@@ -226,6 +229,10 @@ typedef struct {
                            [T, H] F32; BF16 layers its exact three-piece BF16 split
                            [T, 3H] (pieces p1 | p2 | p3 side by side, p1 + p2 + p3 =
                            the FP32 value, p1 = its BF16 rounding, the pooler's input) */
+  float expert_in_scale; /* the FP16 expert_in holds u times this power of two, and */
+  float combined_scale;  /* the FP16 combined holds y times this one: 1 unless
+                            sqrt(P) max|gamma| exceeds 2^15 (then the largest power of
+                            two that keeps u, y below 2^15 in magnitude); 1 for F32 */
 } latent_moe_views;
 
 int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v);

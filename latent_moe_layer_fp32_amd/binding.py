@@ -59,7 +59,7 @@ class Views(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "ids", "weights", "counts", "offsets", "perm_token", "pair_row", "pooled",
         "row_scale", "act", "expert_out", "combined", "expert_in", "expert_in_scales", "act_scales",
-        "x_norm")]
+        "x_norm")] + [("expert_in_scale", ctypes.c_float), ("combined_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -271,6 +271,12 @@ class LatentMoE:
             a = np.empty(shape, dt)
             _memcpy_d2h(a.ctypes.data, ptr, a.nbytes)
             res[name] = a
+        # FP16 u and y are stored times a power of two (1 for ordinary gammas): the
+        # views hold their values (exact in FP32)
+        if not f32 and not mxa and "expert_in" in res:
+            res["expert_in"] = res["expert_in"].astype(np.float32) / np.float32(v.expert_in_scale)
+        if not f32 and "combined" in res:
+            res["combined"] = res["combined"].astype(np.float32) / np.float32(v.combined_scale)
         if split_norm and "x_norm" in res:  # FP32 value = sum of the three BF16 pieces (exact)
             H = self.hidden
             pcs = (res["x_norm"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -432,6 +432,7 @@ struct GateUpProb {
   const void* su = nullptr;
   const float* dsg = nullptr;  // FP16 operands: 2^-s per gate / up weight row [E*I]
   const float* dsu = nullptr;
+  float u_up = 1.0f;           // FP16 operands: u is stored times 1 / u_up (a power of two)
   const E* pooled;  // FP16 operands: the normed u [T, P]; FP32 layers: gamma_p * h
   const E* wg;
   const E* wu;
@@ -480,8 +481,8 @@ struct GateUpProb {
     const int col = t.n0 + wn * 32 + (lane & 31);
     float dg = 1.0f, du = 1.0f;
     if constexpr (kScaledW) {
-      dg = dsg[(size_t)t.e * I + col];
-      du = dsu[(size_t)t.e * I + col];
+      dg = dsg[(size_t)t.e * I + col] * u_up;
+      du = dsu[(size_t)t.e * I + col] * u_up;
     }
     auto put = [&](int tm, int i) {
       const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
@@ -591,6 +592,7 @@ struct UnpoolerProb {
   const E* y;
   const E* w;
   const float* ds = nullptr;  // [H] or none
+  float y_up = 1.0f;          // y is stored times 1 / y_up (a power of two)
   float* out;  // [T, H]
   int T, H, P, mt, nt;
 
@@ -624,7 +626,7 @@ struct UnpoolerProb {
     for (int tn = 0; tn < Cfg::TN; ++tn) {
       const int col = t.n0 + lm_acc_col<Cfg>(wn, tn, lane);
       if (col >= H) continue;
-      const float d = ds ? ds[col] : 1.0f;
+      const float d = (ds ? ds[col] : 1.0f) * y_up;
 #pragma unroll
       for (int tm = 0; tm < Cfg::TM; ++tm)
 #pragma unroll
@@ -648,6 +650,7 @@ struct DenseSplitProb {
   const E* a;   // [T, K]
   const E* w;   // packed [N, K]
   const float* ds = nullptr;  // [N] or none
+  float a_up = 1.0f;          // a is stored times 1 / a_up (a power of two)
   float* part;  // [splits, T, N]
   int T, N, K, mt, nt, splits, kt_per;
 
@@ -681,7 +684,7 @@ struct DenseSplitProb {
     for (int tn = 0; tn < Cfg::TN; ++tn) {
       const int col = t.n0 + lm_acc_col<Cfg>(wn, tn, lane);
       if (col >= N) continue;
-      const float d = ds ? ds[col] : 1.0f;
+      const float d = (ds ? ds[col] : 1.0f) * a_up;
 #pragma unroll
       for (int tm = 0; tm < Cfg::TM; ++tm)
 #pragma unroll
@@ -728,6 +731,21 @@ __global__ void lm_unpool_finish_kernel(const float* part, int splits, int64_t n
 }
 
 // ------------------------------------------------------------ small kernels
+
+// Largest |v| over n FP32 values (NaN ignored) into out[0]; one workgroup
+// (used once, at create, on the norm gammas).
+__global__ __launch_bounds__(256) void lm_absmax_kernel(const float* v, int64_t n, float* out) {
+  __shared__ float red[256];
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < n; i += 256) m = fmaxf(m, fabsf(v[i]));
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = red[0];
+}
 
 __global__ void lm_fill_i32_kernel(int* p, int n, int v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -954,11 +972,12 @@ __global__ void lm_rowscale_kernel(const float* ssq, int nparts, int T, int P, f
 }
 
 // Pre-expert RMSNorm for FP16 expert inputs, one token row per workgroup: the
-// row scale r_t as above, then u = FP16(r_t * pooled32), pooled32 = gamma_p * h
-// in FP32 (|u| <= sqrt(P) max|gamma_p|: within FP16's range).
+// row scale r_t as above, then u = FP16(r_t * pooled32 * down), pooled32 =
+// gamma_p * h in FP32. |r_t * pooled32| <= sqrt(P) max|gamma_p|, and down (a
+// power of two chosen at create) keeps that bound within 2^15.
 __global__ __launch_bounds__(256) void lm_norm_u_kernel(const float* pooled32, const float* ssq,
-                                                        int nparts, int P, float eps, float* rs,
-                                                        _Float16* u) {
+                                                        int nparts, int P, float eps, float down,
+                                                        float* rs, _Float16* u) {
   __shared__ float sr;
   const int t = blockIdx.x;
   if (threadIdx.x == 0) {
@@ -968,10 +987,11 @@ __global__ __launch_bounds__(256) void lm_norm_u_kernel(const float* pooled32, c
   }
   __syncthreads();
   const float r = sr;
+  const float rd = r * down;  // exact: down is a power of two
   const float* src = pooled32 + (size_t)t * P;
   for (int c = threadIdx.x * 8; c < P; c += 256 * 8) {
-    const lm_f32x4 a = *(const lm_f32x4*)(src + c) * r;
-    const lm_f32x4 b = *(const lm_f32x4*)(src + c + 4) * r;
+    const lm_f32x4 a = *(const lm_f32x4*)(src + c) * rd;
+    const lm_f32x4 b = *(const lm_f32x4*)(src + c + 4) * rd;
     lm_u32x4 o;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -986,14 +1006,15 @@ __global__ __launch_bounds__(256) void lm_norm_u_kernel(const float* pooled32, c
 
 // One workgroup per token: y = sum over slots j (in order) of
 // w_j / sqrt(mean(o_j^2) + eps) * gamma_{e_j} * o_j, in FP32. FP32 layers
-// store y [T, P] in FP32, BF16 layers its nearest-even FP16 rounding, the
-// unpooler's operand (|y| <= sqrt(P) max|gamma_e|: within FP16's range).
+// store y [T, P] in FP32, BF16 layers the nearest-even FP16 rounding of
+// y * down, the unpooler's operand: |y| <= sqrt(P) max|gamma_e|, and down (a
+// power of two chosen at create) keeps that bound within 2^15.
 template <typename Y>
 __global__ __launch_bounds__(256) void lm_combine_kernel(const float* O, const float* ossq,
                                                          int nparts, const int* pair_row,
                                                          const int* ids, const float* wts,
                                                          const float* gamma, int k, int P,
-                                                         float eps, Y* y) {
+                                                         float eps, float down, Y* y) {
   __shared__ float s_coef[16];
   __shared__ int s_row[16], s_e[16];
   const int t = blockIdx.x, tid = threadIdx.x;
@@ -1020,7 +1041,7 @@ __global__ __launch_bounds__(256) void lm_combine_kernel(const float* O, const f
       static_assert(std::is_same_v<Y, _Float16>, "FP32 or FP16 y");
       uint16_t hv[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) hv[q] = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[q]));
+      for (int q = 0; q < 4; ++q) hv[q] = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[q] * down));
       lm_u32x2 v;
       v[0] = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
       v[1] = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);

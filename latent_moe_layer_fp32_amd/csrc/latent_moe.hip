@@ -120,6 +120,8 @@ struct latent_moe {
   const float* ds_up;
   const float* ds_down;
   const float* ds_unpooler;
+  float u_down = 1.0f;  // FP16 u and y are stored times these powers of two (see create)
+  float y_down = 1.0f;
   hipStream_t side;                // routing (router, top-k, grouping) runs here, beside the pooler
   hipEvent_t fork, join;           // order the side stream after the caller's and back
   bool prof;                       // record stage events in forward
@@ -447,7 +449,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
                          (int)T, P, c.eps, row_scale);
     } else {
       hipLaunchKernelGGL(lm_norm_u_kernel, dim3((unsigned)T), dim3(256), 0, s, pooled32, pssq, chunks,
-                         P, c.eps, row_scale, (_Float16*)u16);
+                         P, c.eps, h->u_down, row_scale, (_Float16*)u16);
     }
     LM_HIP(hipGetLastError());
     }
@@ -470,7 +472,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     if (F16 && !MXA) {
       if constexpr (F16)
         hipLaunchKernelGGL(lm_norm_u_kernel, dim3((unsigned)T), dim3(256), 0, s, pooled32, pssq, pnt,
-                           P, c.eps, row_scale, u16);
+                           P, c.eps, h->u_down, row_scale, u16);
     } else {
       hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, pssq, pnt,
                          (int)T, P, c.eps, row_scale);
@@ -519,6 +521,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     if constexpr (F16) {
       p.dsg = h->ds_gate;
       p.dsu = h->ds_up;
+      p.u_up = 1.0f / h->u_down;  // exact: a power of two
       p.pooled = u16;
     } else {
       p.pooled = (const Eh*)pooled;
@@ -577,7 +580,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   LM_MARK(8);
   // 7. per-expert norm, routing weight, FP32 sum
   hipLaunchKernelGGL(lm_combine_kernel<Eh>, dim3((unsigned)T), dim3(256), 0, s, O, ossq, dnt, pair_row,
-                     ids, wts, w.expert_gamma, k, P, c.eps, y);
+                     ids, wts, w.expert_gamma, k, P, c.eps, F16 ? h->y_down : 1.0f, y);
   LM_HIP(hipGetLastError());
   LM_MARK(9);
   // 8. unpooler (BF16 layers: FP16 y against the per-row scaled FP16 copy of W)
@@ -589,6 +592,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.a = y;
     p.w = (const Eh*)Wunpool;
     p.ds = h->ds_unpooler;
+    p.a_up = 1.0f / h->y_down;
     p.part = (float*)(ws + L.kpart);
     p.T = (int)T;
     p.N = H;
@@ -607,7 +611,10 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     UnpoolerProb<Ch> p;
     p.y = y;
     p.w = (const Eh*)Wunpool;
-    if constexpr (F16) p.ds = h->ds_unpooler;
+    if constexpr (F16) {
+      p.ds = h->ds_unpooler;
+      p.y_up = 1.0f / h->y_down;
+    }
     p.out = out;
     p.T = (int)T;
     p.H = H;
@@ -744,8 +751,27 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
     unsigned blocks = (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
     hipLaunchKernelGGL(lm_split_router_kernel, dim3(blocks), dim3(256), 0, 0, w->router,
                        (uint16_t*)(h->ws + h->lay.wr3), (int)cfg->experts, (int)cfg->hidden);
+    // FP16 u and y: |u| <= sqrt(P) max|gamma_p| and |y| <= sqrt(P) max|gamma_e| (an
+    // RMS-normed row has no element above sqrt(P) times its gamma, and the routing
+    // weights sum to one); each is stored times a power of two that keeps its bound
+    // within 2^15, undone exactly in FP32 after the product (1 for ordinary gammas).
+    float* gmax = (float*)(h->ws + h->lay.logits);  // workspace unused until the first forward
+    hipLaunchKernelGGL(lm_absmax_kernel, dim3(1), dim3(256), 0, 0, w->pool_gamma, (int64_t)P, gmax);
+    hipLaunchKernelGGL(lm_absmax_kernel, dim3(1), dim3(256), 0, 0, w->expert_gamma, (int64_t)(E * P),
+                       gmax + 1);
+    float gm[2] = {0.0f, 0.0f};
     he = hipGetLastError();
     if (he == hipSuccess) he = hipDeviceSynchronize();
+    if (he == hipSuccess) he = hipMemcpy(gm, gmax, sizeof gm, hipMemcpyDeviceToHost);
+    auto down_for = [&](float g) {
+      const double bound = std::sqrt((double)P) * (double)g;
+      if (!(bound > 32768.0) || !std::isfinite(bound)) return 1.0f;
+      int e = 0;
+      std::frexp(bound / 32768.0, &e);  // bound / 2^15 <= 2^e
+      return std::ldexp(1.0f, -(e < 100 ? e : 100));
+    };
+    h->u_down = down_for(gm[0]);
+    h->y_down = down_for(gm[1]);
     if (he != hipSuccess) {
       (void)hipFree(h->ws);
       (void)hipFree(h->packed);
@@ -841,6 +867,8 @@ int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v) {
   v->act_scales = mxa ? (const uint8_t*)(ws + L.acts) : nullptr;
   v->x_norm = !h->cfg.input_norm ? nullptr
               : h->cfg.act_dtype == LMOE_F32 ? (const void*)(ws + L.xn) : (const void*)(ws + L.xna);
+  v->expert_in_scale = mxa || h->cfg.act_dtype == LMOE_F32 ? 1.0f : h->u_down;
+  v->combined_scale = h->cfg.act_dtype == LMOE_F32 ? 1.0f : h->y_down;
   return LMOE_OK;
 }
 

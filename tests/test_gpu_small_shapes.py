@@ -250,3 +250,68 @@ def test_small_row_magnitudes(torch_dev, tables, name, fmt, T):
 
 def _first(a):
     return (a[0][0], a[1][0]) if isinstance(a, tuple) else a[0]
+
+
+# ------------------------------------------------------ large norm gammas
+
+@pytest.mark.parametrize("fmt,T", [("bf16", 300), ("bf16", 100), ("mxfp4", 300)])
+def test_small_large_gammas(torch_dev, tables, fmt, T):
+    """Norm gammas 2^14 (gamma_p) and 2^15 (gamma_e) times larger, the gate/up
+    weights 2^14 times smaller so that g and v keep their size: u and y then
+    reach ~9e4, beyond FP16's 65504, and are stored times a power of two
+    chosen at create from sqrt(P) max|gamma|, undone after their products.
+    Every output element within 2e-2 x RMS of the oracle on the same inputs."""
+    torch = torch_dev
+    from latent_moe_layer_fp32_amd import LatentMoE
+    from oracle import oracle as orc
+    from oracle.mx import to_f64
+
+    spec = synth.CONFIGS["decode"].with_(name="small", T=T, E=16, k=4, expert_format=fmt, **SMALL)
+    E, H, P, I = spec.E, spec.H, spec.P, spec.I
+    say(f"case: large gammas, {fmt}, T={T}")
+    big, bige = 2.0 ** 14, 2.0 ** 15
+    wts = device_weights(spec, tables)
+    wts["pool_gamma"] = wts["pool_gamma"] * big
+    wts["expert_gamma"] = wts["expert_gamma"] * bige
+    for n in ("w_gate", "w_up"):
+        if fmt == "mxfp4":  # 2^-14 on every block = -14 on each E8M0 code
+            codes, sc = wts[n]
+            wts[n] = (codes, (sc.int() - 14).to(torch.uint8))
+        else:
+            wts[n] = (wts[n].float() / big).to(torch.bfloat16)
+    layer = LatentMoE(hidden=H, pooled=P, experts=E, intermediate=I, top_k=spec.k, eps=spec.eps,
+                      act_dtype=spec.act_dtype, expert_dtype=fmt, max_tokens=512, weights=wts)
+    try:
+        x = synth.device_tensor(spec, "x", tables)
+        ids_d = torch.empty((T, spec.k), dtype=torch.int32, device=x.device)
+        w_d = torch.empty((T, spec.k), dtype=torch.float32, device=x.device)
+        out = layer.forward(x, topk_ids=ids_d, topk_weights=w_d)
+        torch.cuda.synchronize()
+        out, ids, w = out.cpu().numpy(), ids_d.cpu().numpy(), w_d.cpu().numpy()
+        v = layer.views(T, names=("expert_in", "combined"))
+    finally:
+        layer.close()
+    host = HostLayer(spec)
+    hw = host.w
+    scale = {"w_gate": 1.0 / big, "w_up": 1.0 / big, "w_down": 1.0}
+
+    def expert(e):
+        return tuple(to_f64(_first(synth.host(spec, n, experts=(e, e + 1)))) * scale[n]
+                     for n in ("w_gate", "w_up", "w_down"))
+
+    xh = host.x()
+    near, _ = check_routing(ids, w, host.logits(xh), spec.k)
+    force = {int(t): ids[t] for t in near}
+    r = orc.forward(xh, hw["router"], None, hw["pooler"], to_f64(hw["pool_gamma"]) * big, expert,
+                    to_f64(hw["expert_gamma"]) * bige, hw["unpooler"], spec.k, spec.eps,
+                    force_ids=force or None, keep_pairs=False)
+    assert np.array_equal(ids, r.ids)
+    assert np.abs(r.u).max() > 65504 and np.abs(r.y).max() > 65504, "inputs do not exceed FP16's range"
+    e = check_output(out, r.out, 2e-2)
+    if fmt == "bf16":
+        eu = float((np.abs(v["expert_in"] - r.u) / np.abs(r.u).max()).max())
+        assert eu < 1e-3, f"u (stored scaled): max error {eu:.3g} of max|u|"
+    ey = float((np.abs(v["combined"] - r.y) / np.abs(r.y).max()).max())
+    assert ey < 1e-2, f"y (stored scaled): max error {ey:.3g} of max|y|"
+    say(f"large gammas, {fmt}: max|u| {np.abs(r.u).max():.3g}, max|y| {np.abs(r.y).max():.3g}; "
+        f"out max-abs {e:.3g} x RMS over all {T} tokens")
