@@ -70,11 +70,13 @@ typedef struct {
                            LMOE_BF16: the pooler multiplies BF16 x by BF16 Wp;
                            the expert and unpooler GEMMs then run on FP16
                            operands: u, the SwiGLU output a and y are rounded
-                           to FP16 (nearest even; a saturates at +-65504; u
-                           and y, bounded by sqrt(P) max|gamma|, are stored
-                           times a power of two that keeps that bound within
-                           2^15, 1 for ordinary gammas, so they never
-                           saturate), and the
+                           to FP16 (nearest even), each stored times a power
+                           of two chosen at create that keeps a bound on it
+                           within 2^15 (u, y: sqrt(P) max|gamma|; a, per
+                           expert and 32 columns: ||Wg_i|| ||Wu_i|| P
+                           max|gamma_p|^2), 1 for ordinary weights and gammas,
+                           so none of them saturates; the down weights carry
+                           a's power of two. The
                            weights are used as FP16 copies made at create,
                            each weight row times a power of two 2^s that puts
                            its largest magnitude in [2^14, 2^15), undone in
@@ -233,6 +235,11 @@ typedef struct {
   float combined_scale;  /* the FP16 combined holds y times this one: 1 unless
                             sqrt(P) max|gamma| exceeds 2^15 (then the largest power of
                             two that keeps u, y below 2^15 in magnitude); 1 for F32 */
+  const float* act_down; /* BF16 layers without MX expert inputs: [E, I/32] F32, the
+                            FP16 act of a pair routed to expert e holds a times
+                            act_down[e][i/32], a power of two (1 unless the
+                            Cauchy-Schwarz bound |a_i| <= ||Wg_i|| ||Wu_i|| P
+                            max|gamma_p|^2 exceeds 2^15); else NULL */
 } latent_moe_views;
 
 int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v);

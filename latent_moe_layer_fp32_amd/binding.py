@@ -59,7 +59,8 @@ class Views(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "ids", "weights", "counts", "offsets", "perm_token", "pair_row", "pooled",
         "row_scale", "act", "expert_out", "combined", "expert_in", "expert_in_scales", "act_scales",
-        "x_norm")] + [("expert_in_scale", ctypes.c_float), ("combined_scale", ctypes.c_float)]
+        "x_norm")] + [("expert_in_scale", ctypes.c_float), ("combined_scale", ctypes.c_float),
+                      ("act_down", ctypes.c_void_p)]
 
 
 _lib = None
@@ -277,6 +278,13 @@ class LatentMoE:
             res["expert_in"] = res["expert_in"].astype(np.float32) / np.float32(v.expert_in_scale)
         if not f32 and "combined" in res:
             res["combined"] = res["combined"].astype(np.float32) / np.float32(v.combined_scale)
+        if not f32 and not mxa and "act" in res and v.act_down:  # FP16 a times act_down[e][i/32]
+            ad = np.empty((E, I // 32), np.float32)
+            _memcpy_d2h(ad.ctypes.data, v.act_down, ad.nbytes)
+            offs = np.empty((E + 1,), np.int32)
+            _memcpy_d2h(offs.ctypes.data, v.offsets, offs.nbytes)
+            expert_of_row = np.searchsorted(offs[1:], np.arange(T * k), side="right")
+            res["act"] = res["act"].astype(np.float32) / np.repeat(ad[expert_of_row], 32, axis=1)
         if split_norm and "x_norm" in res:  # FP32 value = sum of the three BF16 pieces (exact)
             H = self.hidden
             pcs = (res["x_norm"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)

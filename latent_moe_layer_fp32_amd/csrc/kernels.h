@@ -128,9 +128,12 @@ LM_DEV const lm_u32x4* lm_packed_group(const E* base, int64_t row0, int K) {
 }
 
 // ds == nullptr: BF16 copied as is. Otherwise the BF16 source is written as
-// FP16, each row times 2^s, with 2^-s = ds[row] from lm_row_descale_bf16_kernel.
+// FP16, each row times 2^s, with 2^-s = ds[row] from lm_row_descale_bf16_kernel,
+// and (kc != nullptr) each 32-column block of a row times 2^c as well, c =
+// kc[(row / rows_per_set) * K/32 + block] (the down weights of expert e: the
+// shifts of the SwiGLU output's blocks, see lm_a_shift_kernel).
 __global__ void lm_pack_mfma_kernel(const lm_u32x4* src, lm_u32x4* dst, int64_t rows, int K,
-                                    const float* ds) {
+                                    const float* ds, const int* kc, int64_t rows_per_set) {
   const int64_t n = rows * (K / 8);
   const int ktiles = K / 64;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -144,10 +147,12 @@ __global__ void lm_pack_mfma_kernel(const lm_u32x4* src, lm_u32x4* dst, int64_t 
     lm_u32x4 v = src[row * (K / 8) + kt * 8 + 4 * (lane >> 5) + s];
     if (ds) {
       const float m = lm_pow2(-lm_log2_of_pow2(ds[row]));
+      // the chunk's 8 columns lie in 32-column block 2 kt + h
+      const float mc = kc ? lm_pow2(kc[(row / rows_per_set) * (K / 32) + 2 * kt + (lane >> 5)]) : 1.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const _Float16 lo = (_Float16)(lm_bf16_to_f32((uint16_t)(v[q] & 0xffffu)) * m);
-        const _Float16 hi = (_Float16)(lm_bf16_to_f32((uint16_t)(v[q] >> 16)) * m);
+        const _Float16 lo = (_Float16)(lm_bf16_to_f32((uint16_t)(v[q] & 0xffffu)) * mc * m);
+        const _Float16 hi = (_Float16)(lm_bf16_to_f32((uint16_t)(v[q] >> 16)) * mc * m);
         v[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
       }
     }
@@ -163,9 +168,11 @@ __global__ void lm_pack_mfma_kernel(const lm_u32x4* src, lm_u32x4* dst, int64_t 
 // largest converts exactly (a smaller one rounds, by at most 2^-39 of the
 // largest). The epilogue multiplies the output
 // column by ds[row] = 2^-s (exact). s is clamped to [-100, 100] (an all-zero
-// row gets 2^-100). One wavefront per row.
+// row gets 2^-100). With kc, each 32-column block counts times its 2^c (as
+// lm_pack_mfma_kernel scales it). One wavefront per row.
 __global__ __launch_bounds__(256) void lm_row_descale_bf16_kernel(const uint16_t* w, int64_t rows,
-                                                                  int K, float* ds) {
+                                                                  int K, float* ds, const int* kc,
+                                                                  int64_t rows_per_set) {
   const int lane = threadIdx.x & 63;
   const int64_t waves = (int64_t)gridDim.x * 4;
   for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += waves) {
@@ -173,12 +180,95 @@ __global__ __launch_bounds__(256) void lm_row_descale_bf16_kernel(const uint16_t
     uint32_t m = 0;
     for (int c = lane; c < K / 8; c += 64) {
       const lm_u32x4 q = row[c];
+      // magnitude bits; a block shift adds c to the exponent field of non-zero values
+      const uint32_t add = kc ? (uint32_t)kc[(r / rows_per_set) * (K / 32) + c / 4] << 7 : 0u;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) m = max(m, max(q[j] & 0x7fffu, (q[j] >> 16) & 0x7fffu));
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = q[j] & 0x7fffu, hi = (q[j] >> 16) & 0x7fffu;
+        m = max(m, max(lo ? lo + add : 0u, hi ? hi + add : 0u));
+      }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
     if (lane == 0) ds[r] = lm_pow2(-min(max(141 - (int)(m >> 7), -100), 100));
+  }
+}
+
+// Euclidean norm of each row of a BF16 [rows, K] matrix (FP32 sums), one
+// wavefront per row.
+__global__ __launch_bounds__(256) void lm_row_norm_bf16_kernel(const uint16_t* w, int64_t rows, int K,
+                                                               float* out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += waves) {
+    const lm_u32x4* row = (const lm_u32x4*)(w + r * K);
+    float s = 0.0f;
+    for (int c = lane; c < K / 8; c += 64) {
+      const lm_u32x4 q = row[c];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = __uint_as_float(q[j] << 16), b = __uint_as_float(q[j] & 0xffff0000u);
+        s += a * a + b * b;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
+    if (lane == 0) out[r] = sqrtf(s);
+  }
+}
+
+// The same for MXFP4 [rows, K] (codes [rows, K/2], E8M0 scales [rows, K/32]);
+// each lane decodes one 32-element block at a time.
+__global__ __launch_bounds__(256) void lm_row_norm_mx_kernel(const uint8_t* codes, const uint8_t* sc,
+                                                             int64_t rows, int K, float* out) {
+  const float e2m1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += waves) {
+    float s = 0.0f;
+    for (int b = lane; b < K / 32; b += 64) {
+      const lm_u32x4 q = ((const lm_u32x4*)(codes + r * (K / 2)))[b];
+      const uint32_t code = sc[r * (K / 32) + b];
+      const float x = code == 255 ? __uint_as_float(0x7fc00000u) : ldexpf(1.0f, (int)code - 127);
+      float t = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const float v = e2m1[(q[j >> 3] >> (4 * (j & 7))) & 7u];
+        t += v * v;
+      }
+      s += t * x * x;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
+    if (lane == 0) out[r] = sqrtf(s);
+  }
+}
+
+// Shifts of the FP16 SwiGLU output a: for expert e and intermediate index i,
+// |a_i| = |silu(g_i) v_i| <= |g_i| |v_i| <= ||Wg_i|| ||Wu_i|| ||u||^2
+// (Cauchy-Schwarz, |silu(g)| <= |g|), and ||u||^2 <= u2 = P max(gamma_p)^2
+// (an RMS-normed row). Per block of 32 consecutive i (one MX scale block of
+// the down weights' reduction axis): c = the smallest shift >= 0 with the
+// block's largest bound times 2^-c within 2^15 (at most 60). The gate/up
+// epilogue stores a times a_down = 2^-c; the down weights' copies carry 2^c
+// on those 32 columns, so the products are unchanged.
+__global__ void lm_a_shift_kernel(const float* ng, const float* nu, int64_t nblk, float u2, int* kc,
+                                  float* a_down) {
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk;
+       b += (int64_t)gridDim.x * blockDim.x) {
+    float m = 0.0f;
+    for (int i = 0; i < 32; ++i) m = fmaxf(m, ng[b * 32 + i] * nu[b * 32 + i]);
+    const float bound = m * u2;
+    int c = 0;
+    if (bound > 32768.0f && bound <= 3.0e38f) {
+      int e;
+      frexpf(bound / 32768.0f, &e);  // bound / 2^15 <= 2^e
+      c = min(e, 60);
+    } else if (!(bound <= 32768.0f)) {
+      c = 60;  // infinite (or NaN) bound: the largest shift
+    }
+    kc[b] = c;
+    a_down[b] = lm_pow2(-c);
   }
 }
 
@@ -187,17 +277,20 @@ __global__ __launch_bounds__(256) void lm_row_descale_bf16_kernel(const uint16_t
 // row's largest decoded magnitude (at most 6 x 2^(emax - 127)) in [2^14,
 // 24576]; every E2M1 value of a block whose scale is within 2^35 of emax is
 // then an FP16 number. One thread per row.
-__global__ void lm_row_descale_mx_kernel(const uint8_t* sc, int64_t rows, int K, float* ds) {
+__global__ void lm_row_descale_mx_kernel(const uint8_t* sc, int64_t rows, int K, float* ds,
+                                         const int* kc, int64_t rows_per_set) {
   for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < rows;
        r += (int64_t)gridDim.x * blockDim.x) {
     const lm_u32x4* row = (const lm_u32x4*)(sc + r * (K / 32));
+    const int* rc = kc ? kc + (r / rows_per_set) * (K / 32) : nullptr;
     int m = 0;
     for (int c = 0; c < K / 512; ++c) {
       const lm_u32x4 q = row[c];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int b = (int)((q[j >> 2] >> (8 * (j & 3))) & 0xffu);
-        m = b != 255 ? max(m, b) : m;
+        const int bc = rc ? min(b + rc[c * 16 + j], 254) : b;  // as lm_pack_mx_kernel stores it
+        m = b != 255 ? max(m, bc) : m;
       }
     }
     ds[r] = lm_pow2(-min(max(139 - m, -100), 100));
@@ -218,8 +311,11 @@ LM_DEV const uint32_t* lm_packed_mx_scales(const void* base, int64_t row0, int K
   return (const uint32_t*)base + (row0 / 32) * (int64_t)(K / 256) * 64;
 }
 
+// kc != nullptr: each 32-column block's scale code is raised by its shift c
+// (lm_a_shift_kernel; codes stay at most 254).
 __global__ void lm_pack_mx_kernel(const lm_u32x4* src, const uint8_t* src_scales, lm_u32x4* dst,
-                                  uint8_t* dst_scales, int64_t rows, int K) {
+                                  uint8_t* dst_scales, int64_t rows, int K, const int* kc,
+                                  int64_t rows_per_set) {
   const int64_t n = rows * (K / 32);  // 16-byte chunks (32 codes each)
   const int ktiles = K / 64;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -232,7 +328,9 @@ __global__ void lm_pack_mx_kernel(const lm_u32x4* src, const uint8_t* src_scales
     const int64_t row = g * 32 + (lane & 31);
     const int64_t sidx = row * (K / 32) + 2 * kt + h;  // source chunk == source scale index
     dst[i] = src[sidx];
-    dst_scales[((g * (K / 256) + kt / 4) * 64 + lane) * 4 + (kt & 3)] = src_scales[sidx];
+    int code = src_scales[sidx];
+    if (kc && code != 255) code = min(code + kc[(row / rows_per_set) * (K / 32) + 2 * kt + h], 254);
+    dst_scales[((g * (K / 256) + kt / 4) * 64 + lane) * 4 + (kt & 3)] = (uint8_t)code;
   }
 }
 
@@ -433,6 +531,7 @@ struct GateUpProb {
   const float* dsg = nullptr;  // FP16 operands: 2^-s per gate / up weight row [E*I]
   const float* dsu = nullptr;
   float u_up = 1.0f;           // FP16 operands: u is stored times 1 / u_up (a power of two)
+  const float* a_down = nullptr;  // FP16 operands: a is stored times a_down[e][i / 32]
   const E* pooled;  // FP16 operands: the normed u [T, P]; FP32 layers: gamma_p * h
   const E* wg;
   const E* wu;
@@ -479,10 +578,11 @@ struct GateUpProb {
                        int lane, void* smem) const {
     const float* rs = (const float*)smem;  // row_value() of each tile row
     const int col = t.n0 + wn * 32 + (lane & 31);
-    float dg = 1.0f, du = 1.0f;
+    float dg = 1.0f, du = 1.0f, ad = 1.0f;
     if constexpr (kScaledW) {
       dg = dsg[(size_t)t.e * I + col] * u_up;
       du = dsu[(size_t)t.e * I + col] * u_up;
+      ad = a_down[(size_t)t.e * (I / 32) + (col >> 5)];
     }
     auto put = [&](int tm, int i) {
       const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
@@ -494,7 +594,7 @@ struct GateUpProb {
         g = rs[row] * acc[tm][0][i];
         v = rs[row] * acc[tm][1][i];
       }
-      act[(size_t)(t.m0 + row) * I + col] = LmElem<E>::from_f32(lm_silu(g) * v);
+      act[(size_t)(t.m0 + row) * I + col] = LmElem<E>::from_f32(lm_silu(g) * v * ad);
     };
     if (t.rows == Cfg::BM) {
 #pragma unroll

@@ -122,6 +122,7 @@ struct latent_moe {
   const float* ds_unpooler;
   float u_down = 1.0f;  // FP16 u and y are stored times these powers of two (see create)
   float y_down = 1.0f;
+  const float* a_down;  // FP16 a is stored times a_down[e][i / 32] (see lm_a_shift_kernel)
   hipStream_t side;                // routing (router, top-k, grouping) runs here, beside the pooler
   hipEvent_t fork, join;           // order the side stream after the caller's and back
   bool prof;                       // record stage events in forward
@@ -522,6 +523,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
       p.dsg = h->ds_gate;
       p.dsu = h->ds_up;
       p.u_up = 1.0f / h->u_down;  // exact: a power of two
+      p.a_down = h->a_down;
       p.pooled = u16;
     } else {
       p.pooled = (const Eh*)pooled;
@@ -699,9 +701,10 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
     const bool mx = cfg->expert_dtype == LMOE_MXFP4;
     const size_t sz_pool = H * P * 2, sz_exp = mx ? E * I * P / 2 : E * I * P * 2;
     const size_t sz_sc = mx ? E * I * P / 32 : 0;
-    // per weight row 2^-s: gate, up [E*I], down [E*P], unpooler [H] (FP32)
-    const size_t n_ds = 2 * E * I + E * P + H;
-    h->packed_bytes = 2 * sz_pool + 3 * sz_exp + 3 * sz_sc + n_ds * 4;
+    // per weight row 2^-s: gate, up [E*I], down [E*P], unpooler [H] (FP32); then the
+    // SwiGLU output's block shifts c (int) and 2^-c (FP32), [E, I/32] each
+    const size_t n_ds = 2 * E * I + E * P + H, n_ab = E * I / 32;
+    h->packed_bytes = 2 * sz_pool + 3 * sz_exp + 3 * sz_sc + n_ds * 4 + 2 * n_ab * 4;
     he = hipMalloc((void**)&h->packed, h->packed_bytes);
     if (he != hipSuccess) {
       (void)hipGetLastError();
@@ -722,29 +725,81 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
     h->ds_up = ds + E * I;
     h->ds_down = ds + 2 * E * I;
     h->ds_unpooler = ds + 2 * E * I + E * P;
+    int* a_shift = (int*)(ds + n_ds);
+    float* a_down = (float*)(a_shift + n_ab);
+    // Largest |gamma_p| and |gamma_e| (for the FP16 ranges of u, a and y below).
+    float* gmax = (float*)(h->ws + h->lay.logits);  // workspace unused until the first forward
+    hipLaunchKernelGGL(lm_absmax_kernel, dim3(1), dim3(256), 0, 0, w->pool_gamma, (int64_t)P, gmax);
+    hipLaunchKernelGGL(lm_absmax_kernel, dim3(1), dim3(256), 0, 0, w->expert_gamma, (int64_t)(E * P),
+                       gmax + 1);
+    float gm[2] = {0.0f, 0.0f};
+    he = hipGetLastError();
+    if (he == hipSuccess) he = hipDeviceSynchronize();
+    if (he == hipSuccess) he = hipMemcpy(gm, gmax, sizeof gm, hipMemcpyDeviceToHost);
+    // FP16 a (expert inputs in FP16 only; MX inputs quantise a per block): per
+    // expert and block of 32 intermediate columns, the shift from the norms of
+    // the gate and up rows (lm_a_shift_kernel); the down weights carry it.
+    const int* kc = nullptr;
+    h->a_down = nullptr;
+    if (he == hipSuccess && cfg->expert_act == 0) {
+      float* norms = nullptr;
+      he = hipMalloc((void**)&norms, 2 * E * I * sizeof(float));
+      if (he == hipSuccess) {
+        const unsigned nb = (unsigned)((E * I + 3) / 4 < 65536 ? (E * I + 3) / 4 : 65536);
+        if (mx) {
+          hipLaunchKernelGGL(lm_row_norm_mx_kernel, dim3(nb), dim3(256), 0, 0, (const uint8_t*)w->w_gate,
+                             (const uint8_t*)w->s_gate, (int64_t)(E * I), (int)P, norms);
+          hipLaunchKernelGGL(lm_row_norm_mx_kernel, dim3(nb), dim3(256), 0, 0, (const uint8_t*)w->w_up,
+                             (const uint8_t*)w->s_up, (int64_t)(E * I), (int)P, norms + E * I);
+        } else {
+          hipLaunchKernelGGL(lm_row_norm_bf16_kernel, dim3(nb), dim3(256), 0, 0, (const uint16_t*)w->w_gate,
+                             (int64_t)(E * I), (int)P, norms);
+          hipLaunchKernelGGL(lm_row_norm_bf16_kernel, dim3(nb), dim3(256), 0, 0, (const uint16_t*)w->w_up,
+                             (int64_t)(E * I), (int)P, norms + E * I);
+        }
+        const float u2 = (float)((double)P * (double)gm[0] * (double)gm[0]);
+        hipLaunchKernelGGL(lm_a_shift_kernel, dim3((unsigned)((n_ab + 255) / 256)), dim3(256), 0, 0, norms,
+                           norms + E * I, (int64_t)n_ab, u2, a_shift, a_down);
+        he = hipGetLastError();
+        if (he == hipSuccess) he = hipDeviceSynchronize();
+        (void)hipFree(norms);
+        kc = a_shift;
+        h->a_down = a_down;
+      }
+    }
+    if (he != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipFree(h->ws);
+      (void)hipFree(h->packed);
+      delete h;
+      return fail(LMOE_ERR_HIP, "weight range analysis failed: %s", hipGetErrorString(he));
+    }
     // The pooler stays BF16 (x is BF16). The unpooler and BF16 experts become
     // FP16 copies scaled per row by 2^s; MXFP4 experts keep their codes and
     // get the per-row 2^s applied when they are decoded.
     struct Job { const void* src; const void* src_s; const void* dst; const void* dst_s; int64_t rows; int K;
-                 bool mx; const float* ds; };
+                 bool mx; const float* ds; const int* kc; int64_t rows_per_set; };
     const Job jobs[] = {
-        {w->pooler, nullptr, h->pk_pooler, nullptr, (int64_t)P, (int)H, false, nullptr},
-        {w->unpooler, nullptr, h->pk_unpooler, nullptr, (int64_t)H, (int)P, false, h->ds_unpooler},
-        {w->w_gate, w->s_gate, h->pk_gate, h->pk_sgate, (int64_t)(E * I), (int)P, mx, h->ds_gate},
-        {w->w_up, w->s_up, h->pk_up, h->pk_sup, (int64_t)(E * I), (int)P, mx, h->ds_up},
-        {w->w_down, w->s_down, h->pk_down, h->pk_sdown, (int64_t)(E * P), (int)I, mx, h->ds_down}};
+        {w->pooler, nullptr, h->pk_pooler, nullptr, (int64_t)P, (int)H, false, nullptr, nullptr, 1},
+        {w->unpooler, nullptr, h->pk_unpooler, nullptr, (int64_t)H, (int)P, false, h->ds_unpooler, nullptr, 1},
+        {w->w_gate, w->s_gate, h->pk_gate, h->pk_sgate, (int64_t)(E * I), (int)P, mx, h->ds_gate, nullptr, 1},
+        {w->w_up, w->s_up, h->pk_up, h->pk_sup, (int64_t)(E * I), (int)P, mx, h->ds_up, nullptr, 1},
+        {w->w_down, w->s_down, h->pk_down, h->pk_sdown, (int64_t)(E * P), (int)I, mx, h->ds_down, kc,
+         (int64_t)P}};
     for (const Job& j : jobs) {
       if (j.mx) {
         hipLaunchKernelGGL(lm_row_descale_mx_kernel, dim3((unsigned)((j.rows + 255) / 256)), dim3(256), 0, 0,
-                           (const uint8_t*)j.src_s, j.rows, j.K, (float*)j.ds);
+                           (const uint8_t*)j.src_s, j.rows, j.K, (float*)j.ds, j.kc, j.rows_per_set);
         hipLaunchKernelGGL(lm_pack_mx_kernel, dim3(65536), dim3(256), 0, 0, (const lm_u32x4*)j.src,
-                           (const uint8_t*)j.src_s, (lm_u32x4*)j.dst, (uint8_t*)j.dst_s, j.rows, j.K);
+                           (const uint8_t*)j.src_s, (lm_u32x4*)j.dst, (uint8_t*)j.dst_s, j.rows, j.K, j.kc,
+                           j.rows_per_set);
       } else {
         if (j.ds)
           hipLaunchKernelGGL(lm_row_descale_bf16_kernel, dim3((unsigned)((j.rows + 3) / 4 < 65536 ? (j.rows + 3) / 4 : 65536)),
-                             dim3(256), 0, 0, (const uint16_t*)j.src, j.rows, j.K, (float*)j.ds);
+                             dim3(256), 0, 0, (const uint16_t*)j.src, j.rows, j.K, (float*)j.ds, j.kc,
+                             j.rows_per_set);
         hipLaunchKernelGGL(lm_pack_mfma_kernel, dim3(65536), dim3(256), 0, 0, (const lm_u32x4*)j.src,
-                           (lm_u32x4*)j.dst, j.rows, j.K, j.ds);
+                           (lm_u32x4*)j.dst, j.rows, j.K, j.ds, j.kc, j.rows_per_set);
       }
     }
     const size_t n = (size_t)cfg->experts * cfg->hidden;
@@ -755,14 +810,8 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
     // RMS-normed row has no element above sqrt(P) times its gamma, and the routing
     // weights sum to one); each is stored times a power of two that keeps its bound
     // within 2^15, undone exactly in FP32 after the product (1 for ordinary gammas).
-    float* gmax = (float*)(h->ws + h->lay.logits);  // workspace unused until the first forward
-    hipLaunchKernelGGL(lm_absmax_kernel, dim3(1), dim3(256), 0, 0, w->pool_gamma, (int64_t)P, gmax);
-    hipLaunchKernelGGL(lm_absmax_kernel, dim3(1), dim3(256), 0, 0, w->expert_gamma, (int64_t)(E * P),
-                       gmax + 1);
-    float gm[2] = {0.0f, 0.0f};
     he = hipGetLastError();
     if (he == hipSuccess) he = hipDeviceSynchronize();
-    if (he == hipSuccess) he = hipMemcpy(gm, gmax, sizeof gm, hipMemcpyDeviceToHost);
     auto down_for = [&](float g) {
       const double bound = std::sqrt((double)P) * (double)g;
       if (!(bound > 32768.0) || !std::isfinite(bound)) return 1.0f;
@@ -869,6 +918,7 @@ int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v) {
               : h->cfg.act_dtype == LMOE_F32 ? (const void*)(ws + L.xn) : (const void*)(ws + L.xna);
   v->expert_in_scale = mxa || h->cfg.act_dtype == LMOE_F32 ? 1.0f : h->u_down;
   v->combined_scale = h->cfg.act_dtype == LMOE_F32 ? 1.0f : h->y_down;
+  v->act_down = h->cfg.act_dtype == LMOE_F32 ? nullptr : h->a_down;
   return LMOE_OK;
 }
 

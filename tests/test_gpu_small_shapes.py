@@ -315,3 +315,62 @@ def test_small_large_gammas(torch_dev, tables, fmt, T):
     assert ey < 1e-2, f"y (stored scaled): max error {ey:.3g} of max|y|"
     say(f"large gammas, {fmt}: max|u| {np.abs(r.u).max():.3g}, max|y| {np.abs(r.y).max():.3g}; "
         f"out max-abs {e:.3g} x RMS over all {T} tokens")
+
+
+# ------------------------------------------------- large SwiGLU outputs
+
+@pytest.mark.parametrize("fmt,T", [("bf16", 300), ("bf16", 100), ("mxfp4", 300)])
+def test_small_large_swiglu_output(torch_dev, tables, fmt, T):
+    """Gate and up weights 2^7 times larger: a = silu(g) v reaches ~2e5, beyond
+    FP16's 65504. Per expert and block of 32 intermediate columns, create picks
+    a power of two from the bound ||Wg_i|| ||Wu_i|| P max|gamma_p|^2 that keeps a
+    within 2^15 (the down weights' copies carry its inverse): every output
+    element within 2e-2 x RMS of the oracle, a itself within 1e-2 (relative L2)."""
+    torch = torch_dev
+    from latent_moe_layer_fp32_amd import LatentMoE
+    from oracle import oracle as orc
+    from oracle.mx import to_f64
+
+    spec = synth.CONFIGS["decode"].with_(name="small", T=T, E=16, k=4, expert_format=fmt, **SMALL)
+    E, H, P, I = spec.E, spec.H, spec.P, spec.I
+    say(f"case: large SwiGLU output, {fmt}, T={T}")
+    big = 2.0 ** 7
+    wts = device_weights(spec, tables)
+    for n in ("w_gate", "w_up"):
+        if fmt == "mxfp4":  # 2^7 on every block = +7 on each E8M0 code
+            codes, sc = wts[n]
+            wts[n] = (codes, (sc.int() + 7).to(torch.uint8))
+        else:
+            wts[n] = (wts[n].float() * big).to(torch.bfloat16)
+    layer = LatentMoE(hidden=H, pooled=P, experts=E, intermediate=I, top_k=spec.k, eps=spec.eps,
+                      act_dtype=spec.act_dtype, expert_dtype=fmt, max_tokens=512, weights=wts)
+    try:
+        x = synth.device_tensor(spec, "x", tables)
+        ids_d = torch.empty((T, spec.k), dtype=torch.int32, device=x.device)
+        w_d = torch.empty((T, spec.k), dtype=torch.float32, device=x.device)
+        out = layer.forward(x, topk_ids=ids_d, topk_weights=w_d)
+        torch.cuda.synchronize()
+        out, ids, w = out.cpu().numpy(), ids_d.cpu().numpy(), w_d.cpu().numpy()
+        v = layer.views(T, names=("act", "pair_row"))
+    finally:
+        layer.close()
+    host = HostLayer(spec)
+    hw = host.w
+    scale = {"w_gate": big, "w_up": big, "w_down": 1.0}
+
+    def expert(e):
+        return tuple(to_f64(_first(synth.host(spec, n, experts=(e, e + 1)))) * scale[n]
+                     for n in ("w_gate", "w_up", "w_down"))
+
+    xh = host.x()
+    near, _ = check_routing(ids, w, host.logits(xh), spec.k)
+    force = {int(t): ids[t] for t in near}
+    r = orc.forward(xh, hw["router"], None, hw["pooler"], hw["pool_gamma"], expert, hw["expert_gamma"],
+                    hw["unpooler"], spec.k, spec.eps, force_ids=force or None)
+    assert np.array_equal(ids, r.ids)
+    assert np.abs(r.a).max() > 65504, "a does not exceed FP16's range"
+    pr = v["pair_row"].reshape(T, spec.k)
+    ea = check_rel_l2(v["act"][pr], r.a, 1e-2, "act")
+    e = check_output(out, r.out, 2e-2)
+    say(f"large SwiGLU output, {fmt}: max|a| {np.abs(r.a).max():.3g}; rel L2 act {ea:.3g}; "
+        f"out max-abs {e:.3g} x RMS over all {T} tokens")
