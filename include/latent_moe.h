@@ -43,7 +43,7 @@ extern "C" {
 
 #define LMOE_OK 0
 #define LMOE_ERR_INVALID_ARG (-1)     /* null pointer, bad dimension, misalignment */
-#define LMOE_ERR_UNSUPPORTED (-2)     /* a dtype combination this build lacks */
+#define LMOE_ERR_UNSUPPORTED (-2)     /* a dtype combination not implemented */
 #define LMOE_ERR_OOM (-3)             /* device allocation failed in create */
 #define LMOE_ERR_HIP (-4)             /* any HIP runtime error, including "no device" */
 #define LMOE_ERR_TOO_MANY_TOKENS (-5) /* T > max_tokens of the handle */
