@@ -1033,12 +1033,26 @@ __global__ __launch_bounds__(256) void lm_permute_kernel(const int* ids, int npa
   int base = 0;
   for (int start = 0; start < npairs; start += 256 * 16) {
     const int p0 = start + tid * 16;
+    // this thread's 16 consecutive ids: four 16-byte loads (ids is 256-byte
+    // aligned and p0 a multiple of 16) when all are in range
+    int iv[16];
+    if (p0 + 16 <= npairs) {
+      const lm_u32x4* q = (const lm_u32x4*)(ids + p0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const lm_u32x4 w = q[v];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) iv[4 * v + i] = (int)w[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) iv[i] = p0 + i < npairs ? ids[p0 + i] : -1;
+    }
     unsigned mask = 0;
     int c = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int p = p0 + i;
-      const bool m = p < npairs && ids[p] == e;
+      const bool m = iv[i] == e;
       mask |= (unsigned)m << i;
       c += m;
     }
