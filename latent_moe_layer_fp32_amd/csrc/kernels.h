@@ -893,12 +893,16 @@ LM_DEV uint64_t lm_wave_max_u64(uint64_t v) {
 // threads sum the k-split partial logits of the workgroup's tokens in a fixed
 // order (FP64), add the bias and round once to FP32. Phase 2: one wavefront
 // per token picks the top k by (logit desc, index asc) and takes the softmax
-// over them. Routed pairs per expert are counted in an LDS histogram, one
-// integer atomic per expert and workgroup.
+// over them. Routed pairs per expert are counted in an LDS histogram, then
+// one integer atomic per expert and workgroup into cpad, where each expert's
+// counter sits alone in a 128-byte line (cpad[e * kLmCountStride]) so that
+// the atomics of different experts do not queue on a few lines.
+constexpr int kLmCountStride = 32;  // ints per padded expert counter
+
 template <int NV, int TPB>
 __global__ __launch_bounds__(256) void lm_topk_kernel(const double* part, int splits, int T, int E,
                                                       const float* bias, int k, float* logits,
-                                                      int* ids, float* wts, int* counts) {
+                                                      int* ids, float* wts, int* cpad) {
   static_assert(TPB >= 1 && TPB <= 4, "one wavefront per token");
   __shared__ int hist[1024];
   __shared__ float sl[TPB][NV * 64];
@@ -974,7 +978,7 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const double* part, int sp
   }
   __syncthreads();
   for (int i = tid; i < E; i += 256)
-    if (hist[i]) atomicAdd(&counts[i], hist[i]);
+    if (hist[i]) atomicAdd(&cpad[i * kLmCountStride], hist[i]);
 }
 
 // Exclusive block-wide prefix sum over 256 threads (deterministic).
@@ -1003,16 +1007,17 @@ LM_DEV int lm_block_exscan(int v, int* sbuf, int& total) {
 // One workgroup per expert: its offset and first tile index (prefix over
 // lower experts), then a stable scatter of its routed pairs, in (t, j) order,
 // into the grouped order. Writes perm_token (grouped row -> token) and
-// pair_row (pair t*k+j -> grouped row).
+// pair_row (pair t*k+j -> grouped row), and the per-expert counts, from the
+// padded counters cpad of the top-k kernel, compactly to counts [E].
 __global__ __launch_bounds__(256) void lm_permute_kernel(const int* ids, int npairs, int k,
-                                                         const int* counts, int E, int bm,
-                                                         int* offsets, int* tile_off,
+                                                         const int* cpad, int E, int bm,
+                                                         int* counts, int* offsets, int* tile_off,
                                                          int* perm_token, int* pair_row) {
   __shared__ int sbuf[8];
   const int e = blockIdx.x, tid = threadIdx.x;
   int a = 0, b = 0;
   for (int i = tid; i < e; i += 256) {
-    const int c = counts[i];
+    const int c = cpad[(size_t)i * kLmCountStride];
     a += c;
     b += (c + bm - 1) / bm;
   }
@@ -1020,8 +1025,9 @@ __global__ __launch_bounds__(256) void lm_permute_kernel(const int* ids, int npa
   lm_block_exscan(a, sbuf, ta);
   lm_block_exscan(b, sbuf, tb);
   const int off = ta, tbase = tb;
-  const int cnt = counts[e];
+  const int cnt = cpad[(size_t)e * kLmCountStride];
   if (tid == 0) {
+    counts[e] = cnt;
     offsets[e] = off;
     tile_off[e] = tbase;
     if (e == E - 1) {

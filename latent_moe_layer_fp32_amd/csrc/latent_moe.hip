@@ -75,7 +75,7 @@ constexpr int kMinBN = 128;  // smallest BN of the tile configurations (sizes th
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 struct Layout {
-  size_t part, logits, ids, wts, counts, offsets, tile_off, perm_token, pair_row, pooled, pssq,
+  size_t part, logits, ids, wts, cpad, counts, offsets, tile_off, perm_token, pair_row, pooled, pssq,
       row_scale, act, O, ossq, y, wr3, kpart, xn, xna, uq, us, acts, u16, total;
 };
 
@@ -225,6 +225,7 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
   L.logits = take((size_t)Tm * E * 4);
   L.ids = take((size_t)Mp * 4);
   L.wts = take((size_t)Mp * 4);
+  L.cpad = take((size_t)E * kLmCountStride * 4);
   L.counts = take((size_t)E * 4);
   L.offsets = take((size_t)(E + 1) * 4);
   L.tile_off = take((size_t)(E + 1) * 4);
@@ -322,6 +323,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   float* logits = (float*)(ws + L.logits);
   int* ids = (int*)(ws + L.ids);
   float* wts = (float*)(ws + L.wts);
+  int* cpad = (int*)(ws + L.cpad);
   int* counts = (int*)(ws + L.counts);
   int* offsets = (int*)(ws + L.offsets);
   int* tile_off = (int*)(ws + L.tile_off);
@@ -392,7 +394,8 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     LM_HIP(launch(p, (int64_t)mt * nt * splits, sr));
     LM_MARK(2);
     // 2. top-k + softmax + per-expert counts
-    hipLaunchKernelGGL(lm_fill_i32_kernel, dim3(ceil_div(E, 256)), dim3(256), 0, sr, counts, E, 0);
+    hipLaunchKernelGGL(lm_fill_i32_kernel, dim3(ceil_div(E * kLmCountStride, 256)), dim3(256), 0, sr,
+                       cpad, E * kLmCountStride, 0);
     // few tokens with many k-splits: one token per workgroup spreads the
     // split sums over all threads; otherwise four tokens per workgroup
     const bool one = splits > 4;
@@ -401,10 +404,10 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   do {                                                                                          \
     if (one)                                                                                    \
       hipLaunchKernelGGL((lm_topk_kernel<NV, 1>), g, dim3(256), 0, sr, part, splits, (int)T, E, \
-                         w.router_bias, k, logits, ids, wts, counts);                           \
+                         w.router_bias, k, logits, ids, wts, cpad);                             \
     else                                                                                        \
       hipLaunchKernelGGL((lm_topk_kernel<NV, 4>), g, dim3(256), 0, sr, part, splits, (int)T, E, \
-                         w.router_bias, k, logits, ids, wts, counts);                           \
+                         w.router_bias, k, logits, ids, wts, cpad);                             \
   } while (0)
     if (E <= 64) LM_TOPK(1);
     else if (E <= 128) LM_TOPK(2);
@@ -416,8 +419,8 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   }
   LM_MARK(3);
   // 3. grouping by expert
-  hipLaunchKernelGGL(lm_permute_kernel, dim3(E), dim3(256), 0, sr, ids, npairs, k, counts, E, Cw::BM,
-                     offsets, tile_off, perm_token, pair_row);
+  hipLaunchKernelGGL(lm_permute_kernel, dim3(E), dim3(256), 0, sr, ids, npairs, k, cpad, E, Cw::BM,
+                     counts, offsets, tile_off, perm_token, pair_row);
   LM_HIP(hipGetLastError());
   if (fork) LM_HIP(hipEventRecord(h->join, sr));
   LM_MARK(4);
