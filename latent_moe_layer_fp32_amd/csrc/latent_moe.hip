@@ -225,7 +225,6 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
   L.logits = take((size_t)Tm * E * 4);
   L.ids = take((size_t)Mp * 4);
   L.wts = take((size_t)Mp * 4);
-  L.cpad = take((size_t)E * kLmCountStride * 4);
   L.counts = take((size_t)E * 4);
   L.offsets = take((size_t)(E + 1) * 4);
   L.tile_off = take((size_t)(E + 1) * 4);
@@ -263,6 +262,7 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
   L.xn = take(c.input_norm && c.act_dtype == LMOE_F32 ? (size_t)Tm * c.hidden * 4 : 0);
   L.xna = take(c.input_norm && c.act_dtype == LMOE_BF16 ? (size_t)Tm * 3 * c.hidden * 2 : 0);
   L.u16 = take(c.act_dtype == LMOE_BF16 && !mxa ? (size_t)Tm * P * 2 : 0);  // FP16 u
+  L.cpad = take((size_t)E * kLmCountStride * 4);  // padded per-expert counters
   L.total = o;
   return L;
 }
