@@ -914,8 +914,16 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const double* part, int sp
     if (t >= T) continue;
     const double* src = part + (size_t)t * E + e;
     const size_t stride = (size_t)T * E;
+    // the splits summed in index order; sixteen loads in flight at a time
     double sd = 0.0;
     int sp = 0;
+    for (; sp + 16 <= splits; sp += 16) {
+      double v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = src[(size_t)(sp + i) * stride];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sd += v[i];
+    }
     for (; sp + 4 <= splits; sp += 4) {
       const double a = src[(size_t)sp * stride], b = src[(size_t)(sp + 1) * stride];
       const double c = src[(size_t)(sp + 2) * stride], d = src[(size_t)(sp + 3) * stride];
