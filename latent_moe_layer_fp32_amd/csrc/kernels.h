@@ -1155,25 +1155,47 @@ __global__ __launch_bounds__(256) void lm_combine_kernel(const float* O, const f
     s_e[tid] = ids[(size_t)t * k + tid];
   }
   __syncthreads();
-  for (int c = tid * 4; c < P; c += 1024) {
-    lm_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j = 0; j < k; ++j) {
-      // each expert-output row is read once: streaming (non-temporal) load
-      const lm_f32x4 o = __builtin_nontemporal_load((const lm_f32x4*)(O + (size_t)s_row[j] * P + c));
-      const lm_f32x4 g = *(const lm_f32x4*)(gamma + (size_t)s_e[j] * P + c);
-      acc += s_coef[j] * (g * o);
-    }
-    if constexpr (sizeof(Y) == 4) {
-      *(lm_f32x4*)((float*)y + (size_t)t * P + c) = acc;
-    } else {
-      static_assert(std::is_same_v<Y, _Float16>, "FP32 or FP16 y");
-      uint16_t hv[4];
+  // Four 4-column chunks per thread (1024 columns apart) at a time, so that
+  // each slot's eight loads are in flight together; every column still sums
+  // its slots in order.
+  constexpr int kC = 4;
+  for (int c0 = tid * 4; c0 < P; c0 += kC * 1024) {
+    lm_f32x4 acc[kC];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) hv[q] = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[q] * down));
-      lm_u32x2 v;
-      v[0] = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-      v[1] = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-      *(lm_u32x2*)((uint16_t*)y + (size_t)t * P + c) = v;
+    for (int q = 0; q < kC; ++q) acc[q] = lm_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < k; ++j) {
+      const float* orow = O + (size_t)s_row[j] * P;
+      const float* grow = gamma + (size_t)s_e[j] * P;
+      lm_f32x4 o[kC], g[kC];
+#pragma unroll
+      for (int q = 0; q < kC; ++q) {
+        const int c = c0 + q * 1024;
+        if (c < P) {
+          // each expert-output row is read once: streaming (non-temporal) load
+          o[q] = __builtin_nontemporal_load((const lm_f32x4*)(orow + c));
+          g[q] = *(const lm_f32x4*)(grow + c);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kC; ++q)
+        if (c0 + q * 1024 < P) acc[q] += s_coef[j] * (g[q] * o[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < kC; ++q) {
+      const int c = c0 + q * 1024;
+      if (c >= P) continue;
+      if constexpr (sizeof(Y) == 4) {
+        *(lm_f32x4*)((float*)y + (size_t)t * P + c) = acc[q];
+      } else {
+        static_assert(std::is_same_v<Y, _Float16>, "FP32 or FP16 y");
+        uint16_t hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[q][i] * down));
+        lm_u32x2 v;
+        v[0] = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+        v[1] = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+        *(lm_u32x2*)((uint16_t*)y + (size_t)t * P + c) = v;
+      }
     }
   }
 }
