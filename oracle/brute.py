@@ -84,6 +84,29 @@ def _mxfp4(v):
     return out
 
 
+def _f16(v: float, scale: float) -> float:
+    """v times scale (a power of two) stored in IEEE half precision (nearest,
+    ties to even, by Python's own half-precision packing), saturating at
+    +-65504, then divided by the scale again."""
+    z = max(-65504.0, min(65504.0, v * scale))
+    return struct.unpack("<e", struct.pack("<e", z))[0] / scale
+
+
+def _down(bound: float, cap: int) -> float:
+    """2^-c for the smallest c in [0, cap] with bound * 2^-c <= 2^15."""
+    if bound != bound or bound == math.inf:
+        return 2.0 ** -cap
+    c = 0
+    while c < cap and bound > 32768.0 * 2.0 ** c:
+        c += 1
+    return 2.0 ** -c
+
+
+def _silu(z: float) -> float:
+    """z * sigma(z); for z below -700, e^-z overflows a double and z e^z is used."""
+    return z / (1.0 + math.exp(-z)) if z >= -700.0 else z * math.exp(z)
+
+
 def _matvec(W, v):
     return [math.fsum(W[r][c] * v[c] for c in range(len(v))) for r in range(len(W))]
 
@@ -96,14 +119,46 @@ def _rmsnorm(v, gamma, eps):
 
 def forward(x, router, bias, pooler, pool_gamma, w_gate, w_up, w_down, expert_gamma,
             unpooler, k, eps, input_gamma=None, bf16_acts=False, mxfp8_acts=False,
-            mxfp4_acts=False):
+            mxfp4_acts=False, f16_points=False):
     """Returns (out [T][H], ids [T][k], w [T][k]) as Python lists.
 
     input_gamma: x is the pre-norm residual; the router reads its RMSNorm
     (times input_gamma) rounded to FP32, the pooler the same value rounded
     on to BF16 when bf16_acts, else the FP32 value. mxfp8_acts / mxfp4_acts:
-    the expert GEMMs read u and a MX-quantised to FP8 E4M3 / FP4 E2M1."""
+    the expert GEMMs read u and a MX-quantised to FP8 E4M3 / FP4 E2M1.
+    f16_points: u, a (unless MX-quantised), the expert output o and y are
+    stored in FP16 times a power of two each, as the layer with BF16
+    activations stores them: the largest 2^-c keeping a bound within 2^15 --
+    u: sqrt(P) max|gamma_p|, y: sqrt(P) max|gamma_e|, a (per expert, 32
+    outputs at a time): the largest ||Wg row|| ||Wu row|| of the block times
+    P max(gamma_p)^2, o (per expert): see o_scale; the per-expert norm takes
+    the RMS of the unrounded o."""
     T, E = len(x), len(router)
+    if f16_points:
+        P0 = len(pooler)
+        gpm = max(abs(float(g)) for g in pool_gamma)
+        gem = max(abs(float(g)) for row in expert_gamma for g in row)
+        su = _down(math.sqrt(P0) * gpm, 100)
+        sy = _down(math.sqrt(P0) * gem, 100)
+
+        def o_scale(e):
+            """2^-c keeping max_p ||Wd row p|| P max(gamma_p)^2 sqrt(sum_i (||Wg row i||
+            ||Wu row i||)^2) (twice that with MX activations) within 2^15."""
+            nd = max(math.sqrt(math.fsum(float(z) * float(z) for z in row)) for row in w_down[e])
+            s2 = math.fsum((math.sqrt(math.fsum(float(z) * float(z) for z in w_gate[e][i]))
+                            * math.sqrt(math.fsum(float(z) * float(z) for z in w_up[e][i]))) ** 2
+                           for i in range(len(w_gate[e])))
+            amp = 2.0 if (mxfp8_acts or mxfp4_acts) else 1.0
+            return _down(nd * P0 * gpm * gpm * math.sqrt(s2) * amp, 100)
+
+        def a_scale(e, i):
+            b0 = i - i % 32
+            m = 0.0
+            for r in range(b0, b0 + 32):
+                ng = math.sqrt(math.fsum(float(z) * float(z) for z in w_gate[e][r]))
+                nu = math.sqrt(math.fsum(float(z) * float(z) for z in w_up[e][r]))
+                m = max(m, ng * nu)
+            return _down(m * P0 * gpm * gpm, 60)
     outs, all_ids, all_w = [], [], []
     for t in range(T):
         xt = [float(v) for v in x[t]]
@@ -130,6 +185,8 @@ def forward(x, router, bias, pooler, pool_gamma, w_gate, w_up, w_down, expert_ga
         wt = [v / s for v in ex]
 
         u = _rmsnorm(_matvec(pooler, xt), pool_gamma, eps)
+        if f16_points and not (mxfp8_acts or mxfp4_acts):
+            u = [_f16(z, su) for z in u]
         if mxfp8_acts:
             u = _mxfp8(u)
         if mxfp4_acts:
@@ -139,14 +196,23 @@ def forward(x, router, bias, pooler, pool_gamma, w_gate, w_up, w_down, expert_ga
         for j, e in enumerate(chosen):
             g = _matvec(w_gate[e], u)
             v = _matvec(w_up[e], u)
-            a = [g[i] / (1.0 + math.exp(-g[i])) * v[i] for i in range(len(g))]
+            a = [_silu(g[i]) * v[i] for i in range(len(g))]
+            if f16_points and not (mxfp8_acts or mxfp4_acts):
+                a = [_f16(a[i], a_scale(e, i)) for i in range(len(a))]
             if mxfp8_acts:
                 a = _mxfp8(a)
             if mxfp4_acts:
                 a = _mxfp4(a)
             o = _matvec(w_down[e], a)
             oh = _rmsnorm(o, expert_gamma[e], eps)
+            if f16_points:  # o stored in FP16 times its expert's power of two; the norm of o itself
+                so = o_scale(e)
+                ms = math.fsum(z * z for z in o) / len(o)
+                d = math.sqrt(ms + eps)
+                oh = [_f16(o[i], so) / d * float(expert_gamma[e][i]) for i in range(len(o))]
             y = [y[p] + wt[j] * oh[p] for p in range(P)]
+        if f16_points:
+            y = [_f16(z, sy) for z in y]
         outs.append(_matvec(unpooler, y))
         all_ids.append(chosen)
         all_w.append(wt)

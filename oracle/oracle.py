@@ -39,6 +39,27 @@ input values; BF16/FP32 inputs widen exactly, MXFP4 weights decode exactly):
 8. Unpooler back to the model width ([lmsys] same MoE section; [vllm]
    "潜空间 MoE"): out_t = Wun y_t.
 
+Emulation mode (emulate="f16"): the same steps with the layer's own rounding
+points applied, so that a kernel can be checked far tighter than the FP64
+bound. With BF16 activations the expert and unpooler products run on FP16
+operands that the layer forms itself: u (step 4), the SwiGLU output a (step 5)
+and the combined y (step 7) are each rounded to FP16 (nearest even,
+saturating at 65504) after multiplication by a power of two fixed at create,
+and divided by it again after the product (the products themselves are exact
+in FP16 x FP16 -> FP32 up to FP32 accumulation). The powers of two follow
+bounds on each value: |u_i| <= sqrt(P) max|gamma_p| and |y_i| <= sqrt(P)
+max|gamma_e| (no element of an RMS-normed row exceeds sqrt(P) times its
+gamma; routing weights sum to one), and per expert and block of 32 SwiGLU
+outputs |a_i| <= ||Wg_i|| ||Wu_i|| P max(gamma_p)^2 (Cauchy-Schwarz, |silu(g)|
+<= |g|); each value is stored times the largest power of two that keeps its
+bound within 2^15 (1 when the bound already is). The expert output o (step
+5) is stored in FP16 too, one power of two per expert from |o_p| <=
+||Wd_p|| ||a|| <= max_p ||Wd_p|| P max(gamma_p)^2 sqrt(sum_i (||Wg_i||
+||Wu_i||)^2) (twice that with MX activations: a code may exceed its value by
+up to a factor 1.5); its per-expert RMS (step 6) is that of the unrounded o.
+With MX activations (act_quant) u and a are the MX codes instead and only o
+and y are FP16.
+
 Readings where the pages are silent (each listed in the design notes): without
 an input gamma, x is already the normed token (the sandwich norm sits outside
 the layer, [vllm] "三明治归一化"); gammas multiply directly; one eps for all
@@ -49,7 +70,7 @@ per-expert gamma has shape [E, P].
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import Callable, Sequence
+from typing import Callable
 
 import numpy as np
 
@@ -140,16 +161,19 @@ def experts_from_arrays(w_gate, w_up, w_down) -> ExpertFn:
 def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, expert_gamma,
             unpooler, k: int, eps: float, *, force_ids: dict | None = None,
             order: str = "norm_then_sum", keep_pairs: bool = True,
-            round_bf16: Sequence[str] = (), input_gamma=None,
-            act_quant: str | None = None, force_u: dict | None = None) -> OracleResult:
+            emulate=None, input_gamma=None,
+            act_quant: str | None = None, force_u: dict | None = None):
     """Layer forward on tokens x [T, H] (any stored dtype).
 
     force_ids: {token: ids sequence} replaces the selection for those tokens
       (weights recomputed from this oracle's own FP64 logits).
     order: "norm_then_sum" is the layer; "sum_then_norm" normalises the
       combined vector instead (used only to show that the two differ).
-    round_bf16: diagnostic emulation; any of "u", "a", "y" rounds that
-      intermediate to BF16 (nearest even) the way a BF16 datapath would.
+    emulate: None (the exact definition) or "f16": u, a and y rounded to FP16
+      at the layer's declared points with their power-of-two range scalings
+      (module docstring; f16_scales). A tuple of these returns a list of
+      results, one per mode, computed in one pass over the experts (each
+      expert's weights fetched once).
     input_gamma: [H] gamma of the boundary norm (step 0); x is then the
       pre-norm residual.
     act_quant: None, "mxfp8" or "mxfp4": the expert GEMMs read u and a
@@ -159,6 +183,10 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
       rounded either way by a kernel that forms it in lower precision; the
       caller checks that the rows differ from this oracle's only there).
     """
+    modes = tuple(emulate) if isinstance(emulate, (tuple, list)) else (emulate,)
+    for m in modes:
+        if m not in (None, "f16"):
+            raise ValueError(f"unknown emulation {m!r}")
     act_bf16 = np.asarray(x).dtype == np.uint16
     x = to_f64(x)
     xn = None
@@ -174,7 +202,6 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
     ge = to_f64(expert_gamma)
     Wun = to_f64(unpooler)
     T = x.shape[0]
-    E = Wr.shape[0]
     P = Wp.shape[0]
 
     logits = router_logits(x_router, Wr, b)
@@ -187,61 +214,111 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
     near = (gaps < NEAR_TIE).any(axis=-1)
 
     h = x @ Wp.T
-    u = rms_norm(h, gp, eps)
-    if "u" in round_bf16:
-        u = _bf16_round(u)
+    u_exact = rms_norm(h, gp, eps)
+    sc = f16_scales(gp, ge, P) if "f16" in modes else None
     u_pre = None
     if act_quant:
-        u_pre = u
-        u = quantize_mx(u, act_quant)[0]
+        u_pre = u_exact
+        uq = quantize_mx(u_exact, act_quant)[0]
         if force_u:
-            u = u.copy()
+            uq = uq.copy()
             for t, row in force_u.items():
-                u[t] = row
+                uq[t] = row
 
-    I = None
-    ohat = np.zeros((T, k, P))
-    o_all = np.zeros((T, k, P)) if keep_pairs else None
-    a_all = None
+    # per mode: the expert input u and the per-slot results
+    st = []
+    for m in modes:
+        u = uq if act_quant else (f16_round(u_exact, sc["u"]) if m == "f16" else u_exact)
+        st.append(dict(u=u, ohat=np.zeros((T, k, P)), o=np.zeros((T, k, P)) if keep_pairs else None, a=None))
+
     for e in np.unique(ids):
         tt, jj = np.nonzero(ids == e)
         Wg, Wu, Wd = experts(int(e))
-        if I is None:
-            I = Wg.shape[0]
-            a_all = np.zeros((T, k, I)) if keep_pairs else None
-        U = u[tt]
-        g = U @ Wg.T
-        v = U @ Wu.T
-        a = silu(g) * v
-        if "a" in round_bf16:
-            a = _bf16_round(a)
-        if act_quant:
-            a = quantize_mx(a, act_quant)[0]
-        o = a @ Wd.T
-        if keep_pairs:
-            a_all[tt, jj] = a
-            o_all[tt, jj] = o
-        if order == "norm_then_sum":
-            ohat[tt, jj] = rms_norm(o, ge[e], eps)
-        else:
-            ohat[tt, jj] = o
+        asc = np.repeat(a_scales(Wg, Wu, P, gp), 32) if "f16" in modes and not act_quant else None
+        osc = o_scale(Wg, Wu, Wd, P, gp, 2.0 if act_quant else 1.0) if "f16" in modes else None
+        for m, S in zip(modes, st):
+            U = S["u"][tt]
+            g = U @ Wg.T
+            v = U @ Wu.T
+            a = silu(g) * v
+            if m == "f16" and not act_quant:
+                a = f16_round(a, asc)
+            if act_quant:
+                a = quantize_mx(a, act_quant)[0]
+            o = a @ Wd.T
+            o_st = f16_round(o, osc) if m == "f16" else o  # o as stored; its norm uses o
+            if keep_pairs:
+                if S["a"] is None:
+                    S["a"] = np.zeros((T, k, Wg.shape[0]))
+                S["a"][tt, jj] = a
+                S["o"][tt, jj] = o_st
+            if order == "norm_then_sum":
+                S["ohat"][tt, jj] = o_st / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps) * ge[e]
+            else:
+                S["ohat"][tt, jj] = o_st
 
-    y = np.zeros((T, P))
-    for j in range(k):  # slot order
-        y = y + w[:, j : j + 1] * ohat[:, j]
-    if order == "sum_then_norm":
-        y = rms_norm(y, np.ones(P), eps)
-    if "y" in round_bf16:
-        y = _bf16_round(y)
-    out = y @ Wun.T
-    return OracleResult(out=out, ids=ids, w=w, logits=logits, gaps=gaps, h=h, u=u, a=a_all,
-                        o=o_all, ohat=ohat if keep_pairs else None, y=y, near_tie=near, xn=xn,
-                        u_pre=u_pre)
+    res = []
+    for m, S in zip(modes, st):
+        y = np.zeros((T, P))
+        for j in range(k):  # slot order
+            y = y + w[:, j : j + 1] * S["ohat"][:, j]
+        if order == "sum_then_norm":
+            y = rms_norm(y, np.ones(P), eps)
+        if m == "f16":
+            y = f16_round(y, sc["y"])
+        out = y @ Wun.T
+        res.append(OracleResult(out=out, ids=ids, w=w, logits=logits, gaps=gaps, h=h, u=S["u"], a=S["a"],
+                                o=S["o"], ohat=S["ohat"] if keep_pairs else None, y=y, near_tie=near, xn=xn,
+                                u_pre=u_pre))
+    return res if isinstance(emulate, (tuple, list)) else res[0]
+
+
+def f16_round(v: np.ndarray, scale) -> np.ndarray:
+    """v stored as FP16 times `scale` (a power of two): nearest even, saturating
+    at the largest finite FP16 value, then divided by the scale again."""
+    z = np.clip(np.asarray(v, np.float64) * scale, -65504.0, 65504.0)
+    return z.astype(np.float16).astype(np.float64) / scale
+
+
+def pow2_down(bound: float, cap: int) -> float:
+    """The largest power of two 2^-c (0 <= c <= cap) with bound * 2^-c <= 2^15;
+    2^-cap for an infinite or NaN bound."""
+    if not np.isfinite(bound):
+        return 2.0 ** -cap
+    c = 0
+    while bound * 2.0 ** -c > 32768.0 and c < cap:
+        c += 1
+    return 2.0 ** -c
+
+
+def f16_scales(pool_gamma, expert_gamma, P: int) -> dict:
+    """Powers of two u and y are stored with in FP16 (module docstring): from
+    the bounds sqrt(P) max|gamma_p| and sqrt(P) max|gamma_e|."""
+    return {"u": pow2_down(np.sqrt(P) * float(np.max(np.abs(pool_gamma))), 100),
+            "y": pow2_down(np.sqrt(P) * float(np.max(np.abs(expert_gamma))), 100)}
+
+
+def a_scales(Wg, Wu, P: int, pool_gamma) -> np.ndarray:
+    """Powers of two one expert's SwiGLU outputs are stored with in FP16, per
+    block of 32 outputs [I/32]: from max over the block of ||Wg_i|| ||Wu_i||
+    times P max(gamma_p)^2 (module docstring)."""
+    gp = float(np.max(np.abs(pool_gamma)))
+    m = (np.linalg.norm(Wg, axis=1) * np.linalg.norm(Wu, axis=1)).reshape(-1, 32).max(axis=1)
+    return np.array([pow2_down(b * P * gp * gp, 60) for b in m])
+
+
+def o_scale(Wg, Wu, Wd, P: int, pool_gamma, amp: float = 1.0) -> float:
+    """Power of two one expert's outputs are stored with in FP16: from
+    max_p ||Wd_p|| P max(gamma_p)^2 sqrt(sum_i (||Wg_i|| ||Wu_i||)^2), times
+    amp (module docstring)."""
+    gp = float(np.max(np.abs(pool_gamma)))
+    na = np.sqrt(np.sum((np.linalg.norm(Wg, axis=1) * np.linalg.norm(Wu, axis=1)) ** 2))
+    return pow2_down(float(np.linalg.norm(Wd, axis=1).max()) * P * gp * gp * na * amp, 100)
 
 
 def _bf16_round(v: np.ndarray) -> np.ndarray:
     """FP64 -> FP32 (nearest) -> BF16 (nearest even) -> FP64 (the boundary
-    norm's BF16 output, and the diagnostic emulation)."""
+    norm's BF16 output)."""
     f = v.astype(np.float32)
     u = f.view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
