@@ -24,8 +24,9 @@
  *     when the handle was created; tensors are dense, row-major, in the
  *     [out_features, in_features] convention of the linear maps above.
  *   - Every pointer must be 16-byte aligned; H and P must be multiples of
- *     64, I a multiple of 128 (with BF16 activations, whatever the expert
- *     format, all three multiples of 512); 1 <= E <= 1024.
+ *     64, I a multiple of 128, 1 <= E <= 1024 (else INVALID_ARG). Layers with
+ *     BF16 activations, whatever the expert format, are built for H, P and I
+ *     multiples of 512 (other valid sizes: UNSUPPORTED).
  *   - Calls return 0 (LMOE_OK) or a negative error code; no exception or
  *     abort crosses the ABI. latent_moe_last_error() then holds a message for
  *     the calling thread. All argument checks run on the host before any GPU
@@ -47,6 +48,7 @@ extern "C" {
 #define LMOE_ERR_OOM (-3)             /* device allocation failed in create */
 #define LMOE_ERR_HIP (-4)             /* any HIP runtime error, including "no device" */
 #define LMOE_ERR_TOO_MANY_TOKENS (-5) /* T > max_tokens of the handle */
+#define LMOE_ERR_CORRUPT (-6)         /* debug mode only: workspace guard words overwritten */
 
 /* Element formats. */
 #define LMOE_F32 0   /* IEEE binary32 */
@@ -64,7 +66,7 @@ typedef struct {
   int64_t pooled;       /* P: expert width after the pooler (4096) */
   int64_t experts;      /* E: routed experts per layer (256) */
   int64_t intermediate; /* I: SwiGLU intermediate width per expert */
-  int32_t top_k;        /* k: experts per token, 1 <= k <= min(E, 16) */
+  int32_t top_k;        /* k: experts per token, 1 <= k <= min(E, 32) */
   float eps;            /* RMSNorm epsilon for both norms, finite, >= 0 */
   int32_t act_dtype;    /* x, pooler and unpooler: LMOE_F32 or LMOE_BF16.
                            LMOE_BF16: the pooler multiplies BF16 x by BF16 Wp;
@@ -118,14 +120,16 @@ typedef struct {
                            act_dtype LMOE_BF16 and change the numerics. */
 } latent_moe_config;
 
-/* Layer weights (device pointers), read in place unless stated otherwise; the
- * caller keeps them alive and unchanged until latent_moe_destroy returns.
- * With BF16 activations, create() also copies pooler, unpooler and the three
- * expert matrices into library-owned memory in a matrix-core tiled layout
- * (blocks of 32 rows x 64 columns ordered as the MFMA B fragments; MXFP4
- * codes and scales likewise, the scale bytes of four k-tiles side by side),
- * and splits the router into three BF16 pieces; forward then reads those
- * copies. An MXFP4 scale byte 0xFF (NaN in E8M0) makes its 32 elements NaN.
+/* Layer weights (device pointers, on the device current at create). They are
+ * BORROWED FOR THE DURATION OF latent_moe_create ONLY: create copies every
+ * tensor the forward reads into library-owned device memory and synchronises
+ * its stream before returning, so the caller may free or overwrite them as
+ * soon as create returns. FP32 layers keep the copies as given; BF16 layers
+ * keep the pooler in BF16, the unpooler and the three expert matrices in a
+ * matrix-core tiled layout (blocks of 32 rows x 64 columns ordered as the
+ * MFMA B fragments; MXFP4 codes and scales likewise, the scale bytes of four
+ * k-tiles side by side), and the router as its exact three-piece BF16 split.
+ * An MXFP4 scale byte 0xFF (NaN in E8M0) makes its 32 elements NaN.
  *   router       [E, H]   F32
  *   router_bias  [E]      F32, or NULL for no bias (added to the logits)
  *   pooler       [P, H]   act_dtype
@@ -153,17 +157,26 @@ typedef struct {
   const float* input_gamma; /* [H] F32 when cfg.input_norm, else ignored */
 } latent_moe_weights;
 
-/* Create a handle on the current device. Validates cfg and w, allocates the
- * workspace for cfg->max_tokens tokens (never reallocated later) and, for
- * BF16 activations, the repacked weight copies (about the size of the expert
- * weights again), creates the handle's routing stream (default priority),
- * and synchronises the device before returning.
- * Errors: INVALID_ARG, UNSUPPORTED, OOM, HIP. On error *out is set to NULL
- * and nothing is leaked. */
-int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const latent_moe_weights* w);
+/* Create a handle on the current device. Validates cfg and w on the host,
+ * allocates the workspace for cfg->max_tokens tokens (never reallocated
+ * later) and one buffer for the weight copies (about the size of the given
+ * weights), runs the copy and repack kernels on `stream` (a hipStream_t; NULL
+ * = the null stream), creates the handle's routing stream (default priority)
+ * and synchronises `stream` (not the device) before returning. Nothing of `w`
+ * is referenced after create returns.
+ * Errors: INVALID_ARG, UNSUPPORTED, OOM, HIP. On error *out is set to NULL and
+ * everything create allocated is released.
+ * Test hooks (environment, read at create): LATENT_MOE_FAULT=alloc (or
+ * alloc:N) makes the first (N-th) device allocation of create fail with OOM;
+ * LATENT_MOE_DEBUG=poison fills the workspace with 0xFF bytes at create and
+ * before every forward (a stage that reads a value not written earlier in the
+ * same forward then sees NaN) and puts guard words after it, checked by
+ * destroy (LMOE_ERR_CORRUPT). */
+int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const latent_moe_weights* w,
+                      void* stream);
 
-/* Bytes of device workspace a handle with this config allocates (beyond the
- * borrowed weights). Errors as for create's validation. */
+/* Bytes of device workspace a handle with this config allocates (besides its
+ * copies of the weights). Errors as for create's validation. */
 int latent_moe_workspace_bytes(const latent_moe_config* cfg, size_t* bytes);
 
 /* Run the layer on T tokens, asynchronously on `stream` (a hipStream_t; NULL =
@@ -202,7 +215,8 @@ int latent_moe_forward(latent_moe_t* h, const void* x, int64_t T, float* out, in
  *   row_scale [T] F32: 1/sqrt(mean((Wp x_t)^2) + eps)
  *   act      [T*k, I] (F32 if expert_dtype is F32, else FP16): SwiGLU
  *            output, grouped order
- *   expert_out [T*k, P] F32: o (before the per-expert norm), grouped order
+ *   expert_out [T*k, P]: o (before the per-expert norm), grouped order; F32
+ *            in FP32 layers, FP16 times expert_out_down[e] in BF16 layers
  *   combined y [T, P]: F32 in FP32 layers, FP16 in BF16 layers          */
 typedef struct {
   const float* logits;
@@ -215,7 +229,7 @@ typedef struct {
   const void* pooled;
   const float* row_scale;
   const void* act;
-  const float* expert_out;
+  const void* expert_out;
   const void* combined;
   const uint8_t* expert_in;        /* the expert GEMMs' input u as they read it:
                                       MX expert inputs: codes, [T, P] E4M3 bytes
@@ -240,6 +254,11 @@ typedef struct {
                             act_down[e][i/32], a power of two (1 unless the
                             Cauchy-Schwarz bound |a_i| <= ||Wg_i|| ||Wu_i|| P
                             max|gamma_p|^2 exceeds 2^15); else NULL */
+  const float* expert_out_down; /* BF16 layers: [E] F32, expert_out holds FP16 o times
+                            expert_out_down[e] for a pair routed to expert e, a power
+                            of two keeping ||Wd_p|| ||u||^2 sqrt(sum_i (||Wg_i||
+                            ||Wu_i||)^2) within 2^15; FP32 layers: NULL (expert_out
+                            is F32) */
 } latent_moe_views;
 
 int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v);
@@ -260,8 +279,11 @@ int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v);
 int latent_moe_set_profiling(latent_moe_t* h, int enable);
 int latent_moe_stage_times(latent_moe_t* h, float* ms, int n);
 
-/* Wait for the handle's work, free its workspace and the handle. NULL returns
- * INVALID_ARG. Using a handle after destroy is undefined. */
+/* Wait for the handle's work (device synchronisation), free its workspace,
+ * weight copies, routing stream and the handle. NULL returns INVALID_ARG.
+ * CORRUPT (debug mode only): guard words after the workspace were overwritten
+ * (the handle is freed all the same). Using a handle after destroy is
+ * undefined. */
 int latent_moe_destroy(latent_moe_t* h);
 
 /* Message for the last failed call on this thread ("" if none). The string is

@@ -23,6 +23,7 @@ LMOE_ERR_UNSUPPORTED = -2
 LMOE_ERR_OOM = -3
 LMOE_ERR_HIP = -4
 LMOE_ERR_TOO_MANY_TOKENS = -5
+LMOE_ERR_CORRUPT = -6
 LMOE_F32, LMOE_BF16, LMOE_MXFP4, LMOE_MXFP8 = 0, 1, 2, 3
 DTYPE_CODES = {"f32": LMOE_F32, "bf16": LMOE_BF16, "mxfp4": LMOE_MXFP4, "mxfp8": LMOE_MXFP8}
 
@@ -60,7 +61,7 @@ class Views(ctypes.Structure):
         "logits", "ids", "weights", "counts", "offsets", "perm_token", "pair_row", "pooled",
         "row_scale", "act", "expert_out", "combined", "expert_in", "expert_in_scales", "act_scales",
         "x_norm")] + [("expert_in_scale", ctypes.c_float), ("combined_scale", ctypes.c_float),
-                      ("act_down", ctypes.c_void_p)]
+                      ("act_down", ctypes.c_void_p), ("expert_out_down", ctypes.c_void_p)]
 
 
 _lib = None
@@ -78,7 +79,7 @@ def lib():
             raise ImportError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
         L = ctypes.CDLL(LIB_PATH)
         L.latent_moe_create.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(Config),
-                                        ctypes.POINTER(Weights)]
+                                        ctypes.POINTER(Weights), ctypes.c_void_p]
         L.latent_moe_create.restype = ctypes.c_int
         L.latent_moe_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_size_t)]
         L.latent_moe_workspace_bytes.restype = ctypes.c_int
@@ -128,9 +129,9 @@ def latent_moe_workspace_bytes(cfg: Config) -> int:
     return n.value
 
 
-def latent_moe_create(cfg: Config, w: Weights) -> int:
+def latent_moe_create(cfg: Config, w: Weights, stream: int | None = None) -> int:
     h = ctypes.c_void_p(0)
-    _check(lib().latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)))
+    _check(lib().latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w), stream))
     return h.value
 
 
@@ -170,15 +171,84 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def weight_specs(hidden, pooled, experts, intermediate, act_dtype, expert_dtype, input_norm=False,
+                 router_bias=False) -> dict:
+    """Expected (shape, torch dtype name) of each weight tensor; MXFP4 expert
+    tensors are (packed codes, scales) pairs, given as a pair of specs."""
+    H, P, E, I = hidden, pooled, experts, intermediate
+    act = {"f32": "float32", "bf16": "bfloat16"}[act_dtype]
+    spec = {"router": ((E, H), "float32"), "pooler": ((P, H), act), "pool_gamma": ((P,), "float32"),
+            "expert_gamma": ((E, P), "float32"), "unpooler": ((H, P), act)}
+    if router_bias:
+        spec["router_bias"] = ((E,), "float32")
+    if input_norm:
+        spec["input_gamma"] = ((H,), "float32")
+    for name, n, k in (("w_gate", I, P), ("w_up", I, P), ("w_down", P, I)):
+        if expert_dtype == "mxfp4":
+            spec[name] = (((E, n, k // 2), "uint8"), ((E, n, k // 32), "uint8"))
+        else:
+            spec[name] = ((E, n, k), {"f32": "float32", "bf16": "bfloat16"}[expert_dtype])
+    return spec
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is missing")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if str(t.dtype).replace("torch.", "") not in (dtype, "int16" if dtype == "bfloat16" else dtype):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def validate_weights(weights: dict, specs: dict, device) -> None:
+    """Shape, dtype (BF16 may come as its int16 bits), device and contiguity of
+    every weight; ValueError names the first mismatch."""
+    # input_gamma is ignored without input_norm (as the C ABI ignores it); any
+    # other name the layer does not take is an error
+    extra = set(k for k, v in weights.items() if v is not None) - set(specs) - {"input_gamma"}
+    if extra:
+        raise ValueError(f"unexpected weights {sorted(extra)}")
+    for name, sp in specs.items():
+        v = weights.get(name)
+        if isinstance(sp[0][0], tuple):  # MXFP4 pair
+            if not isinstance(v, tuple) or len(v) != 2:
+                raise ValueError(f"{name} must be a (codes, scales) pair for MXFP4 experts")
+            _check_tensor(name + " codes", v[0], sp[0][0], sp[0][1], device)
+            _check_tensor(name + " scales", v[1], sp[1][0], sp[1][1], device)
+        else:
+            _check_tensor(name, v, sp[0], sp[1], device)
+
+
+def validate_forward(x, out, topk_ids, topk_weights, hidden, top_k, act_dtype, device) -> None:
+    """x [T, hidden] in the activation dtype; out F32 [T, hidden]; optional
+    topk_ids int32 and topk_weights F32 [T, top_k]; all contiguous on device."""
+    if x.dim() != 2 or x.shape[1] != hidden:
+        raise ValueError(f"x must be [T, {hidden}], got {tuple(x.shape)}")
+    T = x.shape[0]
+    act = {"f32": "float32", "bf16": "bfloat16"}[act_dtype]
+    _check_tensor("x", x, (T, hidden), act, device)
+    if out is not None:
+        _check_tensor("out", out, (T, hidden), "float32", device)
+    if topk_ids is not None:
+        _check_tensor("topk_ids", topk_ids, (T, top_k), "int32", device)
+    if topk_weights is not None:
+        _check_tensor("topk_weights", topk_weights, (T, top_k), "float32", device)
+
+
 class LatentMoE:
-    """A layer handle over borrowed torch device tensors.
+    """A layer handle created from torch device tensors.
 
     weights: dict with router, router_bias (or None), pooler, pool_gamma,
     w_gate, w_up, w_down (MXFP4: (packed, scales) pairs), expert_gamma,
     unpooler, and input_gamma when input_norm (x is then the pre-norm
     residual). expert_act="mxfp8" or "mxfp4" runs the expert GEMMs on MX FP8 or
-    MX FP4 activations (MXFP4 experts only). The tensors are referenced by this object so they
-    outlive the handle.
+    MX FP4 activations (MXFP4 experts only). Shapes, dtypes and devices are
+    checked here; the library copies what it needs during create (on the
+    current stream), so the tensors need not outlive the constructor.
     """
 
     def __init__(self, *, hidden, pooled, experts, intermediate, top_k, eps, act_dtype,
@@ -193,7 +263,10 @@ class LatentMoE:
         self.top_k, self.hidden, self.pooled, self.experts = top_k, hidden, pooled, experts
         self.intermediate = intermediate
         self.act_dtype, self.expert_dtype = act_dtype, expert_dtype
-        self._keep = dict(weights)
+        self.device = torch.device("cuda", torch.cuda.current_device())
+        specs = weight_specs(hidden, pooled, experts, intermediate, act_dtype, expert_dtype, input_norm,
+                             weights.get("router_bias") is not None)
+        validate_weights(weights, specs, self.device)
         w = Weights()
         for name in ("router", "router_bias", "pooler", "pool_gamma", "expert_gamma", "unpooler",
                      "input_gamma"):
@@ -205,18 +278,12 @@ class LatentMoE:
                 setattr(w, sname, _ptr(v[1]))
             else:
                 setattr(w, name, _ptr(v))
-        for name, v in weights.items():
-            for t in (v if isinstance(v, tuple) else (v,)):
-                if t is not None and (not t.is_cuda or not t.is_contiguous()):
-                    raise ValueError(f"weight {name} must be a contiguous device tensor")
-        self.device = torch.device("cuda", torch.cuda.current_device())
-        self.handle = latent_moe_create(self.cfg, w)
+        self.handle = latent_moe_create(self.cfg, w, torch.cuda.current_stream(self.device).cuda_stream)
 
     def forward(self, x, out=None, topk_ids=None, topk_weights=None, stream=None):
         import torch
 
-        if not (x.is_cuda and x.is_contiguous() and x.dim() == 2 and x.shape[1] == self.hidden):
-            raise ValueError("x must be a contiguous [T, hidden] device tensor")
+        validate_forward(x, out, topk_ids, topk_weights, self.hidden, self.top_k, self.act_dtype, self.device)
         T = x.shape[0]
         if out is None:
             out = torch.empty((T, self.hidden), dtype=torch.float32, device=x.device)
@@ -252,7 +319,7 @@ class LatentMoE:
             "pooled": (v.pooled, (T, P), np.float32),
             "row_scale": (v.row_scale, (T,), np.float32),
             "act": (v.act, (T * k, I // cb), exp_np),
-            "expert_out": (v.expert_out, (T * k, P), np.float32),
+            "expert_out": (v.expert_out, (T * k, P), np.float32 if f32 else np.float16),
             "combined": (v.combined, (T, P), np.float32 if f32 else np.float16),
         }
         if not f32 and not mxa:  # the FP16 u the expert GEMMs read
@@ -278,13 +345,18 @@ class LatentMoE:
             res["expert_in"] = res["expert_in"].astype(np.float32) / np.float32(v.expert_in_scale)
         if not f32 and "combined" in res:
             res["combined"] = res["combined"].astype(np.float32) / np.float32(v.combined_scale)
-        if not f32 and not mxa and "act" in res and v.act_down:  # FP16 a times act_down[e][i/32]
-            ad = np.empty((E, I // 32), np.float32)
-            _memcpy_d2h(ad.ctypes.data, v.act_down, ad.nbytes)
+        if not f32 and (("act" in res and not mxa and v.act_down) or "expert_out" in res):
             offs = np.empty((E + 1,), np.int32)
             _memcpy_d2h(offs.ctypes.data, v.offsets, offs.nbytes)
             expert_of_row = np.searchsorted(offs[1:], np.arange(T * k), side="right")
-            res["act"] = res["act"].astype(np.float32) / np.repeat(ad[expert_of_row], 32, axis=1)
+            if "act" in res and not mxa and v.act_down:  # FP16 a times act_down[e][i/32]
+                ad = np.empty((E, I // 32), np.float32)
+                _memcpy_d2h(ad.ctypes.data, v.act_down, ad.nbytes)
+                res["act"] = res["act"].astype(np.float32) / np.repeat(ad[expert_of_row], 32, axis=1)
+            if "expert_out" in res:  # FP16 o times expert_out_down[e]
+                od = np.empty((E,), np.float32)
+                _memcpy_d2h(od.ctypes.data, v.expert_out_down, od.nbytes)
+                res["expert_out"] = res["expert_out"].astype(np.float32) / od[expert_of_row][:, None]
         if split_norm and "x_norm" in res:  # FP32 value = sum of the three BF16 pieces (exact)
             H = self.hidden
             pcs = (res["x_norm"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)

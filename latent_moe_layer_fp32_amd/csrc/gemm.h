@@ -75,7 +75,8 @@ struct LmGemmCfg {
   static constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   static constexpr int FLUSH = FLUSH_;
   static constexpr int KT = 8 * LmElem<E>::kPerChunk;  // elements per k-tile
-  static_assert(WM * WN == 4 || (WM == 1 && WN == 8), "four wavefronts per workgroup, or eight along N");
+  static_assert(WM * WN == 4 || (WM == 1 && WN == 8) || (WM == 2 && WN == 4),
+                "four wavefronts per workgroup, or eight (along N, or 2 x 4)");
 };
 
 struct LmTile {

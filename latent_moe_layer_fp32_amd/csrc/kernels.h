@@ -272,6 +272,53 @@ __global__ void lm_a_shift_kernel(const float* ng, const float* nu, int64_t nblk
   }
 }
 
+// Powers of two of the FP16 expert outputs, one per expert: |o_p| = |Wd_p . a|
+// <= ||Wd_p|| ||a|| and ||a|| <= ||u||^2 sqrt(sum_i (||Wg_i|| ||Wu_i||)^2)
+// (each |a_i| <= ||Wg_i|| ||Wu_i|| ||u||^2, as for lm_a_shift_kernel), with
+// ||u||^2 <= u2; amp (1, or 2 where a is MX-quantised: a code can exceed its
+// value by at most a factor 1.5) scales the bound. o_down = the largest 2^-c,
+// 0 <= c <= 100, keeping the bound within 2^15; o_up = 2^c. One workgroup per
+// expert: ng, nu [E, I] (gate / up row norms), nd [E, P] (down row norms).
+__global__ __launch_bounds__(256) void lm_o_shift_kernel(const float* ng, const float* nu, const float* nd,
+                                                         int I, int P, float u2, float amp, float* o_down,
+                                                         float* o_up) {
+  __shared__ double red[256];
+  __shared__ float redm[256];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  double s = 0.0;
+  for (int i = tid; i < I; i += 256) {
+    const double q = (double)ng[(size_t)e * I + i] * (double)nu[(size_t)e * I + i];
+    s += q * q;
+  }
+  float m = 0.0f;
+  for (int p = tid; p < P; p += 256) m = fmaxf(m, nd[(size_t)e * P + p]);
+  red[tid] = s;
+  redm[tid] = m;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) {
+      red[tid] += red[tid + o];
+      redm[tid] = fmaxf(redm[tid], redm[tid + o]);
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const double bound = (double)redm[0] * (double)u2 * sqrt(red[0]) * (double)amp;
+    int c = 0;
+    if (!(bound <= 32768.0)) {  // above 2^15, infinite or NaN
+      if (bound <= 1e300) {
+        int ex;
+        frexp(bound / 32768.0, &ex);  // bound / 2^15 <= 2^ex
+        c = min(ex, 100);
+      } else {
+        c = 100;
+      }
+    }
+    o_down[e] = lm_pow2(-c);
+    o_up[e] = lm_pow2(c);
+  }
+}
+
 // The same for MXFP4 weights, from their E8M0 scales [rows, K/32]: with emax
 // the row's largest scale code (255, NaN, ignored), s = 139 - emax puts the
 // row's largest decoded magnitude (at most 6 x 2^(emax - 127)) in [2^14,
@@ -524,6 +571,7 @@ struct GateUpProb {
   static constexpr int kCols = Cfg::WN * 32;
   static constexpr bool kMx = MX_;  // weights in the packed MXFP4 layout
   static constexpr bool kWeightsOnce = true;
+  static constexpr bool kPairedB = true;  // B tile: WN gate groups, then the WN up groups
   static constexpr bool kScaledW = std::is_same_v<E, _Float16>;  // per-row 2^s weight copies
   static constexpr bool kRowValue = !kScaledW;                    // r applied in the epilogue
   const void* sg = nullptr;  // packed scales (MXFP4)
@@ -629,7 +677,9 @@ struct DownProb {
   const int* counts;
   const int* offsets;
   const int* tile_off;
-  float* out;  // [pairs, P]
+  float* out;  // [pairs, P] FP32, or
+  _Float16* out16 = nullptr;      // [pairs, P] FP16: o times o_down[e] (a power of two)
+  const float* o_down = nullptr;  // [E], with out16
   float* ssq;  // [pairs, nt]
   int P, I, Ex, nt;
 
@@ -667,6 +717,8 @@ struct DownProb {
     lm_tile_row_ssq<Cfg>(acc, wm, wn, lane, P - t.n0, red, [&](float v, int tn, int) { return v * dd[tn]; });
     if ((int)threadIdx.x < t.rows)
       ssq[(size_t)(t.m0 + threadIdx.x) * nt + t.nt] = red[Cfg::WN * Cfg::BM + threadIdx.x];
+    // the sums of squares come from the FP32 o; FP16 O rounds o times o_down[e]
+    const float od = out16 ? o_down[t.e] : 1.0f;
 #pragma unroll
     for (int tn = 0; tn < Cfg::TN; ++tn) {
       const int col = t.n0 + lm_acc_col<Cfg>(wn, tn, lane);
@@ -676,7 +728,10 @@ struct DownProb {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
-          if (row < t.rows) out[(size_t)(t.m0 + row) * P + col] = acc[tm][tn][i] * dd[tn];
+          if (row >= t.rows) continue;
+          const float o = acc[tm][tn][i] * dd[tn];
+          if (out16) out16[(size_t)(t.m0 + row) * P + col] = lm_f32_to_f16_sat(o * od);
+          else out[(size_t)(t.m0 + row) * P + col] = o;
         }
     }
   }
@@ -898,6 +953,7 @@ LM_DEV uint64_t lm_wave_max_u64(uint64_t v) {
 // counter sits alone in a 128-byte line (cpad[e * kLmCountStride]) so that
 // the atomics of different experts do not queue on a few lines.
 constexpr int kLmCountStride = 32;  // ints per padded expert counter
+constexpr int kLmMaxK = 32;         // largest top-k the kernels take
 
 template <int NV, int TPB>
 __global__ __launch_bounds__(256) void lm_topk_kernel(const double* part, int splits, int T, int E,
@@ -947,10 +1003,10 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const double* part, int sp
       const int e = lane + 64 * v;
       key[v] = e < E ? ((uint64_t)lm_ord(sl[tt][e]) << 32) | (uint32_t)(~(uint32_t)e) : 0;
     }
-    float selv[16];
-    int seli[16];
+    float selv[kLmMaxK];
+    int seli[kLmMaxK];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < kLmMaxK; ++j) {
       if (j < k) {
         uint64_t best = 0;
 #pragma unroll
@@ -966,17 +1022,17 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const double* part, int sp
         }
       }
     }
-    float ex[16];
+    float ex[kLmMaxK];
     float sum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < kLmMaxK; ++j) {
       if (j < k) {
         ex[j] = expf(selv[j] - selv[0]);
         sum += ex[j];
       }
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < kLmMaxK; ++j) {
       if (j < k && j == lane) {
         ids[(size_t)t * k + j] = seli[j];
         wts[(size_t)t * k + j] = ex[j] / sum;
@@ -1133,68 +1189,87 @@ __global__ __launch_bounds__(256) void lm_norm_u_kernel(const float* pooled32, c
 }
 
 // One workgroup per token: y = sum over slots j (in order) of
-// w_j / sqrt(mean(o_j^2) + eps) * gamma_{e_j} * o_j, in FP32. FP32 layers
-// store y [T, P] in FP32, BF16 layers the nearest-even FP16 rounding of
-// y * down, the unpooler's operand: |y| <= sqrt(P) max|gamma_e|, and down (a
-// power of two chosen at create) keeps that bound within 2^15.
-template <typename Y>
-__global__ __launch_bounds__(256) void lm_combine_kernel(const float* O, const float* ossq,
-                                                         int nparts, const int* pair_row,
-                                                         const int* ids, const float* wts,
-                                                         const float* gamma, int k, int P,
+// w_j / sqrt(mean(o_j^2) + eps) * gamma_{e_j} * o_j, in FP32. O is FP32
+// (FP32 layers) or FP16 holding o times o_down[e] (BF16 layers; o_up[e] =
+// 1 / o_down[e] is folded into the slot's coefficient, exactly: a power of
+// two); the sums of squares are those of the FP32 o. FP32 layers store y
+// [T, P] in FP32, BF16 layers the nearest-even FP16 rounding of y * down, the
+// unpooler's operand: |y| <= sqrt(P) max|gamma_e|, and down (a power of two
+// chosen at create) keeps that bound within 2^15.
+template <typename OT, typename Y>
+__global__ __launch_bounds__(256) void lm_combine_kernel(const OT* O, const float* ossq, int nparts,
+                                                         const int* pair_row, const int* ids, const float* wts,
+                                                         const float* gamma, const float* o_up, int k, int P,
                                                          float eps, float down, Y* y) {
-  __shared__ float s_coef[16];
-  __shared__ int s_row[16], s_e[16];
+  __shared__ float s_coef[kLmMaxK];
+  __shared__ int s_row[kLmMaxK], s_e[kLmMaxK];
   const int t = blockIdx.x, tid = threadIdx.x;
   if (tid < k) {
     const int p = pair_row[(size_t)t * k + tid];
+    const int e = ids[(size_t)t * k + tid];
     float s = 0.0f;
     for (int i = 0; i < nparts; ++i) s += ossq[(size_t)p * nparts + i];
-    s_coef[tid] = wts[(size_t)t * k + tid] * (1.0f / sqrtf(s / (float)P + eps));
+    s_coef[tid] = wts[(size_t)t * k + tid] * (1.0f / sqrtf(s / (float)P + eps)) * (o_up ? o_up[e] : 1.0f);
     s_row[tid] = p;
-    s_e[tid] = ids[(size_t)t * k + tid];
+    s_e[tid] = e;
   }
   __syncthreads();
-  // Four 4-column chunks per thread (1024 columns apart) at a time, so that
-  // each slot's eight loads are in flight together; every column still sums
+  // Eight-column chunks, two per thread (2048 columns apart) at a time, so
+  // that each slot's loads are in flight together; every column still sums
   // its slots in order.
-  constexpr int kC = 4;
-  for (int c0 = tid * 4; c0 < P; c0 += kC * 1024) {
-    lm_f32x4 acc[kC];
+  constexpr int kC = 2;
+  for (int c0 = tid * 8; c0 < P; c0 += kC * 2048) {
+    lm_f32x4 acc[kC][2];
 #pragma unroll
-    for (int q = 0; q < kC; ++q) acc[q] = lm_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q = 0; q < kC; ++q) acc[q][0] = acc[q][1] = lm_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int j = 0; j < k; ++j) {
-      const float* orow = O + (size_t)s_row[j] * P;
+      const OT* orow = O + (size_t)s_row[j] * P;
       const float* grow = gamma + (size_t)s_e[j] * P;
-      lm_f32x4 o[kC], g[kC];
+      lm_f32x4 o[kC][2], g[kC][2];
 #pragma unroll
       for (int q = 0; q < kC; ++q) {
-        const int c = c0 + q * 1024;
+        const int c = c0 + q * 2048;
         if (c < P) {
-          // each expert-output row is read once: streaming (non-temporal) load
-          o[q] = __builtin_nontemporal_load((const lm_f32x4*)(orow + c));
-          g[q] = *(const lm_f32x4*)(grow + c);
+          // each expert-output row is read once: streaming (non-temporal) loads
+          if constexpr (sizeof(OT) == 4) {
+            o[q][0] = __builtin_nontemporal_load((const lm_f32x4*)(orow + c));
+            o[q][1] = __builtin_nontemporal_load((const lm_f32x4*)(orow + c + 4));
+          } else {
+            const lm_u32x4 hv = __builtin_nontemporal_load((const lm_u32x4*)(orow + c));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              o[q][i >> 1][2 * (i & 1)] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hv[i] & 0xffffu));
+              o[q][i >> 1][2 * (i & 1) + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hv[i] >> 16));
+            }
+          }
+          g[q][0] = *(const lm_f32x4*)(grow + c);
+          g[q][1] = *(const lm_f32x4*)(grow + c + 4);
         }
       }
 #pragma unroll
       for (int q = 0; q < kC; ++q)
-        if (c0 + q * 1024 < P) acc[q] += s_coef[j] * (g[q] * o[q]);
+        if (c0 + q * 2048 < P) {
+          acc[q][0] += s_coef[j] * (g[q][0] * o[q][0]);
+          acc[q][1] += s_coef[j] * (g[q][1] * o[q][1]);
+        }
     }
 #pragma unroll
     for (int q = 0; q < kC; ++q) {
-      const int c = c0 + q * 1024;
+      const int c = c0 + q * 2048;
       if (c >= P) continue;
       if constexpr (sizeof(Y) == 4) {
-        *(lm_f32x4*)((float*)y + (size_t)t * P + c) = acc[q];
+        *(lm_f32x4*)((float*)y + (size_t)t * P + c) = acc[q][0];
+        *(lm_f32x4*)((float*)y + (size_t)t * P + c + 4) = acc[q][1];
       } else {
         static_assert(std::is_same_v<Y, _Float16>, "FP32 or FP16 y");
-        uint16_t hv[4];
+        lm_u32x4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hv[i] = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[q][i] * down));
-        lm_u32x2 v;
-        v[0] = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-        v[1] = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-        *(lm_u32x2*)((uint16_t*)y + (size_t)t * P + c) = v;
+        for (int i = 0; i < 4; ++i) {
+          const uint16_t lo = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[q][i >> 1][2 * (i & 1)] * down));
+          const uint16_t hi = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[q][i >> 1][2 * (i & 1) + 1] * down));
+          v[i] = (uint32_t)lo | ((uint32_t)hi << 16);
+        }
+        *(lm_u32x4*)((uint16_t*)y + (size_t)t * P + c) = v;
       }
     }
   }

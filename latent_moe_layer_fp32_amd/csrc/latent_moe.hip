@@ -14,12 +14,14 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
 #include <type_traits>
 
 #include "../../include/latent_moe.h"
+#include "gemm_lds.h"
 #include "gemm_stream.h"
 #include "kernels.h"
 #include "mx_act.h"
@@ -46,6 +48,50 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Test hooks, read from the environment at create:
+//   LATENT_MOE_FAULT=alloc    the first device allocation of create fails (as
+//   LATENT_MOE_FAULT=alloc:N  out of memory), or the N-th (1-based)
+//   LATENT_MOE_DEBUG=poison   the workspace is filled with 0xFF bytes (NaN
+//                             floats, -1 integers) at create and before every
+//                             forward, so a stage reading a value no earlier
+//                             stage of the same forward wrote shows up as NaN;
+//                             guard words after the workspace are checked by
+//                             destroy (LMOE_ERR_CORRUPT if any was overwritten).
+struct AllocCtl {
+  int fail_at = 0;  // 0: no injected failure
+  int n = 0;        // allocations so far
+};
+AllocCtl alloc_ctl_from_env() {
+  AllocCtl c;
+  const char* e = getenv("LATENT_MOE_FAULT");
+  if (e && strncmp(e, "alloc", 5) == 0) c.fail_at = e[5] == ':' ? atoi(e + 6) : 1;
+  return c;
+}
+hipError_t lm_malloc(AllocCtl& c, void** p, size_t bytes) {
+  if (++c.n == c.fail_at) return hipErrorOutOfMemory;
+  return hipMalloc(p, bytes);
+}
+bool debug_poison() {
+  const char* e = getenv("LATENT_MOE_DEBUG");
+  return e && strstr(e, "poison") != nullptr;
+}
+constexpr size_t kGuardBytes = 65536;
+constexpr uint32_t kGuardWord = 0x5A17C0DEu;
+
+__global__ void lm_fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+// Fill `bytes` (a multiple of 4) with a 32-bit word, by a kernel (no memset
+// node, so the call is safe inside a captured stream).
+hipError_t lm_fill_launch(void* p, size_t bytes, uint32_t v, hipStream_t s) {
+  const size_t n = bytes / 4;
+  if (!n) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255) / 256 < 16384 ? (n + 255) / 256 : 16384);
+  hipLaunchKernelGGL(lm_fill_u32_kernel, dim3(blocks), dim3(256), 0, s, (uint32_t*)p, n, v);
+  return hipGetLastError();
+}
+
 // Tile configurations: "wide" for many rows per expert (prefill-sized),
 // "narrow" for few (decode-sized). 16-bit operands run the streaming-B kernel
 // (four or eight waves along N, 64 output columns each); FP32 runs the
@@ -65,6 +111,20 @@ using CfgWide = std::conditional_t<
     std::is_same_v<E, _Float16>, LmGemmCfg<E, 1, LM_EXPERT_WN, LM_WIDE_TM, 2>,
     std::conditional_t<sizeof(E) == 2, LmGemmCfg<E, 1, 4, LM_WIDE_TM, 2>, LmGemmCfg<E, 2, 2, 2, 2>>>;
 template <typename E> using CfgNarrow = LmGemmCfg<E, 1, 4, 1, 2>;
+// Prefill-sized 16-bit GEMMs with both operands staged in LDS by direct loads
+// (lm_gemm_lds_kernel): 256 x 256 tiles of eight waves, two k-tile stages.
+// BF16 experts and the dense projections; MXFP4 experts keep the streaming
+// kernel.
+// Expert outputs O of BF16 layers in FP16 (o times a per-expert power of two)
+// or, with 0, in FP32.
+#ifndef LM_O_F16
+#define LM_O_F16 1
+#endif
+// Off by default: slower than the streaming kernel on the prefill shapes.
+#ifndef LM_LDS_GEMM
+#define LM_LDS_GEMM 0
+#endif
+template <typename E> using CfgLds = LmGemmCfg<E, 2, 4, 4, 2>;
 // Router: FP32 chains of one k-tile (64 BF16 products per lane pair), FP64 beyond.
 template <typename E> using CfgRouterWide = LmGemmCfg<E, 2, 2, 1, 2, 1>;
 template <typename E> using CfgRouterNarrow = LmGemmCfg<E, 1, 4, 1, 2, 1>;
@@ -76,7 +136,7 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 struct Layout {
   size_t part, logits, ids, wts, cpad, counts, offsets, tile_off, perm_token, pair_row, pooled, pssq,
-      row_scale, act, O, ossq, y, wr3, kpart, xn, xna, uq, us, acts, u16, total;
+      row_scale, act, O, ossq, y, kpart, xn, xna, uq, us, acts, u16, total;
 };
 
 // Split-K plan for a dense BF16 projection: split only when the output tiles
@@ -101,14 +161,14 @@ constexpr int kStages = LMOE_NUM_STAGES;
 
 struct latent_moe {
   latent_moe_config cfg;
-  latent_moe_weights w;
+  latent_moe_weights w;            // points into `owned` after create (nothing is borrowed)
   int device;
-  char* ws;
+  char* ws;                        // workspace (+ guard words in poison mode)
   Layout lay;
   size_t part_floats;
-  char* packed;                    // BF16: weights in the matrix-core layout
-  size_t packed_bytes;
-  const void* pk_pooler;
+  char* owned;                     // library-owned copies of every weight the forward reads
+  size_t owned_bytes;
+  const void* pk_pooler;           // BF16 layers: weights in the matrix-core layout
   const void* pk_unpooler;
   const void* pk_gate;
   const void* pk_up;
@@ -116,6 +176,7 @@ struct latent_moe {
   const void* pk_sgate;  // MXFP4: packed scales
   const void* pk_sup;
   const void* pk_sdown;
+  const void* wr3;       // BF16 layers: the router's exact three-piece BF16 split [E, 3H]
   const float* ds_gate;  // 2^-s per weight row of the FP16 / MXFP4 copies
   const float* ds_up;
   const float* ds_down;
@@ -123,11 +184,15 @@ struct latent_moe {
   float u_down = 1.0f;  // FP16 u and y are stored times these powers of two (see create)
   float y_down = 1.0f;
   const float* a_down;  // FP16 a is stored times a_down[e][i / 32] (see lm_a_shift_kernel)
-  hipStream_t side;                // routing (router, top-k, grouping) runs here, beside the pooler
-  hipEvent_t fork, join;           // order the side stream after the caller's and back
-  bool prof;                       // record stage events in forward
-  bool prof_valid;                 // a forward has recorded a full set
-  hipEvent_t ev[kStages + 1];      // created by latent_moe_set_profiling
+  const float* o_down = nullptr;  // FP16 expert outputs are stored times o_down[e] (lm_o_shift_kernel)
+  const float* o_up = nullptr;    // 1 / o_down[e]
+  bool side_ok = false;            // the routing stream and its events exist
+  hipStream_t side = nullptr;      // routing (router, top-k, grouping) runs here, beside the pooler
+  hipEvent_t fork = nullptr, join = nullptr;  // order the side stream after the caller's and back
+  bool poison = false;             // debug: workspace refilled with 0xFF bytes before each forward
+  bool prof = false;               // record stage events in forward
+  bool prof_valid = false;         // a forward has recorded a full set
+  hipEvent_t ev[kStages + 1] = {};  // created by latent_moe_set_profiling
 };
 
 namespace {
@@ -172,8 +237,8 @@ int validate_config(const latent_moe_config* c) {
     return fail(LMOE_ERR_INVALID_ARG, "dimension too large");
   if (c->experts < 1 || c->experts > 1024)
     return fail(LMOE_ERR_INVALID_ARG, "experts must be in [1, 1024]");
-  if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->experts)
-    return fail(LMOE_ERR_INVALID_ARG, "top_k must be in [1, min(experts, 16)]");
+  if (c->top_k < 1 || c->top_k > kLmMaxK || c->top_k > c->experts)
+    return fail(LMOE_ERR_INVALID_ARG, "top_k must be in [1, min(experts, %d)]", kLmMaxK);
   if (!std::isfinite(c->eps) || c->eps < 0.0f)
     return fail(LMOE_ERR_INVALID_ARG, "eps must be finite and >= 0");
   if (c->max_tokens < 1 || c->max_tokens * c->top_k > (1 << 28))
@@ -185,8 +250,8 @@ int validate_config(const latent_moe_config* c) {
   if ((c->act_dtype == LMOE_F32) != (c->expert_dtype == LMOE_F32))
     return fail(LMOE_ERR_UNSUPPORTED, "FP32 experts need FP32 activations and vice versa");
   if (c->act_dtype == LMOE_BF16 && (c->hidden % 512 || c->pooled % 512 || c->intermediate % 512))
-    return fail(LMOE_ERR_INVALID_ARG,
-                "BF16 layers need hidden, pooled and intermediate to be multiples of 512");
+    return fail(LMOE_ERR_UNSUPPORTED,
+                "BF16 layers are built for hidden, pooled and intermediate multiples of 512");
   if (c->input_norm != 0 && c->input_norm != 1)
     return fail(LMOE_ERR_INVALID_ARG, "input_norm must be 0 or 1");
   if (c->expert_act != 0 && c->expert_act != LMOE_MXFP8 && c->expert_act != LMOE_MXFP4)
@@ -236,10 +301,9 @@ Layout make_layout(const latent_moe_config& c, size_t* part_floats) {
   L.pssq = take((size_t)Tm * parts * 4);
   L.row_scale = take((size_t)Tm * 4);
   L.act = take((size_t)Mp * I * esize_exp(c));
-  L.O = take((size_t)Mp * P * 4);
+  L.O = take((size_t)Mp * P * (c.act_dtype == LMOE_BF16 && LM_O_F16 ? 2 : 4));  // expert outputs: FP16 (BF16 layers) or FP32
   L.ossq = take((size_t)Mp * parts * 4);
   L.y = take((size_t)Tm * P * esize_act(c));  // FP32 or FP16 [T, P]
-  L.wr3 = take(c.act_dtype == LMOE_BF16 ? (size_t)E * 3 * c.hidden * 2 : 0);
   size_t kp = 0;
   if (c.act_dtype == LMOE_BF16) {
     for (int64_t T = 1; T <= (Tm < 65536 ? Tm : 65536); ++T) {
@@ -271,7 +335,9 @@ template <class Prob>
 hipError_t launch(const Prob& p, int64_t units, hipStream_t s) {
   if (units <= 0) return hipSuccess;
   const int64_t g = (units + 7) / 8 * 8;
-  if constexpr (sizeof(typename Prob::Cfg::E) == 2 && Prob::Cfg::WM == 1 && !Prob::Cfg::FLUSH)
+  if constexpr (Prob::Cfg::WM * Prob::Cfg::WN == 8 && Prob::Cfg::WM == 2)
+    hipLaunchKernelGGL(lm_gemm_lds_kernel<Prob>, dim3((unsigned)g), dim3(512), 0, s, p);
+  else if constexpr (sizeof(typename Prob::Cfg::E) == 2 && Prob::Cfg::WM == 1 && !Prob::Cfg::FLUSH)
     hipLaunchKernelGGL(lm_gemm_stream_kernel<Prob>, dim3((unsigned)g), dim3(64 * Prob::Cfg::WN), 0, s, p);
   else
     hipLaunchKernelGGL(lm_gemm_kernel<Prob>, dim3((unsigned)g), dim3(256), 0, s, p);
@@ -319,6 +385,12 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   // MX expert inputs, prefill-sized down GEMM: as many waves along N as the FP16
   // GEMMs (measured faster; the MX gate/up kernel measured slower on eight waves)
   using Cx = std::conditional_t<MXA && Cw::TM == 4, LmGemmCfg<Et, 1, Ch::WN, Cw::TM, 2>, Cw>;
+  // prefill-sized BF16 layers with BF16 experts: the LDS-staged 256 x 256 kernel
+  // for the pooler, gate/up, down and unpooler
+  constexpr bool kLds = LM_LDS_GEMM && F16 && !MX && !MXA && Cw::TM == 4;
+  using Cp = std::conditional_t<kLds, CfgLds<Et>, Cw>;  // pooler
+  using Ce = std::conditional_t<kLds, CfgLds<Eh>, Ch>;  // gate/up, down, unpooler
+  constexpr int kBmGroup = kLds ? Ce::BM : Cw::BM;      // rows per grouped-GEMM tile
   double* part = (double*)(ws + L.part);
   float* logits = (float*)(ws + L.logits);
   int* ids = (int*)(ws + L.ids);
@@ -335,10 +407,11 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   float* row_scale = (float*)(ws + L.row_scale);
   Eh* u16 = (Eh*)(ws + L.u16);  // BF16 layers without MX inputs: the FP16 u
   Eh* act = (Eh*)(ws + L.act);
-  float* O = (float*)(ws + L.O);
+  float* O = (float*)(ws + L.O);  // FP32 layers; BF16 layers: FP16 (o times o_down[e])
   float* ossq = (float*)(ws + L.ossq);
   Eh* y = (Eh*)(ws + L.y);
 
+  if (h->poison) LM_HIP(lm_fill_launch(ws, L.total, 0xFFFFFFFFu, s));
   LM_MARK(0);
   // 0. boundary norm (optional): x is the pre-norm residual. FP32 layers: the
   // router and pooler read the FP32 norm. BF16 layers: its exact three-piece
@@ -363,7 +436,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   // handle's side stream, forked from and joined back into the caller's
   // stream, so the two overlap. With stage profiling on, every step runs in
   // order on the caller's stream so the per-stage times are separable.
-  const bool fork = !h->prof;
+  const bool fork = !h->prof && h->side_ok;
   hipStream_t sr = s;
   if (fork) {
     LM_HIP(hipEventRecord(h->fork, s));
@@ -376,7 +449,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     router_split(c, T, splits, kt_per, mt, nt);
     RouterProb<Cr> p;
     p.x = (const Et*)xr;
-    p.w = sizeof(Et) == 2 ? (const Et*)(ws + L.wr3) : (const Et*)w.router;
+    p.w = sizeof(Et) == 2 ? (const Et*)h->wr3 : (const Et*)w.router;
     p.part = part;
     p.T = (int)T;
     p.Ew = E;
@@ -419,15 +492,15 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   }
   LM_MARK(3);
   // 3. grouping by expert
-  hipLaunchKernelGGL(lm_permute_kernel, dim3(E), dim3(256), 0, sr, ids, npairs, k, cpad, E, Cw::BM,
+  hipLaunchKernelGGL(lm_permute_kernel, dim3(E), dim3(256), 0, sr, ids, npairs, k, cpad, E, kBmGroup,
                      counts, offsets, tile_off, perm_token, pair_row);
   LM_HIP(hipGetLastError());
   if (fork) LM_HIP(hipEventRecord(h->join, sr));
   LM_MARK(4);
   // 4. pooler + norm statistics
-  const int pnt = ceil_div(P, Cw::BN);
+  const int pnt = ceil_div(P, Cp::BN);
   int psplits = 1, pkt = 0;
-  if (packed) dense_split(T, P, H, Cw::BM, Cw::BN, psplits, pkt);
+  if (packed) dense_split(T, P, H, Cp::BM, Cp::BN, psplits, pkt);
   if (psplits > 1) {
     if constexpr (sizeof(Et) == 2) {
     DenseSplitProb<Cw> p;
@@ -458,7 +531,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     LM_HIP(hipGetLastError());
     }
   } else {
-    PoolerProb<Cw> p;
+    PoolerProb<Cp> p;
     if (F16) p.pooled32 = pooled32;
     p.x = xp;
     p.lda = xp_ld;
@@ -469,7 +542,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.T = (int)T;
     p.H = H;
     p.P = P;
-    p.mt = ceil_div(T, Cw::BM);
+    p.mt = ceil_div(T, Cp::BM);
     p.nt = pnt;
     LM_HIP(launch(p, (int64_t)p.mt * p.nt, s));
     LM_MARK(5);
@@ -492,7 +565,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   }
   LM_MARK(6);
   if (fork) LM_HIP(hipStreamWaitEvent(s, h->join, 0));
-  const int64_t max_tiles = ceil_div(npairs, Cw::BM) + (npairs < E ? npairs : E);
+  const int64_t max_tiles = ceil_div(npairs, kBmGroup) + (npairs < E ? npairs : E);
   // 5. gate/up + SwiGLU
   if constexpr (MXA) {
     GateUpMxaProb<Cw, AB> p;
@@ -517,7 +590,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.as = (uint8_t*)(ws + L.acts);
     LM_HIP(launch_mxa(p, max_tiles * p.nt, s));
   } else {
-    GateUpProb<Ch, MX> p;
+    GateUpProb<Ce, MX> p;
     if constexpr (MX) {
       p.sg = h->pk_sgate;
       p.su = h->pk_sup;
@@ -542,12 +615,12 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.P = P;
     p.I = I;
     p.Ex = E;
-    p.nt = I / GateUpProb<Ch, MX>::kCols;
+    p.nt = I / GateUpProb<Ce, MX>::kCols;
     LM_HIP(launch(p, max_tiles * p.nt, s));
   }
   LM_MARK(7);
   // 6. down + per-row sum of squares partials
-  const int dnt = ceil_div(P, MXA ? Cx::BN : Ch::BN);
+  const int dnt = ceil_div(P, MXA ? Cx::BN : Ce::BN);
   if constexpr (MXA) {
     DownMxaProb<Cx, AB> p;
     p.sd = h->pk_sdown;
@@ -557,6 +630,10 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.offsets = offsets;
     p.tile_off = tile_off;
     p.out = O;
+    if (LM_O_F16) {
+      p.out16 = (_Float16*)O;
+      p.o_down = h->o_down;
+    }
     p.ssq = ossq;
     p.P = P;
     p.I = I;
@@ -566,7 +643,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.as = (const uint8_t*)(ws + L.acts);
     LM_HIP(launch_mxa(p, max_tiles * p.nt, s));
   } else {
-    DownProb<Ch, MX> p;
+    DownProb<Ce, MX> p;
     if constexpr (MX) p.sd = h->pk_sdown;
     if constexpr (F16) p.dsd = h->ds_down;
     p.act = act;
@@ -575,6 +652,10 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.offsets = offsets;
     p.tile_off = tile_off;
     p.out = O;
+    if constexpr (F16 && LM_O_F16) {
+      p.out16 = (_Float16*)O;
+      p.o_down = h->o_down;
+    }
     p.ssq = ossq;
     p.P = P;
     p.I = I;
@@ -584,13 +665,16 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   }
   LM_MARK(8);
   // 7. per-expert norm, routing weight, FP32 sum
-  hipLaunchKernelGGL(lm_combine_kernel<Eh>, dim3((unsigned)T), dim3(256), 0, s, O, ossq, dnt, pair_row,
-                     ids, wts, w.expert_gamma, k, P, c.eps, F16 ? h->y_down : 1.0f, y);
+  constexpr bool kO16 = F16 && LM_O_F16;
+  using OT = std::conditional_t<kO16, _Float16, float>;
+  hipLaunchKernelGGL((lm_combine_kernel<OT, Eh>), dim3((unsigned)T), dim3(256), 0, s, (const OT*)O, ossq, dnt,
+                     pair_row, ids, wts, w.expert_gamma, kO16 ? h->o_up : nullptr, k, P, c.eps,
+                     F16 ? h->y_down : 1.0f, y);
   LM_HIP(hipGetLastError());
   LM_MARK(9);
   // 8. unpooler (BF16 layers: FP16 y against the per-row scaled FP16 copy of W)
   int usplits = 1, ukt = 0;
-  if (packed) dense_split(T, H, P, Ch::BM, Ch::BN, usplits, ukt);
+  if (packed) dense_split(T, H, P, Ce::BM, Ce::BN, usplits, ukt);
   if (usplits > 1) {
     if constexpr (F16) {
     DenseSplitProb<Ch> p;
@@ -613,7 +697,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     LM_HIP(hipGetLastError());
     }
   } else {
-    UnpoolerProb<Ch> p;
+    UnpoolerProb<Ce> p;
     p.y = y;
     p.w = (const Eh*)Wunpool;
     if constexpr (F16) {
@@ -624,8 +708,8 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.T = (int)T;
     p.H = H;
     p.P = P;
-    p.mt = ceil_div(T, Ch::BM);
-    p.nt = ceil_div(H, Ch::BN);
+    p.mt = ceil_div(T, Ce::BM);
+    p.nt = ceil_div(H, Ce::BN);
     LM_HIP(launch(p, (int64_t)p.mt * p.nt, s));
   }
   LM_MARK(10);
@@ -649,7 +733,8 @@ int latent_moe_workspace_bytes(const latent_moe_config* cfg, size_t* bytes) {
   return LMOE_OK;
 }
 
-int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const latent_moe_weights* w) {
+int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const latent_moe_weights* w,
+                      void* stream) {
   g_err.clear();
   if (!out) return fail(LMOE_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
@@ -685,98 +770,175 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
     return fail(LMOE_ERR_HIP, "no HIP device available (%s)", hipGetErrorString(he));
   int dev = 0;
   LM_HIP(hipGetDevice(&dev));
+  const hipStream_t s = (hipStream_t)stream;
 
   latent_moe* h = new (std::nothrow) latent_moe();
   if (!h) return fail(LMOE_ERR_OOM, "host allocation failed");
   h->cfg = *cfg;
-  h->w = *w;
   h->device = dev;
   h->lay = make_layout(*cfg, &h->part_floats);
-  he = hipMalloc((void**)&h->ws, h->lay.total);
-  if (he != hipSuccess) {
-    delete h;
+  h->poison = debug_poison();
+  AllocCtl actl = alloc_ctl_from_env();
+  // Every failure below releases what was made so far: the handle, its two
+  // device allocations, the routing stream and its events.
+  auto cleanup = [&](int code, const char* what, hipError_t e) {
     (void)hipGetLastError();
-    return fail(LMOE_ERR_OOM, "hipMalloc of %zu workspace bytes failed: %s", h->lay.total,
-                hipGetErrorString(he));
+    if (h->ws || h->owned) (void)hipStreamSynchronize(s);  // no kernel of this call still reads them
+    if (h->join) (void)hipEventDestroy(h->join);
+    if (h->fork) (void)hipEventDestroy(h->fork);
+    if (h->side) (void)hipStreamDestroy(h->side);
+    if (h->ws) (void)hipFree(h->ws);
+    if (h->owned) (void)hipFree(h->owned);
+    delete h;
+    return fail(code, "%s: %s", what, hipGetErrorString(e));
+  };
+
+  // 1. workspace (sized by max_tokens), plus the guard words in poison mode
+  const size_t ws_bytes = h->lay.total + (h->poison ? kGuardBytes : 0);
+  he = lm_malloc(actl, (void**)&h->ws, ws_bytes);
+  if (he != hipSuccess) {
+    h->ws = nullptr;
+    char what[96];
+    snprintf(what, sizeof what, "device allocation of %zu workspace bytes failed", ws_bytes);
+    return cleanup(LMOE_ERR_OOM, what, he);
   }
-  if (cfg->act_dtype == LMOE_BF16) {
-    const size_t E = cfg->experts, H = cfg->hidden, P = cfg->pooled, I = cfg->intermediate;
-    const bool mx = cfg->expert_dtype == LMOE_MXFP4;
-    const size_t sz_pool = H * P * 2, sz_exp = mx ? E * I * P / 2 : E * I * P * 2;
-    const size_t sz_sc = mx ? E * I * P / 32 : 0;
-    // per weight row 2^-s: gate, up [E*I], down [E*P], unpooler [H] (FP32); then the
-    // SwiGLU output's block shifts c (int) and 2^-c (FP32), [E, I/32] each
-    const size_t n_ds = 2 * E * I + E * P + H, n_ab = E * I / 32;
-    h->packed_bytes = 2 * sz_pool + 3 * sz_exp + 3 * sz_sc + n_ds * 4 + 2 * n_ab * 4;
-    he = hipMalloc((void**)&h->packed, h->packed_bytes);
-    if (he != hipSuccess) {
-      (void)hipGetLastError();
-      (void)hipFree(h->ws);
-      delete h;
-      return fail(LMOE_ERR_OOM, "hipMalloc of %zu bytes for packed weights failed", h->packed_bytes);
-    }
-    h->pk_pooler = h->packed;
-    h->pk_unpooler = h->packed + sz_pool;
-    h->pk_gate = h->packed + 2 * sz_pool;
-    h->pk_up = h->packed + 2 * sz_pool + sz_exp;
-    h->pk_down = h->packed + 2 * sz_pool + 2 * sz_exp;
-    h->pk_sgate = h->packed + 2 * sz_pool + 3 * sz_exp;
-    h->pk_sup = h->packed + 2 * sz_pool + 3 * sz_exp + sz_sc;
-    h->pk_sdown = h->packed + 2 * sz_pool + 3 * sz_exp + 2 * sz_sc;
-    float* ds = (float*)(h->packed + 2 * sz_pool + 3 * sz_exp + 3 * sz_sc);
+
+  // 2. one allocation for the library's own copies of everything forward
+  // reads: gammas, bias, and the weights (FP32 layers: as given; BF16 layers:
+  // the router split and the packed matrix-core copies with their scales)
+  const size_t E = cfg->experts, H = cfg->hidden, P = cfg->pooled, I = cfg->intermediate;
+  const bool bf16 = cfg->act_dtype == LMOE_BF16;
+  const bool mx = cfg->expert_dtype == LMOE_MXFP4;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += up256(bytes);
+    return at;
+  };
+  const size_t o_bias = take(w->router_bias ? E * 4 : 0), o_gp = take(P * 4), o_ge = take(E * P * 4),
+               o_gin = take(cfg->input_norm ? H * 4 : 0);
+  // FP32 layers
+  const size_t o_r = take(bf16 ? 0 : E * H * 4), o_p = take(bf16 ? 0 : P * H * 4),
+               o_g = take(bf16 ? 0 : E * I * P * 4), o_u = take(bf16 ? 0 : E * I * P * 4),
+               o_d = take(bf16 ? 0 : E * P * I * 4), o_un = take(bf16 ? 0 : H * P * 4);
+  // BF16 layers
+  const size_t sz_pool = bf16 ? H * P * 2 : 0, sz_exp = !bf16 ? 0 : mx ? E * I * P / 2 : E * I * P * 2;
+  const size_t sz_sc = bf16 && mx ? E * I * P / 32 : 0;
+  // per weight row 2^-s: gate, up [E*I], down [E*P], unpooler [H] (FP32); the SwiGLU
+  // output's block shifts c (int) and 2^-c (FP32), [E, I/32] each; row norms of the
+  // gate and up weights [2*E*I] (create-time scratch); largest |gamma_p|, |gamma_e|
+  const size_t n_ds = bf16 ? 2 * E * I + E * P + H : 0, n_ab = bf16 ? E * I / 32 : 0;
+  const size_t o_wr3 = take(bf16 ? E * 3 * H * 2 : 0), o_pp = take(sz_pool), o_pu = take(sz_pool),
+               o_pg = take(sz_exp), o_pup = take(sz_exp), o_pd = take(sz_exp), o_sg = take(sz_sc),
+               o_su = take(sz_sc), o_sd = take(sz_sc), o_ds = take(n_ds * 4), o_ash = take(n_ab * 4),
+               o_ad = take(n_ab * 4), o_norm = take(bf16 ? (2 * E * I + E * P) * 4 : 0), o_gmax = take(bf16 ? 8 : 0),
+               o_od = take(bf16 ? 2 * E * 4 : 0);
+  h->owned_bytes = o;
+  he = lm_malloc(actl, (void**)&h->owned, h->owned_bytes);
+  if (he != hipSuccess) {
+    h->owned = nullptr;
+    char what[96];
+    snprintf(what, sizeof what, "device allocation of %zu bytes for the weight copies failed", h->owned_bytes);
+    return cleanup(LMOE_ERR_OOM, what, he);
+  }
+  char* ob = h->owned;
+  auto copy = [&](size_t at, const void* src, size_t bytes) {
+    return bytes ? hipMemcpyAsync(ob + at, src, bytes, hipMemcpyDeviceToDevice, s) : hipSuccess;
+  };
+  latent_moe_weights& hw = h->w;
+  hw = latent_moe_weights{};
+  he = copy(o_gp, w->pool_gamma, P * 4);
+  if (he == hipSuccess) he = copy(o_ge, w->expert_gamma, E * P * 4);
+  if (he == hipSuccess && w->router_bias) he = copy(o_bias, w->router_bias, E * 4);
+  if (he == hipSuccess && cfg->input_norm) he = copy(o_gin, w->input_gamma, H * 4);
+  hw.pool_gamma = (const float*)(ob + o_gp);
+  hw.expert_gamma = (const float*)(ob + o_ge);
+  hw.router_bias = w->router_bias ? (const float*)(ob + o_bias) : nullptr;
+  hw.input_gamma = cfg->input_norm ? (const float*)(ob + o_gin) : nullptr;
+  if (he == hipSuccess && !bf16) {
+    he = copy(o_r, w->router, E * H * 4);
+    if (he == hipSuccess) he = copy(o_p, w->pooler, P * H * 4);
+    if (he == hipSuccess) he = copy(o_g, w->w_gate, E * I * P * 4);
+    if (he == hipSuccess) he = copy(o_u, w->w_up, E * I * P * 4);
+    if (he == hipSuccess) he = copy(o_d, w->w_down, E * P * I * 4);
+    if (he == hipSuccess) he = copy(o_un, w->unpooler, H * P * 4);
+    hw.router = (const float*)(ob + o_r);
+    hw.pooler = ob + o_p;
+    hw.w_gate = ob + o_g;
+    hw.w_up = ob + o_u;
+    hw.w_down = ob + o_d;
+    hw.unpooler = ob + o_un;
+  }
+  if (he != hipSuccess) return cleanup(LMOE_ERR_HIP, "weight copy failed", he);
+
+  if (bf16) {
+    h->wr3 = ob + o_wr3;
+    h->pk_pooler = ob + o_pp;
+    h->pk_unpooler = ob + o_pu;
+    h->pk_gate = ob + o_pg;
+    h->pk_up = ob + o_pup;
+    h->pk_down = ob + o_pd;
+    h->pk_sgate = ob + o_sg;
+    h->pk_sup = ob + o_su;
+    h->pk_sdown = ob + o_sd;
+    float* ds = (float*)(ob + o_ds);
     h->ds_gate = ds;
     h->ds_up = ds + E * I;
     h->ds_down = ds + 2 * E * I;
     h->ds_unpooler = ds + 2 * E * I + E * P;
-    int* a_shift = (int*)(ds + n_ds);
-    float* a_down = (float*)(a_shift + n_ab);
+    int* a_shift = (int*)(ob + o_ash);
+    float* a_down = (float*)(ob + o_ad);
+    float* norms = (float*)(ob + o_norm);
+    float* gmax = (float*)(ob + o_gmax);
     // Largest |gamma_p| and |gamma_e| (for the FP16 ranges of u, a and y below).
-    float* gmax = (float*)(h->ws + h->lay.logits);  // workspace unused until the first forward
-    hipLaunchKernelGGL(lm_absmax_kernel, dim3(1), dim3(256), 0, 0, w->pool_gamma, (int64_t)P, gmax);
-    hipLaunchKernelGGL(lm_absmax_kernel, dim3(1), dim3(256), 0, 0, w->expert_gamma, (int64_t)(E * P),
-                       gmax + 1);
+    hipLaunchKernelGGL(lm_absmax_kernel, dim3(1), dim3(256), 0, s, hw.pool_gamma, (int64_t)P, gmax);
+    hipLaunchKernelGGL(lm_absmax_kernel, dim3(1), dim3(256), 0, s, hw.expert_gamma, (int64_t)(E * P), gmax + 1);
     float gm[2] = {0.0f, 0.0f};
     he = hipGetLastError();
-    if (he == hipSuccess) he = hipDeviceSynchronize();
-    if (he == hipSuccess) he = hipMemcpy(gm, gmax, sizeof gm, hipMemcpyDeviceToHost);
-    // FP16 a (expert inputs in FP16 only; MX inputs quantise a per block): per
-    // expert and block of 32 intermediate columns, the shift from the norms of
-    // the gate and up rows (lm_a_shift_kernel); the down weights carry it.
+    if (he == hipSuccess) he = hipMemcpyAsync(gm, gmax, sizeof gm, hipMemcpyDeviceToHost, s);
+    if (he == hipSuccess) he = hipStreamSynchronize(s);
+    // Row norms of the gate, up and down weights: the FP16 ranges of a and of
+    // the expert outputs follow from them.
     const int* kc = nullptr;
     h->a_down = nullptr;
-    if (he == hipSuccess && cfg->expert_act == 0) {
-      float* norms = nullptr;
-      he = hipMalloc((void**)&norms, 2 * E * I * sizeof(float));
-      if (he == hipSuccess) {
-        const unsigned nb = (unsigned)((E * I + 3) / 4 < 65536 ? (E * I + 3) / 4 : 65536);
-        if (mx) {
-          hipLaunchKernelGGL(lm_row_norm_mx_kernel, dim3(nb), dim3(256), 0, 0, (const uint8_t*)w->w_gate,
-                             (const uint8_t*)w->s_gate, (int64_t)(E * I), (int)P, norms);
-          hipLaunchKernelGGL(lm_row_norm_mx_kernel, dim3(nb), dim3(256), 0, 0, (const uint8_t*)w->w_up,
-                             (const uint8_t*)w->s_up, (int64_t)(E * I), (int)P, norms + E * I);
-        } else {
-          hipLaunchKernelGGL(lm_row_norm_bf16_kernel, dim3(nb), dim3(256), 0, 0, (const uint16_t*)w->w_gate,
-                             (int64_t)(E * I), (int)P, norms);
-          hipLaunchKernelGGL(lm_row_norm_bf16_kernel, dim3(nb), dim3(256), 0, 0, (const uint16_t*)w->w_up,
-                             (int64_t)(E * I), (int)P, norms + E * I);
-        }
-        const float u2 = (float)((double)P * (double)gm[0] * (double)gm[0]);
-        hipLaunchKernelGGL(lm_a_shift_kernel, dim3((unsigned)((n_ab + 255) / 256)), dim3(256), 0, 0, norms,
+    const float u2 = (float)((double)P * (double)gm[0] * (double)gm[0]);
+    if (he == hipSuccess) {
+      const unsigned nb = (unsigned)((E * I + 3) / 4 < 65536 ? (E * I + 3) / 4 : 65536);
+      const unsigned nbd = (unsigned)((E * P + 3) / 4 < 65536 ? (E * P + 3) / 4 : 65536);
+      if (mx) {
+        hipLaunchKernelGGL(lm_row_norm_mx_kernel, dim3(nb), dim3(256), 0, s, (const uint8_t*)w->w_gate,
+                           (const uint8_t*)w->s_gate, (int64_t)(E * I), (int)P, norms);
+        hipLaunchKernelGGL(lm_row_norm_mx_kernel, dim3(nb), dim3(256), 0, s, (const uint8_t*)w->w_up,
+                           (const uint8_t*)w->s_up, (int64_t)(E * I), (int)P, norms + E * I);
+        hipLaunchKernelGGL(lm_row_norm_mx_kernel, dim3(nbd), dim3(256), 0, s, (const uint8_t*)w->w_down,
+                           (const uint8_t*)w->s_down, (int64_t)(E * P), (int)I, norms + 2 * E * I);
+      } else {
+        hipLaunchKernelGGL(lm_row_norm_bf16_kernel, dim3(nb), dim3(256), 0, s, (const uint16_t*)w->w_gate,
+                           (int64_t)(E * I), (int)P, norms);
+        hipLaunchKernelGGL(lm_row_norm_bf16_kernel, dim3(nb), dim3(256), 0, s, (const uint16_t*)w->w_up,
+                           (int64_t)(E * I), (int)P, norms + E * I);
+        hipLaunchKernelGGL(lm_row_norm_bf16_kernel, dim3(nbd), dim3(256), 0, s, (const uint16_t*)w->w_down,
+                           (int64_t)(E * P), (int)I, norms + 2 * E * I);
+      }
+      // FP16 expert outputs: one power of two per expert (lm_o_shift_kernel);
+      // an MX-quantised a may exceed silu(g) v by up to a factor 1.5
+      float* od = (float*)(ob + o_od);
+      hipLaunchKernelGGL(lm_o_shift_kernel, dim3((unsigned)E), dim3(256), 0, s, norms, norms + E * I,
+                         norms + 2 * E * I, (int)I, (int)P, u2, cfg->expert_act ? 2.0f : 1.0f, od, od + E);
+      h->o_down = od;
+      h->o_up = od + E;
+      // FP16 a (expert inputs in FP16 only; MX inputs quantise a per block): per
+      // expert and block of 32 intermediate columns, the shift from the norms of
+      // the gate and up rows (lm_a_shift_kernel); the down weights carry it.
+      if (cfg->expert_act == 0) {
+        hipLaunchKernelGGL(lm_a_shift_kernel, dim3((unsigned)((n_ab + 255) / 256)), dim3(256), 0, s, norms,
                            norms + E * I, (int64_t)n_ab, u2, a_shift, a_down);
-        he = hipGetLastError();
-        if (he == hipSuccess) he = hipDeviceSynchronize();
-        (void)hipFree(norms);
         kc = a_shift;
         h->a_down = a_down;
       }
+      he = hipGetLastError();
     }
-    if (he != hipSuccess) {
-      (void)hipGetLastError();
-      (void)hipFree(h->ws);
-      (void)hipFree(h->packed);
-      delete h;
-      return fail(LMOE_ERR_HIP, "weight range analysis failed: %s", hipGetErrorString(he));
-    }
+    if (he != hipSuccess) return cleanup(LMOE_ERR_HIP, "weight range analysis failed", he);
     // The pooler stays BF16 (x is BF16). The unpooler and BF16 experts become
     // FP16 copies scaled per row by 2^s; MXFP4 experts keep their codes and
     // get the per-row 2^s applied when they are decoded.
@@ -791,30 +953,30 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
          (int64_t)P}};
     for (const Job& j : jobs) {
       if (j.mx) {
-        hipLaunchKernelGGL(lm_row_descale_mx_kernel, dim3((unsigned)((j.rows + 255) / 256)), dim3(256), 0, 0,
+        hipLaunchKernelGGL(lm_row_descale_mx_kernel, dim3((unsigned)((j.rows + 255) / 256)), dim3(256), 0, s,
                            (const uint8_t*)j.src_s, j.rows, j.K, (float*)j.ds, j.kc, j.rows_per_set);
-        hipLaunchKernelGGL(lm_pack_mx_kernel, dim3(65536), dim3(256), 0, 0, (const lm_u32x4*)j.src,
+        hipLaunchKernelGGL(lm_pack_mx_kernel, dim3(65536), dim3(256), 0, s, (const lm_u32x4*)j.src,
                            (const uint8_t*)j.src_s, (lm_u32x4*)j.dst, (uint8_t*)j.dst_s, j.rows, j.K, j.kc,
                            j.rows_per_set);
       } else {
         if (j.ds)
           hipLaunchKernelGGL(lm_row_descale_bf16_kernel, dim3((unsigned)((j.rows + 3) / 4 < 65536 ? (j.rows + 3) / 4 : 65536)),
-                             dim3(256), 0, 0, (const uint16_t*)j.src, j.rows, j.K, (float*)j.ds, j.kc,
+                             dim3(256), 0, s, (const uint16_t*)j.src, j.rows, j.K, (float*)j.ds, j.kc,
                              j.rows_per_set);
-        hipLaunchKernelGGL(lm_pack_mfma_kernel, dim3(65536), dim3(256), 0, 0, (const lm_u32x4*)j.src,
+        hipLaunchKernelGGL(lm_pack_mfma_kernel, dim3(65536), dim3(256), 0, s, (const lm_u32x4*)j.src,
                            (lm_u32x4*)j.dst, j.rows, j.K, j.ds, j.kc, j.rows_per_set);
       }
     }
-    const size_t n = (size_t)cfg->experts * cfg->hidden;
+    const size_t n = E * H;
     unsigned blocks = (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
-    hipLaunchKernelGGL(lm_split_router_kernel, dim3(blocks), dim3(256), 0, 0, w->router,
-                       (uint16_t*)(h->ws + h->lay.wr3), (int)cfg->experts, (int)cfg->hidden);
+    hipLaunchKernelGGL(lm_split_router_kernel, dim3(blocks), dim3(256), 0, s, w->router, (uint16_t*)h->wr3,
+                       (int)E, (int)H);
+    he = hipGetLastError();
+    if (he != hipSuccess) return cleanup(LMOE_ERR_HIP, "weight repack failed", he);
     // FP16 u and y: |u| <= sqrt(P) max|gamma_p| and |y| <= sqrt(P) max|gamma_e| (an
     // RMS-normed row has no element above sqrt(P) times its gamma, and the routing
     // weights sum to one); each is stored times a power of two that keeps its bound
     // within 2^15, undone exactly in FP32 after the product (1 for ordinary gammas).
-    he = hipGetLastError();
-    if (he == hipSuccess) he = hipDeviceSynchronize();
     auto down_for = [&](float g) {
       const double bound = std::sqrt((double)P) * (double)g;
       if (!(bound > 32768.0) || !std::isfinite(bound)) return 1.0f;
@@ -824,26 +986,21 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
     };
     h->u_down = down_for(gm[0]);
     h->y_down = down_for(gm[1]);
-    if (he != hipSuccess) {
-      (void)hipFree(h->ws);
-      (void)hipFree(h->packed);
-      delete h;
-      return fail(LMOE_ERR_HIP, "weight repack failed: %s", hipGetErrorString(he));
-    }
+  }
+  if (h->poison) {  // workspace all 0xFF bytes (NaN floats, -1 ints), guard words after it
+    he = lm_fill_launch(h->ws, h->lay.total, 0xFFFFFFFFu, s);
+    if (he == hipSuccess) he = lm_fill_launch(h->ws + h->lay.total, kGuardBytes, kGuardWord, s);
+    if (he != hipSuccess) return cleanup(LMOE_ERR_HIP, "workspace poison failed", he);
   }
   // side stream for routing (default priority) and its fork / join events
   he = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
   if (he == hipSuccess) he = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
   if (he == hipSuccess) he = hipEventCreateWithFlags(&h->join, hipEventDisableTiming);
-  if (he != hipSuccess) {
-    if (h->join) (void)hipEventDestroy(h->join);
-    if (h->fork) (void)hipEventDestroy(h->fork);
-    if (h->side) (void)hipStreamDestroy(h->side);
-    (void)hipFree(h->ws);
-    if (h->packed) (void)hipFree(h->packed);
-    delete h;
-    return fail(LMOE_ERR_HIP, "stream / event creation failed: %s", hipGetErrorString(he));
-  }
+  if (he != hipSuccess) return cleanup(LMOE_ERR_HIP, "stream / event creation failed", he);
+  h->side_ok = true;
+  // the copies are complete before create returns: the caller may free its tensors
+  he = hipStreamSynchronize(s);
+  if (he != hipSuccess) return cleanup(LMOE_ERR_HIP, "create", he);
   *out = h;
   return LMOE_OK;
 }
@@ -910,7 +1067,7 @@ int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v) {
   v->pooled = ws + L.pooled;
   v->row_scale = (const float*)(ws + L.row_scale);
   v->act = ws + L.act;
-  v->expert_out = (const float*)(ws + L.O);
+  v->expert_out = (const void*)(ws + L.O);
   v->combined = ws + L.y;
   const bool mxa = h->cfg.expert_act != 0;
   v->expert_in = mxa ? (const uint8_t*)(ws + L.uq)
@@ -922,6 +1079,7 @@ int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v) {
   v->expert_in_scale = mxa || h->cfg.act_dtype == LMOE_F32 ? 1.0f : h->u_down;
   v->combined_scale = h->cfg.act_dtype == LMOE_F32 ? 1.0f : h->y_down;
   v->act_down = h->cfg.act_dtype == LMOE_F32 ? nullptr : h->a_down;
+  v->expert_out_down = h->cfg.act_dtype == LMOE_F32 ? nullptr : h->o_down;
   return LMOE_OK;
 }
 
@@ -962,17 +1120,28 @@ int latent_moe_destroy(latent_moe_t* h) {
   (void)hipGetDevice(&cur);
   (void)hipSetDevice(h->device);
   hipError_t e1 = hipDeviceSynchronize();
+  size_t bad = 0;
+  if (h->poison && e1 == hipSuccess) {  // guard words after the workspace
+    uint32_t* g = (uint32_t*)malloc(kGuardBytes);
+    if (g && hipMemcpy(g, h->ws + h->lay.total, kGuardBytes, hipMemcpyDeviceToHost) == hipSuccess)
+      for (size_t i = 0; i < kGuardBytes / 4; ++i) bad += g[i] != kGuardWord;
+    free(g);
+  }
   hipError_t e2 = hipFree(h->ws);
-  if (h->packed && e2 == hipSuccess) e2 = hipFree(h->packed);
+  if (h->owned) {
+    hipError_t e3 = hipFree(h->owned);
+    if (e2 == hipSuccess) e2 = e3;
+  }
   for (int i = 0; i <= kStages; ++i)
     if (h->ev[i]) (void)hipEventDestroy(h->ev[i]);
-  (void)hipEventDestroy(h->join);
-  (void)hipEventDestroy(h->fork);
-  (void)hipStreamDestroy(h->side);
+  if (h->join) (void)hipEventDestroy(h->join);
+  if (h->fork) (void)hipEventDestroy(h->fork);
+  if (h->side) (void)hipStreamDestroy(h->side);
   if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
   delete h;
   if (e1 != hipSuccess || e2 != hipSuccess)
     return fail(LMOE_ERR_HIP, "destroy: %s", hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+  if (bad) return fail(LMOE_ERR_CORRUPT, "destroy: %zu guard words after the workspace were overwritten", bad);
   return LMOE_OK;
 }
 

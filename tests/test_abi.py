@@ -34,9 +34,9 @@ def test_library_exports_every_header_symbol():
 
 def test_workspace_bytes_real_shapes():
     n = B.latent_moe_workspace_bytes(real_cfg())
-    # act FP16 [T*k, I], expert out FP32 [T*k, P], pooled FP32 [T, P], u and y FP16 [T, P] ...
+    # act FP16 [T*k, I], expert out FP16 [T*k, P], pooled FP32 [T, P], u and y FP16 [T, P] ...
     T, k, P, I = 16384, 8, 4096, 4096
-    floor = T * k * I * 2 + T * k * P * 4 + T * P * (4 + 2 + 2)
+    floor = T * k * I * 2 + T * k * P * 2 + T * P * (4 + 2 + 2)
     assert floor <= n <= floor * 1.2
 
 
@@ -47,7 +47,7 @@ def test_workspace_bytes_real_shapes():
     (dict(experts=0), B.LMOE_ERR_INVALID_ARG),
     (dict(experts=2000), B.LMOE_ERR_INVALID_ARG),
     (dict(top_k=0), B.LMOE_ERR_INVALID_ARG),
-    (dict(top_k=17), B.LMOE_ERR_INVALID_ARG),
+    (dict(top_k=33), B.LMOE_ERR_INVALID_ARG),
     (dict(experts=4, top_k=5), B.LMOE_ERR_INVALID_ARG),
     (dict(eps=float("nan")), B.LMOE_ERR_INVALID_ARG),
     (dict(eps=-1.0), B.LMOE_ERR_INVALID_ARG),
@@ -55,8 +55,9 @@ def test_workspace_bytes_real_shapes():
     (dict(act_dtype=7), B.LMOE_ERR_INVALID_ARG),
     (dict(act_dtype="f32", expert_dtype="bf16"), B.LMOE_ERR_UNSUPPORTED),
     (dict(act_dtype="f32", expert_dtype="mxfp4"), B.LMOE_ERR_UNSUPPORTED),
-    (dict(intermediate=4096 + 256), B.LMOE_ERR_INVALID_ARG),  # BF16: multiples of 512
-    (dict(expert_dtype="mxfp4", pooled=4096 + 256), B.LMOE_ERR_INVALID_ARG),
+    (dict(intermediate=4096 + 256), B.LMOE_ERR_UNSUPPORTED),  # valid, BF16 built for multiples of 512
+    (dict(expert_dtype="mxfp4", pooled=4096 + 256), B.LMOE_ERR_UNSUPPORTED),
+    (dict(intermediate=4096 + 64), B.LMOE_ERR_INVALID_ARG),  # not a multiple of 128
     (dict(input_norm=2), B.LMOE_ERR_INVALID_ARG),
     (dict(expert_act=5), B.LMOE_ERR_INVALID_ARG),
     (dict(expert_act="mxfp8"), B.LMOE_ERR_UNSUPPORTED),  # BF16 experts
@@ -75,18 +76,23 @@ def test_create_rejects_null_and_misaligned_weights():
     L = B.lib()
     cfg = real_cfg()
     h = ctypes.c_void_p(123)
-    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), None) == B.LMOE_ERR_INVALID_ARG
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), None, None) == B.LMOE_ERR_INVALID_ARG
     assert h.value is None  # *out cleared on failure
     w = B.Weights()
     for n in ("router", "pooler", "pool_gamma", "w_gate", "w_up", "w_down", "expert_gamma", "unpooler"):
         setattr(w, n, 4096)
     w.pooler = None
-    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w), None) == B.LMOE_ERR_INVALID_ARG
     assert "pooler" in B.latent_moe_last_error()
     w.pooler = 4096 + 8
-    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w), None) == B.LMOE_ERR_INVALID_ARG
     assert "aligned" in B.latent_moe_last_error()
-    assert L.latent_moe_create(None, ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+    assert L.latent_moe_create(None, ctypes.byref(cfg), ctypes.byref(w), None) == B.LMOE_ERR_INVALID_ARG
+
+
+def test_top_k_up_to_32_accepted():
+    for k in (16, 17, 32):
+        assert B.latent_moe_workspace_bytes(real_cfg(top_k=k)) > 0
 
 
 def test_mx_activations_accepted_with_mxfp4_experts():
@@ -111,10 +117,10 @@ def test_input_norm_needs_gamma_and_sizes_workspace():
     w = B.Weights()
     for n in ("router", "pooler", "pool_gamma", "w_gate", "w_up", "w_down", "expert_gamma", "unpooler"):
         setattr(w, n, 4096)
-    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w), None) == B.LMOE_ERR_INVALID_ARG
     assert "input_gamma" in B.latent_moe_last_error()
     w.input_gamma = 4096 + 4
-    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w), None) == B.LMOE_ERR_INVALID_ARG
     assert "aligned" in B.latent_moe_last_error()
 
 
@@ -128,10 +134,10 @@ def test_mxfp4_accepted_and_scales_required():
     for n in ("router", "pooler", "pool_gamma", "w_gate", "w_up", "w_down", "expert_gamma", "unpooler",
               "s_gate", "s_up"):
         setattr(w, n, 4096)
-    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w), None) == B.LMOE_ERR_INVALID_ARG
     assert "s_down" in B.latent_moe_last_error()
     w.s_down = 4096 + 4
-    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_INVALID_ARG
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w), None) == B.LMOE_ERR_INVALID_ARG
     assert "aligned" in B.latent_moe_last_error()
 
 
@@ -143,7 +149,7 @@ def test_create_without_device_reports_hip_error():
     for n in ("router", "pooler", "pool_gamma", "w_gate", "w_up", "w_down", "expert_gamma", "unpooler"):
         setattr(w, n, 4096)
     h = ctypes.c_void_p(0)
-    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w)) == B.LMOE_ERR_HIP
+    assert L.latent_moe_create(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(w), None) == B.LMOE_ERR_HIP
     assert "device" in B.latent_moe_last_error()
 
 

@@ -248,3 +248,20 @@ def test_oracle_mxfp4_activations_match_brute_force():
     # FP4 activations move the output by far more than FP8 ones (one mantissa bit)
     rel = np.abs(r.out - plain.out).max() / np.sqrt(np.mean(plain.out ** 2))
     assert 2e-2 < rel < 1.0
+
+
+def test_fast_f64_equals_to_f64():
+    """The tests' fast weight decoder (torch CPU kernels) gives the oracle's
+    decoded values exactly, for BF16 bits and MXFP4 (codes, scales)."""
+    import sys, os
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from layer_cases import fast_f64
+    from oracle.mx import to_f64
+
+    rng = np.random.default_rng(3)
+    bf = rng.integers(0, 1 << 16, size=(64, 256), dtype=np.uint16)
+    bf = bf[(bf & 0x7F80) != 0x7F80].reshape(-1)[:4096].reshape(16, 256)  # no inf / NaN patterns
+    assert np.array_equal(fast_f64(bf), to_f64(bf))
+    codes = rng.integers(0, 256, size=(3, 8, 64), dtype=np.uint8)
+    scales = rng.integers(100, 150, size=(3, 8, 4), dtype=np.uint8)
+    assert np.array_equal(fast_f64((codes, scales)), to_f64((codes, scales)))
