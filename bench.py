@@ -13,7 +13,15 @@ weights are measured in the same run and reported under their workload names.
 Prints one JSON line with tokens/s, the roofline of the dominant kernel (the
 gate/up grouped GEMM: HBM-bound at decode, MFMA-bound at prefill; its time
 comes from HIP events recorded on the forward's stream) and the FP64 CPU
-oracle timed on a bounded token sample on this host's cores.
+oracle timed on a bounded token sample on this host's cores (the first 48
+decode tokens, and a seeded 2048-token subset of the prefill batch).
+
+Timing: every timed step is preceded by writing a 1 GiB buffer, which evicts
+the layer's weights and activations from L2 and the 256 MB MALL, and is timed
+alone with HIP events; `value` and `ms_per_step` come from the median of
+these cold steps (p10 and p90 reported beside it). A warm-cache mean (steps
+back to back) is reported separately and labelled as such. The tiny FP32
+layer is reported in microseconds per forward.
 """
 from __future__ import annotations
 
@@ -94,15 +102,24 @@ def layer_flops(spec, T):
     return T * (2 * H * P * 2 + k * 2 * P * 2 * I + k * 2 * I * P)
 
 
+FLUSH_BYTES = 1 << 30  # written before each cold step: larger than L2 (8 x 4 MB) plus the 256 MB MALL
+
+
 def measure(spec, layer, xs, steps, warmup, torch):
     """One step = one forward per chunk in xs (a single batch, or the chunks
-    of a long prompt in order). Returns ms per step, wall seconds, per-stage
-    ms summed over the chunks of a step, and the last chunk's expert counts."""
+    of a long prompt in order). Cold steps: before each, a 1 GiB buffer is
+    written (evicting the layer's weights and activations from L2 and the
+    MALL) and the step is timed alone with HIP events on the forward's stream.
+    Warm steps: back to back, caches as the previous step left them. Returns
+    the per-step cold times (ms), the warm mean (ms), the wall time of the
+    cold loop, per-stage ms (summed over the chunks of a step) and the last
+    chunk's expert counts."""
     from latent_moe_layer_fp32_amd import binding as B
 
     stream = torch.cuda.current_stream()
     T = xs[0].shape[0]
     out = torch.empty((T, spec.H), dtype=torch.float32, device=xs[0].device)
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=xs[0].device)
 
     def step():
         for x in xs:
@@ -111,16 +128,25 @@ def measure(spec, layer, xs, steps, warmup, torch):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        scratch.fill_(1.0)  # a fill kernel on the same stream, outside the timed events
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cold = [a.elapsed_time(b) for a, b in evs]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    t0 = time.perf_counter()
     for _ in range(steps):
         step()
     end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / steps
-    # per-stage HIP events on the same stream, over the same number of steps
+    warm = start.elapsed_time(end) / steps
+    del scratch
+    # per-stage HIP events on the same stream, over the same number of (warm) steps
     B.latent_moe_set_profiling(layer.handle, True)
     acc = None
     for _ in range(steps):
@@ -130,11 +156,36 @@ def measure(spec, layer, xs, steps, warmup, torch):
             acc = st if acc is None else {k: acc[k] + v for k, v in st.items()}
     B.latent_moe_set_profiling(layer.handle, False)
     stages = {k: v / steps for k, v in acc.items()}
-    return ms, wall, stages, layer.views(T, names=("counts",))["counts"]
+    return cold, warm, wall, stages, layer.views(T, names=("counts",))["counts"]
 
 
-def cpu_baseline(spec, xh, sample_tokens, budget_s=30.0):
-    """The FP64 oracle on the first tokens of the batch (bounded sample)."""
+def host_info() -> dict:
+    """CPU model and the BLAS numpy calls (for the CPU baseline's record)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+
+        libs = [f"{d.get('internal_api')} {d.get('version')} ({d.get('num_threads')} threads)"
+                for d in threadpool_info() if d.get("user_api") == "blas"]
+        blas = "; ".join(libs) or blas
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas}
+
+
+def cpu_baseline(spec, xs, experts=None):
+    """The FP64 oracle on tokens xs of the workload (a bounded sample). Expert
+    weights are fetched by `experts` (e -> host arrays as stored) or generated
+    on the host; only the oracle's own work is timed (its conversions of the
+    stored weights included), not the fetch."""
     import numpy as np
 
     from oracle import oracle as orc
@@ -143,27 +194,31 @@ def cpu_baseline(spec, xh, sample_tokens, budget_s=30.0):
 
     host = {n: synth.host(spec, n) for n in ("router", "router_bias", "pooler", "pool_gamma",
                                             "expert_gamma", "unpooler")}
-    xs = xh[:sample_tokens]
     gin = synth.host(spec, "input_gamma") if spec.input_norm else None
-    xr = to_f64(xs) if gin is None else orc.rms_norm(to_f64(xs), to_f64(gin), spec.eps).astype(np.float32)
-    lg = orc.router_logits(to_f64(xr), to_f64(host["router"]),
-                           None if host["router_bias"] is None else to_f64(host["router_bias"]))
-    ids, _ = orc.select_topk(lg, spec.k)
-    raw = {int(e): tuple(synth.host(spec, n, experts=(int(e), int(e) + 1)) for n in ("w_gate", "w_up", "w_down"))
-           for e in np.unique(ids)}
+    fetch_s = [0.0]
 
     def first(a):
         return (a[0][0], a[1][0]) if isinstance(a, tuple) else a[0]
 
     def expert(e):
-        return tuple(to_f64(first(a)) for a in raw[e])
+        t = time.perf_counter()
+        raw = (experts(e) if experts is not None else
+               tuple(first(synth.host(spec, n, experts=(e, e + 1))) for n in ("w_gate", "w_up", "w_down")))
+        fetch_s[0] += time.perf_counter() - t
+        return tuple(to_f64(a) for a in raw)
 
     t0 = time.perf_counter()
-    orc.forward(xs, host["router"], host["router_bias"], host["pooler"], host["pool_gamma"], expert,
-                host["expert_gamma"], host["unpooler"], spec.k, spec.eps, keep_pairs=False, input_gamma=gin,
-                act_quant=spec.expert_act)
-    dt = time.perf_counter() - t0
-    return sample_tokens / dt, dt, len(raw)
+    r = orc.forward(xs, host["router"], host["router_bias"], host["pooler"], host["pool_gamma"], expert,
+                    host["expert_gamma"], host["unpooler"], spec.k, spec.eps, keep_pairs=False, input_gamma=gin,
+                    act_quant=spec.expert_act)
+    dt = time.perf_counter() - t0 - fetch_s[0]
+    return len(xs) / dt, dt, len(np.unique(r.ids))
+
+
+def pct(v, q):
+    import numpy as np
+
+    return float(np.percentile(np.asarray(v), q))
 
 
 def main():
@@ -175,10 +230,13 @@ def main():
                     choices=["decode", "prefill", "skew", "mxfp4", "mxfp4_decode", "mxfp8", "mxfp8_decode",
                              "mxfp4act", "mxfp4act_decode", "decode_norm", "prefill_norm"])
     # skew: five 16384-token chunks of one long prompt (81920 tokens per step)
-    ap.add_argument("--also", default="prefill,skew,decode_norm,prefill_norm,mxfp4_decode,mxfp4,mxfp8_decode,mxfp8,"
-                                      "mxfp4act_decode,mxfp4act",
+    ap.add_argument("--also", default="tiny,prefill,skew,decode_norm,prefill_norm,mxfp4_decode,mxfp4,mxfp8_decode,"
+                                      "mxfp8,mxfp4act_decode,mxfp4act",
                     help="extra workloads measured in the same run (comma list)")
-    ap.add_argument("--cpu-tokens", type=int, default=48, help="token sample for the CPU oracle (0: skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=48,
+                    help="token sample for the CPU oracle on the main workload (0: skip all CPU baselines)")
+    ap.add_argument("--cpu-prefill-tokens", type=int, default=2048,
+                    help="seeded token subset for the CPU oracle on the 16384-token prefill (0: skip)")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="also time torch's BF16 batched GEMM (hipBLASLt) on the gate/up shape, for reference")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -227,25 +285,58 @@ def main():
         log(f"copy calibration: 3 x {args.copy_bytes} bytes")
         del src, dst
 
+    def expert_fetch(w):
+        """Expert e of the device weights as host arrays, as stored (BF16 bits,
+        or MXFP4 codes and scales); the device copies equal the host
+        generator's output bit for bit."""
+        def fetch(e):
+            out = []
+            for n in ("w_gate", "w_up", "w_down"):
+                t = w[n]
+                if isinstance(t, tuple):
+                    out.append((t[0][e].cpu().numpy(), t[1][e].cpu().numpy()))
+                elif t.dtype == torch.bfloat16:
+                    out.append(t[e].view(torch.int16).cpu().numpy().view(np.uint16))
+                else:
+                    out.append(t[e].cpu().numpy())
+            return tuple(out)
+        return fetch
+
+    hinfo = host_info()
+    cores = len(os.sched_getaffinity(0))
     results = {}
     for wl in [args.workload] + [w for w in args.also.split(",") if w and w != args.workload]:
         spec = synth.CONFIGS[wl]
-        w = dict(weights_for(spec))
+        if spec.act_dtype == "f32":  # the tiny all-FP32 layer: its own weights
+            w = {n: synth.device_tensor(spec, n, tables) for n in synth.WEIGHT_NAMES}
+        else:
+            w = dict(weights_for(spec))
         if spec.input_norm:
             w["input_gamma"] = synth.device_tensor(spec, "input_gamma", tables)
         if spec.router_bias != "none":
             w["router_bias"] = synth.device_tensor(spec, "router_bias", tables)
         layer = make_layer(spec, w, max_tokens=spec.T)
         xs = [synth.device_tensor(spec, "x", tables, chunk=c) for c in range(spec.chunks)]
-        steps = args.steps if wl == args.workload else max(3, args.steps // 4)
-        warm = args.warmup if wl == args.workload else max(1, args.warmup // 2)
+        prefill_sized = spec.T * spec.k >= 64 * spec.E
+        if wl == args.workload:
+            steps, warm = args.steps, args.warmup
+        else:  # at least 20 timed steps of a single batch, 5 of the five-chunk prompt
+            steps = 5 if spec.chunks > 1 else max(20, args.steps)
+            warm = max(2, args.warmup // 2)
         log(f"{wl}: T={spec.T} x {spec.chunks} chunk(s), {warm} warmup + {steps} timed steps")
-        ms, wall, stages, counts = measure(spec, layer, xs, steps, warm, torch)
+        cold, warm_ms, wall, stages, counts = measure(spec, layer, xs, steps, warm, torch)
+        ms = pct(cold, 50)
         lb, touched = layer_bytes(spec, counts, spec.T)
         r = dict(spec=spec, ms=ms, wall=wall, stages=stages, touched=touched, layer_bytes=lb,
-                 tokens_per_s=spec.T * spec.chunks / (ms / 1e3), steps=steps, warmup=warm)
+                 tokens_per_s=spec.T * spec.chunks / (ms / 1e3), steps=steps, warmup=warm,
+                 cold={"p10": round(pct(cold, 10), 4), "p50": round(ms, 4), "p90": round(pct(cold, 90), 4)},
+                 warm_ms=round(warm_ms, 4))
         gu = stages["gate_up"] / 1e3
-        if spec.T * spec.k < 64 * spec.E:  # decode-sized: the expert weights stream once
+        if spec.act_dtype == "f32":
+            r["roofline"] = None  # launch-latency bound (21 MFLOP): reported in microseconds
+            r["us_per_forward"] = {"cold_p50": round(ms * 1e3, 1), "warm": round(warm_ms * 1e3, 1)}
+            r["layer_frac"] = None
+        elif not prefill_sized:  # decode-sized: the expert weights stream once
             ach = gate_up_bytes(spec, counts, spec.T) / gu / 1e9
             r["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
@@ -264,8 +355,24 @@ def main():
                              "kernel": "gate_up grouped GEMM + SwiGLU",
                              "kernel_ms": round(stages["gate_up"], 4)}
             r["layer_frac"] = round(layer_flops(spec, spec.T * spec.chunks) / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)
-        log(f"{wl}: {ms:.3f} ms/step, {r['tokens_per_s']:.0f} tok/s, stages "
+        log(f"{wl}: cold {ms:.3f} ms/step (p10 {r['cold']['p10']:.3f}, p90 {r['cold']['p90']:.3f}), "
+            f"warm {warm_ms:.3f}, {r['tokens_per_s']:.0f} tok/s, stages "
             + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
+        cpu_n = 0
+        if args.cpu_tokens > 0 and wl == args.workload:
+            cpu_n, sample_desc = args.cpu_tokens, f"first {args.cpu_tokens} tokens of the {wl} batch"
+            idx = np.arange(cpu_n)
+        elif args.cpu_tokens > 0 and wl == "prefill" and args.cpu_prefill_tokens > 0:
+            cpu_n = args.cpu_prefill_tokens
+            idx = np.sort(np.random.default_rng(0).choice(spec.T, cpu_n, replace=False))
+            sample_desc = f"seeded subset of {cpu_n} of the {spec.T} prefill tokens (exact: the layer is token-local)"
+        if cpu_n:
+            log(f"{wl}: cpu oracle on {cpu_n} tokens")
+            xh = synth.host(spec, "x")[idx]
+            v, dt, ne = cpu_baseline(spec, xh, expert_fetch(w) if spec.act_dtype != "f32" else None)
+            r["cpu_baseline"] = {"value": round(v, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                                 "sample": f"{sample_desc} ({ne} experts), FP64 numpy, {dt:.1f} s",
+                                 **hinfo}
         results[wl] = r
         layer.close()
         del xs
@@ -292,16 +399,23 @@ def main():
                    "global_batch": spec.T * spec.chunks, "parallelism": "none (one GPU)"},
         "roofline": main_r["roofline"],
         "layer_frac": main_r["layer_frac"],
+        "timing": {"value_from": "median of cold steps (1 GiB written before each; HIP events per step)",
+                   "cold_ms": main_r["cold"], "warm_ms": main_r["warm_ms"],
+                   "warm_tokens_per_s": round(spec.T * spec.chunks / (main_r["warm_ms"] / 1e3), 1)},
         "stages_ms": {k: round(v, 4) for k, v in main_r["stages"].items()},
         "experts_touched": main_r["touched"],
     }
     for wl, r in results.items():
         if wl == args.workload:
             continue
-        line[wl] = {"value": round(r["tokens_per_s"], 1), "unit": "tokens/s", "ms_per_step": round(r["ms"], 4),
-                    "tokens_per_step": r["spec"].T * r["spec"].chunks,
-                    "steps": r["steps"], "roofline": r["roofline"], "layer_frac": r["layer_frac"],
-                    "stages_ms": {k: round(v, 4) for k, v in r["stages"].items()}}
+        sub = {"value": round(r["tokens_per_s"], 1), "unit": "tokens/s", "ms_per_step": round(r["ms"], 4),
+               "tokens_per_step": r["spec"].T * r["spec"].chunks, "steps": r["steps"],
+               "cold_ms": r["cold"], "warm_ms": r["warm_ms"], "roofline": r["roofline"],
+               "layer_frac": r["layer_frac"], "stages_ms": {k: round(v, 4) for k, v in r["stages"].items()}}
+        for key in ("us_per_forward", "cpu_baseline"):
+            if key in r:
+                sub[key] = r[key]
+        line[wl] = sub
     if args.vendor_gemm:
         # 256 experts x 512 rows (uniform routing), K = P, N = 2I; contiguous operands, no gather
         E_, M_, K_, N_ = 256, 512, 4096, 8192
@@ -319,14 +433,8 @@ def main():
         line["vendor_bf16_gemm"] = {"shape": f"bmm {E_} x [{M_} x {K_}] x [{K_} x {N_}]", "ms": round(vms, 4),
                                     "TFLOP/s": round(2 * E_ * M_ * K_ * N_ / vms / 1e9, 1)}
         del a, b
-    if args.cpu_tokens > 0:
-        xh = synth.host(spec, "x")
-        log(f"cpu oracle on {args.cpu_tokens} tokens")
-        v, dt, ne = cpu_baseline(spec, xh, args.cpu_tokens)
-        line["cpu_baseline"] = {"value": round(v, 4), "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
-                                "kind": "oracle",
-                                "sample": f"first {args.cpu_tokens} tokens of the {args.workload} batch "
-                                          f"({ne} experts), FP64 numpy, {dt:.1f} s"}
+    if "cpu_baseline" in main_r:
+        line["cpu_baseline"] = main_r["cpu_baseline"]
     print(json.dumps(line), flush=True)
 
 
