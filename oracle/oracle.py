@@ -91,6 +91,8 @@ class OracleResult:
     a: np.ndarray | None  # [T, k, I] SwiGLU output per slot
     o: np.ndarray | None  # [T, k, P] expert output per slot (before its norm)
     ohat: np.ndarray | None  # [T, k, P] normed expert output per slot
+    # a, o and ohat hold the rows of all tokens, or (keep_pairs given as token
+    # indices) of those tokens only, in the order given
     y: np.ndarray  # [T, P] combined
     near_tie: np.ndarray  # [T] bool: some gap j <= k below NEAR_TIE
     xn: np.ndarray | None = None  # [T, H] FP32 boundary-norm output (input gamma given)
@@ -182,6 +184,9 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
       (an element whose value sits on the midpoint between two codes may be
       rounded either way by a kernel that forms it in lower precision; the
       caller checks that the rows differ from this oracle's only there).
+    keep_pairs: True keeps the per-slot a, o and ohat of every token; False
+      none; a sequence of token indices keeps those tokens' rows only (in
+      that order). The output is the same in every case.
     """
     modes = tuple(emulate) if isinstance(emulate, (tuple, list)) else (emulate,)
     for m in modes:
@@ -225,17 +230,33 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
             for t, row in force_u.items():
                 uq[t] = row
 
+    # tokens whose per-slot rows are kept, and each token's row among them (-1: not kept)
+    if keep_pairs is True:
+        kept = np.arange(T)
+    elif keep_pairs is False or keep_pairs is None:
+        kept = np.zeros(0, dtype=np.int64)
+    else:
+        kept = np.asarray(keep_pairs, dtype=np.int64)
+    slot_row = np.full(T, -1, dtype=np.int64)
+    slot_row[kept] = np.arange(len(kept))
+    keep = keep_pairs is not False and keep_pairs is not None
+
     # per mode: the expert input u and the per-slot results
     st = []
     for m in modes:
         u = uq if act_quant else (f16_round(u_exact, sc["u"]) if m == "f16" else u_exact)
-        st.append(dict(u=u, ohat=np.zeros((T, k, P)), o=np.zeros((T, k, P)) if keep_pairs else None, a=None))
+        st.append(dict(u=u, ohat=np.zeros((T, k, P)), o=np.zeros((len(kept), k, P)) if keep else None, a=None,
+                       ohat_kept=np.zeros((len(kept), k, P)) if keep else None))
 
     for e in np.unique(ids):
         tt, jj = np.nonzero(ids == e)
         Wg, Wu, Wd = experts(int(e))
-        asc = np.repeat(a_scales(Wg, Wu, P, gp), 32) if "f16" in modes and not act_quant else None
-        osc = o_scale(Wg, Wu, Wd, P, gp, 2.0 if act_quant else 1.0) if "f16" in modes else None
+        asc = osc = None
+        if "f16" in modes:
+            asc, osc = expert_scales(Wg, Wu, Wd, P, gp, 2.0 if act_quant else 1.0)
+            asc = None if act_quant else np.repeat(asc, 32)
+        kr = slot_row[tt]
+        ks = kr >= 0
         for m, S in zip(modes, st):
             U = S["u"][tt]
             g = U @ Wg.T
@@ -247,15 +268,25 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
                 a = quantize_mx(a, act_quant)[0]
             o = a @ Wd.T
             o_st = f16_round(o, osc) if m == "f16" else o  # o as stored; its norm uses o
-            if keep_pairs:
-                if S["a"] is None:
-                    S["a"] = np.zeros((T, k, Wg.shape[0]))
-                S["a"][tt, jj] = a
-                S["o"][tt, jj] = o_st
             if order == "norm_then_sum":
                 S["ohat"][tt, jj] = o_st / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps) * ge[e]
             else:
                 S["ohat"][tt, jj] = o_st
+            if keep:
+                if S["a"] is None:
+                    S["a"] = np.zeros((len(kept), k, Wg.shape[0]))
+                S["a"][kr[ks], jj[ks]] = a[ks]
+                S["o"][kr[ks], jj[ks]] = o_st[ks]
+                S["ohat_kept"][kr[ks], jj[ks]] = S["ohat"][tt[ks], jj[ks]]
+
+    # a token kept at several positions: its rows were written at the last of them
+    src = slot_row[kept]
+    dup = src != np.arange(len(kept))
+    if keep and dup.any():
+        for S in st:
+            for name in ("a", "o", "ohat_kept"):
+                if S[name] is not None:
+                    S[name][dup] = S[name][src[dup]]
 
     res = []
     for m, S in zip(modes, st):
@@ -268,7 +299,7 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
             y = f16_round(y, sc["y"])
         out = y @ Wun.T
         res.append(OracleResult(out=out, ids=ids, w=w, logits=logits, gaps=gaps, h=h, u=S["u"], a=S["a"],
-                                o=S["o"], ohat=S["ohat"] if keep_pairs else None, y=y, near_tie=near, xn=xn,
+                                o=S["o"], ohat=S["ohat_kept"], y=y, near_tie=near, xn=xn,
                                 u_pre=u_pre))
     return res if isinstance(emulate, (tuple, list)) else res[0]
 
@@ -298,22 +329,40 @@ def f16_scales(pool_gamma, expert_gamma, P: int) -> dict:
             "y": pow2_down(np.sqrt(P) * float(np.max(np.abs(expert_gamma))), 100)}
 
 
+def row_norms(W: np.ndarray) -> np.ndarray:
+    """Euclidean norm of each row of W."""
+    return np.sqrt(np.einsum("ij,ij->i", W, W))
+
+
+def scales_from_norms(ng, nu, nd, P: int, pool_gamma, amp: float = 1.0):
+    """The FP16 range scalings of one expert from the row norms of its gate,
+    up and down weights (ng, nu [I], nd [P]): the SwiGLU outputs' powers of
+    two per block of 32 outputs [I/32], from max over the block of
+    ||Wg_i|| ||Wu_i|| times P max(gamma_p)^2, and the outputs' power of two,
+    from max_p ||Wd_p|| P max(gamma_p)^2 sqrt(sum_i (||Wg_i|| ||Wu_i||)^2)
+    times amp (module docstring)."""
+    gp = float(np.max(np.abs(pool_gamma)))
+    gu = ng * nu
+    m = gu.reshape(-1, 32).max(axis=1)
+    asc = np.array([pow2_down(b * P * gp * gp, 60) for b in m])
+    osc = pow2_down(float(nd.max()) * P * gp * gp * float(np.sqrt(np.sum(gu * gu))) * amp, 100)
+    return asc, osc
+
+
+def expert_scales(Wg, Wu, Wd, P: int, pool_gamma, amp: float = 1.0):
+    """scales_from_norms of one expert's weights."""
+    return scales_from_norms(row_norms(Wg), row_norms(Wu), row_norms(Wd), P, pool_gamma, amp)
+
+
 def a_scales(Wg, Wu, P: int, pool_gamma) -> np.ndarray:
     """Powers of two one expert's SwiGLU outputs are stored with in FP16, per
-    block of 32 outputs [I/32]: from max over the block of ||Wg_i|| ||Wu_i||
-    times P max(gamma_p)^2 (module docstring)."""
-    gp = float(np.max(np.abs(pool_gamma)))
-    m = (np.linalg.norm(Wg, axis=1) * np.linalg.norm(Wu, axis=1)).reshape(-1, 32).max(axis=1)
-    return np.array([pow2_down(b * P * gp * gp, 60) for b in m])
+    block of 32 outputs [I/32] (scales_from_norms)."""
+    return scales_from_norms(row_norms(Wg), row_norms(Wu), np.zeros(1), P, pool_gamma)[0]
 
 
 def o_scale(Wg, Wu, Wd, P: int, pool_gamma, amp: float = 1.0) -> float:
-    """Power of two one expert's outputs are stored with in FP16: from
-    max_p ||Wd_p|| P max(gamma_p)^2 sqrt(sum_i (||Wg_i|| ||Wu_i||)^2), times
-    amp (module docstring)."""
-    gp = float(np.max(np.abs(pool_gamma)))
-    na = np.sqrt(np.sum((np.linalg.norm(Wg, axis=1) * np.linalg.norm(Wu, axis=1)) ** 2))
-    return pow2_down(float(np.linalg.norm(Wd, axis=1).max()) * P * gp * gp * na * amp, 100)
+    """Power of two one expert's outputs are stored with in FP16 (scales_from_norms)."""
+    return expert_scales(Wg, Wu, Wd, P, pool_gamma, amp)[1]
 
 
 def _bf16_round(v: np.ndarray) -> np.ndarray:

@@ -23,6 +23,7 @@ class HostLayer:
         self.w = {n: synth.host(spec, n) for n in NON_EXPERT}
         self.dev = dev
         self._cache = {}
+        self._norms = {}
 
     def expert(self, e: int):
         if e not in self._cache:
@@ -35,6 +36,19 @@ class HostLayer:
             else:
                 self._cache[e] = tuple(to_f64(_first(synth.host(s, n, experts=(e, e + 1)))) for n in names)
         return self._cache[e]
+
+    def norms(self, e: int):
+        """Row norms of expert e's gate, up and down weights (kept for the
+        layer's lifetime: three short vectors per expert)."""
+        if e not in self._norms:
+            self._norms[e] = tuple(orc.row_norms(W) for W in self.expert(e))
+        return self._norms[e]
+
+    def scales(self, e: int, amp: float = 1.0):
+        """Expert e's FP16 range scalings (a per block of 32, o), as the
+        oracle derives them."""
+        ng, nu, nd = self.norms(e)
+        return orc.scales_from_norms(ng, nu, nd, self.spec.P, self.w["pool_gamma"].astype(np.float64), amp)
 
     def x(self, chunk: int = 0):
         return synth.host(self.spec, "x", chunk=chunk)
@@ -237,57 +251,74 @@ def _check_acc(gpu, ref, mag, what):
     return float((err / np.maximum(mag, 1e-300)).max())
 
 
-def check_stage_chain(v: dict, rows, ids_rows, w_rows, host: HostLayer, u_exact: np.ndarray) -> dict:
-    """Chained stage checks (above) for the tokens `rows` of the last forward
-    of a BF16-activation layer whose expert inputs are FP16 (views `v` with
-    pooled, row_scale, expert_in, act, expert_out, combined, pair_row; out
-    passed as v["out"]). u_exact: the oracle's u of those rows. Returns the
-    flip fractions and largest accumulation errors."""
+def gather_rows(v: dict, rows, k: int, out: np.ndarray) -> dict:
+    """The stage values of the tokens `rows` of the last forward (views `v`
+    and its output `out`), as host arrays per token: expert_in, pooled and
+    row_scale [n, ...], act and expert_out per slot [n, k, ...], combined,
+    and out. Rows of several forwards concatenate (concat_rows)."""
+    rows = np.asarray(rows)
+    pr = v["pair_row"].reshape(-1, k)[rows]
+    return dict(expert_in=v["expert_in"][rows].astype(np.float64), pooled=v["pooled"][rows].astype(np.float32),
+                row_scale=v["row_scale"][rows].astype(np.float32), act=v["act"][pr].astype(np.float64),
+                expert_out=v["expert_out"][pr].astype(np.float64),
+                combined=v["combined"][rows].astype(np.float64), out=out[rows].astype(np.float64))
+
+
+def concat_rows(parts) -> dict:
+    return {n: np.concatenate([p[n] for p in parts]) for n in parts[0]}
+
+
+def check_stage_chain(g: dict, ids_rows, w_rows, host: HostLayer, u_exact: np.ndarray) -> dict:
+    """Chained stage checks (above) on gathered rows `g` (gather_rows) of a
+    BF16-activation layer whose expert inputs are FP16; ids_rows, w_rows: the
+    GPU's selection and weights of those rows; u_exact: the oracle's u of
+    those rows. The FP32 accumulation slack of a product x W^T is taken as
+    2^-15 ||x|| ||W_row|| (Cauchy-Schwarz bound on sum |x w|). Returns the flip
+    fractions and the largest accumulation error of out."""
     spec = host.spec
     P, k = spec.P, spec.k
     hw = host.w
     gp, ge = to_f64(hw["pool_gamma"]), to_f64(hw["expert_gamma"])
     sc = orc.f16_scales(gp, ge, P)
     res = {}
-    u16 = v["expert_in"][rows].astype(np.float64)
-    rd = (v["row_scale"][rows].astype(np.float32) * np.float32(sc["u"]))[:, None]
-    u32 = v["pooled"][rows].astype(np.float32) * rd  # the kernel's FP32 product
+    u16 = g["expert_in"]
+    rd = (g["row_scale"] * np.float32(sc["u"]))[:, None]
+    u32 = g["pooled"] * rd  # the kernel's FP32 product
     ref_u = np.clip(u32, -65504, 65504).astype(np.float16).astype(np.float64) / sc["u"]
     assert np.array_equal(u16, ref_u), "u: not the FP16 rounding of the kernel's FP32 u"
     res["u_flips"] = float((u16 != orc.f16_round(u_exact, sc["u"])).mean())  # against the exact u
-    pr = v["pair_row"].reshape(-1, k)[rows]
-    a_gpu = v["act"].astype(np.float64)
-    o_gpu = v["expert_out"].astype(np.float64)
+    n = len(u16)
     fa, eo = [], []
-    ohat = np.zeros((len(rows), k, P))
-    mag = np.zeros((len(rows), k, P))
+    ohat = np.zeros((n, k, P))
     for e in np.unique(ids_rows):
         tt, jj = np.nonzero(ids_rows == e)
         Wg, Wu, Wd = host.expert(int(e))
+        ng, nu, nd = host.norms(int(e))
+        asc, osc = host.scales(int(e))
+        asc = np.repeat(asc, 32)
         U = u16[tt]
-        g, vv = U @ Wg.T, U @ Wu.T
-        a_ref = orc.silu(g) * vv
+        nU = orc.row_norms(U)[:, None]
+        g_, vv = U @ Wg.T, U @ Wu.T
+        a_ref = orc.silu(g_) * vv
         # FP32 error of the kernel's silu(g) v: from g and v (FP32 sums) and the
         # FP32 evaluation of silu (exp and reciprocal, a few ulp)
-        dg, dv = ACC_REL * (np.abs(U) @ np.abs(Wg).T), ACC_REL * (np.abs(U) @ np.abs(Wu).T)
-        slack = 1.1 * (dg * np.abs(vv) + np.abs(g) * dv) + 2.0 ** -20 * np.abs(a_ref)
-        asc = np.repeat(orc.a_scales(Wg, Wu, P, gp), 32)
-        a16 = a_gpu[pr[tt, jj]]
+        dg, dv = ACC_REL * nU * ng[None, :], ACC_REL * nU * nu[None, :]
+        slack = 1.1 * (dg * np.abs(vv) + np.abs(g_) * dv) + 2.0 ** -20 * np.abs(a_ref)
+        a16 = g["act"][tt, jj]
         fa.append(_check_f16(a16, orc.f16_round(a_ref, asc), asc, slack, f"act, expert {e}"))
-        o16 = o_gpu[pr[tt, jj]]
+        o16 = g["expert_out"][tt, jj]
         o_ref = a16 @ Wd.T
-        osc = orc.o_scale(Wg, Wu, Wd, P, gp)
-        eo.append(_check_f16(o16, orc.f16_round(o_ref, osc), osc, ACC_REL * (np.abs(a16) @ np.abs(Wd).T),
+        eo.append(_check_f16(o16, orc.f16_round(o_ref, osc), osc, ACC_REL * orc.row_norms(a16)[:, None] * nd[None, :],
                              f"expert out, expert {e}"))
         ohat[tt, jj] = o16 / np.sqrt(np.mean(o_ref * o_ref, axis=-1, keepdims=True) + spec.eps) * ge[e]
-        mag[tt, jj] = np.abs(ohat[tt, jj])
     res["a_flips"] = float(np.mean(fa))
     res["o_flips"] = float(np.mean(eo))
     wr = w_rows.astype(np.float64)
     y_ref = np.einsum("tj,tjp->tp", wr, ohat)
-    y_slack = 2.0 ** -17 * np.einsum("tj,tjp->tp", np.abs(wr), mag)  # FP32 sums of squares, norm, k-term sum
-    y16 = v["combined"][rows].astype(np.float64)
+    y_slack = 2.0 ** -17 * np.einsum("tj,tjp->tp", np.abs(wr), np.abs(ohat))  # FP32 sums of squares, norm, k-term sum
+    y16 = g["combined"]
     res["y_flips"] = _check_f16(y16, orc.f16_round(y_ref, sc["y"]), sc["y"], y_slack, "y")
     Wun = to_f64(hw["unpooler"])
-    res["out_acc"] = _check_acc(v["out"][rows].astype(np.float64), y16 @ Wun.T, np.abs(y16) @ np.abs(Wun).T, "out")
+    mag = orc.row_norms(y16)[:, None] * orc.row_norms(Wun)[None, :]
+    res["out_acc"] = _check_acc(g["out"], y16 @ Wun.T, mag, "out")
     return res

@@ -13,8 +13,8 @@ import numpy as np
 import pytest
 
 import synth
-from layer_cases import (HostLayer, bf16_to_f64, check_expert_input, check_output, check_rel_l2, check_routing,
-                         check_stage_chain, device_weights)
+from layer_cases import (HostLayer, check_expert_input, check_output, check_rel_l2, check_routing, check_stage_chain,
+                         concat_rows, device_weights, gather_rows)
 from oracle import oracle as orc
 from oracle.mx import to_f64
 
@@ -132,46 +132,64 @@ def real_norm(torch_dev, tables):
     layer.close()
 
 
-@pytest.mark.parametrize("wl,T", [("decode", 64), ("prefill", 4097), ("prefill", 16384)])
-def test_real_input_norm_sampled_parity(torch_dev, tables, real_norm, wl, T):
+def _sample(T, n, seed):
+    if n >= T:
+        return np.arange(T)
+    s = np.sort(np.random.default_rng(seed).choice(T, n, replace=False))
+    s[-1] = T - 1
+    return np.unique(s)
+
+
+def test_real_input_norm_parity(torch_dev, tables, real_norm):
+    """Decode (64 tokens), 4097 and 16384 tokens with the boundary norm: the
+    norm's FP32 output on every token (one ulp), its BF16 rounding, logits and
+    routing on every token; outputs against the exact oracle (2e-2 x RMS) and
+    the FP16 emulation, stages and the stage chain on all 64 decode tokens and
+    256 tokens of each prefill batch (one oracle pass over the 576 tokens)."""
     torch = torch_dev
     spec, layer, host, gin = real_norm
-    wspec = synth.CONFIGS[wl]
-    say(f"case: {wl} BF16 with boundary norm, T={T}")
-    r_dev = (synth.device_tensor(wspec, "x", tables)[:T] * SCALE).contiguous()
-    rh = residual_host(wspec)[:T]
-    out, ids, w = run(torch, layer, r_dev)
-    v = layer.views(T)
-    xn_ref = oracle_xn(host, rh, gin)
-    nd = check_xn(v["x_norm"], xn_ref)
-    # the split's first piece is the BF16 rounding (nearest even) of the FP32 norm
-    f = v["x_norm"].view(np.uint32).astype(np.uint64)
-    rne = ((f + 0x7FFF + ((f >> 16) & 1)) >> 16).astype(np.uint16)
-    assert np.array_equal(v["x_norm_split"][:, :spec.H], rne)
-    logits64 = orc.router_logits(xn_ref, to_f64(host.w["router"]), None)
-    near, _ = check_routing(ids, w, logits64, spec.k)
-    if near:
-        say(f"{wl}: near-ties at tokens {near}")
-    dl = np.abs(v["logits"].astype(np.float64) - logits64)
-    assert np.all(dl <= 2.0 ** -24 * np.abs(logits64) + 2.5e-7), f"logit error {dl.max():.3g}"
-    if T <= 64:
-        sample = np.arange(T)
-    else:
-        sample = np.sort(np.random.default_rng(T).choice(T, 256, replace=False))
-        sample[-1] = T - 1
-    force = {i: ids[t] for i, t in enumerate(sample) if t in near}
-    ref, em = host.oracle(rh[sample], input_gamma=gin, force_ids=force or None, emulate=(None, "f16"))
-    assert np.array_equal(ids[sample], ref.ids)
-    pr = v["pair_row"].reshape(T, spec.k)[sample]
-    check_expert_input(v, sample, ref.u)
-    check_rel_l2(bf16_to_f64(v["act"][pr]), ref.a, 1e-2, "act")
-    e = check_output(out[sample], ref.out, 2e-2)
-    rms = float(np.sqrt(np.mean(ref.out ** 2)))
-    d = out[sample].astype(np.float64) - em.out
-    ee = (float(np.abs(d).max() / rms), float(np.sqrt(np.mean(d * d)) / rms))
-    v["out"] = out
-    ch = check_stage_chain(v, sample, ids[sample], w[sample], host, ref.u)
-    say(f"{wl} norm T={T}: x_norm {nd} elements 1 ulp off (all tokens); max |logit err| {dl.max():.3g}; "
-        f"out max-abs {e:.3g} x RMS on {len(sample)} tokens, vs emulation max {ee[0]:.3g} rms {ee[1]:.3g}; "
-        f"stage flips u {ch['u_flips']:.2g} a {ch['a_flips']:.2g} o {ch['o_flips']:.2g} y {ch['y_flips']:.2g}")
-    assert ee[0] <= 4e-3 and ee[1] <= 6e-4, f"vs FP16 emulation: max {ee[0]:.3g}, rms {ee[1]:.3g}"
+    k = spec.k
+    r_all = (synth.device_tensor(spec, "x", tables) * SCALE).contiguous()
+    rh_all = residual_host(spec)
+    cases = []
+    for T, n in ((64, 64), (4097, 256), (16384, 256)):
+        say(f"case: BF16 with boundary norm, T={T}")
+        out, ids, w = run(torch, layer, r_all[:T].contiguous())
+        v = layer.views(T)
+        xn_ref = oracle_xn(host, rh_all[:T], gin)
+        nd = check_xn(v["x_norm"], xn_ref)
+        # the split's first piece is the BF16 rounding (nearest even) of the FP32 norm
+        f = v["x_norm"].view(np.uint32).astype(np.uint64)
+        rne = ((f + 0x7FFF + ((f >> 16) & 1)) >> 16).astype(np.uint16)
+        assert np.array_equal(v["x_norm_split"][:, :spec.H], rne)
+        logits64 = orc.router_logits(xn_ref, to_f64(host.w["router"]), None)
+        near, _ = check_routing(ids, w, logits64, k)
+        dl = np.abs(v["logits"].astype(np.float64) - logits64)
+        assert np.all(dl <= 2.0 ** -24 * np.abs(logits64) + 2.5e-7), f"logit error {dl.max():.3g}"
+        sample = _sample(T, n, T)
+        say(f"T={T}: x_norm {nd} elements 1 ulp off (all tokens); max |logit err| {dl.max():.3g}; near-ties {near}")
+        cases.append(dict(T=T, rh=rh_all[sample], out=out[sample], ids=ids[sample], w=w[sample],
+                          near=np.isin(sample, near), g=gather_rows(v, sample, k, out)))
+    X = np.concatenate([c["rh"] for c in cases])
+    IDS = np.concatenate([c["ids"] for c in cases])
+    force = {int(i): IDS[i] for i in np.nonzero(np.concatenate([c["near"] for c in cases]))[0]}
+    ref, em = host.oracle(X, input_gamma=gin, force_ids=force or None, emulate=(None, "f16"), keep_pairs=True)
+    assert np.array_equal(IDS, ref.ids)
+    G = concat_rows([c["g"] for c in cases])
+    n0 = 0
+    for c in cases:
+        sl = slice(n0, n0 + len(c["out"]))
+        n0 += len(c["out"])
+        rms = float(np.sqrt(np.mean(ref.out[sl] ** 2)))
+        e = check_output(c["out"], ref.out[sl], 2e-2, rms=rms)
+        d = c["out"].astype(np.float64) - em.out[sl]
+        ee = (float(np.abs(d).max() / rms), float(np.sqrt(np.mean(d * d)) / rms))
+        say(f"T={c['T']}: out max-abs {e:.3g} x RMS on {len(c['out'])} tokens, vs emulation max {ee[0]:.3g} "
+            f"rms {ee[1]:.3g}")
+        assert ee[0] <= 4e-3 and ee[1] <= 6e-4, f"T={c['T']} vs FP16 emulation: max {ee[0]:.3g}, rms {ee[1]:.3g}"
+    n = len(X)
+    check_expert_input(G, np.arange(n), ref.u)
+    check_rel_l2(G["act"], ref.a, 1e-2, "act")
+    ch = check_stage_chain(G, IDS, np.concatenate([c["w"] for c in cases]), host, ref.u)
+    say(f"boundary norm, {n} tokens: stage flips u {ch['u_flips']:.2g} a {ch['a_flips']:.2g} "
+        f"o {ch['o_flips']:.2g} y {ch['y_flips']:.2g}, FP32 acc out {ch['out_acc']:.2g}")

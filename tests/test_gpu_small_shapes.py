@@ -16,7 +16,7 @@ import pytest
 
 import synth
 from layer_cases import (HostLayer, bf16_to_f64, check_output, check_rel_l2, check_routing, check_stage_chain,
-                         device_weights, mx_u_ties)
+                         device_weights, gather_rows, mx_u_ties)
 
 pytestmark = pytest.mark.gpu
 
@@ -80,12 +80,12 @@ def test_small_full_parity(torch_dev, tables, name, over, T):
         assert np.array_equal(layer.forward(x).cpu().numpy(), out), "second forward differs"
         host = HostLayer(spec)
         xh = host.x()
-        r0 = host.oracle(xh, input_gamma=gin, keep_pairs=False)
-        near, _ = check_routing(ids, w, r0.logits, spec.k)
+        r, re_ = host.oracle(xh, input_gamma=gin, emulate=(None, "f16"))
+        near, _ = check_routing(ids, w, r.logits, spec.k)
         force = {int(t): ids[t] for t in near}
-        r = host.oracle(xh, input_gamma=gin, force_ids=force or None) if near else host.oracle(xh, input_gamma=gin)
         if near:
             say(f"{name}: near-ties at tokens {near}")
+            r, re_ = host.oracle(xh, input_gamma=gin, force_ids=force, emulate=(None, "f16"))
         assert np.array_equal(ids, r.ids)
         order = np.argsort(ids.ravel(), kind="stable")
         assert np.array_equal(v["perm_token"], order // spec.k)
@@ -98,9 +98,7 @@ def test_small_full_parity(torch_dev, tables, name, over, T):
         # each stage against its declared FP16 rounding of the GPU's own inputs (to one
         # FP16 ulp, or an FP32 accumulation bound), and end to end against the oracle
         # emulating the FP16 rounding points
-        v["out"] = out
-        ch = check_stage_chain(v, np.arange(T), ids, w, host, r.u)
-        re_ = host.oracle(xh, input_gamma=gin, force_ids=force or None, emulate="f16", keep_pairs=False)
+        ch = check_stage_chain(gather_rows(v, np.arange(T), spec.k, out), ids, w, host, r.u)
         rms = float(np.sqrt(np.mean(r.out ** 2)))
         d = out.astype(np.float64) - re_.out
         em = (float(np.abs(d).max() / rms), float(np.sqrt(np.mean(d * d)) / rms))

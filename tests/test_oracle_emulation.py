@@ -94,3 +94,39 @@ def test_emulation_with_mx_activations_matches_brute_force(fmt):
     out, ids, _ = run_brute(d, 2, f16_points=True, **{fmt + "_acts": True})
     assert np.array_equal(r.ids, np.array(ids))
     close(r.out, out, 1e-11)
+
+
+def test_kept_rows_are_the_full_rows():
+    """keep_pairs given as token indices keeps exactly those tokens' per-slot
+    rows (in the order given, repeats allowed), for both modes in one pass,
+    and changes no output."""
+    rng = np.random.default_rng(12)
+    d = rand_layer(rng, T=9, H=8, P=32, E=5, I=64, k=2)
+    full = orc.forward_inputs(d, 2, 1e-6, emulate=(None, "f16"))
+    rows = [7, 0, 3, 7]
+    part = orc.forward_inputs(d, 2, 1e-6, emulate=(None, "f16"), keep_pairs=rows)
+    none = orc.forward_inputs(d, 2, 1e-6, emulate=(None, "f16"), keep_pairs=False)
+    for f, p, n in zip(full, part, none):
+        assert np.array_equal(f.out, p.out) and np.array_equal(f.out, n.out)
+        for name in ("a", "o", "ohat"):
+            assert np.array_equal(getattr(f, name)[rows], getattr(p, name))
+        assert n.a is None and n.o is None and n.ohat is None
+
+
+def test_scales_from_row_norms_match_the_bounds():
+    """The range scalings follow their bounds: every stored value of the
+    emulation lies within 2^15 after its scaling, and halving the scaling
+    (the next power of two down) is never needed: the bound itself times the
+    scaling lies in (2^14, 2^15] unless the scaling is 1."""
+    rng = np.random.default_rng(13)
+    P, I = 16, 64
+    Wg, Wu = rng.standard_normal((I, P)) * 40, rng.standard_normal((I, P))
+    Wd = rng.standard_normal((P, I)) * 30
+    gp = np.full(P, 3.0)
+    asc, osc = orc.expert_scales(Wg, Wu, Wd, P, gp)
+    ng, nu, nd = (np.sqrt((W * W).sum(1)) for W in (Wg, Wu, Wd))
+    ba = (ng * nu).reshape(-1, 32).max(1) * P * 9.0
+    bo = nd.max() * P * 9.0 * np.sqrt(((ng * nu) ** 2).sum())
+    for b, s in list(zip(ba, asc)) + [(bo, osc)]:
+        assert b * s <= 32768.0 and (s == 1.0 or b * s > 16384.0)
+    assert np.array_equal(asc, orc.a_scales(Wg, Wu, P, gp)) and osc == orc.o_scale(Wg, Wu, Wd, P, gp)
