@@ -53,8 +53,18 @@ LM_DEV float lm_e8m0_shifted(uint32_t code, int s) {
 
 // The register budget allows two waves per SIMD: two four-wave workgroups
 // per CU, or one eight-wave workgroup (see kLeanA, kLeanB below).
+// Decode-sized tiles with MXFP4 weights need fewer registers (a quarter of
+// the B bytes per k-tile) and run LM_MX_NARROW_WAVES waves per SIMD.
+#ifndef LM_MX_NARROW_WAVES
+#define LM_MX_NARROW_WAVES 2
+#endif
 template <class Prob>
-__global__ __launch_bounds__(64 * Prob::Cfg::WN) __attribute__((amdgpu_waves_per_eu(LM_WAVES_MAX, LM_WAVES_MAX)))
+struct LmWavesPerEu
+    : std::integral_constant<int, Prob::Cfg::TM == 1 && LmIsMx<Prob>::value ? LM_MX_NARROW_WAVES : LM_WAVES_MAX> {};
+
+template <class Prob>
+__global__ __launch_bounds__(64 * Prob::Cfg::WN)
+__attribute__((amdgpu_waves_per_eu(LmWavesPerEu<Prob>::value, LmWavesPerEu<Prob>::value)))
 void lm_gemm_stream_kernel(const Prob p) {
   using Cfg = typename Prob::Cfg;
   static_assert(Cfg::WM == 1 && (Cfg::WN == 4 || Cfg::WN == 8), "streaming-B layout: four or eight waves along N");

@@ -718,7 +718,33 @@ struct DownProb {
     if ((int)threadIdx.x < t.rows)
       ssq[(size_t)(t.m0 + threadIdx.x) * nt + t.nt] = red[Cfg::WN * Cfg::BM + threadIdx.x];
     // the sums of squares come from the FP32 o; FP16 O rounds o times o_down[e]
-    const float od = out16 ? o_down[t.e] : 1.0f;
+    if (out16) {
+      // Two columns per 4-byte store: lanes 2m and 2m + 1 hold columns c, c + 1
+      // of the same rows; they swap one of each row pair (i, i + 1) (DPP quad
+      // permutation 1,0,3,2), so the even lane stores row i and the odd lane
+      // row i + 1, both at columns c, c + 1. P is even, so a pair's columns are
+      // both inside or both beyond P; every lane takes part in the swap.
+      const float od = o_down[t.e];
+      const bool odd = lane & 1;
+#pragma unroll
+      for (int tn = 0; tn < Cfg::TN; ++tn) {
+        const int col = t.n0 + lm_acc_col<Cfg>(wn, tn, lane);
+        const bool cok = col < P;
+        _Float16* dst = out16 + (size_t)t.m0 * P + (col & ~1);
+#pragma unroll
+        for (int tm = 0; tm < Cfg::TM; ++tm)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            const uint32_t h0 = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[tm][tn][i] * dd[tn] * od));
+            const uint32_t h1 = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[tm][tn][i + 1] * dd[tn] * od));
+            const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? h0 : h1), 0xB1, 0xF, 0xF, true);
+            const int row = lm_acc_row<Cfg>(wm, tm, i, lane) + (odd ? 1 : 0);
+            if (cok && row < t.rows)
+              *(uint32_t*)(dst + (size_t)row * P) = odd ? (other | (h1 << 16)) : (h0 | (other << 16));
+          }
+      }
+      return;
+    }
 #pragma unroll
     for (int tn = 0; tn < Cfg::TN; ++tn) {
       const int col = t.n0 + lm_acc_col<Cfg>(wn, tn, lane);
@@ -729,9 +755,7 @@ struct DownProb {
         for (int i = 0; i < 16; ++i) {
           const int row = lm_acc_row<Cfg>(wm, tm, i, lane);
           if (row >= t.rows) continue;
-          const float o = acc[tm][tn][i] * dd[tn];
-          if (out16) out16[(size_t)(t.m0 + row) * P + col] = lm_f32_to_f16_sat(o * od);
-          else out[(size_t)(t.m0 + row) * P + col] = o;
+          out[(size_t)(t.m0 + row) * P + col] = acc[tm][tn][i] * dd[tn];
         }
     }
   }
@@ -851,6 +875,22 @@ struct DenseSplitProb {
   }
 };
 
+// Sum of p[0], p[stride], ..., p[(splits - 1) stride] in index order, with
+// eight loads in flight at a time.
+LM_DEV float lm_sum_splits(const float* p, size_t stride, int splits) {
+  float v = 0.0f;
+  int sp = 0;
+  for (; sp + 8 <= splits; sp += 8) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = p[(size_t)(sp + i) * stride];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v += x[i];
+  }
+  for (; sp < splits; ++sp) v += p[(size_t)sp * stride];
+  return v;
+}
+
 // Pooler finish, one workgroup per (token, 256 columns): h = sum of the
 // split partials in split order; pooled32 = gamma_p * h (FP32); the chunk's
 // sum of h^2 (fixed tree over the workgroup) goes to ssq[t][chunk], from
@@ -863,7 +903,7 @@ __global__ __launch_bounds__(256) void lm_pool_finish_kernel(const float* part, 
   const int c = chunk * 256 + tid;
   float h = 0.0f;
   if (c < P) {
-    for (int sp = 0; sp < splits; ++sp) h += part[((size_t)sp * T + t) * P + c];
+    h = lm_sum_splits(part + (size_t)t * P + c, (size_t)T * P, splits);
     pooled32[(size_t)t * P + c] = h * gamma[c];
   }
   red[tid] = h * h;
@@ -879,9 +919,7 @@ __global__ __launch_bounds__(256) void lm_pool_finish_kernel(const float* part, 
 __global__ void lm_unpool_finish_kernel(const float* part, int splits, int64_t n, float* out) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
-    float v = 0.0f;
-    for (int sp = 0; sp < splits; ++sp) v += part[(size_t)sp * n + i];
-    out[i] = v;
+    out[i] = lm_sum_splits(part + i, (size_t)n, splits);
   }
 }
 
@@ -970,9 +1008,16 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const double* part, int sp
     if (t >= T) continue;
     const double* src = part + (size_t)t * E + e;
     const size_t stride = (size_t)T * E;
-    // the splits summed in index order; sixteen loads in flight at a time
+    // the splits summed in index order; 32 loads in flight at a time
     double sd = 0.0;
     int sp = 0;
+    for (; sp + 32 <= splits; sp += 32) {
+      double v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = src[(size_t)(sp + i) * stride];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) sd += v[i];
+    }
     for (; sp + 16 <= splits; sp += 16) {
       double v[16];
 #pragma unroll
