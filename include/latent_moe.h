@@ -199,6 +199,25 @@ int latent_moe_workspace_bytes(const latent_moe_config* cfg, size_t* bytes);
 int latent_moe_forward(latent_moe_t* h, const void* x, int64_t T, float* out, int32_t* topk_ids,
                        float* topk_weights, void* stream);
 
+/* For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the FP32 layer's
+ * forward without a handle. It takes the config and the weights as create
+ * does and x, out, topk_ids, topk_weights and stream as forward does, reads
+ * the weights in place (they must stay valid and unchanged until the stream
+ * passes this call), and keeps its whole workspace in a static device array
+ * of LMOE_STATIC_SCRATCH_BYTES (16 MiB) that the library holds on each device
+ * it runs on until the process ends; it calls no allocating routine. Every
+ * call on one device shares that device's array, which keeps the last call's
+ * contents: calls that overlap on one device (different streams or threads)
+ * race. cfg->max_tokens is ignored; T is limited by the array (the tiny
+ * layer, H 256, P 128, I 128, E 8, k 2, fits about 4900 tokens).
+ * Errors: INVALID_ARG and UNSUPPORTED as for create's validation (BF16
+ * layers are UNSUPPORTED: they run on weight copies made by create);
+ * TOO_MANY_TOKENS when the workspace for T tokens exceeds the array; HIP. */
+#define LMOE_STATIC_SCRATCH_BYTES (16u << 20)
+int latent_moe_forward_static(const latent_moe_config* cfg, const latent_moe_weights* w, const void* x,
+                              int64_t T, float* out, int32_t* topk_ids, float* topk_weights, void* stream);
+
 /* Views of the last forward's intermediates, for inspection and per-stage
  * tests. Pointers are into the handle's workspace (device memory), valid
  * until the next forward or destroy; rows beyond the last forward's T (or

@@ -87,6 +87,10 @@ def lib():
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p]
         L.latent_moe_forward.restype = ctypes.c_int
+        L.latent_moe_forward_static.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), ctypes.c_void_p,
+                                                ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        L.latent_moe_forward_static.restype = ctypes.c_int
         L.latent_moe_debug_views.argtypes = [ctypes.c_void_p, ctypes.POINTER(Views)]
         L.latent_moe_debug_views.restype = ctypes.c_int
         L.latent_moe_set_profiling.argtypes = [ctypes.c_void_p, ctypes.c_int]
@@ -138,6 +142,12 @@ def latent_moe_create(cfg: Config, w: Weights, stream: int | None = None) -> int
 def latent_moe_forward(h: int, x: int, T: int, out: int, topk_ids: int | None,
                        topk_weights: int | None, stream: int | None) -> None:
     _check(lib().latent_moe_forward(h, x, T, out, topk_ids, topk_weights, stream))
+
+
+def latent_moe_forward_static(cfg: Config, w: Weights, x: int, T: int, out: int, topk_ids: int | None,
+                              topk_weights: int | None, stream: int | None) -> None:
+    _check(lib().latent_moe_forward_static(ctypes.byref(cfg), ctypes.byref(w), x, T, out, topk_ids, topk_weights,
+                                           stream))
 
 
 def latent_moe_debug_views(h: int) -> Views:

@@ -16,6 +16,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <type_traits>
@@ -1049,6 +1050,88 @@ int latent_moe_forward(latent_moe_t* h, const void* x, int64_t T, float* out, in
                ? LMOE_OK : fail(LMOE_ERR_HIP, "copy of topk_weights failed");
   }
   if (cur != h->device) (void)hipSetDevice(cur);
+  return rc;
+}
+
+// ------------------------------------------------------------ no allocation
+// latent_moe_forward_static: the FP32 layer's forward with its workspace in a
+// file-scope device array instead of a handle's allocation. In host code
+// `scratch` names a host-side stand-in, not device memory: its device address
+// comes from hipGetSymbolAddress, once per device (each device holds its own
+// copy), and only that address is handed to kernels.
+}  // extern "C"
+
+static __device__ __align__(256) char scratch[LMOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of this device's scratch array (the current device).
+int scratch_address(int dev, char** p) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(LMOE_ERR_HIP, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* q = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !q)
+      return fail(LMOE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_dev[dev] = q;
+  }
+  *p = (char*)g_scratch_dev[dev];
+  return LMOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int latent_moe_forward_static(const latent_moe_config* cfg, const latent_moe_weights* w, const void* x,
+                              int64_t T, float* out, int32_t* topk_ids, float* topk_weights, void* stream) {
+  g_err.clear();
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (cfg->act_dtype != LMOE_F32)
+    return fail(LMOE_ERR_UNSUPPORTED, "the static-workspace forward runs FP32 layers only (BF16 layers use "
+                                      "weight copies made by latent_moe_create)");
+  if (!w) return fail(LMOE_ERR_INVALID_ARG, "weights is NULL");
+  const void* req[] = {w->router, w->pooler, w->pool_gamma, w->w_gate, w->w_up,
+                       w->w_down, w->expert_gamma, w->unpooler};
+  for (int i = 0; i < 8; ++i)
+    if (!req[i] || !aligned16(req[i])) return fail(LMOE_ERR_INVALID_ARG, "a weight is NULL or misaligned");
+  if ((w->router_bias && !aligned16(w->router_bias)) ||
+      (cfg->input_norm && (!w->input_gamma || !aligned16(w->input_gamma))))
+    return fail(LMOE_ERR_INVALID_ARG, "router_bias or input_gamma misaligned or missing");
+  if (T < 0) return fail(LMOE_ERR_INVALID_ARG, "T must be >= 0");
+  if (T == 0) return LMOE_OK;
+  if (!x || !out) return fail(LMOE_ERR_INVALID_ARG, "x and out must be non-NULL");
+  if (!aligned16(x) || !aligned16(out) || (topk_ids && !aligned16(topk_ids)) ||
+      (topk_weights && !aligned16(topk_weights)))
+    return fail(LMOE_ERR_INVALID_ARG, "x, out, topk_ids and topk_weights must be 16-byte aligned");
+  latent_moe hs{};
+  hs.cfg = *cfg;
+  hs.cfg.max_tokens = T;
+  if (T * cfg->top_k > (1 << 28)) return fail(LMOE_ERR_TOO_MANY_TOKENS, "T too large");
+  hs.lay = make_layout(hs.cfg, &hs.part_floats);
+  if (hs.lay.total > (size_t)LMOE_STATIC_SCRATCH_BYTES)
+    return fail(LMOE_ERR_TOO_MANY_TOKENS, "T=%lld needs %zu workspace bytes, above the static scratch of %zu",
+                (long long)T, hs.lay.total, (size_t)LMOE_STATIC_SCRATCH_BYTES);
+  int dev = 0;
+  LM_HIP(hipGetDevice(&dev));
+  rc = scratch_address(dev, &hs.ws);
+  if (rc) return rc;
+  hs.w = *w;  // read in place for the duration of the call
+  hs.device = dev;
+  const hipStream_t s = (hipStream_t)stream;
+  rc = narrow_for(hs.cfg, T) ? forward_impl<float, CfgNarrow, CfgRouterNarrow>(&hs, x, T, out, s)
+                             : forward_impl<float, CfgWide, CfgRouterWide>(&hs, x, T, out, s);
+  if (rc == LMOE_OK) {
+    const size_t nk = (size_t)T * cfg->top_k;
+    if (topk_ids && hipMemcpyAsync(topk_ids, hs.ws + hs.lay.ids, nk * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return fail(LMOE_ERR_HIP, "copy of topk_ids failed");
+    if (topk_weights && hipMemcpyAsync(topk_weights, hs.ws + hs.lay.wts, nk * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return fail(LMOE_ERR_HIP, "copy of topk_weights failed");
+  }
   return rc;
 }
 
