@@ -707,6 +707,47 @@ struct DownProb {
     return dsd + (int64_t)t.e * P + min(t.n0 + (wv * Cfg::TN + j) * 32, P - 32);
   }
   LM_DEV int a_ktile(int kt) const { return kt; }
+  // Prefill-sized tiles (one row band, 128 rows): the FP16 outputs go out in
+  // whole 128-byte lines. Each wave stages 16 rows x its 64 columns (2 KB of
+  // its own LDS region; the caller's LDS holds at least WN x 2 KB) as 4-byte
+  // column pairs (lanes 2m, 2m + 1 swap one value of each row pair with a DPP
+  // quad permutation, so each writes two columns of one row), then reads it
+  // back as 16-byte row segments and writes 8 rows of 128 bytes per store.
+  // A wave reads only what it wrote, and a wave's LDS operations complete in
+  // order, so no barrier is needed between the two phases.
+  LM_DEV void store16_staged(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wn, int lane,
+                             const float (&dd)[Cfg::TN], void* smem) const {
+    static_assert(Cfg::TN == 2, "64 columns per wave");
+    __syncthreads();  // every thread has read the row sums of squares out of the LDS
+    const float od = o_down[t.e];
+    const bool odd = lane & 1;
+    uint32_t* st = (uint32_t*)smem + wn * 512;  // 16 rows x 32 column pairs
+    const lm_u32x4* ld = (const lm_u32x4*)st;
+    const int col = t.n0 + wn * 64 + (lane & 7) * 8;  // the lane's 8 columns when reading back
+#pragma unroll
+    for (int tm = 0; tm < Cfg::TM; ++tm)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int tn = 0; tn < Cfg::TN; ++tn)
+#pragma unroll
+          for (int i = 8 * h; i < 8 * h + 8; i += 2) {
+            const uint32_t h0 = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[tm][tn][i] * dd[tn] * od));
+            const uint32_t h1 = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[tm][tn][i + 1] * dd[tn] * od));
+            const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? h0 : h1), 0xB1, 0xF, 0xF, true);
+            const int lr = 8 * ((i >> 2) & 1) + 4 * (lane >> 5) + (i & 3) + (odd ? 1 : 0);  // row in the 16
+            st[lr * 32 + tn * 16 + ((lane & 31) >> 1)] = odd ? (other | (h1 << 16)) : (h0 | (other << 16));
+          }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const lm_u32x4 v = ld[j * 64 + lane];
+          const int row = tm * 32 + h * 16 + j * 8 + (lane >> 3);
+          if (row < t.rows && col < P) *(lm_u32x4*)(out16 + (size_t)(t.m0 + row) * P + col) = v;
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+  }
   LM_DEV void epilogue(const LmTile& t, const lm_f32x16 (&acc)[Cfg::TM][Cfg::TN], int wm, int wn,
                        int lane, void* smem) const {
     float* red = (float*)smem;
@@ -718,6 +759,12 @@ struct DownProb {
     if ((int)threadIdx.x < t.rows)
       ssq[(size_t)(t.m0 + threadIdx.x) * nt + t.nt] = red[Cfg::WN * Cfg::BM + threadIdx.x];
     // the sums of squares come from the FP32 o; FP16 O rounds o times o_down[e]
+    if constexpr (Cfg::WM == 1 && Cfg::TM == 4) {
+      if (out16) {
+        store16_staged(t, acc, wn, lane, dd, smem);
+        return;
+      }
+    }
     if (out16) {
       // Two columns per 4-byte store: lanes 2m and 2m + 1 hold columns c, c + 1
       // of the same rows; they swap one of each row pair (i, i + 1) (DPP quad
