@@ -234,8 +234,10 @@ int latent_moe_forward_static(const latent_moe_config* cfg, const latent_moe_wei
  *   row_scale [T] F32: 1/sqrt(mean((Wp x_t)^2) + eps)
  *   act      [T*k, I] (F32 if expert_dtype is F32, else FP16): SwiGLU
  *            output, grouped order
- *   expert_out [T*k, P]: o (before the per-expert norm), grouped order; F32
- *            in FP32 layers, FP16 times expert_out_down[e] in BF16 layers
+ *   expert_out [T*k, P]: grouped order; FP32 layers: o (before the
+ *            per-expert norm) in F32; BF16 layers: gamma_e * o (the expert's
+ *            norm gamma applied, the norm's 1/rms not) in FP16 times
+ *            expert_out_down[e]
  *   combined y [T, P]: F32 in FP32 layers, FP16 in BF16 layers          */
 typedef struct {
   const float* logits;
@@ -273,11 +275,11 @@ typedef struct {
                             act_down[e][i/32], a power of two (1 unless the
                             Cauchy-Schwarz bound |a_i| <= ||Wg_i|| ||Wu_i|| P
                             max|gamma_p|^2 exceeds 2^15); else NULL */
-  const float* expert_out_down; /* BF16 layers: [E] F32, expert_out holds FP16 o times
-                            expert_out_down[e] for a pair routed to expert e, a power
-                            of two keeping ||Wd_p|| ||u||^2 sqrt(sum_i (||Wg_i||
-                            ||Wu_i||)^2) within 2^15; FP32 layers: NULL (expert_out
-                            is F32) */
+  const float* expert_out_down; /* BF16 layers: [E] F32, expert_out holds FP16 gamma_e * o
+                            times expert_out_down[e] for a pair routed to expert e, a
+                            power of two keeping ||Wd_p|| ||u||^2 sqrt(sum_i (||Wg_i||
+                            ||Wu_i||)^2) max|gamma_e| within 2^15; FP32 layers: NULL
+                            (expert_out is F32 o) */
 } latent_moe_views;
 
 int latent_moe_debug_views(const latent_moe_t* h, latent_moe_views* v);

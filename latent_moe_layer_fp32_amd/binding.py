@@ -363,7 +363,7 @@ class LatentMoE:
                 ad = np.empty((E, I // 32), np.float32)
                 _memcpy_d2h(ad.ctypes.data, v.act_down, ad.nbytes)
                 res["act"] = res["act"].astype(np.float32) / np.repeat(ad[expert_of_row], 32, axis=1)
-            if "expert_out" in res:  # FP16 o times expert_out_down[e]
+            if "expert_out" in res:  # FP16 gamma_e * o times expert_out_down[e]
                 od = np.empty((E,), np.float32)
                 _memcpy_d2h(od.ctypes.data, v.expert_out_down, od.nbytes)
                 res["expert_out"] = res["expert_out"].astype(np.float32) / od[expert_of_row][:, None]

@@ -272,38 +272,45 @@ __global__ void lm_a_shift_kernel(const float* ng, const float* nu, int64_t nblk
   }
 }
 
-// Powers of two of the FP16 expert outputs, one per expert: |o_p| = |Wd_p . a|
-// <= ||Wd_p|| ||a|| and ||a|| <= ||u||^2 sqrt(sum_i (||Wg_i|| ||Wu_i||)^2)
-// (each |a_i| <= ||Wg_i|| ||Wu_i|| ||u||^2, as for lm_a_shift_kernel), with
-// ||u||^2 <= u2; amp (1, or 2 where a is MX-quantised: a code can exceed its
-// value by at most a factor 1.5) scales the bound. o_down = the largest 2^-c,
-// 0 <= c <= 100, keeping the bound within 2^15; o_up = 2^c. One workgroup per
-// expert: ng, nu [E, I] (gate / up row norms), nd [E, P] (down row norms).
+// Powers of two of the FP16 expert outputs, which hold o times the expert's
+// gamma, one per expert: |o_p| = |Wd_p . a| <= ||Wd_p|| ||a|| and ||a|| <=
+// ||u||^2 sqrt(sum_i (||Wg_i|| ||Wu_i||)^2) (each |a_i| <= ||Wg_i|| ||Wu_i||
+// ||u||^2, as for lm_a_shift_kernel), with ||u||^2 <= u2; the bound on
+// |o_p gamma_p| takes max_p |gamma_p| as well; amp (1, or 2 where a is
+// MX-quantised: a code can exceed its value by at most a factor 1.5) scales
+// it. o_down = the largest 2^-c, 0 <= c <= 100, keeping the bound within
+// 2^15; o_up = 2^c. One workgroup per expert: ng, nu [E, I] (gate / up row
+// norms), nd [E, P] (down row norms), gamma [E, P].
 __global__ __launch_bounds__(256) void lm_o_shift_kernel(const float* ng, const float* nu, const float* nd,
-                                                         int I, int P, float u2, float amp, float* o_down,
-                                                         float* o_up) {
+                                                         const float* gamma, int I, int P, float u2, float amp,
+                                                         float* o_down, float* o_up) {
   __shared__ double red[256];
-  __shared__ float redm[256];
+  __shared__ float redm[256], redg[256];
   const int e = blockIdx.x, tid = threadIdx.x;
   double s = 0.0;
   for (int i = tid; i < I; i += 256) {
     const double q = (double)ng[(size_t)e * I + i] * (double)nu[(size_t)e * I + i];
     s += q * q;
   }
-  float m = 0.0f;
-  for (int p = tid; p < P; p += 256) m = fmaxf(m, nd[(size_t)e * P + p]);
+  float m = 0.0f, gm = 0.0f;
+  for (int p = tid; p < P; p += 256) {
+    m = fmaxf(m, nd[(size_t)e * P + p]);
+    gm = fmaxf(gm, fabsf(gamma[(size_t)e * P + p]));
+  }
   red[tid] = s;
   redm[tid] = m;
+  redg[tid] = gm;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
     if (tid < o) {
       red[tid] += red[tid + o];
       redm[tid] = fmaxf(redm[tid], redm[tid + o]);
+      redg[tid] = fmaxf(redg[tid], redg[tid + o]);
     }
     __syncthreads();
   }
   if (tid == 0) {
-    const double bound = (double)redm[0] * (double)u2 * sqrt(red[0]) * (double)amp;
+    const double bound = (double)redm[0] * (double)u2 * sqrt(red[0]) * (double)amp * (double)redg[0];
     int c = 0;
     if (!(bound <= 32768.0)) {  // above 2^15, infinite or NaN
       if (bound <= 1e300) {
@@ -678,8 +685,9 @@ struct DownProb {
   const int* offsets;
   const int* tile_off;
   float* out;  // [pairs, P] FP32, or
-  _Float16* out16 = nullptr;      // [pairs, P] FP16: o times o_down[e] (a power of two)
+  _Float16* out16 = nullptr;      // [pairs, P] FP16: o times gamma_e times o_down[e] (a power of two)
   const float* o_down = nullptr;  // [E], with out16
+  const float* gamma = nullptr;   // [E, P] per-expert norm gamma, with out16
   float* ssq;  // [pairs, nt]
   int P, I, Ex, nt;
 
@@ -720,6 +728,12 @@ struct DownProb {
     static_assert(Cfg::TN == 2, "64 columns per wave");
     __syncthreads();  // every thread has read the row sums of squares out of the LDS
     const float od = o_down[t.e];
+    float gg[Cfg::TN];  // the lane's column of the expert's gamma
+#pragma unroll
+    for (int tn = 0; tn < Cfg::TN; ++tn) {
+      const int c = t.n0 + lm_acc_col<Cfg>(wn, tn, lane);
+      gg[tn] = c < P ? gamma[(size_t)t.e * P + c] : 0.0f;
+    }
     const bool odd = lane & 1;
     uint32_t* st = (uint32_t*)smem + wn * 512;  // 16 rows x 32 column pairs
     const lm_u32x4* ld = (const lm_u32x4*)st;
@@ -732,8 +746,10 @@ struct DownProb {
         for (int tn = 0; tn < Cfg::TN; ++tn)
 #pragma unroll
           for (int i = 8 * h; i < 8 * h + 8; i += 2) {
-            const uint32_t h0 = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[tm][tn][i] * dd[tn] * od));
-            const uint32_t h1 = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[tm][tn][i + 1] * dd[tn] * od));
+            const uint32_t h0 =
+                __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[tm][tn][i] * dd[tn] * gg[tn] * od));
+            const uint32_t h1 =
+                __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[tm][tn][i + 1] * dd[tn] * gg[tn] * od));
             const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? h0 : h1), 0xB1, 0xF, 0xF, true);
             const int lr = 8 * ((i >> 2) & 1) + 4 * (lane >> 5) + (i & 3) + (odd ? 1 : 0);  // row in the 16
             st[lr * 32 + tn * 16 + ((lane & 31) >> 1)] = odd ? (other | (h1 << 16)) : (h0 | (other << 16));
@@ -758,7 +774,8 @@ struct DownProb {
     lm_tile_row_ssq<Cfg>(acc, wm, wn, lane, P - t.n0, red, [&](float v, int tn, int) { return v * dd[tn]; });
     if ((int)threadIdx.x < t.rows)
       ssq[(size_t)(t.m0 + threadIdx.x) * nt + t.nt] = red[Cfg::WN * Cfg::BM + threadIdx.x];
-    // the sums of squares come from the FP32 o; FP16 O rounds o times o_down[e]
+    // the sums of squares come from the FP32 o; FP16 O rounds o times gamma_e
+    // times o_down[e]
     if constexpr (Cfg::WM == 1 && Cfg::TM == 4) {
       if (out16) {
         store16_staged(t, acc, wn, lane, dd, smem);
@@ -777,13 +794,14 @@ struct DownProb {
       for (int tn = 0; tn < Cfg::TN; ++tn) {
         const int col = t.n0 + lm_acc_col<Cfg>(wn, tn, lane);
         const bool cok = col < P;
+        const float g = cok ? gamma[(size_t)t.e * P + col] : 0.0f;
         _Float16* dst = out16 + (size_t)t.m0 * P + (col & ~1);
 #pragma unroll
         for (int tm = 0; tm < Cfg::TM; ++tm)
 #pragma unroll
           for (int i = 0; i < 16; i += 2) {
-            const uint32_t h0 = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[tm][tn][i] * dd[tn] * od));
-            const uint32_t h1 = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[tm][tn][i + 1] * dd[tn] * od));
+            const uint32_t h0 = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[tm][tn][i] * dd[tn] * g * od));
+            const uint32_t h1 = __builtin_bit_cast(uint16_t, lm_f32_to_f16_sat(acc[tm][tn][i + 1] * dd[tn] * g * od));
             const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? h0 : h1), 0xB1, 0xF, 0xF, true);
             const int row = lm_acc_row<Cfg>(wm, tm, i, lane) + (odd ? 1 : 0);
             if (cok && row < t.rows)
@@ -1282,9 +1300,10 @@ __global__ __launch_bounds__(256) void lm_norm_u_kernel(const float* pooled32, c
 
 // One workgroup per token: y = sum over slots j (in order) of
 // w_j / sqrt(mean(o_j^2) + eps) * gamma_{e_j} * o_j, in FP32. O is FP32
-// (FP32 layers) or FP16 holding o times o_down[e] (BF16 layers; o_up[e] =
-// 1 / o_down[e] is folded into the slot's coefficient, exactly: a power of
-// two); the sums of squares are those of the FP32 o. FP32 layers store y
+// (FP32 layers; gamma read here) or FP16 holding gamma_e * o times
+// o_down[e] (BF16 layers: the down GEMM applied gamma; o_up[e] = 1 /
+// o_down[e] is folded into the slot's coefficient, exactly: a power of two);
+// the sums of squares are those of the FP32 o. FP32 layers store y
 // [T, P] in FP32, BF16 layers the nearest-even FP16 rounding of y * down, the
 // unpooler's operand: |y| <= sqrt(P) max|gamma_e|, and down (a power of two
 // chosen at create) keeps that bound within 2^15.
@@ -1334,15 +1353,22 @@ __global__ __launch_bounds__(256) void lm_combine_kernel(const OT* O, const floa
               o[q][i >> 1][2 * (i & 1) + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hv[i] >> 16));
             }
           }
-          g[q][0] = *(const lm_f32x4*)(grow + c);
-          g[q][1] = *(const lm_f32x4*)(grow + c + 4);
+          if constexpr (sizeof(OT) == 4) {
+            g[q][0] = *(const lm_f32x4*)(grow + c);
+            g[q][1] = *(const lm_f32x4*)(grow + c + 4);
+          }
         }
       }
 #pragma unroll
       for (int q = 0; q < kC; ++q)
         if (c0 + q * 2048 < P) {
-          acc[q][0] += s_coef[j] * (g[q][0] * o[q][0]);
-          acc[q][1] += s_coef[j] * (g[q][1] * o[q][1]);
+          if constexpr (sizeof(OT) == 4) {
+            acc[q][0] += s_coef[j] * (g[q][0] * o[q][0]);
+            acc[q][1] += s_coef[j] * (g[q][1] * o[q][1]);
+          } else {  // gamma is in O
+            acc[q][0] += s_coef[j] * o[q][0];
+            acc[q][1] += s_coef[j] * o[q][1];
+          }
         }
     }
 #pragma unroll

@@ -634,6 +634,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     if (LM_O_F16) {
       p.out16 = (_Float16*)O;
       p.o_down = h->o_down;
+      p.gamma = w.expert_gamma;
     }
     p.ssq = ossq;
     p.P = P;
@@ -656,6 +657,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     if constexpr (F16 && LM_O_F16) {
       p.out16 = (_Float16*)O;
       p.o_down = h->o_down;
+      p.gamma = w.expert_gamma;
     }
     p.ssq = ossq;
     p.P = P;
@@ -925,7 +927,8 @@ int latent_moe_create(latent_moe_t** out, const latent_moe_config* cfg, const la
       // an MX-quantised a may exceed silu(g) v by up to a factor 1.5
       float* od = (float*)(ob + o_od);
       hipLaunchKernelGGL(lm_o_shift_kernel, dim3((unsigned)E), dim3(256), 0, s, norms, norms + E * I,
-                         norms + 2 * E * I, (int)I, (int)P, u2, cfg->expert_act ? 2.0f : 1.0f, od, od + E);
+                         norms + 2 * E * I, hw.expert_gamma, (int)I, (int)P, u2, cfg->expert_act ? 2.0f : 1.0f,
+                         od, od + E);
       h->o_down = od;
       h->o_up = od + E;
       // FP16 a (expert inputs in FP16 only; MX inputs quantise a per block): per

@@ -126,13 +126,13 @@ def forward(x, router, bias, pooler, pool_gamma, w_gate, w_up, w_down, expert_ga
     (times input_gamma) rounded to FP32, the pooler the same value rounded
     on to BF16 when bf16_acts, else the FP32 value. mxfp8_acts / mxfp4_acts:
     the expert GEMMs read u and a MX-quantised to FP8 E4M3 / FP4 E2M1.
-    f16_points: u, a (unless MX-quantised), the expert output o and y are
-    stored in FP16 times a power of two each, as the layer with BF16
-    activations stores them: the largest 2^-c keeping a bound within 2^15 --
-    u: sqrt(P) max|gamma_p|, y: sqrt(P) max|gamma_e|, a (per expert, 32
-    outputs at a time): the largest ||Wg row|| ||Wu row|| of the block times
-    P max(gamma_p)^2, o (per expert): see o_scale; the per-expert norm takes
-    the RMS of the unrounded o."""
+    f16_points: u, a (unless MX-quantised), the expert output times its
+    expert's gamma (gamma_e o) and y are stored in FP16 times a power of two
+    each, as the layer with BF16 activations stores them: the largest 2^-c
+    keeping a bound within 2^15 -- u: sqrt(P) max|gamma_p|, y: sqrt(P)
+    max|gamma_e|, a (per expert, 32 outputs at a time): the largest ||Wg row||
+    ||Wu row|| of the block times P max(gamma_p)^2, gamma_e o (per expert):
+    see o_scale; the per-expert norm takes the RMS of the unrounded o."""
     T, E = len(x), len(router)
     if f16_points:
         P0 = len(pooler)
@@ -143,13 +143,14 @@ def forward(x, router, bias, pooler, pool_gamma, w_gate, w_up, w_down, expert_ga
 
         def o_scale(e):
             """2^-c keeping max_p ||Wd row p|| P max(gamma_p)^2 sqrt(sum_i (||Wg row i||
-            ||Wu row i||)^2) (twice that with MX activations) within 2^15."""
+            ||Wu row i||)^2) max|gamma_e| (twice that with MX activations) within 2^15."""
             nd = max(math.sqrt(math.fsum(float(z) * float(z) for z in row)) for row in w_down[e])
             s2 = math.fsum((math.sqrt(math.fsum(float(z) * float(z) for z in w_gate[e][i]))
                             * math.sqrt(math.fsum(float(z) * float(z) for z in w_up[e][i]))) ** 2
                            for i in range(len(w_gate[e])))
             amp = 2.0 if (mxfp8_acts or mxfp4_acts) else 1.0
-            return _down(nd * P0 * gpm * gpm * math.sqrt(s2) * amp, 100)
+            gmx = max(abs(float(g)) for g in expert_gamma[e])
+            return _down(nd * P0 * gpm * gpm * math.sqrt(s2) * amp * gmx, 100)
 
         def a_scale(e, i):
             b0 = i - i % 32
@@ -205,11 +206,11 @@ def forward(x, router, bias, pooler, pool_gamma, w_gate, w_up, w_down, expert_ga
                 a = _mxfp4(a)
             o = _matvec(w_down[e], a)
             oh = _rmsnorm(o, expert_gamma[e], eps)
-            if f16_points:  # o stored in FP16 times its expert's power of two; the norm of o itself
+            if f16_points:  # gamma_e o stored in FP16 times its expert's power of two; the norm of o itself
                 so = o_scale(e)
                 ms = math.fsum(z * z for z in o) / len(o)
                 d = math.sqrt(ms + eps)
-                oh = [_f16(o[i], so) / d * float(expert_gamma[e][i]) for i in range(len(o))]
+                oh = [_f16(o[i] * float(expert_gamma[e][i]), so) / d for i in range(len(o))]
             y = [y[p] + wt[j] * oh[p] for p in range(P)]
         if f16_points:
             y = [_f16(z, sy) for z in y]

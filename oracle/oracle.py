@@ -52,12 +52,13 @@ max|gamma_e| (no element of an RMS-normed row exceeds sqrt(P) times its
 gamma; routing weights sum to one), and per expert and block of 32 SwiGLU
 outputs |a_i| <= ||Wg_i|| ||Wu_i|| P max(gamma_p)^2 (Cauchy-Schwarz, |silu(g)|
 <= |g|); each value is stored times the largest power of two that keeps its
-bound within 2^15 (1 when the bound already is). The expert output o (step
-5) is stored in FP16 too, one power of two per expert from |o_p| <=
-||Wd_p|| ||a|| <= max_p ||Wd_p|| P max(gamma_p)^2 sqrt(sum_i (||Wg_i||
-||Wu_i||)^2) (twice that with MX activations: a code may exceed its value by
-up to a factor 1.5); its per-expert RMS (step 6) is that of the unrounded o.
-With MX activations (act_quant) u and a are the MX codes instead and only o
+bound within 2^15 (1 when the bound already is). The expert output, times
+its expert's gamma (step 6's gamma_e * o), is stored in FP16 too, one power of
+two per expert from |o_p gamma_p| <= ||Wd_p|| ||a|| max|gamma_e| <= max_p
+||Wd_p|| P max(gamma_p)^2 sqrt(sum_i (||Wg_i|| ||Wu_i||)^2) max|gamma_e|
+(twice that with MX activations: a code may exceed its value by up to a
+factor 1.5); the per-expert RMS (step 6) is that of the unrounded o. With MX
+activations (act_quant) u and a are the MX codes instead and only gamma_e * o
 and y are FP16.
 
 Readings where the pages are silent (each listed in the design notes): without
@@ -89,7 +90,7 @@ class OracleResult:
     h: np.ndarray  # [T, P] pooled, before the norm
     u: np.ndarray  # [T, P] pooled and normed expert input
     a: np.ndarray | None  # [T, k, I] SwiGLU output per slot
-    o: np.ndarray | None  # [T, k, P] expert output per slot (before its norm)
+    o: np.ndarray | None  # [T, k, P] expert output per slot before its norm (emulation: gamma_e * o as stored)
     ohat: np.ndarray | None  # [T, k, P] normed expert output per slot
     # a, o and ohat hold the rows of all tokens, or (keep_pairs given as token
     # indices) of those tokens only, in the order given
@@ -253,7 +254,7 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
         Wg, Wu, Wd = experts(int(e))
         asc = osc = None
         if "f16" in modes:
-            asc, osc = expert_scales(Wg, Wu, Wd, P, gp, 2.0 if act_quant else 1.0)
+            asc, osc = expert_scales(Wg, Wu, Wd, P, gp, 2.0 if act_quant else 1.0, float(np.max(np.abs(ge[e]))))
             asc = None if act_quant else np.repeat(asc, 32)
         kr = slot_row[tt]
         ks = kr >= 0
@@ -267,9 +268,11 @@ def forward(x, router, router_bias, pooler, pool_gamma, experts: ExpertFn, exper
             if act_quant:
                 a = quantize_mx(a, act_quant)[0]
             o = a @ Wd.T
-            o_st = f16_round(o, osc) if m == "f16" else o  # o as stored; its norm uses o
+            # emulation: gamma_e * o as stored; its norm uses o
+            o_st = f16_round(o * ge[e], osc) if m == "f16" else o
             if order == "norm_then_sum":
-                S["ohat"][tt, jj] = o_st / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps) * ge[e]
+                inv = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+                S["ohat"][tt, jj] = o_st * inv if m == "f16" else o_st * inv * ge[e]
             else:
                 S["ohat"][tt, jj] = o_st
             if keep:
@@ -334,24 +337,24 @@ def row_norms(W: np.ndarray) -> np.ndarray:
     return np.sqrt(np.einsum("ij,ij->i", W, W))
 
 
-def scales_from_norms(ng, nu, nd, P: int, pool_gamma, amp: float = 1.0):
+def scales_from_norms(ng, nu, nd, P: int, pool_gamma, amp: float = 1.0, ge_max: float = 1.0):
     """The FP16 range scalings of one expert from the row norms of its gate,
     up and down weights (ng, nu [I], nd [P]): the SwiGLU outputs' powers of
     two per block of 32 outputs [I/32], from max over the block of
     ||Wg_i|| ||Wu_i|| times P max(gamma_p)^2, and the outputs' power of two,
     from max_p ||Wd_p|| P max(gamma_p)^2 sqrt(sum_i (||Wg_i|| ||Wu_i||)^2)
-    times amp (module docstring)."""
+    times amp and the largest |gamma_e| of the expert (module docstring)."""
     gp = float(np.max(np.abs(pool_gamma)))
     gu = ng * nu
     m = gu.reshape(-1, 32).max(axis=1)
     asc = np.array([pow2_down(b * P * gp * gp, 60) for b in m])
-    osc = pow2_down(float(nd.max()) * P * gp * gp * float(np.sqrt(np.sum(gu * gu))) * amp, 100)
+    osc = pow2_down(float(nd.max()) * P * gp * gp * float(np.sqrt(np.sum(gu * gu))) * amp * ge_max, 100)
     return asc, osc
 
 
-def expert_scales(Wg, Wu, Wd, P: int, pool_gamma, amp: float = 1.0):
+def expert_scales(Wg, Wu, Wd, P: int, pool_gamma, amp: float = 1.0, ge_max: float = 1.0):
     """scales_from_norms of one expert's weights."""
-    return scales_from_norms(row_norms(Wg), row_norms(Wu), row_norms(Wd), P, pool_gamma, amp)
+    return scales_from_norms(row_norms(Wg), row_norms(Wu), row_norms(Wd), P, pool_gamma, amp, ge_max)
 
 
 def a_scales(Wg, Wu, P: int, pool_gamma) -> np.ndarray:
@@ -360,9 +363,9 @@ def a_scales(Wg, Wu, P: int, pool_gamma) -> np.ndarray:
     return scales_from_norms(row_norms(Wg), row_norms(Wu), np.zeros(1), P, pool_gamma)[0]
 
 
-def o_scale(Wg, Wu, Wd, P: int, pool_gamma, amp: float = 1.0) -> float:
+def o_scale(Wg, Wu, Wd, P: int, pool_gamma, amp: float = 1.0, ge_max: float = 1.0) -> float:
     """Power of two one expert's outputs are stored with in FP16 (scales_from_norms)."""
-    return expert_scales(Wg, Wu, Wd, P, pool_gamma, amp)[1]
+    return expert_scales(Wg, Wu, Wd, P, pool_gamma, amp, ge_max)[1]
 
 
 def _bf16_round(v: np.ndarray) -> np.ndarray:

@@ -45,10 +45,16 @@ class HostLayer:
         return self._norms[e]
 
     def scales(self, e: int, amp: float = 1.0):
-        """Expert e's FP16 range scalings (a per block of 32, o), as the
-        oracle derives them."""
+        """Expert e's FP16 range scalings (a per block of 32, gamma_e o), as
+        the oracle derives them."""
         ng, nu, nd = self.norms(e)
-        return orc.scales_from_norms(ng, nu, nd, self.spec.P, self.w["pool_gamma"].astype(np.float64), amp)
+        ge = float(np.max(np.abs(self.w["expert_gamma"][e].astype(np.float64))))
+        return orc.scales_from_norms(ng, nu, nd, self.spec.P, self.w["pool_gamma"].astype(np.float64), amp, ge)
+
+    def gamma_o(self, ids) -> np.ndarray:
+        """The expert gammas of the selected experts [..., P] (the BF16-activation
+        layer stores gamma_e * o as its expert outputs)."""
+        return to_f64(self.w["expert_gamma"])[np.asarray(ids)]
 
     def x(self, chunk: int = 0):
         return synth.host(self.spec, "x", chunk=chunk)
@@ -215,9 +221,9 @@ def mx_u_ties(v: dict, rows, uq_gpu: np.ndarray, r, fmt: str):
 #   u  = FP16(r * (gamma_p * h)) from the GPU's FP32 gamma_p * h and row
 #        scale: bit for bit (the same FP32 product rounded to FP16)
 #   a  = FP16(silu(Wg u16) * (Wu u16))            from the GPU's FP16 u
-#   o  = FP16(Wd a16) (FP32 accumulation)          from the GPU's FP16 a
-#   y  = FP16(sum_j w_j o16_j / rms(o_j) gamma_e)  from the GPU's FP16 o, the
-#        RMS of the unrounded o (the GPU's FP32 sums of squares)
+#   o  = FP16(gamma_e (Wd a16)) (FP32 accumulation) from the GPU's FP16 a
+#   y  = FP16(sum_j w_j o16_j / rms(o_j))          from the GPU's FP16 gamma_e o,
+#        the RMS of the unrounded o (the GPU's FP32 sums of squares)
 #   out = Wun y16 (FP32 accumulation)             from the GPU's FP16 y
 # FP16 stages a, o and y: within one FP16 unit in the last place of the
 # reference plus the FP32 error of the value the GPU rounds (the GPU rounds
@@ -306,11 +312,13 @@ def check_stage_chain(g: dict, ids_rows, w_rows, host: HostLayer, u_exact: np.nd
         slack = 1.1 * (dg * np.abs(vv) + np.abs(g_) * dv) + 2.0 ** -20 * np.abs(a_ref)
         a16 = g["act"][tt, jj]
         fa.append(_check_f16(a16, orc.f16_round(a_ref, asc), asc, slack, f"act, expert {e}"))
-        o16 = g["expert_out"][tt, jj]
+        o16 = g["expert_out"][tt, jj]  # gamma_e o as stored
         o_ref = a16 @ Wd.T
-        eo.append(_check_f16(o16, orc.f16_round(o_ref, osc), osc, ACC_REL * orc.row_norms(a16)[:, None] * nd[None, :],
-                             f"expert out, expert {e}"))
-        ohat[tt, jj] = o16 / np.sqrt(np.mean(o_ref * o_ref, axis=-1, keepdims=True) + spec.eps) * ge[e]
+        go = o_ref * ge[e]
+        # FP32 accumulation of o, times |gamma|, plus the FP32 rounding of the product
+        slack_o = ACC_REL * orc.row_norms(a16)[:, None] * (nd * np.abs(ge[e]))[None, :] + 2.0 ** -23 * np.abs(go)
+        eo.append(_check_f16(o16, orc.f16_round(go, osc), osc, slack_o, f"expert out, expert {e}"))
+        ohat[tt, jj] = o16 / np.sqrt(np.mean(o_ref * o_ref, axis=-1, keepdims=True) + spec.eps)
     res["a_flips"] = float(np.mean(fa))
     res["o_flips"] = float(np.mean(eo))
     wr = w_rows.astype(np.float64)

@@ -312,7 +312,7 @@ def check_batch(torch, layer, ref, name, tol):
         pr = v["pair_row"].reshape(T, k)[stage]
         eu = check_expert_input(v, stage, r.u[tk])
         ea = check_rel_l2(bf16_to_f64(v["act"][pr]), r.a[kr], STAGE_L2, "act")
-        eo = check_rel_l2(v["expert_out"][pr], r.o[kr], STAGE_L2, "expert out")
+        eo = check_rel_l2(v["expert_out"][pr], r.o[kr] * ref.host.gamma_o(ids[stage]), STAGE_L2, "expert out")
         ey = check_rel_l2(bf16_to_f64(v["combined"][stage]), r.y[tk], STAGE_L2, "y")
         msg += f"; stages on {len(stage)} tokens: u max rel {eu:.3g}, rel L2 act {ea:.3g} o {eo:.3g} y {ey:.3g}"
         if chain:
@@ -430,7 +430,7 @@ def test_skewed_prompt_parity(torch_dev, tables, real):
     n = len(X)
     eu = check_expert_input(G, np.arange(n), r.u)
     ea = check_rel_l2(G["act"], r.a, STAGE_L2, "act")
-    eo = check_rel_l2(G["expert_out"], r.o, STAGE_L2, "expert out")
+    eo = check_rel_l2(G["expert_out"], r.o * host.gamma_o(IDS), STAGE_L2, "expert out")
     ey = check_rel_l2(G["combined"], r.y, STAGE_L2, "y")
     ch = check_stage_chain(G, IDS, W, host, r.u)
     say(f"skew, {n} tokens: u max rel {eu:.3g}, rel L2 act {ea:.3g} o {eo:.3g} y {ey:.3g}; stage chain flips "

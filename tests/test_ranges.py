@@ -6,8 +6,9 @@ bound that holds for every token:
   |u_i| <= sqrt(P) max|gamma_p|              (an RMS-normed row: sum u^2 <= P max gamma^2)
   |y_i| <= sqrt(P) max|gamma_e|              (normed expert rows, weights summing to one)
   |a_i| <= ||Wg_i|| ||Wu_i|| P max|gamma_p|^2 (|silu(g)| <= |g|, Cauchy-Schwarz, ||u||^2 bound)
-and the expert output o (before its norm) in FP16, one power of two per expert:
-  |o_p| <= ||Wd_p|| ||a|| <= max_p ||Wd_p|| P max|gamma_p|^2 sqrt(sum_i (||Wg_i|| ||Wu_i||)^2)
+and the expert output times its expert's gamma in FP16, one power of two per expert:
+  |o_p gamma_p| <= ||Wd_p|| ||a|| max|gamma_e| <= max_p ||Wd_p|| P max|gamma_p|^2
+                   sqrt(sum_i (||Wg_i|| ||Wu_i||)^2) max|gamma_e|
 These tests check the bounds on random layers of several scales and on inputs
 that attain the u bound (a one-hot pooled row).
 """
@@ -44,13 +45,14 @@ def bounds(d):
 
 
 def o_bound(d):
-    """Per expert: max_p ||Wd_p|| times the bound on ||a||."""
+    """Per expert: max_p ||Wd_p|| times the bound on ||a|| times max|gamma_e|."""
     P = d["pooler"].shape[0]
     gp = np.abs(d["pool_gamma"]).max()
     ng = np.linalg.norm(d["w_gate"], axis=-1)
     nu = np.linalg.norm(d["w_up"], axis=-1)
     nd = np.linalg.norm(d["w_down"], axis=-1).max(axis=-1)  # [E]
-    return nd * P * gp * gp * np.sqrt(((ng * nu) ** 2).sum(axis=-1))
+    gm = np.abs(d["expert_gamma"]).max(axis=-1)  # [E]
+    return nd * P * gp * gp * np.sqrt(((ng * nu) ** 2).sum(axis=-1)) * gm
 
 
 @pytest.mark.parametrize("seed,scale", [(0, 1.0), (1, 0.1), (2, 10.0), (3, 3.0)])
@@ -66,7 +68,7 @@ def test_bounds_hold_on_random_layers(seed, scale):
         for j in range(k):
             e = r.ids[t, j]
             assert np.all(np.abs(r.a[t, j]) <= ba[e] * (1 + 1e-12))
-            assert np.all(np.abs(r.o[t, j]) <= bo[e] * (1 + 1e-12))
+            assert np.all(np.abs(r.o[t, j] * d["expert_gamma"][e]) <= bo[e] * (1 + 1e-12))
 
 
 def test_u_bound_is_attained_by_a_one_hot_row():
