@@ -667,9 +667,10 @@ struct GateUpProb {
 };
 
 // -------------------------------------------------------------------- down
-// o = act Wd_e^T for the rows of expert e; writes o (FP32) and per row and
-// n-tile the partial sum of o^2 for the per-expert RMSNorm. FP16 operands:
-// o is the accumulator times the weight row's 2^-s.
+// o = act Wd_e^T for the rows of expert e; writes o (FP32 layers) or
+// gamma_e * o in FP16 (BF16 layers, out16), and per row and n-tile the
+// partial sum of o^2 for the per-expert RMSNorm. FP16 operands: o is the
+// accumulator times the weight row's 2^-s.
 template <class Cfg_, bool MX_ = false>
 struct DownProb {
   using Cfg = Cfg_;

@@ -408,7 +408,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   float* row_scale = (float*)(ws + L.row_scale);
   Eh* u16 = (Eh*)(ws + L.u16);  // BF16 layers without MX inputs: the FP16 u
   Eh* act = (Eh*)(ws + L.act);
-  float* O = (float*)(ws + L.O);  // FP32 layers; BF16 layers: FP16 (o times o_down[e])
+  float* O = (float*)(ws + L.O);  // FP32 layers: o; BF16 layers: FP16 gamma_e * o times o_down[e]
   float* ossq = (float*)(ws + L.ossq);
   Eh* y = (Eh*)(ws + L.y);
 

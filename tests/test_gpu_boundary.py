@@ -2,7 +2,8 @@
 
 - weights are borrowed for create only: freeing and overwriting the caller's
   tensors right after create leaves the forward's output bit for bit the same;
-- create runs on the caller's stream;
+- create runs on the caller's stream, and two handles forwarding on two
+  streams at once give the results of running them in turn;
 - a device allocation that fails inside create (LATENT_MOE_FAULT=alloc:N)
   returns OOM, names the size, and leaves the device's free memory where it
   was (nothing leaked);
@@ -122,6 +123,39 @@ def test_create_on_caller_stream(torch_dev, tables):
     b.close()
     for u, v in zip(ref, got):
         assert np.array_equal(u, v)
+
+
+def test_handles_on_concurrent_streams(torch_dev, tables):
+    """Two handles forwarding at the same time on two caller streams (each
+    handle also forks its routing onto its own side stream) give bit for bit
+    the results of running them one after the other: handles share no device
+    state."""
+    torch = torch_dev
+    s1, s2 = SPECS["bf16"], SPECS["mxfp4"]
+    say("case: bf16 and mxfp4 handles on two concurrent streams")
+    a, _ = build(s1, tables)
+    b, _ = build(s2, tables)
+    xa = synth.device_tensor(s1, "x", tables)
+    xb = synth.device_tensor(s2, "x", tables)
+    try:
+        ref_a, ref_b = run(torch, a, xa), run(torch, b, xb)
+        sa, sb = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+        outs = []
+        for _ in range(3):
+            sa.wait_stream(torch.cuda.current_stream())
+            sb.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(sa):
+                oa = a.forward(xa)
+            with torch.cuda.stream(sb):
+                ob = b.forward(xb)
+            outs.append((oa, ob))
+        torch.cuda.synchronize()
+        for oa, ob in outs:
+            assert np.array_equal(oa.cpu().numpy(), ref_a[0])
+            assert np.array_equal(ob.cpu().numpy(), ref_b[0])
+    finally:
+        a.close()
+        b.close()
 
 
 def _free_bytes(torch):

@@ -270,7 +270,7 @@ class BatchRef:
         say(f"oracle on all {len(self.xh)} tokens, exact and FP16-emulating: {time.perf_counter() - t0:.0f} s")
 
 
-def check_batch(torch, layer, ref, name, tol):
+def check_batch(torch, layer, ref, name, tol, repeat=False):
     """Run the GPU on the batch of run `name` and compare: routing on every
     token (ids exact but for near-ties, weights 1e-6, logits to FP32 rounding,
     grouping), every output element against the exact oracle (tol x RMS) and
@@ -283,6 +283,9 @@ def check_batch(torch, layer, ref, name, tol):
     x = ref.x_dev[int(tok[0]):int(tok[-1]) + 1]  # the runs' batches are contiguous token ranges
     assert x.shape[0] == len(tok)
     out, ids, w = run_layer(torch, layer, x.contiguous())
+    if repeat:  # run to run, bit for bit (fixed reduction orders, no atomics on values)
+        out2, ids2, w2 = run_layer(torch, layer, x.contiguous())
+        assert np.array_equal(out2, out) and np.array_equal(ids2, ids) and np.array_equal(w2, w), "second run differs"
     T = len(tok)
     r, re_ = ref.r, ref.re
     logits64 = r.logits[tok]
@@ -368,8 +371,9 @@ def test_prefill_parity(torch_dev, real, real_ref, T):
 def test_prefill_every_token(torch_dev, real, real_ref):
     """The whole 16384-token BF16 batch: every output element within 2e-2 x
     RMS of the exact oracle (the largest is expected near 4e-3) and within the
-    emulation bounds of the FP16-emulating oracle; stage chain on 128 tokens."""
-    check_batch(torch_dev, real[2], real_ref, "T=16384", TOL_BF16)
+    emulation bounds of the FP16-emulating oracle; stage chain on 128 tokens;
+    a second forward bit for bit equal to the first."""
+    check_batch(torch_dev, real[2], real_ref, "T=16384", TOL_BF16, repeat=True)
 
 
 def test_skewed_prompt_parity(torch_dev, tables, real):
@@ -476,8 +480,8 @@ def test_mxfp4_prefill_ragged(torch_dev, mx, mx_ref):
 def test_mxfp4_prefill_every_token(torch_dev, mx, mx_ref):
     """The whole 16384-token batch with MXFP4 expert weights: 5e-2 x RMS
     against the oracle on the identically decoded weights, and the emulation
-    bounds against its FP16 emulation."""
-    check_batch(torch_dev, mx[2], mx_ref, "T=16384", TOL_MXFP4)
+    bounds against its FP16 emulation; a second forward bit for bit equal."""
+    check_batch(torch_dev, mx[2], mx_ref, "T=16384", TOL_MXFP4, repeat=True)
 
 
 # ------------------------------ MX FP8 / FP4 activations against MXFP4 weights
