@@ -501,7 +501,9 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   // 4. pooler + norm statistics
   const int pnt = ceil_div(P, Cp::BN);
   int psplits = 1, pkt = 0;
-  if (packed) dense_split(T, P, H, Cp::BM, Cp::BN, psplits, pkt);
+  // the split decision on the split kernel's tiles (Cw), as the workspace
+  // layout sizes its partials
+  if (packed) dense_split(T, P, H, Cw::BM, Cw::BN, psplits, pkt);
   if (psplits > 1) {
     if constexpr (sizeof(Et) == 2) {
     DenseSplitProb<Cw> p;
@@ -677,7 +679,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   LM_MARK(9);
   // 8. unpooler (BF16 layers: FP16 y against the per-row scaled FP16 copy of W)
   int usplits = 1, ukt = 0;
-  if (packed) dense_split(T, H, P, Ce::BM, Ce::BN, usplits, ukt);
+  if (packed) dense_split(T, H, P, Ch::BM, Ch::BN, usplits, ukt);  // the split kernel's tiles, as the layout
   if (usplits > 1) {
     if constexpr (F16) {
     DenseSplitProb<Ch> p;
