@@ -11,7 +11,7 @@
   forward, guard words after it) gives bitwise the same outputs, so no stage
   reads workspace that an earlier stage of the same forward did not write,
   and no stage writes past the workspace;
-- top-k up to 32 against the FP64 oracle, every token.
+- top-k up to 32 and up to 1024 experts against the FP64 oracle, every token.
 """
 import os
 import sys
@@ -219,8 +219,11 @@ def test_poison_mode_bitwise(torch_dev, tables, name):
     layer.close()  # raises LMOE_ERR_CORRUPT if a guard word was overwritten
 
 
-@pytest.mark.parametrize("E,k,T", [(40, 32, 130), (24, 17, 300)])
+@pytest.mark.parametrize("E,k,T", [(40, 32, 130), (24, 17, 300), (1024, 8, 200), (300, 16, 150)])
 def test_top_k_beyond_16(torch_dev, tables, E, k, T):
+    """Top-k up to 32 and expert counts up to the largest the library takes
+    (1024; 300 and 1024 run the selection kernel's wider per-lane layouts),
+    every token against the FP64 oracle."""
     torch = torch_dev
     spec = small(E=E, k=k, T=T)
     say(f"case: bf16, E={E}, top-{k}, T={T}, every token")
