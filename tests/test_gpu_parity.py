@@ -146,6 +146,35 @@ def test_tiny_ragged_token_counts(torch_dev, tiny, T):
     check_output(out, r.out, TOL_F32)
 
 
+def test_tiny_wide_tiles(torch_dev, tables):
+    """The FP32 layer at 1024 tokens (256 routed rows per expert: the
+    prefill-sized FP32 tiles, 128 x 128 per workgroup of 2 x 2 waves), every
+    token and stage against the FP64 oracle."""
+    torch = torch_dev
+    spec = synth.CONFIGS["tiny"].with_(T=1024)
+    say("case: tiny FP32, T=1024 (wide tiles)")
+    layer = make_layer(spec, device_weights(spec, tables), max_tokens=spec.T)
+    try:
+        x = synth.device_tensor(spec, "x", tables)
+        out, ids, w = run_layer(torch, layer, x)
+        v = layer.views(spec.T)
+    finally:
+        layer.close()
+    host = HostLayer(spec)
+    r = host.oracle(host.x())
+    near, _ = check_routing(ids, w, r.logits, spec.k)
+    force = {int(t): ids[t] for t in near}
+    if near:
+        r = host.oracle(host.x(), force_ids=force)
+    assert np.array_equal(ids, r.ids)
+    pr = v["pair_row"].reshape(spec.T, spec.k)
+    check_output(v["act"][pr], r.a, 1e-5, "act")
+    check_output(v["expert_out"][pr], r.o, 1e-5, "expert out")
+    check_output(v["combined"], r.y, 1e-5, "y")
+    e = check_output(out, r.out, TOL_F32)
+    say(f"tiny wide: max-abs/RMS = {e:.3g}, near-ties {near}")
+
+
 def test_tiny_empty_and_errors(torch_dev, tiny):
     torch = torch_dev
     from latent_moe_layer_fp32_amd import binding as B
