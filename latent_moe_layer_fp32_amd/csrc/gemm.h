@@ -133,6 +133,15 @@ template <class P>
 struct LmWeightsOnce<P, std::void_t<decltype(P::kWeightsOnce)>>
     : std::integral_constant<bool, P::kWeightsOnce> {};
 
+// Problems that clear a small counter array before the kernels after them
+// count into it declare clear(block, blocks, thread); every block of the
+// launch runs it first (the router clears the top-k kernel's expert counters,
+// so no separate fill kernel runs between the two).
+template <class P, class = void>
+struct LmHasClear : std::false_type {};
+template <class P>
+struct LmHasClear<P, std::void_t<decltype(std::declval<const P&>().clear(0, 0, 0))>> : std::true_type {};
+
 template <bool NT, class T>
 LM_DEV T lm_wload(const T* p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
@@ -186,6 +195,7 @@ __global__ __launch_bounds__(256) void lm_gemm_kernel(const Prob p) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN;
   constexpr int QA = Cfg::BM / 32, QB = Cfg::BN / 32;
   __shared__ LmGemmSmem<Cfg> sm;
+  if constexpr (LmHasClear<Prob>::value) p.clear(blockIdx.x, gridDim.x, threadIdx.x);
 
   LmTile t;
   if (!p.tile(blockIdx.x, t)) return;
@@ -282,6 +292,105 @@ __global__ __launch_bounds__(256) void lm_gemm_kernel(const Prob p) {
     p.epilogue_f64(t, acc2, wm, wn, lane);
   else
     p.epilogue(t, acc, wm, wn, lane, (void*)&sm);
+}
+
+// Short k ranges with FP64 folding (the router at decode sizes: four k-tiles
+// per k-split): every k-tile of the block's range is loaded into registers at
+// the start, so the block waits for memory once instead of once per k-tile
+// (with cold caches each wait is a whole HBM round trip); the k-tiles then
+// pass through the two LDS buffers in turn, with the same fragment reads,
+// matrix instructions and FP64 folds as lm_gemm_kernel, so the two kernels
+// produce identical sums. Requires t.kt1 - t.kt0 <= KD (checked on the host).
+template <class Prob, int KD>
+__global__ __launch_bounds__(256) void lm_gemm_kdeep_kernel(const Prob p) {
+  using Cfg = typename Prob::Cfg;
+  static_assert(Cfg::WM * Cfg::WN == 4, "four wavefronts");
+  static_assert(Cfg::FLUSH > 0, "problems folding into FP64");
+  using El = LmElem<typename Cfg::E>;
+  constexpr int TM = Cfg::TM, TN = Cfg::TN;
+  constexpr int QA = Cfg::BM / 32, QB = Cfg::BN / 32;
+  __shared__ LmGemmSmem<Cfg> sm;
+  if constexpr (LmHasClear<Prob>::value) p.clear(blockIdx.x, gridDim.x, threadIdx.x);
+
+  LmTile t;
+  if (!p.tile(blockIdx.x, t)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+  const int lc = tid & 7, lr = tid >> 3;
+  const int nk = t.kt1 - t.kt0;
+
+  lm_u32x4 ra[KD][QA], rb[KD][QB];
+  {
+    const lm_u32x4* ap[QA];
+    const lm_u32x4* bp[QB];
+#pragma unroll
+    for (int q = 0; q < QA; ++q) ap[q] = p.a_row(t, lr + 32 * q);
+#pragma unroll
+    for (int q = 0; q < QB; ++q) bp[q] = p.b_row(t, lr + 32 * q);
+#pragma unroll
+    for (int d = 0; d < KD; ++d) {
+      if (d < nk) {
+        const int ka = p.a_ktile(t.kt0 + d), kb = lm_b_ktile(p, t.kt0 + d);
+#pragma unroll
+        for (int q = 0; q < QA; ++q) ra[d][q] = ap[q][ka * 8 + lc];
+#pragma unroll
+        for (int q = 0; q < QB; ++q) rb[d][q] = bp[q][kb * 8 + lc];
+      }
+    }
+  }
+
+  lm_f32x16 acc[TM][TN];
+  double acc2[TM][TN][16];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc[i][j][r] = 0.0f;
+        acc2[i][j][r] = 0.0;
+      }
+
+  // k-tile d goes through LDS buffer d & 1. The store of k-tile d + 2 into
+  // the same buffer comes after the barrier of k-tile d + 1, which every wave
+  // reaches only once its reads of k-tile d are done.
+#pragma unroll
+  for (int d = 0; d < KD; ++d) {
+    if (d < nk) {
+      const int buf = d & 1;
+#pragma unroll
+      for (int q = 0; q < QA; ++q) sm.a[buf][lm_swz(lr + 32 * q, lc)] = ra[d][q];
+#pragma unroll
+      for (int q = 0; q < QB; ++q) sm.b[buf][lm_swz(lr + 32 * q, lc)] = rb[d][q];
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int ch = 2 * s + (lane >> 5);
+        lm_u32x4 fa[TM], fb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[i] = sm.a[buf][lm_swz(wm * TM * 32 + i * 32 + (lane & 31), ch)];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[j] = sm.b[buf][lm_swz(wn * TN * 32 + j * 32 + (lane & 31), ch)];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) El::mma(acc[i][j], fa[i], fb[j]);
+      }
+      if (((d + 1) % Cfg::FLUSH) == 0 || d + 1 == nk) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              acc2[i][j][r] += (double)acc[i][j][r];
+              acc[i][j][r] = 0.0f;
+            }
+      }
+    }
+  }
+  p.epilogue_f64(t, acc2, wm, wn, lane);
 }
 
 // Per-row sum over the tile's valid columns of v(acc)^2, reduced in a fixed

@@ -411,7 +411,12 @@ struct RouterProb {
   int T, Ew, H, Kw, kta, mt, nt, splits, kt_per;
   int lda = 0;     // row stride of x in elements (0: H)
   int pieces = 1;  // BF16: pieces of x (1 or 3)
+  lm_u32x4* counters = nullptr;  // the top-k kernel's expert counters, cleared here
+  int counter_chunks = 0;        // their size in 16-byte chunks
 
+  LM_DEV void clear(int bid, int nb, int tid) const {
+    for (int i = bid * 256 + tid; i < counter_chunks; i += nb * 256) counters[i] = lm_u32x4{0u, 0u, 0u, 0u};
+  }
   LM_DEV int ktot() const { return pieces == 3 ? 6 * kta : Kw / Cfg::KT; }
   LM_DEV bool tile(int bid, LmTile& t) const {
     int L;
@@ -1006,11 +1011,6 @@ __global__ __launch_bounds__(256) void lm_absmax_kernel(const float* v, int64_t 
   if (threadIdx.x == 0) out[0] = red[0];
 }
 
-__global__ void lm_fill_i32_kernel(int* p, int n, int v) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
-}
-
 // Exact split of FP32 router weights into three BF16 pieces (w = b1 + b2 + b3
 // exactly for normal inputs: each remainder is exactly representable and the
 // third piece holds at most 8 significant bits). Layout [E, 3H]: piece q of
@@ -1074,9 +1074,19 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const double* part, int sp
     if (t >= T) continue;
     const double* src = part + (size_t)t * E + e;
     const size_t stride = (size_t)T * E;
-    // the splits summed in index order; 32 loads in flight at a time
+    // the splits summed in index order; 48 (one token per workgroup: many
+    // splits, few tokens) or 32 loads in flight at a time
     double sd = 0.0;
     int sp = 0;
+    if constexpr (TPB == 1) {
+      for (; sp + 48 <= splits; sp += 48) {
+        double v[48];
+#pragma unroll
+        for (int i = 0; i < 48; ++i) v[i] = src[(size_t)(sp + i) * stride];
+#pragma unroll
+        for (int i = 0; i < 48; ++i) sd += v[i];
+      }
+    }
     for (; sp + 32 <= splits; sp += 32) {
       double v[32];
 #pragma unroll

@@ -205,6 +205,9 @@ bool narrow_for(const latent_moe_config& c, int64_t T) {
   return T * c.top_k < (int64_t)kNarrowRowsPerExpert * c.experts;
 }
 
+// Routers whose k-splits span at most this many k-tiles run lm_gemm_kdeep_kernel.
+constexpr int kRouterDeep = 4;
+
 // Router k-splits: enough blocks to cover the chip, each split at least 4
 // k-tiles, all splits non-empty. FP32 layers: K = H in 32-column k-tiles.
 // BF16 layers: x against the three-piece BF16 split of the router (K = 3H),
@@ -465,11 +468,19 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
       p.lda = 3 * H;
       p.pieces = 3;
     }
-    LM_HIP(launch(p, (int64_t)mt * nt * splits, sr));
+    // the router's blocks also clear the expert counters the top-k kernel counts into
+    p.counters = (lm_u32x4*)cpad;
+    p.counter_chunks = E * kLmCountStride / 4;
+    if (kt_per <= kRouterDeep) {  // decode sizes: each block's k-tiles all in flight at once
+      const int64_t g = ((int64_t)mt * nt * splits + 7) / 8 * 8;
+      hipLaunchKernelGGL((lm_gemm_kdeep_kernel<RouterProb<Cr>, kRouterDeep>), dim3((unsigned)g), dim3(256), 0,
+                         sr, p);
+      LM_HIP(hipGetLastError());
+    } else {
+      LM_HIP(launch(p, (int64_t)mt * nt * splits, sr));
+    }
     LM_MARK(2);
     // 2. top-k + softmax + per-expert counts
-    hipLaunchKernelGGL(lm_fill_i32_kernel, dim3(ceil_div(E * kLmCountStride, 256)), dim3(256), 0, sr,
-                       cpad, E * kLmCountStride, 0);
     // few tokens with many k-splits: one token per workgroup spreads the
     // split sums over all threads; otherwise four tokens per workgroup
     const bool one = splits > 4;
