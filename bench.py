@@ -16,12 +16,17 @@ comes from HIP events recorded on the forward's stream) and the FP64 CPU
 oracle timed on a bounded token sample on this host's cores (the first 48
 decode tokens, and a seeded 2048-token subset of the prefill batch).
 
-Timing: every timed step is preceded by writing a 1 GiB buffer, which evicts
-the layer's weights and activations from L2 and the 256 MB MALL, and is timed
-alone with HIP events; `value` and `ms_per_step` come from the median of
-these cold steps (p10 and p90 reported beside it). A warm-cache mean (steps
-back to back) is reported separately and labelled as such. The tiny FP32
-layer is reported in microseconds per forward.
+Timing: every timed step is preceded by writing a 1 GiB buffer and then
+reading another 1 GiB buffer, which evicts the layer's weights and
+activations from L2 and the 256 MB MALL, and is timed alone with HIP events;
+`value` and `ms_per_step` come from the median of these cold steps (p10 and
+p90 reported beside it). The read leaves the caches holding clean lines of
+unrelated data: after the write alone, up to 256 MB of the buffer's dirty
+lines are still in the MALL and their write-back to HBM lands inside the
+timed step; the median of such steps is reported beside the cold one as
+`cold_after_write_p50`. A warm-cache mean (steps back to back) is reported
+separately and labelled as such. The tiny FP32 layer is reported in
+microseconds per forward.
 """
 from __future__ import annotations
 
@@ -102,24 +107,28 @@ def layer_flops(spec, T):
     return T * (2 * H * P * 2 + k * 2 * P * 2 * I + k * 2 * I * P)
 
 
-FLUSH_BYTES = 1 << 30  # written before each cold step: larger than L2 (8 x 4 MB) plus the 256 MB MALL
+FLUSH_BYTES = 1 << 30  # evicting buffers: larger than L2 (8 x 4 MB) plus the 256 MB MALL
 
 
 def measure(spec, layer, xs, steps, warmup, torch):
     """One step = one forward per chunk in xs (a single batch, or the chunks
     of a long prompt in order). Cold steps: before each, a 1 GiB buffer is
-    written (evicting the layer's weights and activations from L2 and the
-    MALL) and the step is timed alone with HIP events on the forward's stream.
-    Warm steps: back to back, caches as the previous step left them. Returns
-    the per-step cold times (ms), the warm mean (ms), the wall time of the
-    cold loop, per-stage ms (summed over the chunks of a step) and the last
-    chunk's expert counts."""
+    written and another 1 GiB buffer read (evicting the layer's weights and
+    activations from L2 and the MALL, and leaving no dirty line of the write
+    behind) and the step is timed alone with HIP events on the forward's
+    stream. The same steps after the write alone are timed too: then the
+    write-back of the MALL's dirty lines falls inside the step. Warm steps:
+    back to back, caches as the previous step left them. Returns the per-step
+    cold times (ms), the per-step times after the write alone (ms), the warm
+    mean (ms), the wall time of the cold loop, per-stage ms (summed over the
+    chunks of a step) and the last chunk's expert counts."""
     from latent_moe_layer_fp32_amd import binding as B
 
     stream = torch.cuda.current_stream()
     T = xs[0].shape[0]
     out = torch.empty((T, spec.H), dtype=torch.float32, device=xs[0].device)
     scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=xs[0].device)
+    clean = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=xs[0].device)  # only ever read
 
     def step():
         for x in xs:
@@ -132,12 +141,20 @@ def measure(spec, layer, xs, steps, warmup, torch):
     t0 = time.perf_counter()
     for a, b in evs:
         scratch.fill_(1.0)  # a fill kernel on the same stream, outside the timed events
+        clean.sum()  # a reduction reading 1 GiB: the MALL's dirty lines are written back here
         a.record(stream)
         step()
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     cold = [a.elapsed_time(b) for a, b in evs]
+    for a, b in evs:
+        scratch.fill_(1.0)
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    dirty = [a.elapsed_time(b) for a, b in evs]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(steps):
@@ -145,7 +162,7 @@ def measure(spec, layer, xs, steps, warmup, torch):
     end.record(stream)
     torch.cuda.synchronize()
     warm = start.elapsed_time(end) / steps
-    del scratch
+    del scratch, clean
     # per-stage HIP events on the same stream, over the same number of (warm) steps
     B.latent_moe_set_profiling(layer.handle, True)
     acc = None
@@ -156,7 +173,7 @@ def measure(spec, layer, xs, steps, warmup, torch):
             acc = st if acc is None else {k: acc[k] + v for k, v in st.items()}
     B.latent_moe_set_profiling(layer.handle, False)
     stages = {k: v / steps for k, v in acc.items()}
-    return cold, warm, wall, stages, layer.views(T, names=("counts",))["counts"]
+    return cold, dirty, warm, wall, stages, layer.views(T, names=("counts",))["counts"]
 
 
 def host_info() -> dict:
@@ -324,13 +341,13 @@ def main():
             steps = 5 if spec.chunks > 1 else max(20, args.steps)
             warm = max(2, args.warmup // 2)
         log(f"{wl}: T={spec.T} x {spec.chunks} chunk(s), {warm} warmup + {steps} timed steps")
-        cold, warm_ms, wall, stages, counts = measure(spec, layer, xs, steps, warm, torch)
+        cold, dirty, warm_ms, wall, stages, counts = measure(spec, layer, xs, steps, warm, torch)
         ms = pct(cold, 50)
         lb, touched = layer_bytes(spec, counts, spec.T)
         r = dict(spec=spec, ms=ms, wall=wall, stages=stages, touched=touched, layer_bytes=lb,
                  tokens_per_s=spec.T * spec.chunks / (ms / 1e3), steps=steps, warmup=warm,
                  cold={"p10": round(pct(cold, 10), 4), "p50": round(ms, 4), "p90": round(pct(cold, 90), 4)},
-                 warm_ms=round(warm_ms, 4))
+                 cold_after_write_p50=round(pct(dirty, 50), 4), warm_ms=round(warm_ms, 4))
         gu = stages["gate_up"] / 1e3
         if spec.act_dtype == "f32":
             r["roofline"] = None  # launch-latency bound (21 MFLOP): reported in microseconds
@@ -356,6 +373,7 @@ def main():
                              "kernel_ms": round(stages["gate_up"], 4)}
             r["layer_frac"] = round(layer_flops(spec, spec.T * spec.chunks) / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)
         log(f"{wl}: cold {ms:.3f} ms/step (p10 {r['cold']['p10']:.3f}, p90 {r['cold']['p90']:.3f}), "
+            f"after write alone {r['cold_after_write_p50']:.3f}, "
             f"warm {warm_ms:.3f}, {r['tokens_per_s']:.0f} tok/s, stages "
             + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
         cpu_n = 0
@@ -399,8 +417,10 @@ def main():
                    "global_batch": spec.T * spec.chunks, "parallelism": "none (one GPU)"},
         "roofline": main_r["roofline"],
         "layer_frac": main_r["layer_frac"],
-        "timing": {"value_from": "median of cold steps (1 GiB written before each; HIP events per step)",
-                   "cold_ms": main_r["cold"], "warm_ms": main_r["warm_ms"],
+        "timing": {"value_from": "median of cold steps (before each, 1 GiB written, then another 1 GiB "
+                                 "read; HIP events per step)",
+                   "cold_ms": main_r["cold"], "cold_after_write_p50": main_r["cold_after_write_p50"],
+                   "warm_ms": main_r["warm_ms"],
                    "warm_tokens_per_s": round(spec.T * spec.chunks / (main_r["warm_ms"] / 1e3), 1)},
         "stages_ms": {k: round(v, 4) for k, v in main_r["stages"].items()},
         "experts_touched": main_r["touched"],
@@ -410,7 +430,8 @@ def main():
             continue
         sub = {"value": round(r["tokens_per_s"], 1), "unit": "tokens/s", "ms_per_step": round(r["ms"], 4),
                "tokens_per_step": r["spec"].T * r["spec"].chunks, "steps": r["steps"],
-               "cold_ms": r["cold"], "warm_ms": r["warm_ms"], "roofline": r["roofline"],
+               "cold_ms": r["cold"], "cold_after_write_p50": r["cold_after_write_p50"],
+               "warm_ms": r["warm_ms"], "roofline": r["roofline"],
                "layer_frac": r["layer_frac"], "stages_ms": {k: round(v, 4) for k, v in r["stages"].items()}}
         for key in ("us_per_forward", "cpu_baseline"):
             if key in r:
