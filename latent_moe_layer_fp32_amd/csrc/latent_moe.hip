@@ -436,16 +436,21 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   }
   LM_MARK(1);
   // Steps 1-3 (routing) depend only on x, as do the pooler and its norm
-  // statistics (step 4): outside stage profiling, routing runs on the
+  // statistics (step 4): outside stage profiling, the pooler steps run on the
   // handle's side stream, forked from and joined back into the caller's
-  // stream, so the two overlap. With stage profiling on, every step runs in
+  // stream, so the two overlap. Routing, the longer of the two at decode
+  // sizes, stays on the caller's stream: it reaches the join after the side
+  // stream has finished, so the join costs no wait (the other way round, the
+  // caller's stream idled about 10 us at the join for the side stream's last
+  // kernel to be seen complete). With stage profiling on, every step runs in
   // order on the caller's stream so the per-stage times are separable.
   const bool fork = !h->prof && h->side_ok;
-  hipStream_t sr = s;
+  const hipStream_t sr = s;  // routing
+  hipStream_t sp = s;        // pooler and the steps that read only its output
   if (fork) {
     LM_HIP(hipEventRecord(h->fork, s));
     LM_HIP(hipStreamWaitEvent(h->side, h->fork, 0));
-    sr = h->side;
+    sp = h->side;
   }
   // 1. router: partial logits over k-splits
   {
@@ -507,7 +512,6 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
   hipLaunchKernelGGL(lm_permute_kernel, dim3(E), dim3(256), 0, sr, ids, npairs, k, cpad, E, kBmGroup,
                      counts, offsets, tile_off, perm_token, pair_row);
   LM_HIP(hipGetLastError());
-  if (fork) LM_HIP(hipEventRecord(h->join, sr));
   LM_MARK(4);
   // 4. pooler + norm statistics
   const int pnt = ceil_div(P, Cp::BN);
@@ -526,20 +530,20 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.N = P;
     p.K = H;
     p.mt = ceil_div(T, Cw::BM);
-    p.nt = pnt;
+    p.nt = ceil_div(P, Cw::BN);
     p.splits = psplits;
     p.kt_per = pkt;
-    LM_HIP(launch(p, (int64_t)p.mt * p.nt * psplits, s));
+    LM_HIP(launch(p, (int64_t)p.mt * p.nt * psplits, sp));
     LM_MARK(5);
     const int chunks = ceil_div(P, 256);
-    hipLaunchKernelGGL(lm_pool_finish_kernel, dim3((unsigned)T, (unsigned)chunks), dim3(256), 0, s,
+    hipLaunchKernelGGL(lm_pool_finish_kernel, dim3((unsigned)T, (unsigned)chunks), dim3(256), 0, sp,
                        (const float*)(ws + L.kpart), psplits, (int)T, P, w.pool_gamma, pssq, pooled32);
     LM_HIP(hipGetLastError());
     if (MXA) {
-      hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, pssq, chunks,
+      hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, sp, pssq, chunks,
                          (int)T, P, c.eps, row_scale);
     } else {
-      hipLaunchKernelGGL(lm_norm_u_kernel, dim3((unsigned)T), dim3(256), 0, s, pooled32, pssq, chunks,
+      hipLaunchKernelGGL(lm_norm_u_kernel, dim3((unsigned)T), dim3(256), 0, sp, pooled32, pssq, chunks,
                          P, c.eps, h->u_down, row_scale, (_Float16*)u16);
     }
     LM_HIP(hipGetLastError());
@@ -558,27 +562,30 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
     p.P = P;
     p.mt = ceil_div(T, Cp::BM);
     p.nt = pnt;
-    LM_HIP(launch(p, (int64_t)p.mt * p.nt, s));
+    LM_HIP(launch(p, (int64_t)p.mt * p.nt, sp));
     LM_MARK(5);
     if (F16 && !MXA) {
       if constexpr (F16)
-        hipLaunchKernelGGL(lm_norm_u_kernel, dim3((unsigned)T), dim3(256), 0, s, pooled32, pssq, pnt,
+        hipLaunchKernelGGL(lm_norm_u_kernel, dim3((unsigned)T), dim3(256), 0, sp, pooled32, pssq, pnt,
                            P, c.eps, h->u_down, row_scale, u16);
     } else {
-      hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, pssq, pnt,
+      hipLaunchKernelGGL(lm_rowscale_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, sp, pssq, pnt,
                          (int)T, P, c.eps, row_scale);
     }
     LM_HIP(hipGetLastError());
   }
   if constexpr (MXA) {  // u = r * gamma_p * h MX-quantised for the expert GEMMs
     const int64_t nthr = T * (int64_t)(P / 32) * 8;
-    hipLaunchKernelGGL(lm_quant_u_kernel<AB>, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(lm_quant_u_kernel<AB>, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, sp,
                        pooled32, row_scale, (int)T, P, (uint8_t*)(ws + L.uq),
                        (uint8_t*)(ws + L.us));
     LM_HIP(hipGetLastError());
   }
+  if (fork) {
+    LM_HIP(hipEventRecord(h->join, sp));
+    LM_HIP(hipStreamWaitEvent(s, h->join, 0));
+  }
   LM_MARK(6);
-  if (fork) LM_HIP(hipStreamWaitEvent(s, h->join, 0));
   const int64_t max_tiles = ceil_div(npairs, kBmGroup) + (npairs < E ? npairs : E);
   // 5. gate/up + SwiGLU
   if constexpr (MXA) {
