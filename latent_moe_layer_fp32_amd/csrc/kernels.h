@@ -1048,72 +1048,90 @@ LM_DEV uint64_t lm_wave_max_u64(uint64_t v) {
   return v;
 }
 
-// Router logits and top-k, TPB tokens per workgroup. Phase 1: all 256
-// threads sum the k-split partial logits of the workgroup's tokens in a fixed
-// order (FP64), add the bias and round once to FP32. Phase 2: one wavefront
-// per token picks the top k by (logit desc, index asc) and takes the softmax
-// over them. Routed pairs per expert are counted in an LDS histogram, then
-// one integer atomic per expert and workgroup into cpad, where each expert's
+// Router logits and top-k, TPB tokens per workgroup. Phase 1: the k-split
+// partial logits of each (token, expert) are summed in a fixed order (FP64),
+// the bias added and the sum rounded once to FP32. Four tokens per workgroup
+// (256 threads): one thread per (token, expert), splits in index order. One
+// token per workgroup (decode sizes, many splits; 1024 threads): Q = 1024 /
+// (64 NV) threads per expert, thread q summing the q-th contiguous range of
+// splits in index order, then the Q range sums added in q order, so that
+// each thread has few loads to wait for. Phase 2: one wavefront per token
+// picks the top k by (logit desc, index asc) and takes the softmax over
+// them. Routed pairs per expert are counted in an LDS histogram, then one
+// integer atomic per expert and workgroup into cpad, where each expert's
 // counter sits alone in a 128-byte line (cpad[e * kLmCountStride]) so that
 // the atomics of different experts do not queue on a few lines.
 constexpr int kLmCountStride = 32;  // ints per padded expert counter
 constexpr int kLmMaxK = 32;         // largest top-k the kernels take
 
+// Sum of src[sp * stride] for sp in [lo, hi), in index order, up to 32 loads
+// in flight: whole batches of 32, then a rest of more than four as one batch
+// of 32 loads with the index clamped to the last split (loads never sit
+// behind a branch, which would make the compiler wait for all of them at the
+// join), the clamped repeats left out of the sum; a rest of at most four one
+// by one.
+LM_DEV double lm_sum_splits_f64(const double* src, size_t stride, int lo, int hi) {
+  double sd = 0.0;
+  int sp = lo;
+  for (; sp + 32 <= hi; sp += 32) {
+    double v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = src[(size_t)(sp + i) * stride];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sd += v[i];
+  }
+  const int n = hi - sp;
+  if (n > 4) {
+    double v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = src[(size_t)(sp + min(i, n - 1)) * stride];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sd = i < n ? sd + v[i] : sd;
+  } else {
+    for (; sp < hi; ++sp) sd += src[(size_t)sp * stride];
+  }
+  return sd;
+}
+
 template <int NV, int TPB>
-__global__ __launch_bounds__(256) void lm_topk_kernel(const double* part, int splits, int T, int E,
-                                                      const float* bias, int k, float* logits,
-                                                      int* ids, float* wts, int* cpad) {
-  static_assert(TPB >= 1 && TPB <= 4, "one wavefront per token");
+__global__ __launch_bounds__((TPB == 1 ? 1024 : 256)) void lm_topk_kernel(
+    const double* part, int splits, int T, int E, const float* bias, int k, float* logits, int* ids,
+    float* wts, int* cpad) {
+  static_assert(TPB == 1 || TPB == 4, "one or four tokens per workgroup");
+  constexpr int NTH = TPB == 1 ? 1024 : 256;  // threads (the launch uses the same count)
+  constexpr int ES = NV * 64;                         // expert slots (E <= ES)
+  constexpr int Q = TPB == 1 ? (NTH / ES > 1 ? NTH / ES : 1) : 1;  // threads per expert
   __shared__ int hist[1024];
-  __shared__ float sl[TPB][NV * 64];
+  __shared__ float sl[TPB][ES];
+  __shared__ double red[TPB == 1 ? NTH : 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int t0 = blockIdx.x * TPB;
-  for (int i = tid; i < E; i += 256) hist[i] = 0;
-  for (int i = tid; i < TPB * E; i += 256) {
-    const int tt = i / E, e = i - tt * E, t = t0 + tt;
-    if (t >= T) continue;
-    const double* src = part + (size_t)t * E + e;
-    const size_t stride = (size_t)T * E;
-    // the splits summed in index order; 48 (one token per workgroup: many
-    // splits, few tokens) or 32 loads in flight at a time
-    double sd = 0.0;
-    int sp = 0;
-    if constexpr (TPB == 1) {
-      for (; sp + 48 <= splits; sp += 48) {
-        double v[48];
+  const size_t stride = (size_t)T * E;
+  for (int i = tid; i < E; i += NTH) hist[i] = 0;
+  if constexpr (TPB == 1) {
+    const int q = tid / ES, e = tid - q * ES;
+    if (e < E && t0 < T)
+      red[tid] = lm_sum_splits_f64(part + (size_t)t0 * E + e, stride, q * splits / Q, (q + 1) * splits / Q);
+    __syncthreads();
+    if (tid < E && t0 < T) {
+      double sd = red[tid];
 #pragma unroll
-        for (int i = 0; i < 48; ++i) v[i] = src[(size_t)(sp + i) * stride];
-#pragma unroll
-        for (int i = 0; i < 48; ++i) sd += v[i];
-      }
+      for (int r = 1; r < Q; ++r) sd += red[r * ES + tid];
+      if (bias) sd += (double)bias[tid];
+      const float v = (float)sd + 0.0f;  // one rounding to FP32; -0 -> +0
+      logits[(size_t)t0 * E + tid] = v;
+      sl[0][tid] = v;
     }
-    for (; sp + 32 <= splits; sp += 32) {
-      double v[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = src[(size_t)(sp + i) * stride];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) sd += v[i];
+  } else {
+    for (int i = tid; i < TPB * E; i += NTH) {
+      const int tt = i / E, e = i - tt * E, t = t0 + tt;
+      if (t >= T) continue;
+      double sd = lm_sum_splits_f64(part + (size_t)t * E + e, stride, 0, splits);
+      if (bias) sd += (double)bias[e];
+      const float v = (float)sd + 0.0f;
+      logits[(size_t)t * E + e] = v;
+      sl[tt][e] = v;
     }
-    for (; sp + 16 <= splits; sp += 16) {
-      double v[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = src[(size_t)(sp + i) * stride];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sd += v[i];
-    }
-    for (; sp + 4 <= splits; sp += 4) {
-      const double a = src[(size_t)sp * stride], b = src[(size_t)(sp + 1) * stride];
-      const double c = src[(size_t)(sp + 2) * stride], d = src[(size_t)(sp + 3) * stride];
-      sd += a;
-      sd += b;
-      sd += c;
-      sd += d;
-    }
-    for (; sp < splits; ++sp) sd += src[(size_t)sp * stride];
-    if (bias) sd += (double)bias[e];
-    const float v = (float)sd + 0.0f;  // one rounding to FP32; -0 -> +0
-    logits[(size_t)t * E + e] = v;
-    sl[tt][e] = v;
   }
   __syncthreads();
   const int tt = tid >> 6, t = t0 + tt;
@@ -1124,45 +1142,39 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const double* part, int sp
       const int e = lane + 64 * v;
       key[v] = e < E ? ((uint64_t)lm_ord(sl[tt][e]) << 32) | (uint32_t)(~(uint32_t)e) : 0;
     }
-    float selv[kLmMaxK];
-    int seli[kLmMaxK];
+    // lane j keeps the j-th selection
+    float v0 = 0.0f, myv = 0.0f;
+    int myi = 0;
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < kLmMaxK; ++j) {
-      if (j < k) {
-        uint64_t best = 0;
+      for (int v = 0; v < NV; ++v) best = key[v] > best ? key[v] : best;
+      best = lm_wave_max_u64(best);
+      const int e = (int)(~(uint32_t)best);
+      const float val = lm_unord((uint32_t)(best >> 32));
+      if (j == 0) v0 = val;
+      if (j == lane) {
+        myv = val;
+        myi = e;
+      }
+      if ((e & 63) == lane) {
 #pragma unroll
-        for (int v = 0; v < NV; ++v) best = key[v] > best ? key[v] : best;
-        best = lm_wave_max_u64(best);
-        const int e = (int)(~(uint32_t)best);
-        selv[j] = lm_unord((uint32_t)(best >> 32));
-        seli[j] = e;
-        if ((e & 63) == lane) {
-#pragma unroll
-          for (int v = 0; v < NV; ++v)
-            if (v == (e >> 6)) key[v] = 0;
-        }
+        for (int v = 0; v < NV; ++v)
+          if (v == (e >> 6)) key[v] = 0;
       }
     }
-    float ex[kLmMaxK];
+    // softmax over the selection, the exponentials summed in selection order
+    const float ex = expf(myv - v0);
     float sum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kLmMaxK; ++j) {
-      if (j < k) {
-        ex[j] = expf(selv[j] - selv[0]);
-        sum += ex[j];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kLmMaxK; ++j) {
-      if (j < k && j == lane) {
-        ids[(size_t)t * k + j] = seli[j];
-        wts[(size_t)t * k + j] = ex[j] / sum;
-        atomicAdd(&hist[seli[j]], 1);
-      }
+    for (int j = 0; j < k; ++j) sum += __shfl(ex, j, kWave);
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = myi;
+      wts[(size_t)t * k + lane] = ex / sum;
+      atomicAdd(&hist[myi], 1);
     }
   }
   __syncthreads();
-  for (int i = tid; i < E; i += 256)
+  for (int i = tid; i < E; i += NTH)
     if (hist[i]) atomicAdd(&cpad[i * kLmCountStride], hist[i]);
 }
 

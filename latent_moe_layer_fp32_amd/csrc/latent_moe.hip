@@ -493,7 +493,7 @@ int forward_impl(latent_moe* h, const void* x, int64_t T, float* out, hipStream_
 #define LM_TOPK(NV)                                                                             \
   do {                                                                                          \
     if (one)                                                                                    \
-      hipLaunchKernelGGL((lm_topk_kernel<NV, 1>), g, dim3(256), 0, sr, part, splits, (int)T, E, \
+      hipLaunchKernelGGL((lm_topk_kernel<NV, 1>), g, dim3(1024), 0, sr, part, splits, (int)T, E, \
                          w.router_bias, k, logits, ids, wts, cpad);                             \
     else                                                                                        \
       hipLaunchKernelGGL((lm_topk_kernel<NV, 4>), g, dim3(256), 0, sr, part, splits, (int)T, E, \
