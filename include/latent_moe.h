@@ -190,9 +190,10 @@ int latent_moe_workspace_bytes(const latent_moe_config* cfg, size_t* bytes);
  * T = 0 succeeds and enqueues nothing. One forward in flight per handle: the
  * workspace is shared, so overlapping forwards of one handle on different
  * streams race. The forward never allocates or synchronises the host.
- * Routing (router, top-k, grouping) runs on a stream the handle owns, forked
- * from `stream` by an event and joined back into it before the expert GEMMs,
- * so it overlaps the pooler; all work still completes in `stream`'s order
+ * The pooler steps (pooler GEMM and the pre-expert norm) run on a stream the
+ * handle owns, forked from `stream` by an event and joined back into it
+ * before the expert GEMMs, so they overlap routing (router, top-k, grouping),
+ * which runs on `stream`; all work still completes in `stream`'s order
  * (stage profiling, latent_moe_set_profiling, runs everything on `stream`).
  * Errors: INVALID_ARG (null handle/x/out, misaligned pointer, T < 0),
  * TOO_MANY_TOKENS, HIP (launch failure). */

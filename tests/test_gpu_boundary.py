@@ -127,7 +127,7 @@ def test_create_on_caller_stream(torch_dev, tables):
 
 def test_handles_on_concurrent_streams(torch_dev, tables):
     """Two handles forwarding at the same time on two caller streams (each
-    handle also forks its routing onto its own side stream) give bit for bit
+    handle also forks its pooler steps onto its own side stream) give bit for bit
     the results of running them one after the other: handles share no device
     state."""
     torch = torch_dev
