@@ -241,7 +241,8 @@ def pct(v, q):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100,
+                    help="timed steps of the main workload (default: 100, the 64-token decode)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "skew", "mxfp4", "mxfp4_decode", "mxfp8", "mxfp8_decode",
@@ -337,8 +338,11 @@ def main():
         prefill_sized = spec.T * spec.k >= 64 * spec.E
         if wl == args.workload:
             steps, warm = args.steps, args.warmup
-        else:  # at least 20 timed steps of a single batch, 5 of the five-chunk prompt
-            steps = 5 if spec.chunks > 1 else max(20, args.steps)
+        elif args.steps < 20:  # a short run (profiling): as many steps as the main workload
+            steps = min(5, args.steps) if spec.chunks > 1 else args.steps
+            warm = max(2, args.warmup // 2)
+        else:  # 100 timed steps at decode sizes, 20 at prefill sizes, 5 of the five-chunk prompt
+            steps = 5 if spec.chunks > 1 else (20 if prefill_sized else max(100, args.steps))
             warm = max(2, args.warmup // 2)
         log(f"{wl}: T={spec.T} x {spec.chunks} chunk(s), {warm} warmup + {steps} timed steps")
         cold, dirty, warm_ms, wall, stages, counts = measure(spec, layer, xs, steps, warm, torch)
