@@ -1065,31 +1065,27 @@ constexpr int kLmCountStride = 32;  // ints per padded expert counter
 constexpr int kLmMaxK = 32;         // largest top-k the kernels take
 
 // Sum of src[sp * stride] for sp in [lo, hi), in index order, up to 32 loads
-// in flight: whole batches of 32, then a rest of more than four as one batch
-// of 32 loads with the index clamped to the last split (loads never sit
-// behind a branch, which would make the compiler wait for all of them at the
-// join), the clamped repeats left out of the sum; a rest of at most four one
-// by one.
+// in flight: batches of up to 32 splits, each issued as 32 loads with the
+// index clamped to the batch's last split (no load sits behind a branch,
+// which would make the compiler wait for all of them at the join) and all
+// issued before the first addition (a scheduling barrier; left to itself the
+// compiler interleaved the additions and kept a few loads in flight), the
+// clamped repeats left out of the sum; a rest of at most four one by one.
 LM_DEV double lm_sum_splits_f64(const double* src, size_t stride, int lo, int hi) {
   double sd = 0.0;
   int sp = lo;
-  for (; sp + 32 <= hi; sp += 32) {
+  while (hi - sp > 4) {
+    const int n = min(32, hi - sp);
+    const double* q = src + (size_t)sp * stride;
     double v[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = src[(size_t)(sp + i) * stride];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) sd += v[i];
-  }
-  const int n = hi - sp;
-  if (n > 4) {
-    double v[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = src[(size_t)(sp + min(i, n - 1)) * stride];
+    for (int i = 0; i < 32; ++i) v[i] = q[(size_t)min(i, n - 1) * stride];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 32; ++i) sd = i < n ? sd + v[i] : sd;
-  } else {
-    for (; sp < hi; ++sp) sd += src[(size_t)sp * stride];
+    sp += n;
   }
+  for (; sp < hi; ++sp) sd += src[(size_t)sp * stride];
   return sd;
 }
 
