@@ -1271,10 +1271,25 @@ __global__ __launch_bounds__(256) void lm_permute_kernel(const int* ids, int npa
   }
 }
 
+// p[0] + p[1] + ... + p[n - 1] in FP32, in index order, 16 loads in flight at
+// a time (indices clamped to n - 1 so that no load sits behind a branch, and
+// all issued before the first addition).
+LM_DEV float lm_sum_in_order(const float* p, int n) {
+  float s = 0.0f;
+  for (int i0 = 0; i0 < n; i0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = p[min(i0 + i, n - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s = i0 + i < n ? s + v[i] : s;
+  }
+  return s;
+}
+
 // r_t = 1 / sqrt(sum of the row's pooled partial sums of squares / P + eps).
 LM_DEV float lm_row_rms_scale(const float* ssq, int nparts, int t, int P, float eps) {
-  float s = 0.0f;
-  for (int i = 0; i < nparts; ++i) s += ssq[(size_t)t * nparts + i];
+  const float s = lm_sum_in_order(ssq + (size_t)t * nparts, nparts);
   return 1.0f / sqrtf(s / (float)P + eps);
 }
 __global__ void lm_rowscale_kernel(const float* ssq, int nparts, int T, int P, float eps,
@@ -1337,21 +1352,53 @@ __global__ __launch_bounds__(256) void lm_combine_kernel(const OT* O, const floa
   if (tid < k) {
     const int p = pair_row[(size_t)t * k + tid];
     const int e = ids[(size_t)t * k + tid];
-    float s = 0.0f;
-    for (int i = 0; i < nparts; ++i) s += ossq[(size_t)p * nparts + i];
+    const float s = lm_sum_in_order(ossq + (size_t)p * nparts, nparts);
     s_coef[tid] = wts[(size_t)t * k + tid] * (1.0f / sqrtf(s / (float)P + eps)) * (o_up ? o_up[e] : 1.0f);
     s_row[tid] = p;
     s_e[tid] = e;
   }
   __syncthreads();
-  // Eight-column chunks, two per thread (2048 columns apart) at a time, so
-  // that each slot's loads are in flight together; every column still sums
-  // its slots in order.
+  // Eight-column chunks, two per thread (2048 columns apart) at a time;
+  // every column sums its slots in order.
   constexpr int kC = 2;
   for (int c0 = tid * 8; c0 < P; c0 += kC * 2048) {
     lm_f32x4 acc[kC][2];
 #pragma unroll
     for (int q = 0; q < kC; ++q) acc[q][0] = acc[q][1] = lm_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (sizeof(OT) == 2) {
+      // FP16 O: the chunks of eight slots loaded together (slot and column
+      // clamped, so that no load sits behind a branch, and all issued before
+      // the first addition), then added in slot order
+      constexpr int kS = 8;
+      for (int j0 = 0; j0 < k; j0 += kS) {
+        lm_u32x4 hv[kS][kC];
+#pragma unroll
+        for (int jj = 0; jj < kS; ++jj) {
+          const OT* orow = O + (size_t)s_row[min(j0 + jj, k - 1)] * P;
+#pragma unroll
+          for (int q = 0; q < kC; ++q)
+            // each expert-output row is read once: streaming (non-temporal) loads
+            hv[jj][q] = __builtin_nontemporal_load((const lm_u32x4*)(orow + min(c0 + q * 2048, P - 8)));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int jj = 0; jj < kS; ++jj) {
+          if (j0 + jj >= k) break;
+          const float cf = s_coef[j0 + jj];
+#pragma unroll
+          for (int q = 0; q < kC; ++q) {
+            lm_f32x4 o[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              o[i >> 1][2 * (i & 1)] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hv[jj][q][i] & 0xffffu));
+              o[i >> 1][2 * (i & 1) + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hv[jj][q][i] >> 16));
+            }
+            acc[q][0] += cf * o[0];  // gamma is in O
+            acc[q][1] += cf * o[1];
+          }
+        }
+      }
+    } else {
     for (int j = 0; j < k; ++j) {
       const OT* orow = O + (size_t)s_row[j] * P;
       const float* grow = gamma + (size_t)s_e[j] * P;
@@ -1389,6 +1436,7 @@ __global__ __launch_bounds__(256) void lm_combine_kernel(const OT* O, const floa
             acc[q][1] += s_coef[j] * o[q][1];
           }
         }
+    }
     }
 #pragma unroll
     for (int q = 0; q < kC; ++q) {
