@@ -63,46 +63,69 @@ __global__ __launch_bounds__(256) void lm_input_norm_kernel(const Et* r, int H, 
       }
     }
   };
+  // Four chunks per thread in flight (indices clamped, all loads issued
+  // before the arithmetic), processed in chunk order.
+  constexpr int kU = 4;
   double s = 0.0;
-  for (int c = threadIdx.x; c < nch; c += 256) {
-    float v[8];
-    elems(c, v);
+  for (int c0 = threadIdx.x; c0 < nch; c0 += 256 * kU) {
+    float v[kU][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s += (double)v[j] * (double)v[j];
+    for (int u = 0; u < kU; ++u) elems(min(c0 + 256 * u, nch - 1), v[u]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (c0 + 256 * u < nch) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += (double)v[u][j] * (double)v[u][j];
+      }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
   const double inv = 1.0 / sqrt((((red[0] + red[1]) + red[2]) + red[3]) / H + (double)eps);
-  for (int c = threadIdx.x; c < nch; c += 256) {
-    float v[8];
-    elems(c, v);
-    const float4 g0 = ((const float4*)gamma)[2 * c], g1 = ((const float4*)gamma)[2 * c + 1];
-    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    float o[8];
+  for (int c0 = threadIdx.x; c0 < nch; c0 += 256 * kU) {
+    float vv[kU][8];
+    float4 gg[kU][2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = (float)((double)v[j] * inv * (double)g[j]);
-    if (xn) {
-      float4* dst = (float4*)(xn + (size_t)blockIdx.x * H) + 2 * c;
-      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+    for (int u = 0; u < kU; ++u) {
+      const int c = min(c0 + 256 * u, nch - 1);
+      elems(c, vv[u]);
+      gg[u][0] = ((const float4*)gamma)[2 * c];
+      gg[u][1] = ((const float4*)gamma)[2 * c + 1];
     }
-    if (xs) {
-      lm_u32x4 p[3];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint16_t a1, a2, a3, b1, b2, b3;
-        lm_split3(o[2 * j], a1, a2, a3);
-        lm_split3(o[2 * j + 1], b1, b2, b3);
-        p[0][j] = (uint32_t)a1 | ((uint32_t)b1 << 16);
-        p[1][j] = (uint32_t)a2 | ((uint32_t)b2 << 16);
-        p[2][j] = (uint32_t)a3 | ((uint32_t)b3 << 16);
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + 256 * u;
+      if (c >= nch) break;
+      const float* v = vv[u];
+      const float g[8] = {gg[u][0].x, gg[u][0].y, gg[u][0].z, gg[u][0].w,
+                          gg[u][1].x, gg[u][1].y, gg[u][1].z, gg[u][1].w};
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = (float)((double)v[j] * inv * (double)g[j]);
+      if (xn) {
+        float4* dst = (float4*)(xn + (size_t)blockIdx.x * H) + 2 * c;
+        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
       }
-      lm_u32x4* dst = (lm_u32x4*)(xs + (size_t)blockIdx.x * 3 * H);
-      dst[c] = p[0];
-      dst[nch + c] = p[1];
-      dst[2 * nch + c] = p[2];
+      if (xs) {
+        lm_u32x4 p[3];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint16_t a1, a2, a3, b1, b2, b3;
+          lm_split3(o[2 * j], a1, a2, a3);
+          lm_split3(o[2 * j + 1], b1, b2, b3);
+          p[0][j] = (uint32_t)a1 | ((uint32_t)b1 << 16);
+          p[1][j] = (uint32_t)a2 | ((uint32_t)b2 << 16);
+          p[2][j] = (uint32_t)a3 | ((uint32_t)b3 << 16);
+        }
+        lm_u32x4* dst = (lm_u32x4*)(xs + (size_t)blockIdx.x * 3 * H);
+        dst[c] = p[0];
+        dst[nch + c] = p[1];
+        dst[2 * nch + c] = p[2];
+      }
     }
   }
 }
