@@ -140,12 +140,23 @@ def _scale(spec: LayerSpec, name: str) -> float:
 
 @lru_cache(maxsize=1)
 def knot_tables() -> tuple[np.ndarray, np.ndarray]:
-    """Piecewise-linear inverse normal CDF: 65536 equal-probability segments."""
+    """Piecewise-linear inverse normal CDF, 2 x 65536 entries (see synth.hip):
+    [s] for the interior segments s = 1 .. 65534 between the quantiles s/2^16
+    and (s+1)/2^16, [65536 + t] for the lower tail's sub-segments between the
+    quantiles t/2^32 and (t+1)/2^32, the first starting at 2^-33 (ndtri(0) is
+    -inf). Entries 0 and 65535 are unused (the end segments use the tail
+    table)."""
     from scipy.special import ndtri
 
-    q = ndtri((np.arange(65537, dtype=np.float64) + 0.5) / 65537.0)
-    knots = q[:-1].astype(np.float32)
-    slopes = (q[1:] - q[:-1]).astype(np.float32)
+    qi = ndtri(np.arange(65537, dtype=np.float64) / 65536.0)  # -inf, ..., +inf
+    qt = ndtri(np.arange(65537, dtype=np.float64) / 2.0 ** 32)
+    qt[0] = ndtri(2.0 ** -33)
+    knots = np.zeros(131072, dtype=np.float32)
+    slopes = np.zeros(131072, dtype=np.float32)
+    knots[1:65535] = qi[1:65535]
+    slopes[1:65535] = qi[2:65536] - qi[1:65535]
+    knots[65536:] = qt[:-1]
+    slopes[65536:] = qt[1:] - qt[:-1]
     return np.ascontiguousarray(knots), np.ascontiguousarray(slopes)
 
 

@@ -8,11 +8,18 @@
 //              the ones Vigna publishes for splitmix64).
 //   z        = a standard normal variate by inverse-CDF table lookup: the top
 //              16 bits pick one of 65536 equal-probability segments of a
-//              piecewise-linear inverse normal CDF, the next 16 bits place the
-//              sample inside that segment. The knot table is computed on the
-//              host from scipy's ndtri and passed in, so host and device read
-//              the same floats and use only exactly-rounded operations
-//              (fmaf, one multiply, integer rounding), which makes both sides
+//              piecewise-linear inverse normal CDF (segment s spans the
+//              quantiles s/2^16 to (s+1)/2^16), the next 16 bits place the
+//              sample inside that segment. The two end segments (the normal's
+//              tails beyond 4.17 sigma) are split again by the remaining 32
+//              bits: 16 pick one of 65536 equal-probability sub-segments of
+//              the lower tail (sub-segment t spans the quantiles t/2^32 to
+//              (t+1)/2^32; the first starts at 2^-33, so |z| <= 6.36), 16
+//              place the sample inside it, and the upper end segment takes the
+//              mirror image. The knot tables are computed on the host from
+//              scipy's ndtri and passed in, so host and device read the same
+//              floats and use only exactly-rounded operations (fmaf, one
+//              multiply, integer rounding), which makes both sides
 //              bit-identical.
 //   value    = z * scale               (weights, x)
 //            = 1 + 0.1 * z             (RMSNorm gammas)
@@ -52,10 +59,16 @@ SYN_HD uint64_t syn_bits(uint64_t key, uint64_t i) {
   return syn_mix(key + (i + 1) * 0x9E3779B97F4A7C15ULL);
 }
 
+// knots / slopes: 2 x 65536 entries, the interior segments at [s] (s = 1 ..
+// 65534) and the lower tail's sub-segments at [65536 + t].
 SYN_HD float syn_normal(const float* knots, const float* slopes, uint64_t bits) {
-  uint32_t seg = (uint32_t)(bits >> 48);
-  uint32_t frac = (uint32_t)(bits >> 32) & 0xFFFFu;
-  return fmaf(slopes[seg], (float)frac * (1.0f / 65536.0f), knots[seg]);
+  const uint32_t seg = (uint32_t)(bits >> 48);
+  const uint32_t frac = (uint32_t)(bits >> 32) & 0xFFFFu;
+  if (seg != 0u && seg != 0xFFFFu) return fmaf(slopes[seg], (float)frac * (1.0f / 65536.0f), knots[seg]);
+  const uint32_t t = 65536u + ((uint32_t)(bits >> 16) & 0xFFFFu);
+  const uint32_t tfrac = (uint32_t)bits & 0xFFFFu;
+  const float z = fmaf(slopes[t], (float)tfrac * (1.0f / 65536.0f), knots[t]);
+  return seg == 0u ? z : -z;
 }
 
 SYN_HD float syn_value(const float* knots, const float* slopes, uint64_t key, uint64_t i,

@@ -62,6 +62,26 @@ def test_generator_distributions():
     assert abs(x.std() - 1) < 0.02
 
 
+def test_generator_tails():
+    """The normal variate reaches into the tails: 16.8M draws land beyond
+    4.5 sigma about 2 * Q(4.5) * n = 114 times (Poisson), beyond 4.17 sigma
+    (the two end segments, probability 2^-15) about 512 times; a table that
+    stopped at the end segments' inner knots would give none beyond 4.5."""
+    from scipy.special import ndtr
+
+    s = synth.CONFIGS["decode"].with_(E=1, P=4096, I=4096, expert_format="f32")
+    w = synth.host(s, "w_gate").astype(np.float64).ravel()
+    z = w / float(np.float32(1.0 / np.sqrt(s.P)))
+    n = z.size
+    for thr in (4.17, 4.5, 5.0):
+        expect = 2 * ndtr(-thr) * n
+        got = int((np.abs(z) > thr).sum())
+        assert abs(got - expect) < 5 * np.sqrt(expect) + 1, (thr, got, expect)
+    assert np.abs(z).max() <= 6.37
+    # symmetric tails
+    assert abs(int((z > 4.17).sum()) - int((z < -4.17).sum())) < 5 * np.sqrt(256) + 1
+
+
 def test_bf16_tensors_are_rne_of_the_fp32_draw():
     s = synth.CONFIGS["decode"].with_(E=3, I=64, P=96, H=160)
     f = synth.host(s.with_(expert_format="f32"), "w_up")
